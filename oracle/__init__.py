@@ -1,0 +1,180 @@
+"""ctypes binding of the CPU oracle (oracle/oracle.cpp).
+
+TEST INFRASTRUCTURE ONLY: the tests, the package smoke check and the
+benchmark's CPU-baseline leg use this; the product path never imports it.
+
+The oracle is plain C++17 built with g++ -O2 (no fast-math) and OpenMP over
+token rows.  ``build()`` compiles it into oracle/liboracle.so.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.cpp")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.run(["g++", "-std=c++17", "-O2", "-fopenmp", "-fPIC", "-shared",
+                        _SRC, "-o", tmp], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i64 = ctypes.c_int64
+        L.oracle_set_threads.argtypes = [ctypes.c_int]
+        L.oracle_set_threads.restype = ctypes.c_int
+        L.oracle_half_to_double.argtypes = [ctypes.c_uint16]
+        L.oracle_half_to_double.restype = ctypes.c_double
+        L.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+        L.oracle_bf16_to_double.restype = ctypes.c_double
+        L.oracle_dequant_int4.argtypes = [P, P, i64, i64, P]
+        L.oracle_router_logits.argtypes = [P, P, P, i64, i64, i64, P]
+        L.oracle_router_topk.argtypes = [P, i64, i64, i64, ctypes.c_double, P, P, P]
+        L.oracle_permute.argtypes = [P, i64, i64, i64, P, P, P]
+        L.oracle_expert_forward.argtypes = [P] * 6 + [i64, i64, P, P, P]
+        L.oracle_layer.argtypes = [P] * 13 + [i64, P, P, P]
+        _lib = L
+    return _lib
+
+
+class _Shape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("H", ctypes.c_int64), ("E", ctypes.c_int64),
+                ("k", ctypes.c_int64), ("I", ctypes.c_int64), ("SI", ctypes.c_int64),
+                ("route_scale", ctypes.c_double)]
+
+
+def _p(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+def set_threads(n: int) -> int:
+    return lib().oracle_set_threads(int(n))
+
+
+def half_to_double(h: int) -> float:
+    return lib().oracle_half_to_double(int(h))
+
+
+def bf16_to_double(b: int) -> float:
+    return lib().oracle_bf16_to_double(int(b))
+
+
+def dequant(q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """Dense fp64 W[N][K] of one int4 plane (q [N][K/2] u8, s [N][K/32] fp16 bits)."""
+    q = _c(q, np.uint8)
+    s = _c(s, np.uint16)
+    N, K = q.shape[0], q.shape[1] * 2
+    out = np.empty((N, K), dtype=np.float64)
+    lib().oracle_dequant_int4(_p(q), _p(s), N, K, _p(out))
+    return out
+
+
+def router_logits(x: np.ndarray, w_router: np.ndarray, gate_row: Optional[np.ndarray] = None):
+    """fp32 logits [T][E] (or [T][E+1] with the shared gate logit as column E)."""
+    x = _c(x, np.uint16)
+    w_router = _c(w_router, np.float32)
+    gate_row = _c(gate_row, np.float32)
+    T, H = x.shape
+    E = w_router.shape[0]
+    out = np.empty((T, E + (gate_row is not None)), dtype=np.float32)
+    lib().oracle_router_logits(_p(x), _p(w_router), _p(gate_row), T, H, E, _p(out))
+    return out
+
+
+def router_topk(logits: np.ndarray, k: int, route_scale: float = 1.0):
+    """(idx int32 [T][k], w fp32 [T][k], w fp64 [T][k])."""
+    logits = _c(logits, np.float32)
+    T, E = logits.shape
+    idx = np.empty((T, k), dtype=np.int32)
+    w = np.empty((T, k), dtype=np.float32)
+    w64 = np.empty((T, k), dtype=np.float64)
+    lib().oracle_router_topk(_p(logits), T, E, k, float(route_scale), _p(idx), _p(w), _p(w64))
+    return idx, w, w64
+
+
+def permute(idx: np.ndarray, E: int):
+    """(off int32 [E+1], sorted int32 [T*k], row_of int32 [T*k])."""
+    idx = _c(idx, np.int32)
+    T, k = idx.shape
+    off = np.empty(E + 1, dtype=np.int32)
+    srt = np.empty(T * k, dtype=np.int32)
+    row_of = np.empty(T * k, dtype=np.int32)
+    lib().oracle_permute(_p(idx), T, k, E, _p(off), _p(srt), _p(row_of))
+    return off, srt, row_of
+
+
+def expert_forward(gate, up, down, x64: np.ndarray):
+    """One expert on one fp64 row: returns (h fp64 [I], o fp64 [H]).
+
+    gate/up/down are (q, s) pairs of single planes."""
+    (qg, sg), (qu, su), (qd, sd) = [(_c(q, np.uint8), _c(s, np.uint16)) for q, s in (gate, up, down)]
+    I, H = qg.shape[0], qg.shape[1] * 2
+    x64 = _c(x64, np.float64)
+    h = np.empty(I, dtype=np.float64)
+    o = np.empty(H, dtype=np.float64)
+    lib().oracle_expert_forward(_p(qg), _p(sg), _p(qu), _p(su), _p(qd), _p(sd), H, I,
+                                _p(x64), _p(h), _p(o))
+    return h, o
+
+
+def layer(x: np.ndarray, logits: np.ndarray, k: int, planes: Dict[str, tuple],
+          shared: Optional[Dict[str, tuple]] = None, shared_gate: Optional[np.ndarray] = None,
+          rows: Optional[Sequence[int]] = None, route_scale: float = 1.0):
+    """The whole layer on the token rows ``rows`` (default: all).
+
+    planes: {"gate": (q [E][I][H/2], s [E][I][H/32]), "up": ..., "down": (q [E][H][I/2], s)}
+    shared: same keys with single planes, or None.
+    Returns (y fp32 [n][H], idx int32 [n][k], w fp32 [n][k])."""
+    x = _c(x, np.uint16)
+    logits = _c(logits, np.float32)
+    T, H = x.shape
+    E = logits.shape[1]
+    gq, gs = [_c(a, t) for a, t in zip(planes["gate"], (np.uint8, np.uint16))]
+    uq, us = [_c(a, t) for a, t in zip(planes["up"], (np.uint8, np.uint16))]
+    dq, ds = [_c(a, t) for a, t in zip(planes["down"], (np.uint8, np.uint16))]
+    I = gq.shape[1]
+    SI = 0
+    keep = []
+    sq_arr = ss_arr = None
+    if shared is not None:
+        sq = [_c(shared[p][0], np.uint8) for p in ("gate", "up", "down")]
+        ss = [_c(shared[p][1], np.uint16) for p in ("gate", "up", "down")]
+        keep += sq + ss
+        SI = sq[0].shape[0]
+        sq_arr = (ctypes.c_void_p * 3)(*[a.ctypes.data for a in sq])
+        ss_arr = (ctypes.c_void_p * 3)(*[a.ctypes.data for a in ss])
+        keep += [sq_arr, ss_arr]
+        sq_arr = ctypes.cast(sq_arr, ctypes.c_void_p)
+        ss_arr = ctypes.cast(ss_arr, ctypes.c_void_p)
+    shared_gate = _c(shared_gate, np.float32)
+    rows_a = None if rows is None else np.ascontiguousarray(rows, dtype=np.int32)
+    n = T if rows_a is None else len(rows_a)
+    sh = _Shape(T, H, E, k, I, SI, float(route_scale))
+    y = np.empty((n, H), dtype=np.float32)
+    idx = np.empty((n, k), dtype=np.int32)
+    w = np.empty((n, k), dtype=np.float32)
+    lib().oracle_layer(ctypes.byref(sh), _p(x), _p(logits), _p(gq), _p(gs), _p(uq), _p(us),
+                       _p(dq), _p(ds), sq_arr, ss_arr, _p(shared_gate), _p(rows_a), n,
+                       _p(y), _p(idx), _p(w))
+    return y, idx, w

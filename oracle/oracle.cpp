@@ -1,0 +1,287 @@
+// CPU oracle for the fused int4 Mixture-of-Experts layer.
+//
+// TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+// call this file: only the tests, the package's smoke check and the
+// benchmark's CPU-baseline leg use it.  It shares no source with the HIP
+// library: no headers, helpers or tables in common.
+//
+// It is the plain definition of what the layer computes, written as slow,
+// obviously correct loops with fp64 accumulation, outputs rounded to fp32 at
+// the end.  Sources (the web pages this layer is built from):
+//   [colibri]  colibri PR #418, "Vulkan backend: expert tier + dense + MLA
+//              attention on any Vulkan 1.2 GPU": the Correctness section
+//              (int4 offset-binary nibble-8, CPU byte layout) and the later
+//              grouped-scale revision (one scale per gs inputs, fmt=4).
+//   [dasllama] daScript PR #3988, "dasLLAMA vulkan: a MoE that fits the card
+//              serves on the whole-model resident driver": the commit notes on
+//              the routed block (router GEMM, per-row top-k renormalised and
+//              scaled, bucket schedule in slot order, combine), on the shared
+//              expert (one region over every row, sigmoid gate logit as one
+//              more router row) and on the combine folded into add+rms (the
+//              FFN row summed as gated shared row first, then the slots in
+//              order).
+//   [vllmcpp]  vllm.cpp PR #481, "gate(#378): the first DEVICE run of the
+//              warp MoE router": the ungated softmax router with top-k, k
+//              passes of mask-and-reseed over the logit row.
+// Where the pages leave a step open, the reading taken is stated at the
+// function.
+//
+// Parity status: every function here is pinned by the CPU tests
+// (tests/test_oracle_*.py) against brute force, closed forms and invariants.
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+namespace {
+
+// IEEE-754 binary16 -> double, from the format's definition (1 sign bit, 5
+// exponent bits with bias 15, 10 fraction bits; exponent 0 = subnormal).
+double half_to_double(uint16_t h) {
+  const int sign = (h >> 15) & 1;
+  const int ex = (h >> 10) & 0x1f;
+  const int frac = h & 0x3ff;
+  double v;
+  if (ex == 0)
+    v = std::ldexp((double)frac, -24);  // 0.frac * 2^-14
+  else if (ex == 31)
+    v = frac ? NAN : INFINITY;
+  else
+    v = std::ldexp(1024.0 + frac, ex - 25);  // 1.frac * 2^(ex-15)
+  return sign ? -v : v;
+}
+
+// bf16 is the top half of an IEEE binary32.
+double bf16_to_double(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+// Offset-binary int4 with grouped scales ([colibri] Correctness: each nibble
+// stands for nibble minus eight, stored in the host's byte layout; grouped-scale
+// revision: one scale covers gs consecutive inputs, gs a multiple of 8).
+// Reading of the byte layout: element kk of a row sits in byte kk/2, the low
+// nibble holding the even element.  Scales run along the input (K) axis,
+// gs = 32.
+inline double weight(const uint8_t* q, const uint16_t* s, int64_t K, int64_t n, int64_t kk) {
+  const uint8_t byte = q[n * (K / 2) + kk / 2];
+  const int nib = (kk & 1) ? (byte >> 4) : (byte & 0xf);
+  return (double)(nib - 8) * half_to_double(s[n * (K / 32) + kk / 32]);
+}
+
+double sigmoid(double z) { return 1.0 / (1.0 + std::exp(-z)); }
+
+// One expert's SwiGLU MLP in fp64: g = Wg.x, u = Wu.x, h = silu(g)*u,
+// o = Wd.h ([colibri] Summary: the fused expert computes gate and up, the SiLU
+// product, then down; silu(z) = z*sigmoid(z) applied to the gate row).
+void expert_forward(const uint8_t* qg, const uint16_t* sg, const uint8_t* qu,
+                    const uint16_t* su, const uint8_t* qd, const uint16_t* sd,
+                    int64_t H, int64_t I, const double* x, double* h, double* o) {
+  for (int64_t n = 0; n < I; ++n) {
+    double g = 0.0, u = 0.0;
+    for (int64_t kk = 0; kk < H; ++kk) {
+      g += weight(qg, sg, H, n, kk) * x[kk];
+      u += weight(qu, su, H, n, kk) * x[kk];
+    }
+    h[n] = g * sigmoid(g) * u;
+  }
+  for (int64_t n = 0; n < H; ++n) {
+    double acc = 0.0;
+    for (int64_t kk = 0; kk < I; ++kk) acc += weight(qd, sd, I, n, kk) * h[kk];
+    o[n] = acc;
+  }
+}
+
+// Selection for one row of logits: experts ranked by logit, descending, the
+// lower expert index winning a tie; the first k in rank order.  This is the
+// k-pass mask-and-reseed selection of [vllmcpp] (each pass takes the arg-max
+// of what is left).  Reading: the rank key is the logit itself (softmax is
+// monotone, so ranking probabilities gives the same order up to rounding
+// ties); IEEE comparison, so -0.0 and +0.0 tie.
+void select_row(const float* L, int64_t E, int64_t k, int32_t* idx) {
+  std::vector<char> taken(E, 0);
+  for (int64_t j = 0; j < k; ++j) {
+    int64_t best = -1;
+    for (int64_t e = 0; e < E; ++e) {
+      if (taken[e]) continue;
+      if (best < 0 || L[e] > L[best]) best = e;  // strict: the lower index keeps a tie
+    }
+    taken[best] = 1;
+    idx[j] = (int32_t)best;
+  }
+}
+
+// Renormalised softmax weights over the selection: softmax over all E
+// experts, restricted to the picks and renormalised to sum to one, times the
+// routed scale ([dasllama] routed-block commit: the per-row top-k is checked
+// against the CPU selection renormalised and then scaled; [vllmcpp]: the
+// softmax router without expert groups).  The full
+// softmax's denominator cancels in the renormalisation, so this is
+//   w_j = scale * exp(L_j - L_0) / sum_{j'<k} exp(L_j' - L_0),
+// with L_0 the top logit.  Computed in fp64.
+void weights_row(const float* L, const int32_t* idx, int64_t k, double scale, double* w) {
+  const double l0 = (double)L[idx[0]];
+  double den = 0.0;
+  for (int64_t j = 0; j < k; ++j) den += std::exp((double)L[idx[j]] - l0);
+  for (int64_t j = 0; j < k; ++j) w[j] = scale * std::exp((double)L[idx[j]] - l0) / den;
+}
+
+}  // namespace
+
+extern "C" {
+
+// Threads used by oracle_layer's loop over token rows (0 = leave as is);
+// returns the count now in effect.
+int oracle_set_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+  return omp_get_max_threads();
+#else
+  (void)n;
+  return 1;
+#endif
+}
+
+double oracle_half_to_double(uint16_t h) { return half_to_double(h); }
+double oracle_bf16_to_double(uint16_t b) { return bf16_to_double(b); }
+
+// W[n][kk] = (nibble - 8) * scale, exact in fp64 (and in fp32: an fp16 scale
+// times an integer in [-8, 7] needs at most 15 significant bits).
+void oracle_dequant_int4(const uint8_t* q, const uint16_t* s, int64_t N, int64_t K, double* out) {
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t kk = 0; kk < K; ++kk) out[n * K + kk] = weight(q, s, K, n, kk);
+}
+
+// Router logits L[t][e] = sum_h x[t][h] * Wr[e][h] ([dasllama] routed-block
+// commit: the router GEMM over the FFN-normed rows against the f32 router
+// plane).  fp64 accumulation, rounded to fp32.  When gate_row is non-null the
+// shared expert's gate logit a[t] = x[t].g is written as column E (the
+// [dasllama] shared-expert decode commit computes that logit as an extra
+// router row placed after the expert logits); out is then [T][E+1].
+void oracle_router_logits(const uint16_t* x, const float* wr, const float* gate_row,
+                          int64_t T, int64_t H, int64_t E, float* out) {
+  const int64_t ld = E + (gate_row ? 1 : 0);
+  for (int64_t t = 0; t < T; ++t) {
+    for (int64_t e = 0; e < ld; ++e) {
+      const float* row = (e < E) ? wr + e * H : gate_row;
+      double acc = 0.0;
+      for (int64_t h = 0; h < H; ++h) acc += bf16_to_double(x[t * H + h]) * (double)row[h];
+      out[t * ld + e] = (float)acc;
+    }
+  }
+}
+
+// Softmax -> top-k -> renormalise for every token row.  idx [T][k]
+// position-major in rank order, w [T][k] rounded to fp32; w64 (nullable)
+// receives the unrounded fp64 weights.
+void oracle_router_topk(const float* logits, int64_t T, int64_t E, int64_t k, double route_scale,
+                        int32_t* idx, float* w, double* w64) {
+  std::vector<double> wr(k);
+  for (int64_t t = 0; t < T; ++t) {
+    select_row(logits + t * E, E, k, idx + t * k);
+    weights_row(logits + t * E, idx + t * k, k, route_scale, wr.data());
+    for (int64_t j = 0; j < k; ++j) {
+      w[t * k + j] = (float)wr[j];
+      if (w64) w64[t * k + j] = wr[j];
+    }
+  }
+}
+
+// Token-to-expert permutation ([dasllama] routed-block commit: a per-expert
+// count, an exclusive scan placing the buckets, the slot map in slot order).
+// Slot s = t*k + j.  off[E+1] is the exclusive scan of the counts; within a
+// bucket the slots appear in ascending slot order; row_of[s] is the row of
+// slot s in the sorted order, so sorted[row_of[s]] == s.
+void oracle_permute(const int32_t* idx, int64_t T, int64_t k, int64_t E, int32_t* off,
+                    int32_t* sorted, int32_t* row_of) {
+  const int64_t S = T * k;
+  std::vector<int64_t> cnt(E, 0);
+  for (int64_t s = 0; s < S; ++s) cnt[idx[s]]++;
+  off[0] = 0;
+  for (int64_t e = 0; e < E; ++e) off[e + 1] = off[e] + (int32_t)cnt[e];
+  std::vector<int64_t> cur(off, off + E);
+  for (int64_t s = 0; s < S; ++s) {
+    const int64_t r = cur[idx[s]]++;
+    sorted[r] = (int32_t)s;
+    row_of[s] = (int32_t)r;
+  }
+}
+
+// One expert MLP on one activation row (fp64 in/out), for the tests.
+void oracle_expert_forward(const uint8_t* qg, const uint16_t* sg, const uint8_t* qu,
+                           const uint16_t* su, const uint8_t* qd, const uint16_t* sd,
+                           int64_t H, int64_t I, const double* x, double* h, double* o) {
+  std::vector<double> hh(I);
+  expert_forward(qg, sg, qu, su, qd, sd, H, I, x, h ? h : hh.data(), o);
+}
+
+struct oracle_shape {
+  int64_t T, H, E, k, I, SI;
+  double route_scale;
+};
+
+// The whole layer for the token rows listed in `rows` (all T rows when rows is
+// null; nrows = number of rows evaluated).  Steps, in order:
+//   selection + weights from the given logits [T][E];
+//   each selected expert's SwiGLU MLP on the token's activation row;
+//   combine y[t] = [sigma(a_t) * shared(x_t)] + sum_j w_j * o_j, summed in
+//   that order - the gated shared row first, then the slots in rank order
+//   ([dasllama] combine-fold commit) - in fp64, rounded to fp32.
+// The shared expert ([dasllama] shared-expert commits) is present when
+// shared_q[0] is non-null; its gate logit is a_t = x_t . shared_gate in fp64;
+// a null shared_gate means an ungated shared expert, added at weight one.
+// Planes are stacked [E][N][K/2] / [E][N][K/32] (gate, up: N=I, K=H; down:
+// N=H, K=I); shared planes are single [N][K/2] / [N][K/32] with I -> SI.
+// y is [nrows][H]; idx_out [nrows][k] and w_out [nrows][k] are nullable.
+void oracle_layer(const oracle_shape* sh, const uint16_t* x, const float* logits,
+                  const uint8_t* gq, const uint16_t* gs, const uint8_t* uq, const uint16_t* us,
+                  const uint8_t* dq, const uint16_t* ds, const uint8_t* const* shared_q,
+                  const uint16_t* const* shared_s, const float* shared_gate, const int32_t* rows,
+                  int64_t nrows, float* y, int32_t* idx_out, float* w_out) {
+  const int64_t H = sh->H, E = sh->E, k = sh->k, I = sh->I, SI = sh->SI;
+  const bool has_shared = shared_q && shared_q[0];
+  const int64_t gate_plane = I * (H / 2), gate_scales = I * (H / 32);
+  const int64_t down_plane = H * (I / 2), down_scales = H * (I / 32);
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < nrows; ++r) {
+    const int64_t t = rows ? rows[r] : r;
+    std::vector<double> xd(H), o(H), acc(H, 0.0), hbuf(std::max(I, SI));
+    for (int64_t h = 0; h < H; ++h) xd[h] = bf16_to_double(x[t * H + h]);
+    std::vector<int32_t> idx(k);
+    std::vector<double> w(k);
+    select_row(logits + t * E, E, k, idx.data());
+    weights_row(logits + t * E, idx.data(), k, sh->route_scale, w.data());
+    if (has_shared) {
+      double gw = 1.0;
+      if (shared_gate) {
+        double a = 0.0;
+        for (int64_t h = 0; h < H; ++h) a += xd[h] * (double)shared_gate[h];
+        gw = sigmoid(a);
+      }
+      expert_forward(shared_q[0], shared_s[0], shared_q[1], shared_s[1], shared_q[2],
+                     shared_s[2], H, SI, xd.data(), hbuf.data(), o.data());
+      for (int64_t h = 0; h < H; ++h) acc[h] += gw * o[h];
+    }
+    for (int64_t j = 0; j < k; ++j) {
+      const int64_t e = idx[j];
+      expert_forward(gq + e * gate_plane, gs + e * gate_scales, uq + e * gate_plane,
+                     us + e * gate_scales, dq + e * down_plane, ds + e * down_scales, H, I,
+                     xd.data(), hbuf.data(), o.data());
+      for (int64_t h = 0; h < H; ++h) acc[h] += w[j] * o[h];
+    }
+    for (int64_t h = 0; h < H; ++h) y[r * H + h] = (float)acc[h];
+    for (int64_t j = 0; j < k; ++j) {
+      if (idx_out) idx_out[r * k + j] = idx[j];
+      if (w_out) w_out[r * k + j] = (float)w[j];
+    }
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,70 @@
+"""Mutation controls for the oracle's pins.
+
+Each case plants one plausible mistake in a copy of oracle/oracle.cpp (built
+into a temporary directory, on the CPU) and checks that at least one of the
+named pins in test_oracle_pins.py turns red against the mutant.  This shows
+the pins can see the mistakes they are meant to catch.
+"""
+import importlib.util
+import os
+import shutil
+
+import pytest
+
+import test_oracle_pins as pins
+
+ORACLE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
+
+MUTATIONS = {
+    "nibble_order_swapped": (
+        "(kk & 1) ? (byte >> 4) : (byte & 0xf)", "(kk & 1) ? (byte & 0xf) : (byte >> 4)",
+        ["test_dequant_golden"]),
+    "scale_on_wrong_axis": (
+        "s[n * (K / 32) + kk / 32]", "s[(kk / 32) * 0 + n * (K / 32) + (n % (K / 32))]",
+        ["test_dequant_golden"]),
+    "offset_seven": ("(double)(nib - 8)", "(double)(nib - 7)", ["test_dequant_golden"]),
+    "tie_goes_to_higher_index": ("L[e] > L[best]", "L[e] >= L[best]",
+                                 ["test_topk_brute_force_with_ties"]),
+    "denominator_drops_last_pick": (
+        "for (int64_t j = 0; j < k; ++j) den +=", "for (int64_t j = 0; j + 1 < k; ++j) den +=",
+        ["test_weights_sum_and_ratio"]),
+    "unstable_bucket_order": (
+        "std::vector<int64_t> cur(off, off + E);\n  for (int64_t s = 0; s < S; ++s) {",
+        "std::vector<int64_t> cur(off, off + E);\n  for (int64_t s = S - 1; s >= 0; --s) {",
+        ["test_permute_matches_stable_sort"]),
+    "silu_dropped": ("h[n] = g * sigmoid(g) * u;", "h[n] = g * u;",
+                     ["test_expert_closed_form_uniform_planes"]),
+    "down_reads_gate_row_count": (
+        "acc += weight(qd, sd, I, n, kk) * h[kk];", "acc += weight(qd, sd, I, n, kk) * h[0];",
+        ["test_expert_down_plane_orientation"]),
+    "shared_gate_ignored": ("gw = sigmoid(a);", "gw = 1.0;", ["test_layer_shared_expert_gate"]),
+    "combine_uses_first_weight": ("acc[h] += w[j] * o[h];", "acc[h] += w[0] * o[h];",
+                                  ["test_layer_equals_dense_masked_mixture"]),
+}
+
+
+def _load_mutant(tmp_path, name, old, new):
+    d = tmp_path / name
+    shutil.copytree(ORACLE_DIR, d, ignore=shutil.ignore_patterns("*.so", "__pycache__", "*.tmp*"))
+    src = (d / "oracle.cpp").read_text()
+    assert old in src, "mutation anchor not found: %s" % name
+    (d / "oracle.cpp").write_text(src.replace(old, new, 1))
+    spec = importlib.util.spec_from_file_location("oracle_mut_" + name, d / "__init__.py")
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    mod.build(force=True)
+    mod.lib()
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_mutation(tmp_path, name):
+    old, new, tests = MUTATIONS[name]
+    mut = _load_mutant(tmp_path, name, old, new)
+    caught = []
+    for t in tests:
+        try:
+            getattr(pins, t)(mut)
+        except AssertionError:
+            caught.append(t)
+    assert caught, "no pin caught mutation %s" % name

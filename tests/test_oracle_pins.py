@@ -1,0 +1,390 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each check ties an oracle function to something the source pages or the
+mathematics fix: hand-derived golden fixtures (tests/golden/), brute force on
+tiny inputs, closed forms, library routines on special cases, and invariants
+(the sparse layer equals a dense masked mixture over all experts; k = E is the
+dense softmax mixture; identical experts make routing irrelevant).  The checks
+are chosen so that a plausible slip in the oracle - swapped nibbles, a scale
+indexed along the wrong axis, a dropped offset, a transposed plane, a wrong
+tie-break, a missing term in the combine - fails at least one of them.
+"""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+
+import moe_synth as S
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------- formats --
+
+def test_fp16_golden(orc):
+    for line in open(os.path.join(GOLDEN, "fp16_values.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        hx, val = line.split()
+        got = orc.half_to_double(int(hx, 16))
+        assert got == float(val), (hx, got, val)
+        assert math.copysign(1.0, got) == math.copysign(1.0, float(val))
+
+
+def test_fp16_all_patterns_match_numpy(orc):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([orc.half_to_double(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+def test_bf16_decode(orc):
+    rng = np.random.default_rng(1)
+    bits = rng.integers(0, 65536, 4096).astype(np.uint16)
+    bits = bits[(bits & 0x7F80) != 0x7F80]  # finite
+    ref = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    got = np.array([orc.bf16_to_double(int(b)) for b in bits])
+    assert np.array_equal(got, ref)
+    assert orc.bf16_to_double(0x3F80) == 1.0
+    assert orc.bf16_to_double(0xC040) == -3.0
+
+
+# ----------------------------------------------------------------- dequant --
+
+def _read_dequant_golden():
+    rows = {}
+    for line in open(os.path.join(GOLDEN, "dequant_k64.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        tok = line.split()
+        r = int(tok[1])
+        if tok[2] == "bytes":
+            si = tok.index("scales")
+            byts = []
+            for b in tok[3:si]:
+                if "*" in b:
+                    v, n = b.split("*")
+                    byts += [int(v, 16)] * int(n)
+                else:
+                    byts.append(int(b, 16))
+            rows.setdefault(r, {})["q"] = np.array(byts, dtype=np.uint8)
+            rows[r]["s"] = np.array([int(v, 16) for v in tok[si + 1:]], dtype=np.uint16)
+        else:
+            rows.setdefault(r, {})["expect"] = np.array([float(v) for v in tok[3:]])
+    n = len(rows)
+    q = np.stack([rows[r]["q"] for r in range(n)])
+    s = np.stack([rows[r]["s"] for r in range(n)])
+    e = np.stack([rows[r]["expect"] for r in range(n)])
+    return q, s, e
+
+
+def test_dequant_golden(orc):
+    q, s, expect = _read_dequant_golden()
+    assert q.shape == (3, 32) and expect.shape == (3, 64)
+    assert np.array_equal(orc.dequant(q, s), expect)
+
+
+def test_dequant_special_cases(orc):
+    rng = np.random.default_rng(2)
+    N, K = 5, 96
+    s = S.draw_plane(N, K, rng)[1]
+    sv = s.view(np.float16).astype(np.float64)
+    # nibble 8 everywhere -> exactly zero
+    assert np.all(orc.dequant(np.full((N, K // 2), 0x88, np.uint8), s) == 0.0)
+    # nibble 9 everywhere -> the group's scale, broadcast along K
+    assert np.array_equal(orc.dequant(np.full((N, K // 2), 0x99, np.uint8), s),
+                          np.repeat(sv, 32, axis=1))
+    # nibble 0 -> -8 * scale (the extreme of the offset-binary range)
+    assert np.array_equal(orc.dequant(np.zeros((N, K // 2), np.uint8), s),
+                          -8.0 * np.repeat(sv, 32, axis=1))
+
+
+def test_dequant_values_fit_fp32(orc):
+    # (nibble - 8) * fp16 scale needs at most 15 significant bits: exact in fp32.
+    q, s = S.draw_plane(64, 256, np.random.default_rng(3))
+    w = orc.dequant(q, s)
+    assert np.array_equal(w.astype(np.float32).astype(np.float64), w)
+
+
+# ---------------------------------------------------------- router: top-k --
+
+def _brute_topk(L, k):
+    return sorted(range(len(L)), key=lambda e: (-L[e], e))[:k]
+
+
+def test_topk_brute_force_with_ties(orc):
+    rng = np.random.default_rng(4)
+    for E in range(1, 13):
+        for k in range(1, E + 1):
+            L = rng.integers(0, 3, size=(16, E)).astype(np.float32)  # many exact ties
+            idx, _, _ = orc.router_topk(L, k)
+            for t in range(L.shape[0]):
+                assert list(idx[t]) == _brute_topk(list(L[t]), k), (E, k, L[t])
+
+
+def test_topk_brute_force_random(orc):
+    rng = np.random.default_rng(5)
+    for E, k in [(8, 2), (60, 4), (128, 8), (256, 8), (256, 64), (7, 7)]:
+        L = rng.standard_normal((20, E)).astype(np.float32)
+        idx, _, _ = orc.router_topk(L, k)
+        for t in range(20):
+            assert list(idx[t]) == _brute_topk(list(L[t]), k)
+
+
+def test_topk_all_equal_and_signed_zero(orc):
+    L = np.zeros((2, 10), np.float32)
+    L[1, ::2] = -0.0  # -0.0 == +0.0 under IEEE comparison: still a tie
+    idx, w, _ = orc.router_topk(L, 4)
+    assert idx.tolist() == [[0, 1, 2, 3], [0, 1, 2, 3]]
+    assert np.all(w == np.float32(0.25))
+
+
+# -------------------------------------------------------- router: weights --
+
+def test_weights_k1_is_one(orc):
+    L = np.random.default_rng(6).standard_normal((50, 32)).astype(np.float32) * 5
+    _, w, _ = orc.router_topk(L, 1)
+    assert np.all(w == 1.0)
+
+
+def test_weights_sum_and_ratio(orc):
+    rng = np.random.default_rng(7)
+    for E, k in [(8, 2), (128, 8), (256, 8), (60, 4)]:
+        L = (rng.standard_normal((40, E)) * 3).astype(np.float32)
+        idx, w, w64 = orc.router_topk(L, k)
+        assert np.all(np.abs(w64.sum(1) - 1.0) < 1e-15)
+        assert np.all(np.abs(w.astype(np.float64).sum(1) - 1.0) <= k * 2.0 ** -24)
+        # w_i / w_j = exp(L_i - L_j): the softmax ratio identity
+        Ls = np.take_along_axis(L.astype(np.float64), idx, 1)
+        ratio = w64[:, 1:] / w64[:, :1]
+        assert np.allclose(ratio, np.exp(Ls[:, 1:] - Ls[:, :1]), rtol=1e-13, atol=0)
+        # weights are non-increasing in rank order
+        assert np.all(np.diff(w64, axis=1) <= 0)
+
+
+def test_weights_k_equals_E_is_softmax(orc):
+    rng = np.random.default_rng(8)
+    for E in [2, 8, 60, 256]:
+        L = (rng.standard_normal((10, E)) * 2).astype(np.float32)
+        idx, w, w64 = orc.router_topk(L, E)
+        ref = scipy.special.softmax(L.astype(np.float64), axis=1)
+        ref_sel = np.take_along_axis(ref, idx, 1)
+        assert np.allclose(w64, ref_sel, rtol=1e-13, atol=1e-300)
+
+
+def test_route_scale(orc):
+    L = np.random.default_rng(9).standard_normal((5, 16)).astype(np.float32)
+    _, _, w1 = orc.router_topk(L, 4, 1.0)
+    _, _, w2 = orc.router_topk(L, 4, 2.5)
+    assert np.allclose(w2, 2.5 * w1, rtol=1e-15)
+
+
+# ------------------------------------------------------------ router logits --
+
+def test_router_logits_exact_integers(orc):
+    rng = np.random.default_rng(10)
+    T, H, E = 6, 256, 9
+    xv = rng.integers(-3, 4, (T, H)).astype(np.float32)
+    wv = rng.integers(-5, 6, (E, H)).astype(np.float32)
+    g = rng.integers(-2, 3, (H,)).astype(np.float32)
+    x = S.f32_to_bf16_bits(xv)  # small integers are exact in bf16
+    out = orc.router_logits(x, wv, g)
+    exact = np.concatenate([xv.astype(np.int64) @ wv.astype(np.int64).T,
+                            (xv.astype(np.int64) @ g.astype(np.int64))[:, None]], 1)
+    assert np.array_equal(out, exact.astype(np.float32))
+
+
+def test_router_logits_vs_matmul(orc):
+    wl = S.WORKLOADS["decode_batch"]
+    x = S.draw_x(wl)[:8]
+    wr = S.draw_router(wl)
+    out = orc.router_logits(x, wr)
+    ref = S.bf16_bits_to_f32(x).astype(np.float64) @ wr.astype(np.float64).T
+    # both are fp64 sums of the same exact products, then one rounding to fp32
+    assert np.max(np.abs(out - ref) / np.maximum(np.abs(ref), 1e-30)) <= 2.0 ** -24 * 1.0001
+
+
+# ------------------------------------------------------------- permutation --
+
+def test_permute_matches_stable_sort(orc):
+    rng = np.random.default_rng(11)
+    for T, k, E in [(4, 2, 8), (32, 8, 128), (512, 4, 60), (3, 3, 256), (100, 1, 5)]:
+        idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+        off, srt, row_of = orc.permute(idx, E)
+        flat = idx.ravel()
+        assert np.array_equal(off, np.concatenate([[0], np.cumsum(np.bincount(flat, minlength=E))]))
+        assert np.array_equal(srt, np.argsort(flat, kind="stable"))
+        assert np.array_equal(srt[row_of], np.arange(T * k))
+        for e in range(E):
+            assert np.all(flat[srt[off[e]:off[e + 1]]] == e)
+
+
+# -------------------------------------------------------------- expert MLP --
+
+def _tiny_planes(rng, H, I):
+    return [S.draw_plane(*shape, rng) for shape in ((I, H), (I, H), (H, I))]
+
+
+def test_expert_onehot_picks_one_column(orc):
+    """x = one-hot at position c -> g = Wg[:, c], u = Wu[:, c] (pins the K axis)."""
+    rng = np.random.default_rng(12)
+    H, I = 64, 32
+    gate, up, down = _tiny_planes(rng, H, I)
+    Wg, Wu, Wd = orc.dequant(*gate), orc.dequant(*up), orc.dequant(*down)
+    for c in [0, 1, 31, 32, 63]:
+        x = np.zeros(H)
+        x[c] = 1.0
+        h, o = orc.expert_forward(gate, up, down, x)
+        g, u = Wg[:, c], Wu[:, c]
+        # silu(g) * u written as the closed form g / (1 + e^-g) * u
+        assert np.allclose(h, [gi / (1.0 + math.exp(-gi)) * ui for gi, ui in zip(g, u)],
+                           rtol=1e-14, atol=0)
+
+
+def test_expert_down_plane_orientation(orc):
+    """Only gate row r0 is non-zero -> h is one-hot at r0 -> o = Wd[:, r0] * h[r0]."""
+    rng = np.random.default_rng(13)
+    H, I = 64, 64
+    gate, up, down = _tiny_planes(rng, H, I)
+    gq = np.full_like(gate[0], 0x88)  # all zero weights
+    r0 = 37
+    gq[r0] = gate[0][r0]
+    gate = (gq, gate[1])
+    x = S.bf16_bits_to_f32(S.f32_to_bf16_bits(rng.standard_normal(H).astype(np.float32))).astype(np.float64)
+    h, o = orc.expert_forward(gate, up, down, x)
+    assert np.count_nonzero(h) == 1 and h[r0] != 0.0
+    Wd = orc.dequant(*down)
+    assert np.allclose(o, Wd[:, r0] * h[r0], rtol=1e-14, atol=0)
+
+
+def test_expert_closed_form_uniform_planes(orc):
+    """Uniform planes give a hand-computable MLP.
+
+    gate nibble 9, scale 0.125 -> Wg = 0.125; up nibble 10, scale 0.25 -> Wu = 0.5;
+    down nibble 7, scale 0.5 -> Wd = -0.5.  With x = 0.5 everywhere (H = 32):
+    g = 0.125*16 = 2, u = 0.5*16 = 8, h = silu(2)*8, o = -0.5 * I * h."""
+    H, I = 32, 64
+    f16 = lambda v: np.full(1, v, np.float16).view(np.uint16)[0]
+    gate = (np.full((I, H // 2), 0x99, np.uint8), np.full((I, 1), f16(0.125), np.uint16))
+    up = (np.full((I, H // 2), 0xAA, np.uint8), np.full((I, 1), f16(0.25), np.uint16))
+    down = (np.full((H, I // 2), 0x77, np.uint8), np.full((H, 2), f16(0.5), np.uint16))
+    h, o = orc.expert_forward(gate, up, down, np.full(H, 0.5))
+    hv = 2.0 / (1.0 + math.exp(-2.0)) * 8.0
+    assert np.allclose(h, hv, rtol=1e-15)
+    assert np.allclose(o, -0.5 * I * hv, rtol=1e-14)
+
+
+def test_expert_matches_library_matmul(orc):
+    rng = np.random.default_rng(14)
+    H, I = 256, 96
+    gate, up, down = _tiny_planes(rng, H, I)
+    x = rng.standard_normal(H)
+    h, o = orc.expert_forward(gate, up, down, x)
+    Wg, Wu, Wd = orc.dequant(*gate), orc.dequant(*up), orc.dequant(*down)
+    g, u = Wg @ x, Wu @ x
+    href = g * scipy.special.expit(g) * u
+    assert np.allclose(h, href, rtol=1e-10, atol=1e-12)
+    assert np.allclose(o, Wd @ href, rtol=1e-9, atol=1e-10)
+
+
+# ------------------------------------------------------------------- layer --
+
+def _tiny_layer_inputs(seed=15, T=6, H=64, E=6, k=2, I=32, SI=0):
+    rng = np.random.default_rng(seed)
+    x = S.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    planes = {}
+    for p, (N, K) in zip(S.PLANES, ((I, H), (I, H), (H, I))):
+        qs = [S.draw_plane(N, K, rng) for _ in range(E)]
+        planes[p] = (np.stack([a for a, _ in qs]), np.stack([b for _, b in qs]))
+    shared = None
+    if SI:
+        shared = {p: S.draw_plane(N, K, rng)
+                  for p, (N, K) in zip(S.PLANES, ((SI, H), (SI, H), (H, SI)))}
+    return x, logits, planes, shared
+
+
+def _expert_outputs(orc, x, planes, E):
+    """o[t][e] for every token and every expert (dense evaluation)."""
+    T, H = x.shape
+    xd = S.bf16_bits_to_f32(x).astype(np.float64)
+    out = np.zeros((T, E, H))
+    for e in range(E):
+        pl = [(planes[p][0][e], planes[p][1][e]) for p in S.PLANES]
+        for t in range(T):
+            out[t, e] = orc.expert_forward(*pl, xd[t])[1]
+    return out
+
+
+def test_layer_equals_dense_masked_mixture(orc):
+    x, logits, planes, _ = _tiny_layer_inputs()
+    T, E, k = x.shape[0], logits.shape[1], 2
+    y, idx, w = orc.layer(x, logits, k, planes)
+    dense = _expert_outputs(orc, x, planes, E)
+    # mask m_e and renormalised softmax weights over the selected experts
+    p = scipy.special.softmax(logits.astype(np.float64), axis=1)
+    for t in range(T):
+        m = np.zeros(E)
+        m[_brute_topk(list(logits[t]), k)] = 1.0
+        wt = m * p[t] / np.sum(m * p[t])
+        ref = (wt[:, None] * dense[t]).sum(0)
+        assert np.allclose(y[t], ref, rtol=1e-6, atol=1e-6 * np.max(np.abs(ref)))
+        assert sorted(idx[t]) == sorted(np.nonzero(m)[0])
+
+
+def test_layer_k_equals_E_is_dense_softmax_mixture(orc):
+    x, logits, planes, _ = _tiny_layer_inputs(seed=16, E=5)
+    E = 5
+    y, _, _ = orc.layer(x, logits, E, planes)
+    dense = _expert_outputs(orc, x, planes, E)
+    p = scipy.special.softmax(logits.astype(np.float64), axis=1)
+    ref = np.einsum("te,teh->th", p, dense)
+    assert np.allclose(y, ref, rtol=1e-6, atol=1e-6 * np.abs(ref).max())
+
+
+def test_layer_identical_experts_ignore_routing(orc):
+    x, logits, planes, _ = _tiny_layer_inputs(seed=17)
+    E = logits.shape[1]
+    same = {p: (np.repeat(planes[p][0][:1], E, 0), np.repeat(planes[p][1][:1], E, 0))
+            for p in S.PLANES}
+    y, _, _ = orc.layer(x, logits, 3, same)
+    one = _expert_outputs(orc, x, {p: (same[p][0][:1], same[p][1][:1]) for p in S.PLANES}, 1)[:, 0]
+    assert np.allclose(y, one, rtol=1e-6, atol=1e-6 * np.abs(one).max())
+
+
+def test_layer_rows_subset_matches_full(orc):
+    x, logits, planes, shared = _tiny_layer_inputs(seed=18, SI=48)
+    g = np.random.default_rng(1).normal(0, 0.1, x.shape[1]).astype(np.float32)
+    yf, idf, wf = orc.layer(x, logits, 2, planes, shared, g)
+    rows = [4, 0, 2]
+    ys, ids, ws = orc.layer(x, logits, 2, planes, shared, g, rows=rows)
+    assert np.array_equal(ys, yf[rows]) and np.array_equal(ids, idf[rows]) and np.array_equal(ws, wf[rows])
+
+
+def test_layer_shared_expert_gate(orc):
+    """g = 0 -> sigma = 1/2 exactly; zero routed experts isolate the shared term,
+    which must equal the same planes run as a routed expert at weight one."""
+    T, H, E, I, SI = 4, 64, 4, 32, 96
+    x, logits, planes, shared = _tiny_layer_inputs(seed=19, T=T, H=H, E=E, I=I, SI=SI)
+    zero = {p: (np.full_like(planes[p][0], 0x88), planes[p][1]) for p in S.PLANES}
+    y_half, _, _ = orc.layer(x, logits, 2, zero, shared, np.zeros(H, np.float32))
+    y_one, _, _ = orc.layer(x, logits, 2, zero, shared, None)  # ungated: weight one
+    as_routed = {p: (shared[p][0][None], shared[p][1][None]) for p in S.PLANES}
+    y_ref, _, _ = orc.layer(x, np.zeros((T, 1), np.float32), 1, as_routed)
+    assert np.array_equal(y_one, y_ref)
+    assert np.allclose(y_half, 0.5 * y_ref.astype(np.float64), rtol=1e-6, atol=0)
+    # with a real gate vector the shared term scales by sigma(x . g)
+    gvec = np.random.default_rng(2).normal(0, 0.05, H).astype(np.float32)
+    y_g, _, _ = orc.layer(x, logits, 2, zero, shared, gvec)
+    a = S.bf16_bits_to_f32(x).astype(np.float64) @ gvec.astype(np.float64)
+    assert np.allclose(y_g, scipy.special.expit(a)[:, None] * y_ref, rtol=1e-6, atol=1e-7)
+    # and the shared term adds to the routed mixture (no term dropped)
+    y_full, _, _ = orc.layer(x, logits, 2, planes, shared, gvec)
+    y_routed, _, _ = orc.layer(x, logits, 2, planes)
+    assert np.allclose(y_full, y_routed.astype(np.float64) + y_g, rtol=1e-5,
+                       atol=1e-5 * np.abs(y_full).max())
