@@ -1,0 +1,179 @@
+/*
+ * moe.h - C ABI of libmoe, a fused int4 Mixture-of-Experts layer for AMD
+ * Instinct MI355X (gfx950, CDNA4).
+ *
+ * The layer (sources: the colibri Vulkan-backend PR #418, the dasLLAMA vulkan
+ * PR #3988 and the vllm.cpp warp-router PR #481):
+ *   1. router logits L = x . W_router^T (fp32), unless the caller gives L;
+ *   2. softmax over the E experts -> top-k (the lower index wins a tie) ->
+ *      renormalise over the k picks, times route_scale;
+ *   3. token-to-expert permutation: per-expert buckets of slots, slot s = t*k+j;
+ *   4. per expert, the SwiGLU MLP on its bucket's rows:
+ *        h = silu(Wg x) * (Wu x),   o = Wd h,
+ *      with int4 weights: nibble n stands for (n - 8), times an fp16 scale per
+ *      32 consecutive inputs;
+ *   5. combine y[t] = sigma(x_t . g) * shared(x_t) + sum_j w[t][j] * o[t][j]
+ *      (the shared expert optional; without a gate vector it adds at weight 1).
+ *
+ * Conventions for every entry point
+ *   - All data pointers are DEVICE pointers (hipMalloc'd or torch CUDA tensors)
+ *     unless stated otherwise; `shape` structs are HOST pointers.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     returns without a host synchronisation.  The library allocates nothing:
+ *     the caller owns every buffer, scratch space included, and must keep it
+ *     alive until the stream has run the work.
+ *   - Arguments are checked on the host before anything is enqueued; a failed
+ *     check returns an error code and enqueues nothing.  Faults inside kernels
+ *     surface at the caller's next synchronisation, as for any HIP launch.
+ *   - Entry points are thread-safe for distinct streams; two calls that share
+ *     an output or workspace buffer must be ordered by the caller.
+ *   - Logits must be finite; behaviour on NaN/Inf logits is unspecified.
+ *
+ * int4 planes (moe_q4): q = packed nibbles, uint8 [E][N][K/2]: element kk of
+ * row n sits in byte kk/2, low nibble = even kk (the host byte layout, loaded
+ * with a plain copy, no repacking).  s = fp16 scale bits, uint16 [E][N][K/32],
+ * one scale per 32 consecutive inputs along K.  Gate and up planes have N = I,
+ * K = H; down planes have N = H, K = I.  q and s must be 16-byte aligned.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as hipStream_t. */
+typedef struct ihipStream_t *moe_stream_t;
+
+enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* null/misaligned pointer, inconsistent sizes  */
+  MOE_ERR_UNSUPPORTED = 2, /* outside the shapes the kernels serve         */
+  MOE_ERR_WORKSPACE = 3,   /* ws_bytes smaller than moe_workspace_bytes()  */
+  MOE_ERR_HIP = 4,         /* a HIP launch reported an error               */
+};
+
+/* Expert MLP path.  AUTO picks the streaming GEMV when the expected rows per
+ * expert are few (decode) and the grouped MFMA GEMM otherwise (prefill). */
+enum moe_path { MOE_PATH_AUTO = 0, MOE_PATH_GEMV = 1, MOE_PATH_GEMM = 2 };
+
+/* One int4 plane set: q [E][N][K/2] packed nibbles, s [E][N][K/32] fp16 bits. */
+typedef struct {
+  const uint8_t *q;
+  const uint16_t *s;
+} moe_q4;
+
+/* Layer shape.  T tokens, H hidden, E experts, k picks per token, I expert
+ * intermediate, SI shared-expert intermediate (0 = none), group must be 32,
+ * route_scale multiplies the renormalised weights, path is a moe_path.
+ * Served: 1 <= k <= min(E, 64), E <= 256, H % 64 == 0, I % 64 == 0,
+ * SI % 64 == 0, T >= 1, T*k < 2^31. */
+typedef struct {
+  int32_t T, H, E, k, I, SI;
+  int32_t group;
+  float route_scale;
+  int32_t path;
+} moe_shape;
+
+/*
+ * Softmax -> top-k -> renormalise, one 64-lane wave per token (the warp-per-
+ * token router of vllm.cpp PR #481, re-shaped for wave64: expert e lives in
+ * lane e % 64, register e / 64).
+ *   logits : fp32 [T][E], row-major.
+ *   idx    : int32 [T][k] out, expert ids in rank order (largest logit first,
+ *            the lower index first among equal logits).
+ *   w      : fp32 [T][k] out, w[t][j] = route_scale * exp(L_j - L_0) /
+ *            sum_j' exp(L_j' - L_0), evaluated in fp64 and rounded once.
+ * Errors: INVALID_ARG (null pointer, T < 1, k < 1, k > E);
+ *         UNSUPPORTED (E > 256, k > 64).
+ */
+int moe_router_topk(const float *logits, int32_t T, int32_t E, int32_t k, float route_scale,
+                    int32_t *idx, float *w, moe_stream_t stream);
+
+/*
+ * Token-to-expert permutation (the bucket schedule of the dasLLAMA PR's routed
+ * block: per-expert counts, exclusive scan, slots placed in slot order), one
+ * workgroup with an LDS histogram, LDS scan and stable scatter.
+ *   idx    : int32 [T][k] expert picks; slot s = t*k + j.
+ *   off    : int32 [E+1] out, exclusive scan of the per-expert slot counts.
+ *   sorted : int32 [T*k] out, slot ids grouped by expert, ascending within a
+ *            bucket (sorted[off[e] .. off[e+1]) are expert e's slots).
+ *   row_of : int32 [T*k] out, inverse map: sorted[row_of[s]] == s.
+ * A pick outside [0, E) is dropped: it is counted nowhere, sorted holds only
+ * valid slots (off[E] = their number) and row_of[s] = -1 for it.
+ * Errors: INVALID_ARG (null pointer, T < 1, k < 1); UNSUPPORTED (E > 256).
+ */
+int moe_permute(const int32_t *idx, int32_t T, int32_t k, int32_t E, int32_t *off,
+                int32_t *sorted, int32_t *row_of, moe_stream_t stream);
+
+/*
+ * The routed experts' SwiGLU MLPs with the weighted combine fused into the
+ * down projection's epilogue:
+ *   y[t][:] = sum over slots s = t*k+j in the buckets of w[s] * MLP_e(x[t]).
+ *   shape  : host pointer; T, H, E, k, I, group, path are used (SI ignored).
+ *   x      : bf16 bits [T][H].
+ *   off, sorted : as written by moe_permute.
+ *   w      : fp32 [T][k] combine weights (from moe_router_topk).
+ *   gate, up, down : int4 planes (see above).
+ *   y      : fp32 [T][H] out, OVERWRITTEN (not accumulated).
+ *   ws     : device scratch of at least moe_workspace_bytes(shape) bytes,
+ *            256-byte aligned; its contents on entry are ignored.
+ * The order in which a token's k terms are added to y is not fixed (device
+ * atomics); the result differs from an ordered sum only by fp32 rounding.
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.
+ */
+int moe_expert_mlp(const moe_shape *shape, const uint16_t *x, const int32_t *off,
+                   const int32_t *sorted, const float *w, moe_q4 gate, moe_q4 up, moe_q4 down,
+                   float *y, void *ws, size_t ws_bytes, moe_stream_t stream);
+
+/*
+ * The whole layer: router (logits given, or x . W_router^T), top-k, weights,
+ * permutation, expert MLPs, combine, and the optional sigmoid-gated shared
+ * expert (the dasLLAMA PR's shared expert: one bucket over every token with an
+ * identity map, weighted by sigmoid of one more router row).
+ *   logits     : fp32 [T][E], or NULL when w_router is given (exactly one of
+ *                the two must be non-NULL).
+ *   w_router   : fp32 [E][H], or NULL.
+ *   shared     : host array of 3 moe_q4 {gate, up, down} with E = 1 and
+ *                I = shape->SI, or NULL (then shape->SI must be 0).
+ *   shared_gate: fp32 [H] gate vector g, or NULL for an ungated shared expert
+ *                (added at weight one).  Ignored without a shared expert.
+ *   y          : fp32 [T][H] out, overwritten.
+ *   idx_out    : int32 [T][k] out, or NULL.
+ *   w_out      : fp32 [T][k] out, or NULL.
+ *   logits_out : fp32 [T][E] out (the logits used), or NULL.
+ *   ws         : as for moe_expert_mlp.
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.
+ */
+int moe_layer(const moe_shape *shape, const uint16_t *x, const float *logits,
+              const float *w_router, moe_q4 gate, moe_q4 up, moe_q4 down, const moe_q4 *shared,
+              const float *shared_gate, float *y, int32_t *idx_out, float *w_out,
+              float *logits_out, void *ws, size_t ws_bytes, moe_stream_t stream);
+
+/* Scratch bytes moe_layer and moe_expert_mlp need for this shape (0 if the
+ * shape is not served).  Host only; enqueues nothing. */
+size_t moe_workspace_bytes(const moe_shape *shape);
+
+/* Static description of a status code. */
+const char *moe_status_string(int status);
+
+/*
+ * Test hook: runs the kernels' own device int4 decode on one plane and writes
+ * the decoded weights as fp32 [N][K] (device pointer `out`).
+ *   mode 0: the exact value (nibble - 8) * scale, via the decode the GEMV
+ *           kernels use (bf16 offset encoding of the nibble);
+ *   mode 1: the fp16 operand the MFMA kernels feed, widened to fp32 (the
+ *           exact value rounded to fp16, nearest-even).
+ * Errors: INVALID_ARG (null, N < 1, K % 32 != 0, misaligned, bad mode).
+ */
+int moe_debug_dequant_int4(moe_q4 plane, int32_t N, int32_t K, int32_t mode, float *out,
+                           moe_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

@@ -1,0 +1,75 @@
+// Host-side launchers of the libmoe kernels.  Every launcher enqueues on the
+// given stream and returns the launch status; argument checking happens in
+// moe_api.cpp before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Schedule words written by the permutation kernels, read by the expert MLPs:
+//   [0] number of experts with at least one slot (touched experts)
+//   [1] number of MFMA row tiles
+//   [2 .. 2+E)             touched experts, ascending
+//   [tiles_offset(E) ..)   tiles, 4 ints each: {expert, first row, rows, 0}
+constexpr int kGemmTileRows = 128;  // rows (slots) per MFMA tile
+__host__ __device__ constexpr int sched_tiles_offset(int E) { return ((2 + E + 3) / 4) * 4; }
+__host__ __device__ constexpr int64_t sched_max_tiles(int64_t slots, int E) {
+  return (slots + kGemmTileRows - 1) / kGemmTileRows + E;
+}
+__host__ __device__ constexpr int64_t sched_words(int64_t slots, int E) {
+  return sched_tiles_offset(E) + 4 * sched_max_tiles(slots, E);
+}
+
+// Bucket description shared by the expert-MLP kernels.  Routed buckets come
+// from the permutation (off, sorted, sched); the shared expert is one bucket
+// over every token with the identity map (shared_T > 0).
+struct Buckets {
+  const int32_t* off;     // [E+1]
+  const int32_t* sorted;  // [slots]
+  const int32_t* sched;   // schedule words (see above)
+  int32_t k;              // picks per token (slot s belongs to token s / k)
+  int32_t shared_T;       // > 0: identity bucket over shared_T tokens
+  int32_t max_rows;       // upper bound of rows in one bucket (T: a token picks an expert once)
+  int32_t E;              // experts (locates the tile list in sched)
+};
+
+hipError_t launch_router_logits(const uint16_t* x, const float* wr, const float* gate_row, int T,
+                                int H, int E, float* out, int ld, hipStream_t st);
+
+hipError_t launch_topk(const float* logits, int ld, int T, int E, int k, float route_scale,
+                       int32_t* idx, float* w, hipStream_t st);
+
+hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* off,
+                          int32_t* sorted, int32_t* row_of, int32_t* sched, hipStream_t st);
+
+hipError_t launch_schedule_from_offsets(const int32_t* off, int E, int64_t slots, int32_t* sched,
+                                        hipStream_t st);
+
+// Streaming int4 GEMV (decode).  gate/up: h[row][I] = silu(Wg x)*(Wu x) in fp32;
+// down: y[token] += weight * (Wd h[row]).  The gate/up launch also zeroes y.
+hipError_t launch_gemv_gate_up(const Buckets& b, int max_buckets, const uint16_t* x, int H,
+                               int I, const uint8_t* gq, const uint16_t* gs,
+                               const uint8_t* uq, const uint16_t* us, float* h, float* y_zero,
+                               int64_t y_elems, hipStream_t st);
+hipError_t launch_gemv_down(const Buckets& b, int max_buckets, const float* h, int H, int I,
+                            const uint8_t* dq, const uint16_t* ds, const float* w,
+                            const float* gate_logit, int gate_ld, float* y, hipStream_t st);
+bool gemv_supported(int K);
+
+// Grouped MFMA GEMM (prefill), fp16 operands with fp32 accumulation.
+hipError_t launch_convert_x16(const uint16_t* x, int T, int H, uint16_t* x16, float* y_zero,
+                              int64_t y_elems, hipStream_t st);
+hipError_t launch_gemm_gate_up(const Buckets& b, int max_tiles, const uint16_t* x16, int H,
+                               int I, const uint8_t* gq, const uint16_t* gs,
+                               const uint8_t* uq, const uint16_t* us, uint16_t* h16,
+                               hipStream_t st);
+hipError_t launch_gemm_down(const Buckets& b, int max_tiles, const uint16_t* h16, int H, int I,
+                            const uint8_t* dq, const uint16_t* ds, const float* w,
+                            const float* gate_logit, int gate_ld, float* y, hipStream_t st);
+
+hipError_t launch_debug_dequant(const uint8_t* q, const uint16_t* s, int N, int K, int mode,
+                                float* out, hipStream_t st);
+
+}  // namespace moe

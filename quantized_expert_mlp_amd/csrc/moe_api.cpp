@@ -1,0 +1,306 @@
+// libmoe C ABI: argument checks, workspace layout and the launch sequence.
+// The declarations and their contracts are in include/moe.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+
+namespace {
+
+using moe::Buckets;
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Shape checks shared by every entry point that takes a moe_shape.
+int check_shape(const moe_shape* sh) {
+  if (!sh) return MOE_ERR_INVALID_ARG;
+  if (sh->T < 1 || sh->H < 1 || sh->E < 1 || sh->k < 1 || sh->I < 1 || sh->SI < 0)
+    return MOE_ERR_INVALID_ARG;
+  if (sh->k > sh->E) return MOE_ERR_INVALID_ARG;
+  if (sh->group != 32) return MOE_ERR_UNSUPPORTED;
+  if (sh->path < MOE_PATH_AUTO || sh->path > MOE_PATH_GEMM) return MOE_ERR_INVALID_ARG;
+  if (sh->E > 256 || sh->k > 64) return MOE_ERR_UNSUPPORTED;
+  if (sh->H % 64 || sh->I % 64 || sh->SI % 64) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)sh->T * sh->k >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)sh->T * sh->H >= (int64_t)1 << 40) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+bool gemv_ok(const moe_shape* sh) {
+  return moe::gemv_supported(sh->H) && moe::gemv_supported(sh->I) &&
+         (sh->SI == 0 || moe::gemv_supported(sh->SI));
+}
+
+// The grouped MFMA GEMM is taken when an expert's bucket is expected to hold
+// at least 8 rows (slots / E >= 8), or when the GEMV cannot serve the shape.
+int pick_gemm(const moe_shape* sh, bool* gemm) {
+  const int64_t slots = (int64_t)sh->T * sh->k;
+  switch (sh->path) {
+    case MOE_PATH_GEMV:
+      if (!gemv_ok(sh)) return MOE_ERR_UNSUPPORTED;
+      *gemm = false;
+      return MOE_OK;
+    case MOE_PATH_GEMM:
+      *gemm = true;
+      return MOE_OK;
+    default:
+      *gemm = !gemv_ok(sh) || slots >= 8 * (int64_t)sh->E;
+      return MOE_OK;
+  }
+}
+
+struct Layout {
+  size_t logits, gate, idx, w, off, sorted, row_of, sched, x16, h, hs, total;
+  int ld;  // logits row stride in the workspace (E, or E+1 with a gate column)
+};
+
+Layout make_layout(const moe_shape* sh, bool gemm) {
+  const int64_t T = sh->T, E = sh->E, slots = T * sh->k;
+  Layout L{};
+  size_t p = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = p;
+    p += align_up(bytes ? bytes : 1);
+    return at;
+  };
+  L.ld = (int)E + 1;
+  L.logits = take(sizeof(float) * T * (E + 1));
+  L.gate = take(sizeof(float) * T);
+  L.idx = take(sizeof(int32_t) * slots);
+  L.w = take(sizeof(float) * slots);
+  L.off = take(sizeof(int32_t) * (E + 2));
+  L.sorted = take(sizeof(int32_t) * slots);
+  L.row_of = take(sizeof(int32_t) * slots);
+  L.sched = take(sizeof(int32_t) * moe::sched_words(slots, (int)E));
+  const size_t act = gemm ? 2 : 4;  // fp16 activations on the MFMA path, fp32 on the GEMV path
+  L.x16 = take(gemm ? sizeof(uint16_t) * T * sh->H : 0);
+  L.h = take(act * slots * sh->I);
+  L.hs = take(act * T * sh->SI);
+  L.total = p;
+  return L;
+}
+
+template <typename P>
+P* at(void* ws, size_t off) {
+  return reinterpret_cast<P*>(static_cast<char*>(ws) + off);
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+bool plane_ok(const moe_q4& p) {
+  return p.q && p.s && aligned(p.q, 16) && aligned(p.s, 16);
+}
+
+// Expert MLPs over the routed buckets (and the shared expert when given).
+int run_mlp(const moe_shape* sh, bool gemm, const Layout& L, void* ws, const uint16_t* x,
+            const int32_t* off, const int32_t* sorted, const float* w, moe_q4 gate, moe_q4 up,
+            moe_q4 down, const moe_q4* shared, const float* gate_logit, int gate_ld, float* y,
+            hipStream_t st) {
+  const int T = sh->T, H = sh->H, I = sh->I, E = sh->E, k = sh->k;
+  const int64_t slots = (int64_t)T * k;
+  const int32_t* sched = at<int32_t>(ws, L.sched);
+  Buckets routed{off, sorted, sched, k, 0, T, E};
+  Buckets sharedb{nullptr, nullptr, nullptr, 1, T, T, 1};
+  const int64_t y_elems = (int64_t)T * H;
+  hipError_t err;
+  if (!gemm) {
+    float* h = at<float>(ws, L.h);
+    float* hs = at<float>(ws, L.hs);
+    const int max_buckets = (int)(slots < E ? slots : E);
+    err = moe::launch_gemv_gate_up(routed, max_buckets, x, H, I, gate.q, gate.s, up.q, up.s, h, y,
+                                   y_elems, st);
+    if (err != hipSuccess) return MOE_ERR_HIP;
+    if (shared) {
+      err = moe::launch_gemv_gate_up(sharedb, 1, x, H, sh->SI, shared[0].q, shared[0].s,
+                                     shared[1].q, shared[1].s, hs, nullptr, 0, st);
+      if (err != hipSuccess) return MOE_ERR_HIP;
+    }
+    err = moe::launch_gemv_down(routed, max_buckets, h, H, I, down.q, down.s, w, nullptr, 0, y, st);
+    if (err != hipSuccess) return MOE_ERR_HIP;
+    if (shared) {
+      err = moe::launch_gemv_down(sharedb, 1, hs, H, sh->SI, shared[2].q, shared[2].s, nullptr,
+                                  gate_logit, gate_ld, y, st);
+      if (err != hipSuccess) return MOE_ERR_HIP;
+    }
+    return MOE_OK;
+  }
+  uint16_t* x16 = at<uint16_t>(ws, L.x16);
+  uint16_t* h16 = at<uint16_t>(ws, L.h);
+  uint16_t* hs16 = at<uint16_t>(ws, L.hs);
+  const int max_tiles = (int)moe::sched_max_tiles(slots, E);
+  const int shared_tiles = (T + moe::kGemmTileRows - 1) / moe::kGemmTileRows;
+  err = moe::launch_convert_x16(x, T, H, x16, y, y_elems, st);
+  if (err != hipSuccess) return MOE_ERR_HIP;
+  err = moe::launch_gemm_gate_up(routed, max_tiles, x16, H, I, gate.q, gate.s, up.q, up.s, h16, st);
+  if (err != hipSuccess) return MOE_ERR_HIP;
+  if (shared) {
+    err = moe::launch_gemm_gate_up(sharedb, shared_tiles, x16, H, sh->SI, shared[0].q, shared[0].s,
+                                   shared[1].q, shared[1].s, hs16, st);
+    if (err != hipSuccess) return MOE_ERR_HIP;
+  }
+  err = moe::launch_gemm_down(routed, max_tiles, h16, H, I, down.q, down.s, w, nullptr, 0, y, st);
+  if (err != hipSuccess) return MOE_ERR_HIP;
+  if (shared) {
+    err = moe::launch_gemm_down(sharedb, shared_tiles, hs16, H, sh->SI, shared[2].q, shared[2].s,
+                                nullptr, gate_logit, gate_ld, y, st);
+    if (err != hipSuccess) return MOE_ERR_HIP;
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+size_t moe_workspace_bytes(const moe_shape* sh) {
+  if (check_shape(sh) != MOE_OK) return 0;
+  bool gemm = false;
+  if (pick_gemm(sh, &gemm) != MOE_OK) return 0;
+  return make_layout(sh, gemm).total;
+}
+
+int moe_router_topk(const float* logits, int32_t T, int32_t E, int32_t k, float route_scale,
+                    int32_t* idx, float* w, moe_stream_t stream) {
+  if (!logits || !idx || !w || T < 1 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID_ARG;
+  if (!aligned(logits, 4) || !aligned(idx, 4) || !aligned(w, 4)) return MOE_ERR_INVALID_ARG;
+  if (E > 256 || k > 64) return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_topk(logits, E, T, E, k, route_scale, idx, w,
+                                     reinterpret_cast<hipStream_t>(stream)));
+}
+
+int moe_permute(const int32_t* idx, int32_t T, int32_t k, int32_t E, int32_t* off,
+                int32_t* sorted, int32_t* row_of, moe_stream_t stream) {
+  if (!idx || !off || !sorted || !row_of || T < 1 || k < 1 || E < 1) return MOE_ERR_INVALID_ARG;
+  if (!aligned(idx, 4) || !aligned(off, 4) || !aligned(sorted, 4) || !aligned(row_of, 4))
+    return MOE_ERR_INVALID_ARG;
+  if (E > 256) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)T * k >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_permute(idx, T, k, E, off, sorted, row_of, nullptr,
+                                        reinterpret_cast<hipStream_t>(stream)));
+}
+
+int moe_expert_mlp(const moe_shape* sh, const uint16_t* x, const int32_t* off,
+                   const int32_t* sorted, const float* w, moe_q4 gate, moe_q4 up, moe_q4 down,
+                   float* y, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  int rc = check_shape(sh);
+  if (rc != MOE_OK) return rc;
+  if (!x || !off || !sorted || !w || !y || !ws) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(y, 4) || !aligned(w, 4) || !aligned(ws, kAlign))
+    return MOE_ERR_INVALID_ARG;
+  if (!plane_ok(gate) || !plane_ok(up) || !plane_ok(down)) return MOE_ERR_INVALID_ARG;
+  bool gemm = false;
+  rc = pick_gemm(sh, &gemm);
+  if (rc != MOE_OK) return rc;
+  const Layout L = make_layout(sh, gemm);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (moe::launch_schedule_from_offsets(off, sh->E, (int64_t)sh->T * sh->k, at<int32_t>(ws, L.sched),
+                                         st) != hipSuccess)
+    return MOE_ERR_HIP;
+  return run_mlp(sh, gemm, L, ws, x, off, sorted, w, gate, up, down, nullptr, nullptr, 0, y, st);
+}
+
+int moe_layer(const moe_shape* sh, const uint16_t* x, const float* logits,
+              const float* w_router, moe_q4 gate, moe_q4 up, moe_q4 down, const moe_q4* shared,
+              const float* shared_gate, float* y, int32_t* idx_out, float* w_out,
+              float* logits_out, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  int rc = check_shape(sh);
+  if (rc != MOE_OK) return rc;
+  if (!x || !y || !ws) return MOE_ERR_INVALID_ARG;
+  if ((logits == nullptr) == (w_router == nullptr)) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(y, 4) || !aligned(ws, kAlign)) return MOE_ERR_INVALID_ARG;
+  if (logits && !aligned(logits, 4)) return MOE_ERR_INVALID_ARG;
+  if (w_router && !aligned(w_router, 16)) return MOE_ERR_INVALID_ARG;
+  if ((idx_out && !aligned(idx_out, 4)) || (w_out && !aligned(w_out, 4)) ||
+      (logits_out && !aligned(logits_out, 4)))
+    return MOE_ERR_INVALID_ARG;
+  if (!plane_ok(gate) || !plane_ok(up) || !plane_ok(down)) return MOE_ERR_INVALID_ARG;
+  if (shared) {
+    if (sh->SI < 64) return MOE_ERR_INVALID_ARG;
+    for (int i = 0; i < 3; ++i)
+      if (!plane_ok(shared[i])) return MOE_ERR_INVALID_ARG;
+    if (shared_gate && !aligned(shared_gate, 16)) return MOE_ERR_INVALID_ARG;
+  } else if (sh->SI != 0) {
+    return MOE_ERR_INVALID_ARG;
+  }
+  bool gemm = false;
+  rc = pick_gemm(sh, &gemm);
+  if (rc != MOE_OK) return rc;
+  const Layout L = make_layout(sh, gemm);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int T = sh->T, H = sh->H, E = sh->E, k = sh->k;
+  const bool gated = shared && shared_gate;
+
+  // 1. logits (and the shared gate logit as one more router row)
+  const float* Lp = logits;
+  int ldL = E;
+  const float* gate_logit = nullptr;
+  int gate_ld = 1;
+  if (w_router) {
+    float* Lw = at<float>(ws, L.logits);
+    const int ld = gated ? E + 1 : E;
+    if (moe::launch_router_logits(x, w_router, gated ? shared_gate : nullptr, T, H, E, Lw, ld, st) !=
+        hipSuccess)
+      return MOE_ERR_HIP;
+    Lp = Lw;
+    ldL = ld;
+    if (gated) {
+      gate_logit = Lw + E;
+      gate_ld = ld;
+    }
+  } else if (gated) {
+    float* gl = at<float>(ws, L.gate);
+    if (moe::launch_router_logits(x, nullptr, shared_gate, T, H, 0, gl, 1, st) != hipSuccess)
+      return MOE_ERR_HIP;
+    gate_logit = gl;
+    gate_ld = 1;
+  }
+  if (logits_out) {
+    if (hipMemcpy2DAsync(logits_out, sizeof(float) * E, Lp, sizeof(float) * ldL,
+                         sizeof(float) * E, T, hipMemcpyDeviceToDevice, st) != hipSuccess)
+      return MOE_ERR_HIP;
+  }
+
+  // 2. top-k + weights
+  int32_t* idx = idx_out ? idx_out : at<int32_t>(ws, L.idx);
+  float* w = w_out ? w_out : at<float>(ws, L.w);
+  if (moe::launch_topk(Lp, ldL, T, E, k, sh->route_scale, idx, w, st) != hipSuccess)
+    return MOE_ERR_HIP;
+
+  // 3. permutation + schedule
+  int32_t* off = at<int32_t>(ws, L.off);
+  int32_t* sorted = at<int32_t>(ws, L.sorted);
+  if (moe::launch_permute(idx, T, k, E, off, sorted, at<int32_t>(ws, L.row_of),
+                          at<int32_t>(ws, L.sched), st) != hipSuccess)
+    return MOE_ERR_HIP;
+
+  // 4.-5. expert MLPs with the fused combine
+  return run_mlp(sh, gemm, L, ws, x, off, sorted, w, gate, up, down, shared, gate_logit, gate_ld,
+                 y, st);
+}
+
+int moe_debug_dequant_int4(moe_q4 plane, int32_t N, int32_t K, int32_t mode, float* out,
+                           moe_stream_t stream) {
+  if (!plane_ok(plane) || !out || N < 1 || K < 32 || K % 32 || (mode != 0 && mode != 1))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_debug_dequant(plane.q, plane.s, N, K, mode, out,
+                                              reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

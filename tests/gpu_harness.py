@@ -1,0 +1,124 @@
+"""Helpers for the GPU parity tests: device copies of seeded inputs, calls
+through the C ABI (via the package binding), and the comparison bars.
+
+Bars (fixed by the layer's accuracy requirements):
+  * router indices, permutation and int4 decode: bit-exact;
+  * router weights: within 1e-6 relative;
+  * layer output y: per token row, max_h |y - y_ref| <= 2e-3 * max_h |y_ref|.
+"""
+import sys
+
+import numpy as np
+import torch
+
+import moe_synth as S
+import quantized_expert_mlp_amd as moe
+
+Y_TOL = 2e-3
+W_RTOL = 1e-6
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).cuda()
+
+
+def host(t: torch.Tensor, dtype=None) -> np.ndarray:
+    a = t.detach().cpu().numpy()
+    return a.view(dtype) if dtype is not None else a
+
+
+class DeviceLayer:
+    """Device copies of one LayerInputs."""
+
+    def __init__(self, inp: S.LayerInputs):
+        self.inp = inp
+        self.x = dev(inp.x)
+        self.logits = None if inp.logits is None else dev(inp.logits)
+        self.w_router = None if inp.w_router is None else dev(inp.w_router)
+        self.shared_gate = None if inp.shared_gate is None else dev(inp.shared_gate)
+        self.planes = {p: (dev(q), dev(s)) for p, (q, s) in inp.planes.items()}
+        self.shared = None
+        if inp.shared is not None:
+            self.shared = [(dev(inp.shared[p][0]), dev(inp.shared[p][1])) for p in S.PLANES]
+
+
+def run_layer(d: DeviceLayer, logits=None, use_router=False, path=moe.MOE_PATH_AUTO,
+              route_scale=1.0, ws_extra=0):
+    """moe_layer through the C ABI.  logits: host array to feed (given logits),
+    else the inputs' own; use_router: compute logits from w_router."""
+    wl = d.inp.wl
+    T = d.inp.x.shape[0]
+    sh = moe.make_shape(T, wl.H, wl.E, wl.k, wl.I, wl.SI if d.shared else 0,
+                        route_scale=route_scale, path=path)
+    nbytes = moe.moe_workspace_bytes(sh)
+    assert nbytes > 0
+    ws = torch.empty(nbytes + ws_extra, dtype=torch.uint8, device="cuda")
+    ws.fill_(0xFF)  # poison: nothing may depend on the workspace's prior contents
+    y = torch.full((T, wl.H), float("nan"), dtype=torch.float32, device="cuda")
+    idx = torch.full((T, wl.k), -7, dtype=torch.int32, device="cuda")
+    w = torch.full((T, wl.k), float("nan"), dtype=torch.float32, device="cuda")
+    lo = torch.full((T, wl.E), float("nan"), dtype=torch.float32, device="cuda")
+    if use_router:
+        lg, wr = None, d.w_router
+    else:
+        lg = dev(logits.astype(np.float32)) if logits is not None else d.logits
+        wr = None
+    moe.moe_layer(sh, d.x, lg, wr, d.planes["gate"], d.planes["up"], d.planes["down"], d.shared,
+                  d.shared_gate, y, idx, w, lo, ws, nbytes)
+    torch.cuda.synchronize()
+    return host(y), host(idx), host(w), host(lo)
+
+
+def y_errors(y: np.ndarray, y_ref: np.ndarray) -> np.ndarray:
+    """Per-row max|y - y_ref| / max|y_ref|."""
+    num = np.max(np.abs(y.astype(np.float64) - y_ref.astype(np.float64)), axis=1)
+    den = np.maximum(np.max(np.abs(y_ref.astype(np.float64)), axis=1), 1e-30)
+    return num / den
+
+
+def assert_y_close(y, y_ref, what=""):
+    assert np.all(np.isfinite(y)), "%s: non-finite outputs" % what
+    err = y_errors(y, y_ref)
+    worst = float(err.max()) if err.size else 0.0
+    say("  %s: worst row error %.3e of max|y| (bar %.0e)" % (what, worst, Y_TOL))
+    assert worst <= Y_TOL, "%s: row %d error %.3e > %.0e" % (what, int(err.argmax()), worst, Y_TOL)
+    return worst
+
+
+def assert_w_close(w, w_ref, what=""):
+    rel = np.abs(w.astype(np.float64) - w_ref.astype(np.float64)) / np.abs(w_ref.astype(np.float64))
+    worst = float(rel.max())
+    say("  %s: worst router weight rel error %.3e (bar %.0e)" % (what, worst, W_RTOL))
+    assert worst <= W_RTOL, what
+
+
+def logits_bound(x_bits: np.ndarray, w_router: np.ndarray, gate=None) -> np.ndarray:
+    """Forward-error bound of an fp32 dot of length H vs the exact value,
+    (H + 2) * 2^-24 * sum_h |x_h W_eh|, plus the oracle's own rounding."""
+    xa = np.abs(S.bf16_bits_to_f32(x_bits).astype(np.float64))
+    wa = np.abs(w_router.astype(np.float64))
+    H = x_bits.shape[1]
+    return (H + 2) * 2.0 ** -24 * (xa @ wa.T)
+
+
+def valid_topk(idx_row, L_ref_row, bound_row, k):
+    """Is idx_row a top-k of L_ref_row under perturbations within bound_row?"""
+    order = sorted(range(len(L_ref_row)), key=lambda e: (-L_ref_row[e], e))
+    kth = L_ref_row[order[k - 1]]
+    slack = 2 * float(np.max(bound_row)) + 1e-30
+    if len(set(idx_row.tolist())) != k:
+        return False
+    for j, e in enumerate(idx_row):
+        if L_ref_row[e] < kth - slack:
+            return False
+        if j > 0 and L_ref_row[e] > L_ref_row[idx_row[j - 1]] + slack:
+            return False
+    return True

@@ -1,0 +1,133 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before enqueuing
+anything (no HIP call is reached by these cases)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_expert_mlp_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return moe.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    declared = _declared_functions()
+    assert set(declared) == set(moe.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    assert moe.status_string(moe.MOE_OK) == "ok"
+    assert moe.status_string(moe.MOE_ERR_WORKSPACE) == "workspace too small"
+    assert moe.status_string(99) == "unknown status"
+
+
+def _shape(**kw):
+    base = dict(T=4, H=256, E=8, k=2, I=128, SI=0)
+    base.update(kw)
+    return moe.make_shape(**base)
+
+
+def test_workspace_bytes_valid_and_invalid(L):
+    assert moe.moe_workspace_bytes(_shape()) > 0
+    big = moe.moe_workspace_bytes(_shape(T=2048, H=6144, E=256, k=8, I=2048))
+    # fp16 hidden rows for 16384 slots x 2048 plus the fp16 activation copy
+    assert big >= 16384 * 2048 * 2 + 2048 * 6144 * 2
+    for bad in [dict(T=0), dict(k=9), dict(E=300, k=2), dict(k=65, E=128), dict(H=100),
+                dict(I=96), dict(SI=32), dict(group=64)]:
+        assert moe.moe_workspace_bytes(_shape(**bad)) == 0, bad
+    assert moe.moe_workspace_bytes(_shape(path=3)) == 0
+
+
+FAKE = 1 << 20  # a non-null, 256-aligned address; never dereferenced by these cases
+
+
+def test_router_topk_rejects(L):
+    f = L.moe_router_topk
+    assert f(None, 4, 8, 2, 1.0, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(FAKE, 0, 8, 2, 1.0, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(FAKE, 4, 8, 9, 1.0, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(FAKE, 4, 8, 0, 1.0, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(FAKE + 2, 4, 8, 2, 1.0, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(FAKE, 4, 257, 2, 1.0, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert f(FAKE, 4, 256, 65, 1.0, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_permute_rejects(L):
+    f = L.moe_permute
+    assert f(None, 4, 2, 8, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(FAKE, 4, 2, 8, None, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(FAKE, 0, 2, 8, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(FAKE, 4, 2, 257, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+
+
+def _q(ok=True):
+    return moe.moe_q4(FAKE if ok else FAKE + 8, FAKE)
+
+
+def test_layer_rejects(L):
+    sh = _shape()
+    ws_need = moe.moe_workspace_bytes(sh)
+
+    def call(shape=sh, x=FAKE, logits=FAKE, w_router=None, gate=None, shared=None, sg=None,
+             y=FAKE, ws=FAKE, ws_bytes=ws_need):
+        gate = gate or _q()
+        return L.moe_layer(ctypes.byref(shape), x, logits, w_router, gate, _q(), _q(), shared, sg,
+                           y, None, None, None, ws, ws_bytes, None)
+
+    assert call(logits=None) == moe.MOE_ERR_INVALID_ARG            # neither logits nor router
+    assert call(w_router=FAKE) == moe.MOE_ERR_INVALID_ARG          # both
+    assert call(x=None) == moe.MOE_ERR_INVALID_ARG
+    assert call(x=FAKE + 2) == moe.MOE_ERR_INVALID_ARG             # misaligned activations
+    assert call(gate=_q(False)) == moe.MOE_ERR_INVALID_ARG          # misaligned plane
+    assert call(ws=FAKE + 64) == moe.MOE_ERR_INVALID_ARG            # misaligned workspace
+    assert call(ws_bytes=ws_need - 1) == moe.MOE_ERR_WORKSPACE
+    assert call(shape=_shape(SI=64)) == moe.MOE_ERR_INVALID_ARG     # SI without shared planes
+    assert call(shape=_shape(E=512, k=2)) == moe.MOE_ERR_UNSUPPORTED
+    assert call(shape=_shape(H=96)) == moe.MOE_ERR_UNSUPPORTED
+    assert call(shape=_shape(k=0)) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_expert_mlp_rejects(L):
+    sh = _shape()
+    need = moe.moe_workspace_bytes(sh)
+    f = L.moe_expert_mlp
+    args = lambda **kw: [ctypes.byref(kw.get("shape", sh)), kw.get("x", FAKE), FAKE, FAKE, FAKE,
+                         _q(), _q(), _q(), kw.get("y", FAKE), FAKE, kw.get("ws_bytes", need), None]
+    assert f(*args(x=None)) == moe.MOE_ERR_INVALID_ARG
+    assert f(*args(y=None)) == moe.MOE_ERR_INVALID_ARG
+    assert f(*args(ws_bytes=0)) == moe.MOE_ERR_WORKSPACE
+    assert f(*args(shape=_shape(path=moe.MOE_PATH_GEMV, H=16384))) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_debug_dequant_rejects(L):
+    f = L.moe_debug_dequant_int4
+    assert f(_q(), 4, 48, 0, FAKE, None) == moe.MOE_ERR_INVALID_ARG   # K % 32
+    assert f(_q(), 4, 64, 2, FAKE, None) == moe.MOE_ERR_INVALID_ARG   # mode
+    assert f(_q(), 0, 64, 0, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(_q(False), 4, 64, 0, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_product_path_has_no_oracle_dependency():
+    """The product package neither imports nor links the oracle."""
+    pkg = os.path.join(ROOT, "quantized_expert_mlp_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".cpp", ".hip", ".h")):
+                text = open(os.path.join(dirpath, fn)).read()
+                assert "oracle" not in text.replace("oracle-free", ""), fn
