@@ -1,0 +1,287 @@
+#!/usr/bin/env python3
+"""MoE-layer throughput of libmoe on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one moe_layer call through the C ABI: router top-k (logits given)
+or router GEMM + top-k, permutation, gate/up + SiLU*mul, down + weighted
+combine (and the gated shared expert when the workload has one), on one
+batch of synthetic input already resident in HBM.  The default workload is
+the single-token decode layer (T=1, H=6144, E=256, top-8, I=2048, int4 with
+fp16 group-32 scales).  To keep the 256 MB Infinity Cache from serving the
+weights, every expert stays resident and each step routes with a different
+row of a 64-row pool of fresh logits (given-logit workloads), or rotates
+through 4 independent weight sets (router workloads).
+
+Prints one JSON line on stdout: the headline tokens/s, the dominant kernel's
+roofline fraction (its duration measured with HIP events on the launch
+stream through moe_layer_profiled), and the CPU oracle's rate on a bounded
+sample of the same workload.  Details go to stderr.
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import moe_synth as S  # noqa: E402
+
+METRIC = "MoE-layer tokens/s at 1 GPU; decode HBM GB/s %, prefill MFMA % of peak"
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+MFMA_F16_PEAK_TFS = 2500.0  # MI355X dense fp16/bf16 MFMA
+LOGIT_POOL = 64
+WEIGHT_SETS = {"decode_batch": 4, "prefill_shared": 4}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Hip:
+    """hipEvent_t handles through the HIP runtime (torch already loaded it)."""
+
+    def __init__(self):
+        self.L = ctypes.CDLL("libamdhip64.so")
+        self.L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                               ctypes.c_void_p]
+        self.L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self) -> int:
+        e = ctypes.c_void_p()
+        assert self.L.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def ms(self, a: int, b: int) -> float:
+        out = ctypes.c_float()
+        assert self.L.hipEventElapsedTime(ctypes.byref(out), a, b) == 0
+        return out.value
+
+
+def touched_experts(logits: np.ndarray, k: int) -> int:
+    """Distinct experts among the top-k picks of every row (byte accounting)."""
+    picks = np.argpartition(-logits, k - 1, axis=1)[:, :k]
+    return len(np.unique(picks))
+
+
+def stage_work(wl, T, U, gemm):
+    """Algorithmic bytes and flops of the gate/up and down launches of one call.
+
+    Counted: the touched experts' packed nibbles and fp16 scales, activations
+    in, hidden rows out/in, y out.  Not counted: untouched experts."""
+    H, I, slots = wl.H, wl.I, T * wl.k
+    act = 2 if gemm else 4
+    gu_w = U * 2 * (I * H // 2 + I * (H // 32) * 2)
+    dn_w = U * (H * I // 2 + H * (I // 32) * 2)
+    sh_gu = sh_dn = 0
+    if wl.SI:
+        sh_gu = 2 * (wl.SI * H // 2 + wl.SI * (H // 32) * 2) + T * H * 2 + T * wl.SI * act
+        sh_dn = (H * wl.SI // 2 + H * (wl.SI // 32) * 2) + T * wl.SI * act + T * H * 4
+    return {
+        "gate_up": {"bytes": gu_w + T * H * 2 + slots * I * act, "flops": 4.0 * slots * H * I},
+        "down": {"bytes": dn_w + slots * I * act + T * H * 4, "flops": 2.0 * slots * H * I},
+        "shared_gate_up": {"bytes": sh_gu, "flops": 4.0 * T * H * wl.SI},
+        "shared_down": {"bytes": sh_dn, "flops": 2.0 * T * H * wl.SI},
+    }
+
+
+def build_sets(wl, nsets, seed0=0):
+    import torch
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).cuda()
+
+    sets = []
+    for r in range(nsets):
+        inp = S.make_layer_inputs(wl, seed=seed0 + r)
+        d = {
+            "inp": inp,
+            "x": dev(inp.x),
+            "planes": {p: (dev(q), dev(s)) for p, (q, s) in inp.planes.items()},
+            "w_router": None if inp.w_router is None else dev(inp.w_router),
+            "shared": None if inp.shared is None else [
+                (dev(inp.shared[p][0]), dev(inp.shared[p][1])) for p in S.PLANES],
+            "shared_gate": None if inp.shared_gate is None else dev(inp.shared_gate),
+        }
+        sets.append(d)
+        inp.planes = None  # host copies no longer needed
+    return sets
+
+
+def cpu_baseline(wl, seconds_hint: float):
+    """The oracle as it stands, on a bounded sample of the workload's tokens."""
+    import oracle
+    threads = oracle.set_threads(min(16, os.cpu_count() or 1))
+    inp = S.make_layer_inputs(wl, seed=0)
+    if wl.logits == "router":
+        logits = oracle.router_logits(inp.x, inp.w_router)
+    else:
+        logits = inp.logits
+    x = inp.x
+    if wl.T == 1:  # decode: distinct logits rows from the pool, same activation row
+        n = 4 * threads
+        logits = S.draw_logits(S.Workload("pool", wl.wid, n, wl.H, wl.E, wl.k, wl.I, wl.SI,
+                                          wl.logits, ""), seed=1000)
+        x = np.repeat(inp.x, n, axis=0)
+        rows = None
+        sample = "%d decode tokens (distinct logits rows), %d threads" % (n, threads)
+    else:
+        n = {"prefill_skewed": 128, "prefill_shared": 128}.get(wl.name, wl.T)
+        rows = sorted(np.random.default_rng(7).choice(wl.T, n, replace=False).tolist())
+        sample = "%d of %d token rows, %d threads" % (n, wl.T, threads)
+    t0 = time.perf_counter()
+    oracle.layer(x, logits, wl.k, inp.planes, inp.shared, inp.shared_gate, rows=rows)
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": sample, "seconds": round(dt, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--workload", default="decode", choices=list(S.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import quantized_expert_mlp_amd as moe
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    moe.lib()
+    hip = Hip()
+    wl = S.WORKLOADS[args.workload]
+    T = wl.T
+    nsets = WEIGHT_SETS.get(wl.name, 1)
+    log("workload %s: %s; %d weight set(s)" % (wl.name, wl.description, nsets))
+    t0 = time.perf_counter()
+    sets = build_sets(wl, nsets)
+    log("inputs resident in %.1f s" % (time.perf_counter() - t0))
+
+    # per-step inputs: logits pool (given-logit workloads) or weight-set rotation
+    if wl.logits in ("given", "zipf"):
+        pool_np = [S.draw_logits(wl, seed=100 + i) for i in range(LOGIT_POOL)] \
+            if wl.T == 1 else [S.draw_logits(wl, seed=100 + i) for i in range(4)]
+        pool = [torch.from_numpy(p).cuda() for p in pool_np]
+        touched = [touched_experts(p, wl.k) for p in pool_np]
+    else:
+        pool_np, pool = None, None
+        touched = []
+        for s in sets:  # byte accounting only: which experts the router picks
+            L = S.bf16_bits_to_f32(s["inp"].x) @ s["inp"].w_router.T
+            touched.append(touched_experts(L, wl.k))
+    nvar = len(pool) if pool is not None else len(sets)
+
+    sh = moe.make_shape(T, wl.H, wl.E, wl.k, wl.I, wl.SI)
+    gemm = (T * wl.k) >= 8 * wl.E  # the library's AUTO rule (MOE_PATH_AUTO)
+    nbytes = moe.moe_workspace_bytes(sh)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    y = torch.empty((T, wl.H), dtype=torch.float32, device="cuda")
+
+    def call(i, events=None):
+        s = sets[i % len(sets)] if pool is None else sets[0]
+        lg = pool[i % len(pool)] if pool is not None else None
+        wr = s["w_router"] if pool is None else None
+        args_ = (sh, s["x"], lg, wr, s["planes"]["gate"], s["planes"]["up"], s["planes"]["down"],
+                 s["shared"], s["shared_gate"], y, None, None, None, ws, nbytes)
+        if events is None:
+            moe.moe_layer(*args_)
+        else:
+            moe.moe_layer_profiled(*args_, events=events)
+
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly `steps` layer calls
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        call(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    tokens_per_s = T * args.steps / wall
+
+    # ---- per-stage device time (HIP events on the launch stream)
+    ev = [[hip.event() for _ in range(2 * len(moe.STAGES))] for _ in range(args.steps)]
+    for i in range(args.steps):
+        call(i, ev[i])
+    torch.cuda.synchronize()
+    stage_ms = {name: 0.0 for name in moe.STAGES[1:]}
+    for i in range(args.steps):
+        for j in range(1, len(moe.STAGES)):
+            stage_ms[moe.STAGES[j]] += hip.ms(ev[i][2 * j], ev[i][2 * j + 1])
+    for k_ in stage_ms:
+        stage_ms[k_] /= args.steps
+    U = float(np.mean([touched[i % nvar] for i in range(args.steps)]))
+    work = stage_work(wl, T, U, gemm)
+    dom = max(("gate_up", "down", "shared_gate_up", "shared_down"), key=lambda s_: stage_ms[s_])
+    dur_s = stage_ms[dom] * 1e-3
+    if gemm:
+        achieved = work[dom]["flops"] / dur_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFS, 4)}
+    else:
+        achieved = work[dom]["bytes"] / dur_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    roof["kernel"] = dom
+    roof["traffic"] = None
+    layer_bytes = sum(w_["bytes"] for w_ in work.values())
+    layer_flops = sum(w_["flops"] for w_ in work.values())
+    log("stage device time (us): " + ", ".join("%s %.2f" % (k_, v * 1e3)
+                                                for k_, v in stage_ms.items()))
+    log("touched experts per call %.1f; layer: %.2f us/step wall, %.1f GB/s, %.1f TFLOP/s"
+        % (U, ms_per_step * 1e3, layer_bytes / (ms_per_step * 1e-3) / 1e9,
+           layer_flops / (ms_per_step * 1e-3) / 1e12))
+    log("dominant kernel %s: %.2f us, %s" % (dom, stage_ms[dom] * 1e3, roof))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+        log("cpu oracle: %s" % cpu)
+
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if gemm else "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "description": wl.description, "T": T, "H": wl.H,
+                   "E": wl.E, "k": wl.k, "I": wl.I, "SI": wl.SI,
+                   "weights": "int4 offset-binary, fp16 scale per 32 inputs",
+                   "expert_path": "grouped fp16 MFMA GEMM" if gemm else "streaming int4 GEMV",
+                   "input_rotation": ("%d logits rows" % nvar) if pool is not None
+                   else ("%d weight sets" % nvar)},
+        "roofline": roof,
+        "stage_us": {k_: round(v * 1e3, 3) for k_, v in stage_ms.items()},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

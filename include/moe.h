@@ -153,6 +153,36 @@ int moe_layer(const moe_shape *shape, const uint16_t *x, const float *logits,
               const float *shared_gate, float *y, int32_t *idx_out, float *w_out,
               float *logits_out, void *ws, size_t ws_bytes, moe_stream_t stream);
 
+/*
+ * Profiling twin of moe_layer: the same work, with stage i's kernel launched
+ * through hipExtLaunchKernelGGL so that events[2i] and events[2i+1]
+ * (hipEvent_t handles created by the caller) are recorded at that kernel's
+ * start and end on `stream`; hipEventElapsedTime(events[2i], events[2i+1]) is
+ * the kernel's device time (per-stage stamps in the spirit of the dasLLAMA
+ * PR's per-role profile).  A stage the call does not run gets its two events
+ * recorded back to back (zero-length interval).
+ *   events   : host array of n_events hipEvent_t, n_events >= 2*MOE_STAGE_COUNT.
+ * Errors: as moe_layer, plus INVALID_ARG for a null or short event list.
+ */
+enum moe_stage {
+  MOE_STAGE_START = 0,          /* before the first launch                   */
+  MOE_STAGE_LOGITS = 1,         /* router logits (+ shared gate logit)       */
+  MOE_STAGE_TOPK = 2,           /* softmax -> top-k -> renormalise           */
+  MOE_STAGE_PERMUTE = 3,        /* permutation + expert schedule             */
+  MOE_STAGE_ACTIVATIONS = 4,    /* fp16 activation copy (MFMA path only)     */
+  MOE_STAGE_GATE_UP = 5,        /* routed gate/up + SiLU*mul                 */
+  MOE_STAGE_SHARED_GATE_UP = 6, /* shared expert gate/up + SiLU*mul          */
+  MOE_STAGE_DOWN = 7,           /* routed down + weighted combine            */
+  MOE_STAGE_SHARED_DOWN = 8,    /* shared expert down + gated combine        */
+  MOE_STAGE_COUNT = 9
+};
+int moe_layer_profiled(const moe_shape *shape, const uint16_t *x, const float *logits,
+                       const float *w_router, moe_q4 gate, moe_q4 up, moe_q4 down,
+                       const moe_q4 *shared, const float *shared_gate, float *y,
+                       int32_t *idx_out, float *w_out, float *logits_out, void *ws,
+                       size_t ws_bytes, moe_stream_t stream, void *const *events,
+                       int32_t n_events);
+
 /* Scratch bytes moe_layer and moe_expert_mlp need for this shape (0 if the
  * shape is not served).  Host only; enqueues nothing. */
 size_t moe_workspace_bytes(const moe_shape *shape);

@@ -22,7 +22,10 @@ MOE_PATH_AUTO, MOE_PATH_GEMV, MOE_PATH_GEMM = range(3)
 
 # Every symbol include/moe.h declares.
 EXPORTS = ("moe_router_topk", "moe_permute", "moe_expert_mlp", "moe_layer",
-           "moe_workspace_bytes", "moe_status_string", "moe_debug_dequant_int4")
+           "moe_layer_profiled", "moe_workspace_bytes", "moe_status_string",
+           "moe_debug_dequant_int4")
+STAGES = ("start", "logits", "topk", "permute", "activations", "gate_up", "shared_gate_up",
+          "down", "shared_down")
 
 
 class MoeError(RuntimeError):
@@ -59,13 +62,15 @@ def lib() -> ctypes.CDLL:
                                      moe_q4, P, P, ctypes.c_size_t, P]
         L.moe_layer.argtypes = [ctypes.POINTER(moe_shape), P, P, P, moe_q4, moe_q4, moe_q4,
                                 ctypes.POINTER(moe_q4), P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.moe_layer_profiled.argtypes = L.moe_layer.argtypes + [ctypes.POINTER(ctypes.c_void_p),
+                                                                i32]
         L.moe_workspace_bytes.argtypes = [ctypes.POINTER(moe_shape)]
         L.moe_workspace_bytes.restype = ctypes.c_size_t
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_debug_dequant_int4.argtypes = [moe_q4, i32, i32, i32, P, P]
         for name in ("moe_router_topk", "moe_permute", "moe_expert_mlp", "moe_layer",
-                     "moe_debug_dequant_int4"):
+                     "moe_layer_profiled", "moe_debug_dequant_int4"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -138,6 +143,21 @@ def moe_layer(shape: moe_shape, x, logits, w_router, gate, up, down,
         ctypes.byref(shape), _ptr(x), _ptr(logits), _ptr(w_router), q4(gate), q4(up), q4(down),
         sh_arr, _ptr(shared_gate), _ptr(y), _ptr(idx_out), _ptr(w_out), _ptr(logits_out),
         _ptr(ws), int(ws_bytes), _stream(stream)))
+
+
+def moe_layer_profiled(shape: moe_shape, x, logits, w_router, gate, up, down,
+                       shared: Optional[Sequence[Tuple]], shared_gate, y, idx_out, w_out,
+                       logits_out, ws, ws_bytes, events: Sequence[int], stream=None) -> None:
+    """moe_layer with stage i's kernel bracketed by hipEvent_t handles
+    events[2i] (start) and events[2i+1] (end); len(events) >= 2 * len(STAGES)."""
+    sh_arr = None
+    if shared is not None:
+        sh_arr = (moe_q4 * 3)(*[q4(p) for p in shared])
+    ev = (ctypes.c_void_p * len(events))(*events)
+    _check("moe_layer_profiled", lib().moe_layer_profiled(
+        ctypes.byref(shape), _ptr(x), _ptr(logits), _ptr(w_router), q4(gate), q4(up), q4(down),
+        sh_arr, _ptr(shared_gate), _ptr(y), _ptr(idx_out), _ptr(w_out), _ptr(logits_out),
+        _ptr(ws), int(ws_bytes), _stream(stream), ev, len(events)))
 
 
 def moe_debug_dequant_int4(plane, N, K, mode, out, stream=None) -> None:

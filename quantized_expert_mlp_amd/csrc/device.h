@@ -14,6 +14,14 @@ typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
+
+// 16-byte load with the nontemporal hint (streamed weights: read once).
+__device__ __forceinline__ uint4 load_stream16(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float((uint32_t)b << 16);
 }
@@ -30,12 +38,39 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Sum over aligned groups of LPR lanes (LPR a power of two <= 64); every lane
-// of the group receives the group's sum.
+// DPP lane permutations (gfx9 encodings) used by the reductions below.  All
+// of them stay inside a 16-lane DPP row, so every lane reads a live source.
+enum : int {
+  kDppXor1 = 0xB1,        // quad_perm [1,0,3,2]
+  kDppXor2 = 0x4E,        // quad_perm [2,3,0,1]
+  kDppHalfMirror = 0x141, // lane i <-> 7-i inside each half row
+  kDppMirror = 0x140,     // lane i <-> 15-i inside each row
+  kDppBcast15 = 0x142,    // lane 15 of row r -> every lane of row r+1
+  kDppBcast31 = 0x143,    // lane 31 -> every lane of rows 2 and 3
+};
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
+}
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+
+// Sum over aligned groups of LPR lanes (LPR a power of two, 4 <= LPR <= 64)
+// with DPP adds.  The group's sum is valid in its last lane (kl == LPR - 1);
+// for LPR <= 16 every lane of the group holds it.
 template <int LPR>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int o = LPR / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, MOE_WAVE);
+  static_assert(LPR >= 4 && LPR <= 64 && (LPR & (LPR - 1)) == 0, "LPR");
+  v += dpp<kDppXor1>(v);
+  v += dpp<kDppXor2>(v);
+  if (LPR >= 8) v += dpp<kDppHalfMirror>(v);
+  if (LPR >= 16) v += dpp<kDppMirror>(v);
+  if (LPR >= 32) v += dpp<kDppBcast15, 0xA>(v);  // rows 1, 3 += row 0, 2
+  if (LPR >= 64) v += dpp<kDppBcast31, 0x8>(v);  // row 3 += rows 0-1
   return v;
 }
 
@@ -43,10 +78,11 @@ __device__ __forceinline__ float group_sum(float v) {
 // int4 decode, bf16 offset form (GEMV kernels).
 //
 // One 32-bit word holds 8 nibbles e0..e7 (e_i in bits 4i..4i+3, element i of
-// the 8).  With the bf16 exponent of 128 (0x4300) and a nibble OR-ed into the
-// low 4 of the 7 mantissa bits, a 16-bit half is exactly the bf16 value
-// 128 + e.  Shifts by 0, 4, 8, 12 and a mask keeping bits 0-3 of each half
-// give four bf16 pairs:
+// the 8).  t = w & 0x0F0F0F0F holds bytes [e0, e2, e4, e6] and
+// u = (w >> 4) & 0x0F0F0F0F holds [e1, e3, e5, e7]; one v_perm_b32 per pair
+// then interleaves two nibble bytes with the byte 0x43, giving 16-bit halves
+// 0x43 0e = the exact bf16 value 128 + e (exponent of 128, the nibble in the
+// low mantissa bits):
 //   p0 = [128 + e0, 128 + e4]   p1 = [128 + e1, 128 + e5]
 //   p2 = [128 + e2, 128 + e6]   p3 = [128 + e3, 128 + e7]
 // Dotting them with activation pairs a0 = [x0, x4], a1 = [x1, x5],
@@ -58,14 +94,23 @@ struct Q4Pairs {
   uint32_t p0, p1, p2, p3;
 };
 
-__device__ __forceinline__ Q4Pairs q4_bf16_pairs(uint32_t w) {
+// v_perm_b32 selectors: byte k of the result takes byte sel_k of the pair
+// (src0 = bytes 4..7, src1 = bytes 0..3).
+constexpr uint32_t kSelLo = 0x04020400u;  // [src1.b0, src0.b0, src1.b2, src0.b0]
+constexpr uint32_t kSelHi = 0x04030401u;  // [src1.b1, src0.b0, src1.b3, src0.b0]
+
+__device__ __forceinline__ Q4Pairs q4_pairs_with(uint32_t w, uint32_t magic) {
+  const uint32_t t = w & 0x0F0F0F0Fu;
+  const uint32_t u = (w >> 4) & 0x0F0F0F0Fu;
   Q4Pairs r;
-  r.p0 = (w & 0x000F000Fu) | 0x43004300u;
-  r.p1 = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
-  r.p2 = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
-  r.p3 = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
+  r.p0 = __builtin_amdgcn_perm(magic, t, kSelLo);
+  r.p1 = __builtin_amdgcn_perm(magic, u, kSelLo);
+  r.p2 = __builtin_amdgcn_perm(magic, t, kSelHi);
+  r.p3 = __builtin_amdgcn_perm(magic, u, kSelHi);
   return r;
 }
+
+__device__ __forceinline__ Q4Pairs q4_bf16_pairs(uint32_t w) { return q4_pairs_with(w, 0x43434343u); }
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
@@ -77,28 +122,20 @@ __device__ __forceinline__ uint32_t pack2(uint32_t lo, uint32_t hi) { return lo 
 
 // ---------------------------------------------------------------------------
 // int4 decode, fp16 form (MFMA kernels): the MFMA operand is the exact weight
-// (e - 8) * s rounded once to fp16 (nearest even).  With the fp16 exponent of
-// 1024 (0x6400) the 10 mantissa bits hold a nibble either at bits 0-3 or,
-// unshifted, at bits 4-7 (value 1024 + 16 e), so one shift serves two pairs:
-//   [1024 + e0, 1024 + e4] - 1032            -> [e0 - 8, e4 - 8]  (exact)
-//   [1024 + 16 e1, 1024 + 16 e5] / 16 - 72   -> [e1 - 8, e5 - 8]  (exact)
-// then one packed multiply by [s, s] rounds the exact product.  The resulting
-// fp16 vector holds the 8 elements in the order 0,4,1,5,2,6,3,7; the
-// activation operands are stored in the same order (see perm8 below).
+// (e - 8) * s rounded once to fp16 (nearest even).  The same byte interleave
+// with 0x64 gives 16-bit halves 0x64 0e = the exact fp16 value 1024 + e; one
+// packed subtract of 1032 leaves e - 8 exactly, and one packed multiply by
+// [s, s] rounds the exact product.  The fp16 vector holds the 8 elements in
+// the order 0,4,1,5,2,6,3,7; the activation operands are stored in the same
+// order (see perm8_pos below).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ f16x8_t q4_f16x8(uint32_t w, f16x2_t s2) {
-  const uint32_t w8 = w >> 8;
+  const Q4Pairs p = q4_pairs_with(w, 0x64646464u);
   const f16x2_t off = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-  const f16x2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
-  const f16x2_t off2 = {(_Float16)-72.0f, (_Float16)-72.0f};
-  f16x2_t a = __builtin_bit_cast(f16x2_t, (w & 0x000F000Fu) | 0x64006400u) + off;
-  f16x2_t b = __builtin_bit_cast(f16x2_t, (w & 0x00F000F0u) | 0x64006400u) * sixteenth + off2;
-  f16x2_t c = __builtin_bit_cast(f16x2_t, (w8 & 0x000F000Fu) | 0x64006400u) + off;
-  f16x2_t d = __builtin_bit_cast(f16x2_t, (w8 & 0x00F000F0u) | 0x64006400u) * sixteenth + off2;
-  a = a * s2;
-  b = b * s2;
-  c = c * s2;
-  d = d * s2;
+  const f16x2_t a = (__builtin_bit_cast(f16x2_t, p.p0) + off) * s2;
+  const f16x2_t b = (__builtin_bit_cast(f16x2_t, p.p1) + off) * s2;
+  const f16x2_t c = (__builtin_bit_cast(f16x2_t, p.p2) + off) * s2;
+  const f16x2_t d = (__builtin_bit_cast(f16x2_t, p.p3) + off) * s2;
   f16x8_t r;
   r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
   r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];

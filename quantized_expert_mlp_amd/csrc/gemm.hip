@@ -264,20 +264,20 @@ __global__ __launch_bounds__(256) void gemm_kernel(
 hipError_t launch_gemm_gate_up(const Buckets& b, int max_tiles, const uint16_t* x16, int H,
                                int I, const uint8_t* gq, const uint16_t* gs,
                                const uint8_t* uq, const uint16_t* us, uint16_t* h16,
-                               hipStream_t st) {
+                               const Launch& L) {
   constexpr int BN = 4 * 32 * 1;
   dim3 grid((I + BN - 1) / BN, max_tiles);
-  hipLaunchKernelGGL((gemm_kernel<2, 1, 0>), grid, dim3(256), 0, st, b, x16, H, I, gq, gs, uq, us,
+  MOE_LAUNCH(L, (gemm_kernel<2, 1, 0>), grid, dim3(256), 0, b, x16, H, I, gq, gs, uq, us,
                      h16, nullptr, nullptr, 0, nullptr, H, I);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_down(const Buckets& b, int max_tiles, const uint16_t* h16, int H, int I,
                             const uint8_t* dq, const uint16_t* ds, const float* w,
-                            const float* gate_logit, int gate_ld, float* y, hipStream_t st) {
+                            const float* gate_logit, int gate_ld, float* y, const Launch& L) {
   constexpr int BN = 4 * 32 * 2;
   dim3 grid((H + BN - 1) / BN, max_tiles);
-  hipLaunchKernelGGL((gemm_kernel<1, 2, 1>), grid, dim3(256), 0, st, b, h16, I, H, dq, ds, dq, ds,
+  MOE_LAUNCH(L, (gemm_kernel<1, 2, 1>), grid, dim3(256), 0, b, h16, I, H, dq, ds, dq, ds,
                      nullptr, w, gate_logit, gate_ld, y, H, 0);
   return hipGetLastError();
 }

@@ -3,18 +3,37 @@
 // moe_api.cpp before any of these is called.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace moe {
 
+// Where a kernel is enqueued.  With start/stop events set, the launch goes
+// through hipExtLaunchKernelGGL, which records them at the kernel's own start
+// and end on the stream (per-kernel device time without extra packets).
+struct Launch {
+  hipStream_t st;
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
+#define MOE_LAUNCH(L, kernel, grid, block, shmem, ...)                                    \
+  do {                                                                                    \
+    if ((L).start)                                                                        \
+      hipExtLaunchKernelGGL(kernel, grid, block, shmem, (L).st, (L).start, (L).stop, 0,   \
+                            __VA_ARGS__);                                                 \
+    else                                                                                  \
+      hipLaunchKernelGGL(kernel, grid, block, shmem, (L).st, __VA_ARGS__);                \
+  } while (0)
+
 // Schedule words written by the permutation kernels, read by the expert MLPs:
 //   [0] number of experts with at least one slot (touched experts)
 //   [1] number of MFMA row tiles
-//   [2 .. 2+E)             touched experts, ascending
+//   [4 .. 4+4E)            touched experts, ascending: {expert, first row, rows, 0}
 //   [tiles_offset(E) ..)   tiles, 4 ints each: {expert, first row, rows, 0}
 constexpr int kGemmTileRows = 128;  // rows (slots) per MFMA tile
-__host__ __device__ constexpr int sched_tiles_offset(int E) { return ((2 + E + 3) / 4) * 4; }
+__host__ __device__ constexpr int sched_touched_offset() { return 4; }
+__host__ __device__ constexpr int sched_tiles_offset(int E) { return 4 + 4 * E; }
 __host__ __device__ constexpr int64_t sched_max_tiles(int64_t slots, int E) {
   return (slots + kGemmTileRows - 1) / kGemmTileRows + E;
 }
@@ -36,40 +55,66 @@ struct Buckets {
 };
 
 hipError_t launch_router_logits(const uint16_t* x, const float* wr, const float* gate_row, int T,
-                                int H, int E, float* out, int ld, hipStream_t st);
+                                int H, int E, float* out, int ld, const Launch& L);
 
 hipError_t launch_topk(const float* logits, int ld, int T, int E, int k, float route_scale,
-                       int32_t* idx, float* w, hipStream_t st);
+                       int32_t* idx, float* w, const Launch& L);
+
+// Fused top-k + permutation in one workgroup, for up to kRouteMaxSlots slots.
+constexpr int kRouteMaxSlots = 4096;
+hipError_t launch_route(const float* logits, int ld, int T, int E, int k, float route_scale,
+                        int32_t* idx, float* w, int32_t* off, int32_t* sorted, int32_t* row_of,
+                        int32_t* sched, const Launch& L);
 
 hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* off,
-                          int32_t* sorted, int32_t* row_of, int32_t* sched, hipStream_t st);
+                          int32_t* sorted, int32_t* row_of, int32_t* sched, const Launch& L);
 
 hipError_t launch_schedule_from_offsets(const int32_t* off, int E, int64_t slots, int32_t* sched,
-                                        hipStream_t st);
+                                        const Launch& L);
+
+// Routing folded into the gate/up GEMV for very small batches (T <=
+// kFusedRouteMaxT tokens, T*k <= kFusedRouteMaxSlots slots): every workgroup
+// redoes the (cheap, deterministic) top-k and bucket build in LDS, and
+// workgroup (0,0) publishes idx, w, off, sorted, row_of and the schedule for
+// the down launch.
+constexpr int kFusedRouteMaxT = 4;
+constexpr int kFusedRouteMaxSlots = 64;
+struct RouteArgs {
+  const float* logits;  // [T][ld]
+  int ld, E, T;
+  float route_scale;
+  int32_t* idx;     // [T][k]
+  float* w;         // [T][k]
+  int32_t* off;     // [E+1]
+  int32_t* sorted;  // [T*k]
+  int32_t* row_of;  // [T*k]
+  int32_t* sched;   // schedule words
+};
 
 // Streaming int4 GEMV (decode).  gate/up: h[row][I] = silu(Wg x)*(Wu x) in fp32;
 // down: y[token] += weight * (Wd h[row]).  The gate/up launch also zeroes y.
 hipError_t launch_gemv_gate_up(const Buckets& b, int max_buckets, const uint16_t* x, int H,
                                int I, const uint8_t* gq, const uint16_t* gs,
                                const uint8_t* uq, const uint16_t* us, float* h, float* y_zero,
-                               int64_t y_elems, hipStream_t st);
+                               int64_t y_elems, const Launch& L,
+                               const RouteArgs* route = nullptr);
 hipError_t launch_gemv_down(const Buckets& b, int max_buckets, const float* h, int H, int I,
                             const uint8_t* dq, const uint16_t* ds, const float* w,
-                            const float* gate_logit, int gate_ld, float* y, hipStream_t st);
+                            const float* gate_logit, int gate_ld, float* y, const Launch& L);
 bool gemv_supported(int K);
 
 // Grouped MFMA GEMM (prefill), fp16 operands with fp32 accumulation.
 hipError_t launch_convert_x16(const uint16_t* x, int T, int H, uint16_t* x16, float* y_zero,
-                              int64_t y_elems, hipStream_t st);
+                              int64_t y_elems, const Launch& L);
 hipError_t launch_gemm_gate_up(const Buckets& b, int max_tiles, const uint16_t* x16, int H,
                                int I, const uint8_t* gq, const uint16_t* gs,
                                const uint8_t* uq, const uint16_t* us, uint16_t* h16,
-                               hipStream_t st);
+                               const Launch& L);
 hipError_t launch_gemm_down(const Buckets& b, int max_tiles, const uint16_t* h16, int H, int I,
                             const uint8_t* dq, const uint16_t* ds, const float* w,
-                            const float* gate_logit, int gate_ld, float* y, hipStream_t st);
+                            const float* gate_logit, int gate_ld, float* y, const Launch& L);
 
 hipError_t launch_debug_dequant(const uint8_t* q, const uint16_t* s, int N, int K, int mode,
-                                float* out, hipStream_t st);
+                                float* out, const Launch& L);
 
 }  // namespace moe

@@ -32,13 +32,13 @@ __global__ __launch_bounds__(256) void convert_x16_kernel(const uint16_t* __rest
 }
 
 hipError_t launch_convert_x16(const uint16_t* x, int T, int H, uint16_t* x16, float* y_zero,
-                              int64_t y_elems, hipStream_t st) {
+                              int64_t y_elems, const Launch& L) {
   const int64_t blocks8 = (int64_t)T * H / 8;
   const int64_t work = blocks8 > y_elems ? blocks8 : y_elems;
   int grid = (int)((work + 255) / 256);
   if (grid > 8192) grid = 8192;
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(convert_x16_kernel, dim3(grid), dim3(256), 0, st, x, blocks8, x16, y_zero,
+  MOE_LAUNCH(L, convert_x16_kernel, dim3(grid), dim3(256), 0, x, blocks8, x16, y_zero,
                      y_elems);
   return hipGetLastError();
 }
@@ -78,9 +78,9 @@ __global__ __launch_bounds__(256) void debug_dequant_kernel(const uint8_t* __res
 }
 
 hipError_t launch_debug_dequant(const uint8_t* q, const uint16_t* s, int N, int K, int mode,
-                                float* out, hipStream_t st) {
+                                float* out, const Launch& L) {
   const int64_t words = (int64_t)N * K / 8;
-  hipLaunchKernelGGL(debug_dequant_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, st,
+  MOE_LAUNCH(L, debug_dequant_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0,
                      q, s, N, K, mode, out);
   return hipGetLastError();
 }

@@ -3,7 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/moe.h"
+#include "moe.h"
 #include "kernels.h"
 
 namespace {
@@ -91,6 +91,27 @@ P* at(void* ws, size_t off) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// Optional per-stage events (moe_layer_profiled): stage i's kernel is launched
+// with events[2i] / events[2i+1] recorded at its start and end; a stage a call
+// does not run gets both events recorded back to back, so every pair is valid.
+struct Stages {
+  void* const* ev;
+  hipStream_t st;
+  moe::Launch at(int i) const {
+    moe::Launch L{st};
+    if (ev) {
+      L.start = reinterpret_cast<hipEvent_t>(ev[2 * i]);
+      L.stop = reinterpret_cast<hipEvent_t>(ev[2 * i + 1]);
+    }
+    return L;
+  }
+  bool skip(int i) const {
+    if (!ev) return true;
+    return hipEventRecord(reinterpret_cast<hipEvent_t>(ev[2 * i]), st) == hipSuccess &&
+           hipEventRecord(reinterpret_cast<hipEvent_t>(ev[2 * i + 1]), st) == hipSuccess;
+  }
+};
+
 bool plane_ok(const moe_q4& p) {
   return p.q && p.s && aligned(p.q, 16) && aligned(p.s, 16);
 }
@@ -99,7 +120,7 @@ bool plane_ok(const moe_q4& p) {
 int run_mlp(const moe_shape* sh, bool gemm, const Layout& L, void* ws, const uint16_t* x,
             const int32_t* off, const int32_t* sorted, const float* w, moe_q4 gate, moe_q4 up,
             moe_q4 down, const moe_q4* shared, const float* gate_logit, int gate_ld, float* y,
-            hipStream_t st) {
+            hipStream_t st, const Stages& sg, const moe::RouteArgs* route = nullptr) {
   const int T = sh->T, H = sh->H, I = sh->I, E = sh->E, k = sh->k;
   const int64_t slots = (int64_t)T * k;
   const int32_t* sched = at<int32_t>(ws, L.sched);
@@ -111,20 +132,27 @@ int run_mlp(const moe_shape* sh, bool gemm, const Layout& L, void* ws, const uin
     float* h = at<float>(ws, L.h);
     float* hs = at<float>(ws, L.hs);
     const int max_buckets = (int)(slots < E ? slots : E);
+    if (!sg.skip(MOE_STAGE_ACTIVATIONS)) return MOE_ERR_HIP;
     err = moe::launch_gemv_gate_up(routed, max_buckets, x, H, I, gate.q, gate.s, up.q, up.s, h, y,
-                                   y_elems, st);
+                                   y_elems, sg.at(MOE_STAGE_GATE_UP), route);
     if (err != hipSuccess) return MOE_ERR_HIP;
     if (shared) {
       err = moe::launch_gemv_gate_up(sharedb, 1, x, H, sh->SI, shared[0].q, shared[0].s,
-                                     shared[1].q, shared[1].s, hs, nullptr, 0, st);
+                                     shared[1].q, shared[1].s, hs, nullptr, 0,
+                                     sg.at(MOE_STAGE_SHARED_GATE_UP));
       if (err != hipSuccess) return MOE_ERR_HIP;
+    } else if (!sg.skip(MOE_STAGE_SHARED_GATE_UP)) {
+      return MOE_ERR_HIP;
     }
-    err = moe::launch_gemv_down(routed, max_buckets, h, H, I, down.q, down.s, w, nullptr, 0, y, st);
+    err = moe::launch_gemv_down(routed, max_buckets, h, H, I, down.q, down.s, w, nullptr, 0, y,
+                                sg.at(MOE_STAGE_DOWN));
     if (err != hipSuccess) return MOE_ERR_HIP;
     if (shared) {
       err = moe::launch_gemv_down(sharedb, 1, hs, H, sh->SI, shared[2].q, shared[2].s, nullptr,
-                                  gate_logit, gate_ld, y, st);
+                                  gate_logit, gate_ld, y, sg.at(MOE_STAGE_SHARED_DOWN));
       if (err != hipSuccess) return MOE_ERR_HIP;
+    } else if (!sg.skip(MOE_STAGE_SHARED_DOWN)) {
+      return MOE_ERR_HIP;
     }
     return MOE_OK;
   }
@@ -133,21 +161,27 @@ int run_mlp(const moe_shape* sh, bool gemm, const Layout& L, void* ws, const uin
   uint16_t* hs16 = at<uint16_t>(ws, L.hs);
   const int max_tiles = (int)moe::sched_max_tiles(slots, E);
   const int shared_tiles = (T + moe::kGemmTileRows - 1) / moe::kGemmTileRows;
-  err = moe::launch_convert_x16(x, T, H, x16, y, y_elems, st);
+  err = moe::launch_convert_x16(x, T, H, x16, y, y_elems, sg.at(MOE_STAGE_ACTIVATIONS));
   if (err != hipSuccess) return MOE_ERR_HIP;
-  err = moe::launch_gemm_gate_up(routed, max_tiles, x16, H, I, gate.q, gate.s, up.q, up.s, h16, st);
+  err = moe::launch_gemm_gate_up(routed, max_tiles, x16, H, I, gate.q, gate.s, up.q, up.s, h16,
+                                 sg.at(MOE_STAGE_GATE_UP));
   if (err != hipSuccess) return MOE_ERR_HIP;
   if (shared) {
     err = moe::launch_gemm_gate_up(sharedb, shared_tiles, x16, H, sh->SI, shared[0].q, shared[0].s,
-                                   shared[1].q, shared[1].s, hs16, st);
+                                   shared[1].q, shared[1].s, hs16, sg.at(MOE_STAGE_SHARED_GATE_UP));
     if (err != hipSuccess) return MOE_ERR_HIP;
+  } else if (!sg.skip(MOE_STAGE_SHARED_GATE_UP)) {
+    return MOE_ERR_HIP;
   }
-  err = moe::launch_gemm_down(routed, max_tiles, h16, H, I, down.q, down.s, w, nullptr, 0, y, st);
+  err = moe::launch_gemm_down(routed, max_tiles, h16, H, I, down.q, down.s, w, nullptr, 0, y,
+                              sg.at(MOE_STAGE_DOWN));
   if (err != hipSuccess) return MOE_ERR_HIP;
   if (shared) {
     err = moe::launch_gemm_down(sharedb, shared_tiles, hs16, H, sh->SI, shared[2].q, shared[2].s,
-                                nullptr, gate_logit, gate_ld, y, st);
+                                nullptr, gate_logit, gate_ld, y, sg.at(MOE_STAGE_SHARED_DOWN));
     if (err != hipSuccess) return MOE_ERR_HIP;
+  } else if (!sg.skip(MOE_STAGE_SHARED_DOWN)) {
+    return MOE_ERR_HIP;
   }
   return MOE_OK;
 }
@@ -180,7 +214,7 @@ int moe_router_topk(const float* logits, int32_t T, int32_t E, int32_t k, float 
   if (!aligned(logits, 4) || !aligned(idx, 4) || !aligned(w, 4)) return MOE_ERR_INVALID_ARG;
   if (E > 256 || k > 64) return MOE_ERR_UNSUPPORTED;
   return hip_status(moe::launch_topk(logits, E, T, E, k, route_scale, idx, w,
-                                     reinterpret_cast<hipStream_t>(stream)));
+                                     moe::Launch{reinterpret_cast<hipStream_t>(stream)}));
 }
 
 int moe_permute(const int32_t* idx, int32_t T, int32_t k, int32_t E, int32_t* off,
@@ -191,7 +225,7 @@ int moe_permute(const int32_t* idx, int32_t T, int32_t k, int32_t E, int32_t* of
   if (E > 256) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)T * k >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
   return hip_status(moe::launch_permute(idx, T, k, E, off, sorted, row_of, nullptr,
-                                        reinterpret_cast<hipStream_t>(stream)));
+                                        moe::Launch{reinterpret_cast<hipStream_t>(stream)}));
 }
 
 int moe_expert_mlp(const moe_shape* sh, const uint16_t* x, const int32_t* off,
@@ -210,15 +244,17 @@ int moe_expert_mlp(const moe_shape* sh, const uint16_t* x, const int32_t* off,
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (moe::launch_schedule_from_offsets(off, sh->E, (int64_t)sh->T * sh->k, at<int32_t>(ws, L.sched),
-                                         st) != hipSuccess)
+                                         moe::Launch{st}) != hipSuccess)
     return MOE_ERR_HIP;
-  return run_mlp(sh, gemm, L, ws, x, off, sorted, w, gate, up, down, nullptr, nullptr, 0, y, st);
+  return run_mlp(sh, gemm, L, ws, x, off, sorted, w, gate, up, down, nullptr, nullptr, 0, y, st,
+                 Stages{nullptr, st});
 }
 
-int moe_layer(const moe_shape* sh, const uint16_t* x, const float* logits,
-              const float* w_router, moe_q4 gate, moe_q4 up, moe_q4 down, const moe_q4* shared,
-              const float* shared_gate, float* y, int32_t* idx_out, float* w_out,
-              float* logits_out, void* ws, size_t ws_bytes, moe_stream_t stream) {
+static int layer_impl(const moe_shape* sh, const uint16_t* x, const float* logits,
+                      const float* w_router, moe_q4 gate, moe_q4 up, moe_q4 down,
+                      const moe_q4* shared, const float* shared_gate, float* y, int32_t* idx_out,
+                      float* w_out, float* logits_out, void* ws, size_t ws_bytes,
+                      moe_stream_t stream, void* const* events) {
   int rc = check_shape(sh);
   if (rc != MOE_OK) return rc;
   if (!x || !y || !ws) return MOE_ERR_INVALID_ARG;
@@ -246,6 +282,8 @@ int moe_layer(const moe_shape* sh, const uint16_t* x, const float* logits,
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int T = sh->T, H = sh->H, E = sh->E, k = sh->k;
   const bool gated = shared && shared_gate;
+  const Stages sg{events, st};
+  if (!sg.skip(MOE_STAGE_START)) return MOE_ERR_HIP;
 
   // 1. logits (and the shared gate logit as one more router row)
   const float* Lp = logits;
@@ -255,8 +293,8 @@ int moe_layer(const moe_shape* sh, const uint16_t* x, const float* logits,
   if (w_router) {
     float* Lw = at<float>(ws, L.logits);
     const int ld = gated ? E + 1 : E;
-    if (moe::launch_router_logits(x, w_router, gated ? shared_gate : nullptr, T, H, E, Lw, ld, st) !=
-        hipSuccess)
+    if (moe::launch_router_logits(x, w_router, gated ? shared_gate : nullptr, T, H, E, Lw, ld,
+                                  sg.at(MOE_STAGE_LOGITS)) != hipSuccess)
       return MOE_ERR_HIP;
     Lp = Lw;
     ldL = ld;
@@ -266,41 +304,80 @@ int moe_layer(const moe_shape* sh, const uint16_t* x, const float* logits,
     }
   } else if (gated) {
     float* gl = at<float>(ws, L.gate);
-    if (moe::launch_router_logits(x, nullptr, shared_gate, T, H, 0, gl, 1, st) != hipSuccess)
+    if (moe::launch_router_logits(x, nullptr, shared_gate, T, H, 0, gl, 1,
+                                  sg.at(MOE_STAGE_LOGITS)) != hipSuccess)
       return MOE_ERR_HIP;
     gate_logit = gl;
     gate_ld = 1;
+  } else if (!sg.skip(MOE_STAGE_LOGITS)) {
+    return MOE_ERR_HIP;
   }
   if (logits_out) {
     if (hipMemcpy2DAsync(logits_out, sizeof(float) * E, Lp, sizeof(float) * ldL,
                          sizeof(float) * E, T, hipMemcpyDeviceToDevice, st) != hipSuccess)
       return MOE_ERR_HIP;
   }
-
-  // 2. top-k + weights
+  // 2.-3. top-k + weights, permutation + schedule: folded into the gate/up
+  // GEMV for a handful of tokens, one fused workgroup for decode-sized
+  // batches, separate kernels beyond.
   int32_t* idx = idx_out ? idx_out : at<int32_t>(ws, L.idx);
   float* w = w_out ? w_out : at<float>(ws, L.w);
-  if (moe::launch_topk(Lp, ldL, T, E, k, sh->route_scale, idx, w, st) != hipSuccess)
-    return MOE_ERR_HIP;
-
-  // 3. permutation + schedule
   int32_t* off = at<int32_t>(ws, L.off);
   int32_t* sorted = at<int32_t>(ws, L.sorted);
-  if (moe::launch_permute(idx, T, k, E, off, sorted, at<int32_t>(ws, L.row_of),
-                          at<int32_t>(ws, L.sched), st) != hipSuccess)
-    return MOE_ERR_HIP;
+  const bool fold = !gemm && T <= moe::kFusedRouteMaxT && T * k <= moe::kFusedRouteMaxSlots;
+  moe::RouteArgs ra{Lp, ldL, E, T, sh->route_scale, idx, w, off, sorted,
+                    at<int32_t>(ws, L.row_of), at<int32_t>(ws, L.sched)};
+  if (fold) {
+    if (!sg.skip(MOE_STAGE_TOPK) || !sg.skip(MOE_STAGE_PERMUTE)) return MOE_ERR_HIP;
+  } else if ((int64_t)T * k <= moe::kRouteMaxSlots) {
+    if (moe::launch_route(Lp, ldL, T, E, k, sh->route_scale, idx, w, off, sorted,
+                          at<int32_t>(ws, L.row_of), at<int32_t>(ws, L.sched),
+                          sg.at(MOE_STAGE_TOPK)) != hipSuccess ||
+        !sg.skip(MOE_STAGE_PERMUTE))
+      return MOE_ERR_HIP;
+  } else {
+    if (moe::launch_topk(Lp, ldL, T, E, k, sh->route_scale, idx, w, sg.at(MOE_STAGE_TOPK)) !=
+        hipSuccess)
+      return MOE_ERR_HIP;
+    if (moe::launch_permute(idx, T, k, E, off, sorted, at<int32_t>(ws, L.row_of),
+                            at<int32_t>(ws, L.sched), sg.at(MOE_STAGE_PERMUTE)) != hipSuccess)
+      return MOE_ERR_HIP;
+  }
 
   // 4.-5. expert MLPs with the fused combine
   return run_mlp(sh, gemm, L, ws, x, off, sorted, w, gate, up, down, shared, gate_logit, gate_ld,
-                 y, st);
+                 y, st, sg, fold ? &ra : nullptr);
 }
+
+int moe_layer(const moe_shape* sh, const uint16_t* x, const float* logits,
+              const float* w_router, moe_q4 gate, moe_q4 up, moe_q4 down, const moe_q4* shared,
+              const float* shared_gate, float* y, int32_t* idx_out, float* w_out,
+              float* logits_out, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  return layer_impl(sh, x, logits, w_router, gate, up, down, shared, shared_gate, y, idx_out,
+                    w_out, logits_out, ws, ws_bytes, stream, nullptr);
+}
+
+int moe_layer_profiled(const moe_shape* sh, const uint16_t* x, const float* logits,
+                       const float* w_router, moe_q4 gate, moe_q4 up, moe_q4 down,
+                       const moe_q4* shared, const float* shared_gate, float* y,
+                       int32_t* idx_out, float* w_out, float* logits_out, void* ws,
+                       size_t ws_bytes, moe_stream_t stream, void* const* events,
+                       int32_t n_events) {
+  if (!events || n_events < 2 * MOE_STAGE_COUNT) return MOE_ERR_INVALID_ARG;
+  for (int i = 0; i < 2 * MOE_STAGE_COUNT; ++i)
+    if (!events[i]) return MOE_ERR_INVALID_ARG;
+  return layer_impl(sh, x, logits, w_router, gate, up, down, shared, shared_gate, y, idx_out,
+                    w_out, logits_out, ws, ws_bytes, stream, events);
+}
+
+
 
 int moe_debug_dequant_int4(moe_q4 plane, int32_t N, int32_t K, int32_t mode, float* out,
                            moe_stream_t stream) {
   if (!plane_ok(plane) || !out || N < 1 || K < 32 || K % 32 || (mode != 0 && mode != 1))
     return MOE_ERR_INVALID_ARG;
   return hip_status(moe::launch_debug_dequant(plane.q, plane.s, N, K, mode, out,
-                                              reinterpret_cast<hipStream_t>(stream)));
+                                              moe::Launch{reinterpret_cast<hipStream_t>(stream)}));
 }
 
 }  // extern "C"

@@ -1,0 +1,323 @@
+// Routing: router logits GEMM (fp32 MFMA), softmax -> top-k -> renormalise
+// (one wave64 per token), token-to-expert permutation and the expert
+// schedule, and a fused single-workgroup route kernel for small batches.
+//
+// Sources: the dasLLAMA vulkan PR #3988 routed-block commits (router GEMM over
+// the normed rows and the f32 router plane, with a gated shared expert's gate
+// row after the expert rows; per-row top-k with position-major picks and
+// weights; the bucket schedule in one workgroup - a count per expert,
+// exclusive scans placing the buckets and the tiles, the slot map in slot
+// order, an upper-bound dispatch whose unused tail is marked so that surplus
+// workgroups return at once - and its later atomic tally over workgroup
+// memory) and the vllm.cpp PR #481 warp router (one warp per token with the
+// whole logit row in registers, a single read of the row, no shared memory,
+// k rounds of arg-max then mask).
+#include "device.h"
+#include "kernels.h"
+#include "topk.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// Logits L[t][e] = sum_h x[t][h] * Wr[e][h], plus column E = x[t] . g when a
+// gate row is given.  One workgroup computes a 16-token x 16-row tile with
+// v_mfma_f32_16x16x4_f32; its four waves split H in interleaved 16-wide
+// chunks and their partial tiles are added through LDS.  Within a chunk lane
+// (i, q) = (lane % 16, lane / 16) feeds A[i][q] = x[t0+i][c+4q+r] and
+// B[q][i] = Wr[e0+i][c+4q+r] to the r-th of four MFMAs, so the four MFMAs
+// together contract the 16 inputs c..c+15 (each lane reads 4 consecutive
+// inputs with one vector load).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x,
+                                                            const float* __restrict__ wr,
+                                                            const float* __restrict__ gate_row,
+                                                            int T, int H, int E, float* out,
+                                                            int ld) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i = lane & 15, q = lane >> 4;
+  const int t = blockIdx.x * 16 + i;
+  const int e = blockIdx.y * 16 + i;
+  const uint16_t* xrow = (t < T) ? x + (int64_t)t * H : nullptr;
+  const float* wrow = nullptr;
+  if (e < E) wrow = wr + (int64_t)e * H;
+  else if (e == E && gate_row) wrow = gate_row;
+
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int c = wave * 16; c < H; c += 64) {
+    const int kk = c + 4 * q;
+    float a[4] = {0.f, 0.f, 0.f, 0.f}, b[4] = {0.f, 0.f, 0.f, 0.f};
+    if (xrow) {
+      const uint2 v = *reinterpret_cast<const uint2*>(xrow + kk);
+      a[0] = __uint_as_float(v.x << 16);
+      a[1] = __uint_as_float(v.x & 0xFFFF0000u);
+      a[2] = __uint_as_float(v.y << 16);
+      a[3] = __uint_as_float(v.y & 0xFFFF0000u);
+    }
+    if (wrow) {
+      const float4 v = *reinterpret_cast<const float4*>(wrow + kk);
+      b[0] = v.x; b[1] = v.y; b[2] = v.z; b[3] = v.w;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r], b[r], acc, 0, 0, 0);
+  }
+
+  __shared__ f32x4_t part[4][64];
+  part[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    f32x4_t s = part[0][lane];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) s += part[w][lane];
+    // D[4*(lane/16) + r][lane % 16]: row = token, column = router row.
+    const int col = blockIdx.y * 16 + i;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = blockIdx.x * 16 + 4 * q + r;
+      if (row < T && col < ld) out[(int64_t)row * ld + col] = s[r];
+    }
+  }
+}
+
+hipError_t launch_router_logits(const uint16_t* x, const float* wr, const float* gate_row, int T,
+                                int H, int E, float* out, int ld, const Launch& L) {
+  dim3 grid((T + 15) / 16, (ld + 15) / 16);
+  MOE_LAUNCH(L, router_logits_kernel, grid, dim3(256), 0, x, wr, gate_row, T, H, E, out,
+                     ld);
+  return hipGetLastError();
+}
+
+template <int V>
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int ld,
+                                                   int T, int E, int k, float route_scale,
+                                                   int32_t* __restrict__ idx,
+                                                   float* __restrict__ w) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  topk_wave<V>(logits + (int64_t)t * ld, E, k, route_scale, idx + (int64_t)t * k,
+               w + (int64_t)t * k, nullptr);
+}
+
+hipError_t launch_topk(const float* logits, int ld, int T, int E, int k, float route_scale,
+                       int32_t* idx, float* w, const Launch& L) {
+  dim3 grid((T + 3) / 4);
+  switch ((E + 63) / 64) {
+    case 1: MOE_LAUNCH(L, topk_kernel<1>, grid, dim3(256), 0, logits, ld, T, E, k, route_scale, idx, w); break;
+    case 2: MOE_LAUNCH(L, topk_kernel<2>, grid, dim3(256), 0, logits, ld, T, E, k, route_scale, idx, w); break;
+    case 3: MOE_LAUNCH(L, topk_kernel<3>, grid, dim3(256), 0, logits, ld, T, E, k, route_scale, idx, w); break;
+    case 4: MOE_LAUNCH(L, topk_kernel<4>, grid, dim3(256), 0, logits, ld, T, E, k, route_scale, idx, w); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Permutation.  One 1024-thread workgroup: LDS histogram with LDS atomics,
+// LDS scan, then a stable scatter that ranks equal experts inside each wave
+// with ballots and across the 16 waves with per-wave counts, so the
+// within-bucket order is ascending slot order and the result deterministic.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int kMaxE = 256;
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / 64;
+
+// Exclusive scan of v over the workgroup's first 256 threads (the others must
+// pass 0).  Every thread of the workgroup must call it.  tmp: >= kWaves ints.
+__device__ int scan256(int v, int* tmp, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int n = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += n;
+  }
+  if (lane == 63) tmp[wave] = inc;
+  __syncthreads();
+  int pre = 0, tot = 0;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
+    if (w < wave) pre += tmp[w];
+    tot += tmp[w];
+  }
+  *total = tot;
+  __syncthreads();
+  return pre + inc - v;
+}
+
+// Schedule words from the per-expert counts and offsets held in LDS.
+// At most max_tiles tiles are written (the schedule buffer's capacity).
+__device__ void write_schedule(const int* cnt, const int* offs, int E, int max_tiles,
+                               int32_t* sched, int* tmp) {
+  const int e = threadIdx.x;
+  const int c = (e < E) ? cnt[e] : 0;
+  const int touched = c > 0 ? 1 : 0;
+  const int ntile = (c + kGemmTileRows - 1) / kGemmTileRows;
+  int n_touched, n_tiles;
+  const int tpos = scan256(touched, tmp, &n_touched);
+  const int tilepos = scan256(ntile, tmp, &n_tiles);
+  if (e < E) {
+    if (touched)
+      reinterpret_cast<int4*>(sched + sched_touched_offset())[tpos] = make_int4(e, offs[e], c, 0);
+    int4* tiles = reinterpret_cast<int4*>(sched + sched_tiles_offset(E));
+    for (int j = 0; j < ntile && tilepos + j < max_tiles; ++j) {
+      const int rows = min(kGemmTileRows, c - j * kGemmTileRows);
+      tiles[tilepos + j] = make_int4(e, offs[e] + j * kGemmTileRows, rows, 0);
+    }
+  }
+  if (threadIdx.x == 0) {
+    sched[0] = n_touched;
+    sched[1] = min(n_tiles, max_tiles);
+  }
+}
+
+}  // namespace
+
+struct PermuteLds {
+  int cnt[kMaxE];
+  int offs[kMaxE];
+  int cursor[kMaxE];
+  int wcnt[kWaves][kMaxE];
+  int tmp[kWaves];
+};
+
+// idx may point to global or LDS memory.  Every thread of the workgroup calls.
+__device__ void permute_block(const int32_t* idx, int S, int E, int32_t* __restrict__ off,
+                              int32_t* __restrict__ sorted, int32_t* __restrict__ row_of,
+                              int32_t* __restrict__ sched, int max_tiles, PermuteLds& sm) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  for (int i = tid; i < kMaxE; i += kThreads) sm.cnt[i] = 0;
+  __syncthreads();
+  for (int s = tid; s < S; s += kThreads) {
+    const int e = idx[s];
+    if (e >= 0 && e < E) atomicAdd(&sm.cnt[e], 1);
+  }
+  __syncthreads();
+
+  int total;
+  const int pre = scan256((tid < E) ? sm.cnt[tid] : 0, sm.tmp, &total);
+  if (tid < E) {
+    sm.offs[tid] = pre;
+    sm.cursor[tid] = pre;
+    off[tid] = pre;
+  }
+  if (tid == 0) off[E] = total;
+  __syncthreads();
+
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int base = 0; base < S; base += kThreads) {
+    const int s = base + tid;
+    int e = (s < S) ? idx[s] : -1;
+    if (e >= E) e = -1;
+    for (int i = tid; i < kWaves * kMaxE; i += kThreads) (&sm.wcnt[0][0])[i] = 0;
+    __syncthreads();
+    // Lanes of this wave holding the same expert (key e + 1 fits in 9 bits).
+    const int key = e + 1;
+    uint64_t peers = ~0ull;
+#pragma unroll
+    for (int bit = 0; bit < 9; ++bit) {
+      const uint64_t bal = __ballot((key >> bit) & 1);
+      peers &= ((key >> bit) & 1) ? bal : ~bal;
+    }
+    const int rank = __popcll(peers & lt_mask);
+    if (e >= 0 && rank == 0) sm.wcnt[wave][e] = __popcll(peers);
+    __syncthreads();
+    if (e >= 0) {
+      int pos = sm.cursor[e] + rank;
+      for (int w = 0; w < wave; ++w) pos += sm.wcnt[w][e];
+      sorted[pos] = s;
+      row_of[s] = pos;
+    } else if (s < S) {
+      row_of[s] = -1;
+    }
+    __syncthreads();
+    if (tid < E) {
+      int add = 0;
+      for (int w = 0; w < kWaves; ++w) add += sm.wcnt[w][tid];
+      sm.cursor[tid] += add;
+    }
+    __syncthreads();
+  }
+
+  if (sched) write_schedule(sm.cnt, sm.offs, E, max_tiles, sched, sm.tmp);
+}
+
+__global__ __launch_bounds__(kThreads) void permute_kernel(const int32_t* __restrict__ idx, int S,
+                                                           int E, int32_t* __restrict__ off,
+                                                           int32_t* __restrict__ sorted,
+                                                           int32_t* __restrict__ row_of,
+                                                           int32_t* __restrict__ sched,
+                                                           int max_tiles) {
+  __shared__ PermuteLds sm;
+  permute_block(idx, S, E, off, sorted, row_of, sched, max_tiles, sm);
+}
+
+// Fused routing for small batches: the workgroup's 16 waves run the top-k of
+// every token (wave w takes tokens w, w+16, ...), keep the picks in LDS, and
+// the same workgroup then builds the permutation and schedule from them.
+template <int V>
+__global__ __launch_bounds__(kThreads) void route_kernel(const float* __restrict__ logits, int ld,
+                                                         int T, int E, int k, float route_scale,
+                                                         int32_t* __restrict__ idx,
+                                                         float* __restrict__ w,
+                                                         int32_t* __restrict__ off,
+                                                         int32_t* __restrict__ sorted,
+                                                         int32_t* __restrict__ row_of,
+                                                         int32_t* __restrict__ sched,
+                                                         int max_tiles) {
+  __shared__ PermuteLds sm;
+  __shared__ int32_t picks[kRouteMaxSlots];
+  for (int t = threadIdx.x >> 6; t < T; t += kWaves)
+    topk_wave<V>(logits + (int64_t)t * ld, E, k, route_scale, idx + (int64_t)t * k,
+                 w + (int64_t)t * k, picks + t * k);
+  __syncthreads();
+  permute_block(picks, T * k, E, off, sorted, row_of, sched, max_tiles, sm);
+}
+
+hipError_t launch_route(const float* logits, int ld, int T, int E, int k, float route_scale,
+                        int32_t* idx, float* w, int32_t* off, int32_t* sorted, int32_t* row_of,
+                        int32_t* sched, const Launch& L) {
+  const int max_tiles = (int)sched_max_tiles((int64_t)T * k, E);
+  switch ((E + 63) / 64) {
+    case 1: MOE_LAUNCH(L, route_kernel<1>, dim3(1), dim3(kThreads), 0, logits, ld, T, E, k, route_scale, idx, w, off, sorted, row_of, sched, max_tiles); break;
+    case 2: MOE_LAUNCH(L, route_kernel<2>, dim3(1), dim3(kThreads), 0, logits, ld, T, E, k, route_scale, idx, w, off, sorted, row_of, sched, max_tiles); break;
+    case 3: MOE_LAUNCH(L, route_kernel<3>, dim3(1), dim3(kThreads), 0, logits, ld, T, E, k, route_scale, idx, w, off, sorted, row_of, sched, max_tiles); break;
+    case 4: MOE_LAUNCH(L, route_kernel<4>, dim3(1), dim3(kThreads), 0, logits, ld, T, E, k, route_scale, idx, w, off, sorted, row_of, sched, max_tiles); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// The schedule alone, from offsets written earlier (for callers that bring
+// their own permutation).  One 256-thread workgroup.
+__global__ __launch_bounds__(256) void schedule_kernel(const int32_t* __restrict__ off, int E,
+                                                       int32_t* __restrict__ sched,
+                                                       int max_tiles) {
+  __shared__ int cnt[kMaxE];
+  __shared__ int offs[kMaxE];
+  __shared__ int tmp[4];
+  const int e = threadIdx.x;
+  if (e < E) {
+    offs[e] = off[e];
+    cnt[e] = off[e + 1] - off[e];
+  }
+  __syncthreads();
+  write_schedule(cnt, offs, E, max_tiles, sched, tmp);
+}
+
+hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* off,
+                          int32_t* sorted, int32_t* row_of, int32_t* sched, const Launch& L) {
+  const int max_tiles = (int)sched_max_tiles((int64_t)T * k, E);
+  MOE_LAUNCH(L, permute_kernel, dim3(1), dim3(kThreads), 0, idx, T * k, E, off, sorted,
+                     row_of, sched, max_tiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_schedule_from_offsets(const int32_t* off, int E, int64_t slots, int32_t* sched,
+                                        const Launch& L) {
+  MOE_LAUNCH(L, schedule_kernel, dim3(1), dim3(256), 0, off, E, sched,
+                     (int)sched_max_tiles(slots, E));
+  return hipGetLastError();
+}
+
+}  // namespace moe
