@@ -64,6 +64,27 @@ class Hip:
         return out.value
 
 
+def counted_traffic(kernel: str, workload: str, gemm: bool):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (profiles/<workload>_gemv_hbm_counters.md), or None when there is
+    none or the kernel sources changed since the counters were taken."""
+    import hashlib
+    f = os.path.join(ROOT, "profiles", "%s_%s_hbm_counters.md" % (workload, "gemm" if gemm else "gemv"))
+    if not os.path.exists(f):
+        return None
+    kv = {}
+    for line in open(f):
+        if ":" in line and not line.startswith(("#", "|", "`")):
+            k_, v_ = line.split(":", 1)
+            kv[k_.strip()] = v_.strip()
+    h = hashlib.sha256()
+    for src in ("device.h", "kernels.h", "gemm.hip" if gemm else "gemv.hip"):
+        h.update(open(os.path.join(ROOT, "quantized_expert_mlp_amd", "csrc", src), "rb").read())
+    if kv.get("kernel") != kernel or kv.get("source_sha256") != h.hexdigest()[:16]:
+        return None
+    return int(kv["traffic_bytes_per_launch"])
+
+
 def touched_experts(logits: np.ndarray, k: int) -> int:
     """Distinct experts among the top-k picks of every row (byte accounting)."""
     picks = np.argpartition(-logits, k - 1, axis=1)[:, :k]
@@ -151,6 +172,8 @@ def main():
     ap.add_argument("--workload", default="decode", choices=list(S.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 256 MiB device-to-device copy (HBM counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -163,6 +186,16 @@ def main():
     import quantized_expert_mlp_amd as moe
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.calibrate_copy:
+        # A copy of known size: its FETCH_SIZE / WRITE_SIZE counters give the
+        # scale between counter readings and bytes moved.
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(max(1, args.steps)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copied %d x 256 MiB" % max(1, args.steps))
+        return
     moe.lib()
     hip = Hip()
     wl = S.WORKLOADS[args.workload]
@@ -242,7 +275,7 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
     roof["kernel"] = dom
-    roof["traffic"] = None
+    roof["traffic"] = counted_traffic(dom, wl.name, gemm)
     layer_bytes = sum(w_["bytes"] for w_ in work.values())
     layer_flops = sum(w_["flops"] for w_ in work.values())
     log("stage device time (us): " + ", ".join("%s %.2f" % (k_, v * 1e3)

@@ -38,6 +38,16 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Make LDS stores of some lanes of this wave visible to loads of other lanes
+// of the same wave (LDS operations of one wave execute in order; the fences
+// and the wave barrier keep the compiler from reordering or dropping the
+// cross-lane accesses).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // DPP lane permutations (gfx9 encodings) used by the reductions below.  All
 // of them stay inside a 16-lane DPP row, so every lane reads a live source.
 enum : int {

@@ -13,28 +13,31 @@
 // whole launch while the weight rows stream past with one 128-bit load per
 // group (16 bytes = 32 nibbles = one scale group).  A wave walks `nit` row
 // iterations in batches of RB rows held in two register sets: the loads of
-// the next batch are issued before the current batch is reduced, so every
-// wave keeps one to two batches of 16-byte loads in flight.  The grid is
-// sized so that about 4096 waves cover the whole launch, which amortises each
-// wave's serial prologue (bucket entry, token rows, activation registers).  The int4 -> bf16 decode and the exact dot products use
-// v_dot2_f32_bf16 (see device.h); each group's fp32 partial is scaled once;
-// the LPR-lane fold is a DPP add tree.  Gate/up rows are processed in pairs so
-// SiLU(g)*u is formed in registers; the down launch multiplies by the slot's
-// routing weight and adds into y with a hardware fp32 atomic.
+// the next batch are issued before the current batch is reduced, and a
+// wave's first batch is requested before its activation prologue.  When the
+// group count allows (G % 8 == 0) a batch's scales - contiguous in memory -
+// arrive as one 16-byte load per lane and are spread through a wave-private
+// LDS slot, instead of one 2-byte load per lane, row and group.
+//
+// Arithmetic: gate/up decodes nibbles to exact bf16 (128 + e) pairs and dots
+// them with the bf16 activations (v_dot2_f32_bf16, exact products); down
+// decodes to exact fp16 (1024 + e) pairs and dots them with the fp16 hidden
+// row (v_dot2_f32_f16).  A per-group constant removes the offset; each
+// group's fp32 partial is scaled once; the LPR-lane fold is a DPP add tree.
+// Gate/up rows are processed in pairs so SiLU(g)*u is formed in registers and
+// stored as fp16; the down launch multiplies by the slot's routing weight and
+// adds into y with a hardware fp32 atomic.
 #include "device.h"
 #include "kernels.h"
 #include "topk.h"
 
-// Tuning constants (compile-time): waves the row iterations are spread over,
-// the streaming-load hint, and the gate/up row batch at 3 groups per lane.
+// Tuning constants (compile-time): waves per token-register slot the row
+// iterations are spread over, and the streaming-load hint.
 #ifndef MOE_GEMV_WAVES
 #define MOE_GEMV_WAVES 2048
 #endif
 #ifndef MOE_GEMV_NT
 #define MOE_GEMV_NT 1
-#endif
-#ifndef MOE_GEMV_RB3
-#define MOE_GEMV_RB3 1
 #endif
 
 namespace moe {
@@ -53,31 +56,61 @@ __device__ __forceinline__ float half_bits_to_f32(uint32_t v) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)v);
 }
 
-// Re-pair one aligned block of 8 bf16 activations (natural pairs n0..n3 =
-// [x0,x1],[x2,x3],[x4,x5],[x6,x7]) into the operand order of q4_bf16_pairs
-// ([x0,x4],[x1,x5],[x2,x6],[x3,x7]) and return the block's contribution to
-// the offset correction, 136 * sum x.
-__device__ __forceinline__ float pair_block(uint32_t n0, uint32_t n1, uint32_t n2, uint32_t n3,
-                                            uint32_t* a) {
+// Re-pair one aligned block of 8 16-bit activations (natural pairs n0..n3 =
+// [x0,x1],[x2,x3],[x4,x5],[x6,x7]) into the operand order of the decode
+// ([x0,x4],[x1,x5],[x2,x6],[x3,x7]).
+__device__ __forceinline__ void pair_block(uint32_t n0, uint32_t n1, uint32_t n2, uint32_t n3,
+                                           uint32_t* a) {
   a[0] = (n0 & 0xFFFFu) | (n2 << 16);
   a[1] = (n0 >> 16) | (n2 & 0xFFFF0000u);
   a[2] = (n1 & 0xFFFFu) | (n3 << 16);
   a[3] = (n1 >> 16) | (n3 & 0xFFFF0000u);
-  const float sum = bf16_to_f32(n0 & 0xFFFF) + bf16_to_f32(n0 >> 16) + bf16_to_f32(n1 & 0xFFFF) +
-                    bf16_to_f32(n1 >> 16) + bf16_to_f32(n2 & 0xFFFF) + bf16_to_f32(n2 >> 16) +
-                    bf16_to_f32(n3 & 0xFFFF) + bf16_to_f32(n3 >> 16);
-  return 136.0f * sum;
 }
 
-// Dot of one 32-input group (4 packed words) with a paired activation group.
-__device__ __forceinline__ float dot_group(const Q4Pairs* p, const uint32_t* a) {
+__device__ __forceinline__ float sum8_bf16(uint32_t n0, uint32_t n1, uint32_t n2, uint32_t n3) {
+  return bf16_to_f32(n0 & 0xFFFF) + bf16_to_f32(n0 >> 16) + bf16_to_f32(n1 & 0xFFFF) +
+         bf16_to_f32(n1 >> 16) + bf16_to_f32(n2 & 0xFFFF) + bf16_to_f32(n2 >> 16) +
+         bf16_to_f32(n3 & 0xFFFF) + bf16_to_f32(n3 >> 16);
+}
+
+__device__ __forceinline__ float sum8_f16(uint32_t n0, uint32_t n1, uint32_t n2, uint32_t n3) {
+  return half_bits_to_f32(n0 & 0xFFFF) + half_bits_to_f32(n0 >> 16) +
+         half_bits_to_f32(n1 & 0xFFFF) + half_bits_to_f32(n1 >> 16) +
+         half_bits_to_f32(n2 & 0xFFFF) + half_bits_to_f32(n2 >> 16) +
+         half_bits_to_f32(n3 & 0xFFFF) + half_bits_to_f32(n3 >> 16);
+}
+
+__device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c,
+                                false);
+}
+
+// sum_i (128 + e_i) x_i over one 32-input group (4 packed words).
+__device__ __forceinline__ float dot_group_bf16(uint4 w, const uint32_t* a) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
   float s = 0.f;
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
-    s = dot2_bf16(p[d].p0, a[4 * d + 0], s);
-    s = dot2_bf16(p[d].p1, a[4 * d + 1], s);
-    s = dot2_bf16(p[d].p2, a[4 * d + 2], s);
-    s = dot2_bf16(p[d].p3, a[4 * d + 3], s);
+    const Q4Pairs p = q4_bf16_pairs(ws[d]);
+    s = dot2_bf16(p.p0, a[4 * d + 0], s);
+    s = dot2_bf16(p.p1, a[4 * d + 1], s);
+    s = dot2_bf16(p.p2, a[4 * d + 2], s);
+    s = dot2_bf16(p.p3, a[4 * d + 3], s);
+  }
+  return s;
+}
+
+// sum_i (1024 + e_i) h_i over one 32-input group (4 packed words).
+__device__ __forceinline__ float dot_group_f16(uint4 w, const uint32_t* a) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  float s = 0.f;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const Q4Pairs p = q4_pairs_with(ws[d], 0x64646464u);
+    s = dot2_f16(p.p0, a[4 * d + 0], s);
+    s = dot2_f16(p.p1, a[4 * d + 1], s);
+    s = dot2_f16(p.p2, a[4 * d + 2], s);
+    s = dot2_f16(p.p3, a[4 * d + 3], s);
   }
   return s;
 }
@@ -101,10 +134,6 @@ __device__ __forceinline__ bool bucket_of(const Buckets& b, BucketView* v) {
   v->r0 = t.y;
   v->M = t.z;
   return true;
-}
-
-__device__ __forceinline__ int token_of(const Buckets& b, int r) {
-  return b.shared_T > 0 ? r : b.sorted[r] / b.k;
 }
 
 // Bucket build of the fused small-batch routing (see RouteArgs), in LDS.
@@ -177,13 +206,54 @@ __device__ void small_route(const RouteArgs& ra, int k, SmallRoute& sr) {
   __syncthreads();
 }
 
+
+// One row batch's scales for P planes, staged through a wave-private LDS slot.
+// Rows n0 .. n0 + RB*RPI - 1 of a plane are contiguous (RB*RPI*G fp16 = at
+// most 512 bytes), so lane c < P * chunks loads 16-byte chunk c % chunks of
+// plane c / chunks.  Needs G % 8 == 0 (16-byte aligned chunk starts).  Lanes
+// read words other lanes wrote, so the staging is bracketed by wave-level
+// syncs (wave_lds_sync).
+template <int P, int RB, int RPI>
+struct ScaleStage {
+  static constexpr int kMaxPlaneBytes = 512;
+  uint4 v;
+  __device__ __forceinline__ void load(const uint16_t* const* sp, int n0, int N, int G) {
+    const int lane = threadIdx.x & 63;
+    const int pbytes = RB * RPI * G * 2, chunks = pbytes / 16;
+    const int p = lane / chunks, j = lane - p * chunks;
+    const int64_t at = (int64_t)n0 * G * 2 + 16 * j;
+    v = make_uint4(0, 0, 0, 0);
+    if (p < P && at + 16 <= (int64_t)N * G * 2)
+      v = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(sp[p]) + at);
+  }
+  // Publish this batch's chunks; the slot's previous contents (read by other
+  // lanes for the previous batch) are overwritten only after those reads.
+  __device__ __forceinline__ void stage(uint32_t* slot, int G) const {
+    const int lane = threadIdx.x & 63;
+    wave_lds_sync();
+    if (lane < P * (RB * RPI * G * 2 / 16)) {
+      slot[4 * lane + 0] = v.x;
+      slot[4 * lane + 1] = v.y;
+      slot[4 * lane + 2] = v.z;
+      slot[4 * lane + 3] = v.w;
+    }
+    wave_lds_sync();
+  }
+  // fp16 bits of the scale of (plane, row in batch, group).
+  static __device__ __forceinline__ uint32_t get(const uint32_t* slot, int p, int rr, int g,
+                                                 int G) {
+    const int i = p * (RB * RPI * G) + rr * G + g;
+    return (slot[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+  }
+};
+
 }  // namespace
 
-template <int LPR, int GPL, int MT, int RB, int ROUTE_V>
+template <int LPR, int GPL, int MT, int RB, int ROUTE_V, bool SLDS>
 __global__ __launch_bounds__(256) void gemv_gate_up_kernel(
     Buckets b, const uint16_t* __restrict__ x, int H, int I, const uint8_t* __restrict__ gq,
     const uint16_t* __restrict__ gs, const uint8_t* __restrict__ uq,
-    const uint16_t* __restrict__ us, float* __restrict__ h, float* __restrict__ y_zero,
+    const uint16_t* __restrict__ us, uint16_t* __restrict__ h, float* __restrict__ y_zero,
     int64_t y_elems, int nit, RouteArgs ra) {
   if (y_zero) {
     const int64_t nthr = (int64_t)gridDim.x * gridDim.y * blockDim.x;
@@ -193,6 +263,7 @@ __global__ __launch_bounds__(256) void gemv_gate_up_kernel(
   }
   // ROUTE_V > 0: routing folded in (ROUTE_V logit registers per lane).
   __shared__ SmallRoute sr;
+  __shared__ uint32_t sslot[4][ScaleStage<2, RB, 64 / LPR>::kMaxPlaneBytes * 2 / 4];
   BucketView bv;
   const int32_t* rows_sorted = b.sorted;
   if constexpr (ROUTE_V > 0) {
@@ -215,19 +286,22 @@ __global__ __launch_bounds__(256) void gemv_gate_up_kernel(
   const int64_t pb = (int64_t)I * (H / 2), sb = (int64_t)I * G;
   const uint8_t* gqe = gq + bv.e * pb;
   const uint8_t* uqe = uq + bv.e * pb;
-  const uint16_t* gse = gs + bv.e * sb;
-  const uint16_t* use = us + bv.e * sb;
-  const int row0 = (blockIdx.x * 4 + wave) * (nit * RPI) + rl;
+  const uint16_t* spl[2] = {gs + bv.e * sb, us + bv.e * sb};
+  const int rbase = (blockIdx.x * 4 + wave) * (nit * RPI);  // first row of the wave
+  const int row0 = rbase + rl;
+  uint32_t* slot = sslot[wave];
+  using SS = ScaleStage<2, RB, RPI>;
 
   for (int m0 = 0; m0 < bv.M; m0 += MT) {
     const int nt = min(MT, bv.M - m0);
-    // Row batches of RB rows, ping-ponged between two register sets so the
-    // loads of the next batch are in flight while this one is reduced.
+    // Row batches of RB rows, ping-ponged between two register sets.
     struct Batch {
       uint4 g[RB][GPL], u[RB][GPL];
-      uint32_t sg[RB][GPL], su[RB][GPL];  // fp16 bits, widened (keeps the batch in VGPRs)
+      uint32_t sg[RB][GPL], su[RB][GPL];  // per-lane scales (fp16 bits) when !SLDS
+      SS sc;                              // staged scales when SLDS
     };
     auto load = [&](Batch& bt, int i0) {
+      if constexpr (SLDS) bt.sc.load(spl, rbase + i0 * RPI, I, G);
 #pragma unroll
       for (int r = 0; r < RB; ++r) {
         const int n = row0 + (i0 + r) * RPI;
@@ -237,17 +311,20 @@ __global__ __launch_bounds__(256) void gemv_gate_up_kernel(
           if (n < I && g < G) {
             bt.g[r][gi] = load_w16(gqe + (int64_t)n * (H / 2) + 16 * g);
             bt.u[r][gi] = load_w16(uqe + (int64_t)n * (H / 2) + 16 * g);
-            bt.sg[r][gi] = gse[(int64_t)n * G + g];
-            bt.su[r][gi] = use[(int64_t)n * G + g];
+            if constexpr (!SLDS) {
+              bt.sg[r][gi] = spl[0][(int64_t)n * G + g];
+              bt.su[r][gi] = spl[1][(int64_t)n * G + g];
+            }
           } else {
             bt.g[r][gi] = bt.u[r][gi] = make_uint4(0, 0, 0, 0);
-            bt.sg[r][gi] = bt.su[r][gi] = 0;
+            if constexpr (!SLDS) bt.sg[r][gi] = bt.su[r][gi] = 0;
           }
         }
       }
     };
     Batch A, B;
     load(A, 0);  // weights first: they do not wait for the activation prologue
+
     uint32_t xa[MT][GPL][16];
     float corr[MT][GPL];
 #pragma unroll
@@ -268,16 +345,19 @@ __global__ __launch_bounds__(256) void gemv_gate_up_kernel(
 #pragma unroll
           for (int c = 0; c < 16; ++c) nat[c] = 0;
         }
-        float cr = 0.f;
+        float sum = 0.f;
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk)
-          cr += pair_block(nat[4 * blk], nat[4 * blk + 1], nat[4 * blk + 2], nat[4 * blk + 3],
-                           &xa[t][gi][4 * blk]);
-        corr[t][gi] = cr;
+        for (int blk = 0; blk < 4; ++blk) {
+          pair_block(nat[4 * blk], nat[4 * blk + 1], nat[4 * blk + 2], nat[4 * blk + 3],
+                     &xa[t][gi][4 * blk]);
+          sum += sum8_bf16(nat[4 * blk], nat[4 * blk + 1], nat[4 * blk + 2], nat[4 * blk + 3]);
+        }
+        corr[t][gi] = 136.0f * sum;
       }
     }
 
     auto compute = [&](const Batch& bt, int i0) {
+      if constexpr (SLDS) bt.sc.stage(slot, G);
 #pragma unroll
       for (int r = 0; r < RB; ++r) {
         const int n = row0 + (i0 + r) * RPI;
@@ -286,16 +366,22 @@ __global__ __launch_bounds__(256) void gemv_gate_up_kernel(
         for (int t = 0; t < MT; ++t) ag[t] = au[t] = 0.f;
 #pragma unroll
         for (int gi = 0; gi < GPL; ++gi) {
-          const float fsg = half_bits_to_f32(bt.sg[r][gi]), fsu = half_bits_to_f32(bt.su[r][gi]);
-          const Q4Pairs pg[4] = {q4_bf16_pairs(bt.g[r][gi].x), q4_bf16_pairs(bt.g[r][gi].y),
-                                 q4_bf16_pairs(bt.g[r][gi].z), q4_bf16_pairs(bt.g[r][gi].w)};
-          const Q4Pairs pu[4] = {q4_bf16_pairs(bt.u[r][gi].x), q4_bf16_pairs(bt.u[r][gi].y),
-                                 q4_bf16_pairs(bt.u[r][gi].z), q4_bf16_pairs(bt.u[r][gi].w)};
+          const int g = kl + gi * LPR;
+          uint32_t sgb, sub;
+          if constexpr (SLDS) {
+            const int gg = g < G ? g : 0;
+            sgb = SS::get(slot, 0, r * RPI + rl, gg, G);
+            sub = SS::get(slot, 1, r * RPI + rl, gg, G);
+          } else {
+            sgb = bt.sg[r][gi];
+            sub = bt.su[r][gi];
+          }
+          const float fsg = half_bits_to_f32(sgb), fsu = half_bits_to_f32(sub);
 #pragma unroll
           for (int t = 0; t < MT; ++t) {
             if (t < nt) {
-              ag[t] += fsg * (dot_group(pg, xa[t][gi]) - corr[t][gi]);
-              au[t] += fsu * (dot_group(pu, xa[t][gi]) - corr[t][gi]);
+              ag[t] += fsg * (dot_group_bf16(bt.g[r][gi], xa[t][gi]) - corr[t][gi]);
+              au[t] += fsu * (dot_group_bf16(bt.u[r][gi], xa[t][gi]) - corr[t][gi]);
             }
           }
         }
@@ -304,8 +390,10 @@ __global__ __launch_bounds__(256) void gemv_gate_up_kernel(
           if (t < nt) {
             const float gsum = group_sum<LPR>(ag[t]);
             const float usum = group_sum<LPR>(au[t]);
-            if (kl == LPR - 1 && n < I)
-              h[(int64_t)(bv.r0 + m0 + t) * I + n] = gsum / (1.0f + __expf(-gsum)) * usum;
+            if (kl == LPR - 1 && n < I) {
+              const _Float16 hv = (_Float16)(gsum / (1.0f + __expf(-gsum)) * usum);
+              h[(int64_t)(bv.r0 + m0 + t) * I + n] = __builtin_bit_cast(uint16_t, hv);
+            }
           }
         }
       }
@@ -324,11 +412,12 @@ __global__ __launch_bounds__(256) void gemv_gate_up_kernel(
   }
 }
 
-template <int LPR, int GPL, int MT, int RB>
+template <int LPR, int GPL, int MT, int RB, bool SLDS>
 __global__ __launch_bounds__(256) void gemv_down_kernel(
-    Buckets b, const float* __restrict__ h, int H, int I, const uint8_t* __restrict__ dq,
+    Buckets b, const uint16_t* __restrict__ h, int H, int I, const uint8_t* __restrict__ dq,
     const uint16_t* __restrict__ ds, const float* __restrict__ w,
     const float* __restrict__ gate_logit, int gate_ld, float* __restrict__ y, int nit) {
+  __shared__ uint32_t sslot[4][ScaleStage<1, RB, 64 / LPR>::kMaxPlaneBytes / 4];
   BucketView bv;
   if (!bucket_of(b, &bv)) return;
 
@@ -338,16 +427,21 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(
   const int G = I / 32;
   const int64_t pb = (int64_t)H * (I / 2), sb = (int64_t)H * G;
   const uint8_t* dqe = dq + bv.e * pb;
-  const uint16_t* dse = ds + bv.e * sb;
-  const int row0 = (blockIdx.x * 4 + wave) * (nit * RPI) + rl;
+  const uint16_t* spl[1] = {ds + bv.e * sb};
+  const int rbase = (blockIdx.x * 4 + wave) * (nit * RPI);
+  const int row0 = rbase + rl;
+  uint32_t* slot = sslot[wave];
+  using SS = ScaleStage<1, RB, RPI>;
 
   for (int m0 = 0; m0 < bv.M; m0 += MT) {
     const int nt = min(MT, bv.M - m0);
     struct Batch {
       uint4 d[RB][GPL];
-      uint32_t sd[RB][GPL];  // fp16 bits, widened
+      uint32_t sd[RB][GPL];  // per-lane scales (fp16 bits) when !SLDS
+      SS sc;
     };
     auto load = [&](Batch& bt, int i0) {
+      if constexpr (SLDS) bt.sc.load(spl, rbase + i0 * RPI, H, G);
 #pragma unroll
       for (int r = 0; r < RB; ++r) {
         const int n = row0 + (i0 + r) * RPI;
@@ -356,17 +450,18 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(
           const int g = kl + gi * LPR;
           if (n < H && g < G) {
             bt.d[r][gi] = load_w16(dqe + (int64_t)n * (I / 2) + 16 * g);
-            bt.sd[r][gi] = dse[(int64_t)n * G + g];
+            if constexpr (!SLDS) bt.sd[r][gi] = spl[0][(int64_t)n * G + g];
           } else {
             bt.d[r][gi] = make_uint4(0, 0, 0, 0);
-            bt.sd[r][gi] = 0;
+            if constexpr (!SLDS) bt.sd[r][gi] = 0;
           }
         }
       }
     };
     Batch A, B;
     load(A, 0);  // weights first: they do not wait for the activation prologue
-    uint32_t xh[MT][GPL][16], xl[MT][GPL][16];
+
+    uint32_t xa[MT][GPL][16];
     float corr[MT][GPL], wt[MT];
     int tok[MT];
 #pragma unroll
@@ -380,45 +475,35 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(
         tok[t] = s / b.k;
         wt[t] = w[s];
       }
-      const float* hr = h + (int64_t)r * I;
+      const uint16_t* hr = h + (int64_t)r * I;
 #pragma unroll
       for (int gi = 0; gi < GPL; ++gi) {
         const int g = kl + gi * LPR;
-        float v[32];
+        uint32_t nat[16];
         if (t < nt && g < G) {
-          const float4* src = reinterpret_cast<const float4*>(hr + 32 * g);
+          const uint4* src = reinterpret_cast<const uint4*>(hr + 32 * g);
 #pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            const float4 q = src[c];
-            v[4 * c] = q.x; v[4 * c + 1] = q.y; v[4 * c + 2] = q.z; v[4 * c + 3] = q.w;
+          for (int c = 0; c < 4; ++c) {
+            const uint4 v = src[c];
+            nat[4 * c] = v.x; nat[4 * c + 1] = v.y; nat[4 * c + 2] = v.z; nat[4 * c + 3] = v.w;
           }
         } else {
 #pragma unroll
-          for (int c = 0; c < 32; ++c) v[c] = 0.f;
+          for (int c = 0; c < 16; ++c) nat[c] = 0;
         }
-        // h = hi + lo with hi, lo bf16: hi + lo carries ~16 significant bits.
-        uint32_t hi[16], lo[16];
-#pragma unroll
-        for (int c = 0; c < 16; ++c) {
-          const uint32_t h0 = f32_to_bf16_rne(v[2 * c]), h1 = f32_to_bf16_rne(v[2 * c + 1]);
-          const uint32_t l0 = f32_to_bf16_rne(v[2 * c] - bf16_to_f32(h0));
-          const uint32_t l1 = f32_to_bf16_rne(v[2 * c + 1] - bf16_to_f32(h1));
-          hi[c] = pack2(h0, h1);
-          lo[c] = pack2(l0, l1);
-        }
-        float cr = 0.f;
+        float sum = 0.f;
 #pragma unroll
         for (int blk = 0; blk < 4; ++blk) {
-          cr += pair_block(hi[4 * blk], hi[4 * blk + 1], hi[4 * blk + 2], hi[4 * blk + 3],
-                           &xh[t][gi][4 * blk]);
-          cr += pair_block(lo[4 * blk], lo[4 * blk + 1], lo[4 * blk + 2], lo[4 * blk + 3],
-                           &xl[t][gi][4 * blk]);
+          pair_block(nat[4 * blk], nat[4 * blk + 1], nat[4 * blk + 2], nat[4 * blk + 3],
+                     &xa[t][gi][4 * blk]);
+          sum += sum8_f16(nat[4 * blk], nat[4 * blk + 1], nat[4 * blk + 2], nat[4 * blk + 3]);
         }
-        corr[t][gi] = cr;
+        corr[t][gi] = 1032.0f * sum;
       }
     }
 
     auto compute = [&](const Batch& bt, int i0) {
+      if constexpr (SLDS) bt.sc.stage(slot, G);
 #pragma unroll
       for (int r = 0; r < RB; ++r) {
         const int n = row0 + (i0 + r) * RPI;
@@ -427,13 +512,14 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(
         for (int t = 0; t < MT; ++t) acc[t] = 0.f;
 #pragma unroll
         for (int gi = 0; gi < GPL; ++gi) {
-          const float fsd = half_bits_to_f32(bt.sd[r][gi]);
-          const Q4Pairs pd[4] = {q4_bf16_pairs(bt.d[r][gi].x), q4_bf16_pairs(bt.d[r][gi].y),
-                                 q4_bf16_pairs(bt.d[r][gi].z), q4_bf16_pairs(bt.d[r][gi].w)};
+          const int g = kl + gi * LPR;
+          uint32_t sdb;
+          if constexpr (SLDS) sdb = SS::get(slot, 0, r * RPI + rl, g < G ? g : 0, G);
+          else sdb = bt.sd[r][gi];
+          const float fsd = half_bits_to_f32(sdb);
 #pragma unroll
           for (int t = 0; t < MT; ++t)
-            if (t < nt)
-              acc[t] += fsd * (dot_group(pd, xh[t][gi]) + dot_group(pd, xl[t][gi]) - corr[t][gi]);
+            if (t < nt) acc[t] += fsd * (dot_group_f16(bt.d[r][gi], xa[t][gi]) - corr[t][gi]);
         }
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
@@ -482,16 +568,16 @@ int pow2_floor_min(int v, int cap) {
   return r;
 }
 
-// Rows per load batch: 4 (down) or 2 (gate/up pairs) 16-byte loads per group
-// column; two batches are in flight per wave.
-constexpr int rb_for_gate_up(int gpl) { return gpl == 1 ? 4 : gpl == 2 ? 2 : MOE_GEMV_RB3; }
-constexpr int rb_for_down(int gpl) { return gpl == 1 ? 4 : gpl == 2 ? 2 : 1; }
+// Rows per load batch (two batches are in flight per wave).
+constexpr int rb_for(int gpl) { return gpl == 1 ? 4 : gpl == 2 ? 2 : 1; }
 
-// Row iterations per wave: enough waves to fill the chip about twice
-// (256 CUs x 8 waves), every wave streaming a multiple of its batch.
-int rows_per_wave(int N, int rpi, int buckets, int rb) {
+// Row iterations per wave: the launch is spread over about MOE_GEMV_WAVES
+// waves per token held in registers (more tokens, more VALU per byte, more
+// waves), every wave streaming a multiple of its batch.
+int rows_per_wave(int N, int rpi, int buckets, int rb, int mt) {
   const int64_t row_iters = (int64_t)((N + rpi - 1) / rpi) * buckets;
-  int64_t nit = (row_iters + MOE_GEMV_WAVES - 1) / MOE_GEMV_WAVES;
+  const int64_t waves = (int64_t)MOE_GEMV_WAVES * mt;
+  int64_t nit = (row_iters + waves - 1) / waves;
   nit = (nit + rb - 1) / rb * rb;
   if (nit < rb) nit = rb;
   if (nit > 64) nit = 64;
@@ -507,8 +593,9 @@ bool gemv_supported(int K) { return K % 32 == 0 && K / 32 <= 4 * 64; }
 
 hipError_t launch_gemv_gate_up(const Buckets& b, int max_buckets, const uint16_t* x, int H,
                                int I, const uint8_t* gq, const uint16_t* gs,
-                               const uint8_t* uq, const uint16_t* us, float* h, float* y_zero,
-                               int64_t y_elems, const Launch& L, const RouteArgs* route) {
+                               const uint8_t* uq, const uint16_t* us, uint16_t* h,
+                               float* y_zero, int64_t y_elems, const Launch& L,
+                               const RouteArgs* route) {
   const GemvShape sh = pick_shape(H);
   RouteArgs ra{};
   int rv = 0;  // logit registers per lane of the folded routing (0 = routing done earlier)
@@ -520,34 +607,41 @@ hipError_t launch_gemv_gate_up(const Buckets& b, int max_buckets, const uint16_t
   }
   const int mt = pow2_floor_min(b.max_rows, sh.gpl == 1 ? 4 : 2);
   const int buckets = b.shared_T > 0 ? 1 : max_buckets;
-  const int nit = rows_per_wave(I, 64 / sh.lpr, buckets, rb_for_gate_up(sh.gpl));
+  const int nit = rows_per_wave(I, 64 / sh.lpr, buckets, rb_for(sh.gpl), mt);
   const int rpb = 4 * nit * (64 / sh.lpr);
+  const bool slds = (H / 32) % 8 == 0;
   dim3 grid((I + rpb - 1) / rpb, buckets);
-#define GU(LP, GP, MTv, RV)                                                                        \
-  MOE_LAUNCH(L, (gemv_gate_up_kernel<LP, GP, MTv, rb_for_gate_up(GP), RV>), grid, dim3(256), 0, b, \
-             x, H, I, gq, gs, uq, us, h, y_zero, y_elems, nit, ra)
-#define X(LP, GP)                                                                                  \
-  if (sh.lpr == LP && sh.gpl == GP) {                                                              \
-    if (rv > 0) {                                                                                  \
-      switch (rv * 8 + mt) {                                                                       \
-        case 9: GU(LP, GP, 1, 1); break;                                                           \
-        case 10: GU(LP, GP, 2, 1); break;                                                          \
-        case 17: GU(LP, GP, 1, 2); break;                                                          \
-        case 18: GU(LP, GP, 2, 2); break;                                                          \
-        case 25: GU(LP, GP, 1, 3); break;                                                          \
-        case 26: GU(LP, GP, 2, 3); break;                                                          \
-        case 33: GU(LP, GP, 1, 4); break;                                                          \
-        case 34: GU(LP, GP, 2, 4); break;                                                          \
-        default: if (GP == 1 && mt == 4) GU(LP, 1, 4, 4); else return hipErrorInvalidValue;       \
-      }                                                                                            \
-    } else {                                                                                       \
-      switch (mt) {                                                                                \
-        case 1: GU(LP, GP, 1, 0); break;                                                           \
-        case 2: GU(LP, GP, 2, 0); break;                                                           \
-        default: if (GP == 1) GU(LP, 1, 4, 0); break;                                              \
-      }                                                                                            \
-    }                                                                                              \
-    return hipGetLastError();                                                                      \
+#define GU(LP, GP, MTv, RV)                                                                      \
+  do {                                                                                           \
+    if (slds)                                                                                    \
+      MOE_LAUNCH(L, (gemv_gate_up_kernel<LP, GP, MTv, rb_for(GP), RV, true>), grid, dim3(256),   \
+                 0, b, x, H, I, gq, gs, uq, us, h, y_zero, y_elems, nit, ra);                    \
+    else                                                                                         \
+      MOE_LAUNCH(L, (gemv_gate_up_kernel<LP, GP, MTv, rb_for(GP), RV, false>), grid, dim3(256),  \
+                 0, b, x, H, I, gq, gs, uq, us, h, y_zero, y_elems, nit, ra);                    \
+  } while (0)
+#define X(LP, GP)                                                                                \
+  if (sh.lpr == LP && sh.gpl == GP) {                                                            \
+    if (rv > 0) {                                                                                \
+      switch (rv * 8 + mt) {                                                                     \
+        case 9: GU(LP, GP, 1, 1); break;                                                         \
+        case 10: GU(LP, GP, 2, 1); break;                                                        \
+        case 17: GU(LP, GP, 1, 2); break;                                                        \
+        case 18: GU(LP, GP, 2, 2); break;                                                        \
+        case 25: GU(LP, GP, 1, 3); break;                                                        \
+        case 26: GU(LP, GP, 2, 3); break;                                                        \
+        case 33: GU(LP, GP, 1, 4); break;                                                        \
+        case 34: GU(LP, GP, 2, 4); break;                                                        \
+        default: if (GP == 1 && mt == 4) GU(LP, 1, 4, 4); else return hipErrorInvalidValue;     \
+      }                                                                                          \
+    } else {                                                                                     \
+      switch (mt) {                                                                              \
+        case 1: GU(LP, GP, 1, 0); break;                                                         \
+        case 2: GU(LP, GP, 2, 0); break;                                                         \
+        default: if (GP == 1) GU(LP, 1, 4, 0); break;                                            \
+      }                                                                                          \
+    }                                                                                            \
+    return hipGetLastError();                                                                    \
   }
   MOE_GEMV_CASES(X)
 #undef X
@@ -555,26 +649,37 @@ hipError_t launch_gemv_gate_up(const Buckets& b, int max_buckets, const uint16_t
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_gemv_down(const Buckets& b, int max_buckets, const float* h, int H, int I,
+hipError_t launch_gemv_down(const Buckets& b, int max_buckets, const uint16_t* h, int H, int I,
                             const uint8_t* dq, const uint16_t* ds, const float* w,
                             const float* gate_logit, int gate_ld, float* y, const Launch& L) {
   const GemvShape sh = pick_shape(I);
-  const int mt = pow2_floor_min(b.max_rows, sh.gpl == 1 ? 2 : 1);
+  const int mt = pow2_floor_min(b.max_rows, sh.gpl == 1 ? 4 : sh.gpl == 2 ? 2 : 1);
   const int buckets = b.shared_T > 0 ? 1 : max_buckets;
-  const int nit = rows_per_wave(H, 64 / sh.lpr, buckets, rb_for_down(sh.gpl));
+  const int nit = rows_per_wave(H, 64 / sh.lpr, buckets, rb_for(sh.gpl), mt);
   const int rpb = 4 * nit * (64 / sh.lpr);
+  const bool slds = (I / 32) % 8 == 0;
   dim3 grid((H + rpb - 1) / rpb, buckets);
-#define X(LP, GP)                                                                                  \
-  if (sh.lpr == LP && sh.gpl == GP) {                                                              \
-    constexpr int RBv = rb_for_down(GP);                                                           \
-    switch (mt) {                                                                                  \
-      case 1: MOE_LAUNCH(L, (gemv_down_kernel<LP, GP, 1, RBv>), grid, dim3(256), 0, b, h, H, I, dq, ds, w, gate_logit, gate_ld, y, nit); break; \
-      default: if (GP == 1) MOE_LAUNCH(L, (gemv_down_kernel<LP, 1, 2, RBv>), grid, dim3(256), 0, b, h, H, I, dq, ds, w, gate_logit, gate_ld, y, nit); break; \
-    }                                                                                              \
-    return hipGetLastError();                                                                      \
+#define DN(LP, GP, MTv)                                                                          \
+  do {                                                                                           \
+    if (slds)                                                                                    \
+      MOE_LAUNCH(L, (gemv_down_kernel<LP, GP, MTv, rb_for(GP), true>), grid, dim3(256), 0, b, h, \
+                 H, I, dq, ds, w, gate_logit, gate_ld, y, nit);                                  \
+    else                                                                                         \
+      MOE_LAUNCH(L, (gemv_down_kernel<LP, GP, MTv, rb_for(GP), false>), grid, dim3(256), 0, b,   \
+                 h, H, I, dq, ds, w, gate_logit, gate_ld, y, nit);                               \
+  } while (0)
+#define X(LP, GP)                                                                                \
+  if (sh.lpr == LP && sh.gpl == GP) {                                                            \
+    switch (mt) {                                                                                \
+      case 1: DN(LP, GP, 1); break;                                                              \
+      case 2: if (GP <= 2) DN(LP, (GP <= 2 ? GP : 1), 2); break;                                 \
+      default: if (GP == 1) DN(LP, 1, 4); break;                                                 \
+    }                                                                                            \
+    return hipGetLastError();                                                                    \
   }
   MOE_GEMV_CASES(X)
 #undef X
+#undef DN
   return hipErrorInvalidValue;
 }
 

@@ -60,8 +60,10 @@ hipError_t launch_router_logits(const uint16_t* x, const float* wr, const float*
 hipError_t launch_topk(const float* logits, int ld, int T, int E, int k, float route_scale,
                        int32_t* idx, float* w, const Launch& L);
 
-// Fused top-k + permutation in one workgroup, for up to kRouteMaxSlots slots.
+// Fused top-k + permutation in one workgroup, for up to kRouteMaxSlots slots
+// and kRouteMaxT tokens (4 tokens per wave of the 16).
 constexpr int kRouteMaxSlots = 4096;
+constexpr int kRouteMaxT = 64;
 hipError_t launch_route(const float* logits, int ld, int T, int E, int k, float route_scale,
                         int32_t* idx, float* w, int32_t* off, int32_t* sorted, int32_t* row_of,
                         int32_t* sched, const Launch& L);
@@ -91,14 +93,14 @@ struct RouteArgs {
   int32_t* sched;   // schedule words
 };
 
-// Streaming int4 GEMV (decode).  gate/up: h[row][I] = silu(Wg x)*(Wu x) in fp32;
+// Streaming int4 GEMV (decode).  gate/up: h[row][I] = fp16(silu(Wg x)*(Wu x));
 // down: y[token] += weight * (Wd h[row]).  The gate/up launch also zeroes y.
 hipError_t launch_gemv_gate_up(const Buckets& b, int max_buckets, const uint16_t* x, int H,
                                int I, const uint8_t* gq, const uint16_t* gs,
-                               const uint8_t* uq, const uint16_t* us, float* h, float* y_zero,
-                               int64_t y_elems, const Launch& L,
+                               const uint8_t* uq, const uint16_t* us, uint16_t* h,
+                               float* y_zero, int64_t y_elems, const Launch& L,
                                const RouteArgs* route = nullptr);
-hipError_t launch_gemv_down(const Buckets& b, int max_buckets, const float* h, int H, int I,
+hipError_t launch_gemv_down(const Buckets& b, int max_buckets, const uint16_t* h, int H, int I,
                             const uint8_t* dq, const uint16_t* ds, const float* w,
                             const float* gate_logit, int gate_ld, float* y, const Launch& L);
 bool gemv_supported(int K);

@@ -76,7 +76,7 @@ Layout make_layout(const moe_shape* sh, bool gemm) {
   L.sorted = take(sizeof(int32_t) * slots);
   L.row_of = take(sizeof(int32_t) * slots);
   L.sched = take(sizeof(int32_t) * moe::sched_words(slots, (int)E));
-  const size_t act = gemm ? 2 : 4;  // fp16 activations on the MFMA path, fp32 on the GEMV path
+  const size_t act = 2;  // hidden rows are fp16 on both paths
   L.x16 = take(gemm ? sizeof(uint16_t) * T * sh->H : 0);
   L.h = take(act * slots * sh->I);
   L.hs = take(act * T * sh->SI);
@@ -129,8 +129,8 @@ int run_mlp(const moe_shape* sh, bool gemm, const Layout& L, void* ws, const uin
   const int64_t y_elems = (int64_t)T * H;
   hipError_t err;
   if (!gemm) {
-    float* h = at<float>(ws, L.h);
-    float* hs = at<float>(ws, L.hs);
+    uint16_t* h = at<uint16_t>(ws, L.h);
+    uint16_t* hs = at<uint16_t>(ws, L.hs);
     const int max_buckets = (int)(slots < E ? slots : E);
     if (!sg.skip(MOE_STAGE_ACTIVATIONS)) return MOE_ERR_HIP;
     err = moe::launch_gemv_gate_up(routed, max_buckets, x, H, I, gate.q, gate.s, up.q, up.s, h, y,
@@ -329,7 +329,7 @@ static int layer_impl(const moe_shape* sh, const uint16_t* x, const float* logit
                     at<int32_t>(ws, L.row_of), at<int32_t>(ws, L.sched)};
   if (fold) {
     if (!sg.skip(MOE_STAGE_TOPK) || !sg.skip(MOE_STAGE_PERMUTE)) return MOE_ERR_HIP;
-  } else if ((int64_t)T * k <= moe::kRouteMaxSlots) {
+  } else if ((int64_t)T * k <= moe::kRouteMaxSlots && T <= moe::kRouteMaxT) {
     if (moe::launch_route(Lp, ldL, T, E, k, sh->route_scale, idx, w, off, sorted,
                           at<int32_t>(ws, L.row_of), at<int32_t>(ws, L.sched),
                           sg.at(MOE_STAGE_TOPK)) != hipSuccess ||
