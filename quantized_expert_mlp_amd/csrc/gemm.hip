@@ -8,12 +8,13 @@
 // sigmoid of its gate logit) and the colibri PR #418 int4 format (nibble - 8,
 // one fp16 scale per 32 inputs).
 //
-// gfx950 design.  A workgroup (4 waves) owns one row tile of up to 128 bucket
-// rows and a block of output columns; waves split the columns, so each wave
-// decodes its own weight fragment straight from a 128-bit global load into
-// MFMA operand registers (no LDS round trip for weights), while the activation
-// tile - shared by the four waves - is staged through LDS, double-buffered,
-// one barrier per 64-deep K step.  The MFMA is v_mfma_f32_32x32x16_f16:
+// gfx950 design.  A workgroup of kWaves waves (one per SIMD; two workgroups
+// share a CU) owns one row tile of up to 128 bucket rows and a block of output columns.  Waves
+// split the columns, so each wave decodes its own weight fragment straight
+// from a 128-bit global load into MFMA operand registers (no LDS round trip
+// for weights), while the activation tile - shared by all the waves - is
+// staged through LDS, double-buffered, one barrier per 64-deep K step.  The
+// MFMA is v_mfma_f32_32x32x16_f16:
 //   A (32 rows x 16 k)  lane l: row l%32, k 8*(l/32)..+7  (activations)
 //   B (16 k x 32 cols)  lane l: col l%32, k 8*(l/32)..+7  (weights)
 //   D (32 x 32, fp32)   lane l: col l%32, rows 8*(v/4) + 4*(l/32) + v%4.
@@ -27,21 +28,63 @@
 // bytes of scale group 2*step + hf of weight row j; packed word d of it feeds
 // MFMA d.  MFMA d therefore contracts k = 32*hf + 8*d + {0..7}: its A operand
 // is the 16 bytes at k offset 32*hf + 8*d of the LDS activation row.
+//
+// The down pass may split K over blockIdx.z: its epilogue already adds into
+// y with atomics, so partial sums over K ranges combine the same way.
 #include "device.h"
 #include "kernels.h"
+
+#ifndef MOE_GEMM_DA
+#define MOE_GEMM_DA 2  // activation register stages (prefetch distance in K steps)
+#endif
+#ifndef MOE_GEMM_DB
+#define MOE_GEMM_DB 2  // weight register stages
+#endif
+#ifndef MOE_GEMM_OCC
+#define MOE_GEMM_OCC 2  // workgroups per CU
+#endif
+#ifndef MOE_GEMM_GU_NS
+#define MOE_GEMM_GU_NS 1  // 32-column subtiles per wave, gate/up pass
+#endif
+#ifndef MOE_GEMM_DN_NS
+#define MOE_GEMM_DN_NS 2  // 32-column subtiles per wave, down pass
+#endif
+#ifndef MOE_GEMM_WAVES
+#define MOE_GEMM_WAVES 4  // waves per workgroup (column groups)
+#endif
+
+#include <algorithm>
+#include <utility>
 
 namespace moe {
 
 namespace {
 
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>), unrolled.
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+constexpr int gcd_c(int x, int y) { return y == 0 ? x : gcd_c(y, x % y); }
+constexpr int lcm_c(int x, int y) { return x / gcd_c(x, y) * y; }
+
 constexpr int kBM = kGemmTileRows;    // 128 rows per tile
 constexpr int kKS = 64;               // K per step
 constexpr int kPitch = kKS * 2 + 16;  // LDS row pitch in bytes (padding breaks bank conflicts)
+constexpr int kWaves = MOE_GEMM_WAVES;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kChunkRows = kThreads / 8;  // activation rows one pass of the workgroup stages
 
 struct TileView {
   int e, row0, nrows;
 };
 
+// Tile of this workgroup: blockIdx.y indexes the tile list (or, for the
+// shared expert, consecutive 128-row tiles of all tokens).
 __device__ __forceinline__ bool tile_of(const Buckets& b, TileView* v) {
   const int u = blockIdx.y;
   if (b.shared_T > 0) {
@@ -61,107 +104,108 @@ __device__ __forceinline__ bool tile_of(const Buckets& b, TileView* v) {
 // Row-major fp16 position of logical column j in the permuted-by-8 layout.
 __device__ __forceinline__ int perm_col(int j) { return (j & ~7) | perm8_pos(j & 7); }
 
-// Stage one 128 x 64 fp16 activation tile (K step ks) into LDS.  Thread t
-// copies 64 bytes: row t/2, half t%2.  Rows past the tile are zero.
-struct AStage {
-  uint4 v[4];
+// Raw weight operands of one K step for one lane: the 16 bytes of scale
+// group 2*step + hf of each (subtile, plane) weight row, and its fp16 scale.
+template <int P, int NS>
+struct BStage {
+  u32x4_t q[NS][P];
+  uint32_t s[NS][P];
 };
 
-__device__ __forceinline__ void a_load(AStage& s, const uint16_t* const* rowp, int K, int ks) {
-  const int half = threadIdx.x & 1;
-  const uint16_t* p = rowp[threadIdx.x >> 1];
-  if (p) {
-    const uint4* src = reinterpret_cast<const uint4*>(p + (int64_t)ks * kKS + half * 32);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) s.v[c] = src[c];
-  } else {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) s.v[c] = make_uint4(0, 0, 0, 0);
-  }
-  (void)K;
+// Activation operands of one K step as loaded by one thread: NA 16-byte
+// chunks; chunk i is row (tid/8) + kChunkRows*i, bytes 16*(tid%8) of the step.
+template <int NA>
+struct AStage {
+  u32x4_t v[NA];
+};
+
+struct GemmArgs {
+  const uint16_t* act;  // fp16 activations (perm-by-8 order), row stride K
+  int K, N;             // contraction depth and output columns of one plane
+  const uint8_t* q[2];  // weight planes: [E][N][K/2] nibbles
+  const uint16_t* s[2]; // and their [E][N][K/32] fp16 scales
+  uint16_t* hout;       // MODE 0 output, row stride ldh
+  int ldh;
+  const float* w;       // MODE 1 combine weights per slot
+  const float* gate_logit;
+  int gate_ld;
+  float* y;             // MODE 1 output [T][H]
+  int H;
+  int ksplit;           // MODE 1: K ranges over blockIdx.z
+};
+
+template <int MS>
+constexpr int a_chunks() {
+  return (MS * 32 + kChunkRows - 1) / kChunkRows;
 }
 
-__device__ __forceinline__ void a_store(const AStage& s, char* lds) {
-  const int row = threadIdx.x >> 1, half = threadIdx.x & 1;
-  uint4* dst = reinterpret_cast<uint4*>(lds + row * kPitch + half * 64);
-#pragma unroll
-  for (int c = 0; c < 4; ++c) dst[c] = s.v[c];
-}
-
-}  // namespace
-
-// P planes (2 = gate and up, 1 = down), NS 32-column subtiles per wave.
-// MODE 0: gate/up -> h16 = fp16(silu(g) * u) at the tile's rows.
-// MODE 1: down    -> y[token] += weight * acc (fp32 atomics).
-template <int P, int NS, int MODE>
-__global__ __launch_bounds__(256) void gemm_kernel(
-    Buckets b, const uint16_t* __restrict__ act, int K, int N, const uint8_t* __restrict__ q0,
-    const uint16_t* __restrict__ s0, const uint8_t* __restrict__ q1,
-    const uint16_t* __restrict__ s1, uint16_t* __restrict__ hout, const float* __restrict__ w,
-    const float* __restrict__ gate_logit, int gate_ld, float* __restrict__ y, int H, int ldh) {
-  TileView tv;
-  if (!tile_of(b, &tv)) return;
-
-  __shared__ __attribute__((aligned(16))) char lds[2][kBM * kPitch];
-  __shared__ const uint16_t* rowp[kBM];
-  __shared__ int row_tok[kBM];
-  __shared__ float row_w[kBM];
-
+// One tile: MS row subtiles of 32 (compile-time, so the accumulators stay in
+// fixed registers), NS column subtiles of 32 per wave, P weight planes, K
+// steps [k0, k1).
+//
+// Pipeline (one barrier per K step, two LDS buffers, register rings of DA
+// activation and DB weight stages): at step s a wave decodes B(s), issues the
+// global loads of A(s+DA) and B(s+DB), runs the MFMAs of step s, then writes
+// A(s+1) into the idle LDS buffer.  Two workgroups share a CU, so one's
+// decode, LDS traffic and barrier waits overlap the other's MFMAs.
+// Scheduling barriers keep the compiler from sinking the loads below the
+// MFMAs.  Loads past the last step re-read the last step (their data is never
+// used), which keeps the loop free of branches around loads and accumulators.
+template <int P, int NS, int MODE, int MS>
+__device__ __forceinline__ void gemm_tile(const TileView& tv, const GemmArgs& a,
+                                          const uint16_t* const (&arow)[a_chunks<MS>()],
+                                          char (*lds)[kBM * kPitch], const int* row_tok,
+                                          const float* row_w, int k0, int k1) {
+  constexpr int NA = a_chunks<MS>();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = lane & 31, hf = lane >> 5;
-  constexpr int WN = 32 * NS;      // columns per wave
-  constexpr int BN = 4 * WN;       // columns per workgroup
+  constexpr int WN = 32 * NS;
+  constexpr int BN = kWaves * WN;
   const int col0 = blockIdx.x * BN + wave * WN;
+  const int K = a.K, N = a.N;
+  const int n = k1 - k0;  // steps of this workgroup
 
-  // Per-row sources (activation row pointer) and, for the down pass, the
-  // destination token and combine weight.
-  if (threadIdx.x < kBM) {
-    const int i = threadIdx.x;
-    const uint16_t* p = nullptr;
-    int tok = -1;
-    float wt = 0.f;
-    if (i < tv.nrows) {
-      const int r = tv.row0 + i;
-      if (b.shared_T > 0) {
-        tok = r;
-        wt = (MODE == 1 && gate_logit) ? sigmoidf_acc(gate_logit[(int64_t)r * gate_ld]) : 1.0f;
-      } else {
-        const int s = b.sorted[r];
-        tok = s / b.k;
-        wt = (MODE == 1) ? w[s] : 1.0f;
-      }
-      p = (MODE == 0) ? act + (int64_t)tok * K : act + (int64_t)r * K;
-    }
-    rowp[i] = p;
-    row_tok[i] = tok;
-    row_w[i] = wt;
-  }
-  __syncthreads();
-
+  // weight row pointers of this lane (rows past N re-read row N-1; their
+  // columns are never stored)
+  const u32x4_t* bq_ptr[NS][P];
+  const uint16_t* bs_ptr[NS][P];
   const int64_t plane = (int64_t)N * (K / 2), splane = (int64_t)N * (K / 32);
-  const uint8_t* qp[P];
-  const uint16_t* sp[P];
-  qp[0] = q0 + tv.e * plane;
-  sp[0] = s0 + tv.e * splane;
-  if (P > 1) {
-    qp[P - 1] = q1 + tv.e * plane;
-    sp[P - 1] = s1 + tv.e * splane;
-  }
-
-  // Weight row of this lane for subtile ns; columns past N read nothing.
-  int wrow[NS];
-  bool wvalid[NS];
 #pragma unroll
   for (int ns = 0; ns < NS; ++ns) {
-    wrow[ns] = col0 + ns * 32 + j;
-    wvalid[ns] = wrow[ns] < N;
-  }
-  // Row tiles of 32 that hold at least one real row (wave-uniform).
-  const int msub = (tv.nrows + 31) / 32;
-
-  f32x16_t acc[4][NS][P];
+    const int row = min(col0 + ns * 32 + j, N - 1);
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
+    for (int p = 0; p < P; ++p) {
+      bq_ptr[ns][p] = reinterpret_cast<const u32x4_t*>(a.q[p] + tv.e * plane + (int64_t)row * (K / 2)) +
+                      hf + 2 * k0;
+      bs_ptr[ns][p] = a.s[p] + tv.e * splane + (int64_t)row * (K / 32) + hf + 2 * k0;
+    }
+  }
+  auto b_load = [&](BStage<P, NS>& st, int s) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns)
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        st.q[ns][p] = bq_ptr[ns][p][2 * s];
+        st.s[ns][p] = bs_ptr[ns][p][2 * s];
+      }
+  };
+  const int chunk = threadIdx.x & 7;
+  auto a_load = [&](AStage<NA>& st, int s) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i)
+      st.v[i] = reinterpret_cast<const u32x4_t*>(arow[i] + (int64_t)(k0 + s) * kKS)[chunk];
+  };
+  auto a_store = [&](const AStage<NA>& st, char* buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const int r = (threadIdx.x >> 3) + kChunkRows * i;
+      *reinterpret_cast<u32x4_t*>(buf + r * kPitch + chunk * 16) = st.v[i];
+    }
+  };
+
+  f32x16_t acc[MS][NS][P];
+#pragma unroll
+  for (int m = 0; m < MS; ++m)
 #pragma unroll
     for (int ns = 0; ns < NS; ++ns)
 #pragma unroll
@@ -169,77 +213,77 @@ __global__ __launch_bounds__(256) void gemm_kernel(
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[m][ns][p][v] = 0.f;
 
-  const int nks = K / kKS;
-  uint4 bq[NS][P];
-  uint16_t bs[NS][P];
-  auto b_load = [&](int ks) {
+  // Decoded weight operands: word d of a lane's 16 bytes feeds MFMA d.
+  typedef f16x8_t BFrag[NS][P][4];
+  auto decode = [&](const BStage<P, NS>& st, BFrag& bf) __attribute__((always_inline)) {
 #pragma unroll
     for (int ns = 0; ns < NS; ++ns)
 #pragma unroll
       for (int p = 0; p < P; ++p) {
-        if (wvalid[ns]) {
-          const int g = 2 * ks + hf;
-          bq[ns][p] = *reinterpret_cast<const uint4*>(qp[p] + (int64_t)wrow[ns] * (K / 2) + 16 * g);
-          bs[ns][p] = sp[p][(int64_t)wrow[ns] * (K / 32) + g];
-        } else {
-          bq[ns][p] = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
-          bs[ns][p] = 0;
-        }
+        const _Float16 sc = __builtin_bit_cast(_Float16, (uint16_t)st.s[ns][p]);
+        const f16x2_t s2 = {sc, sc};
+#pragma unroll
+        for (int d = 0; d < 4; ++d) bf[ns][p][d] = q4_f16x8(st.q[ns][p][d], s2);
       }
   };
 
-  AStage as;
-  a_load(as, rowp, K, 0);
-  b_load(0);
-  a_store(as, lds[0]);
-  __syncthreads();
+  // Register rings: A(s) lives in as[s % DA] from its load (step s-DA)
+  // until its LDS write (end of step s-1); B(s) lives in bs[s % DB] from its
+  // load (step s-DB) until its decode at the start of step s.
+  constexpr int DA = MOE_GEMM_DA, DB = MOE_GEMM_DB;
+  constexpr int U = lcm_c(DA, DB);
+  AStage<NA> as[DA];
+  BStage<P, NS> bs[DB];
 
-  for (int ks = 0; ks < nks; ++ks) {
-    // decode this step's weights into MFMA operands
-    f16x8_t bf[NS][P][4];
+  // One K step at ring phase u (s % U == u).
+  auto step = [&](int s, auto uc) __attribute__((always_inline)) {
+    constexpr int u = decltype(uc)::value;
+    BFrag bf;
+    decode(bs[u % DB], bf);
+    b_load(bs[u % DB], min(s + DB, n - 1));
+    a_load(as[u % DA], min(s + DA, n - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    const char* cur = lds[s & 1];
 #pragma unroll
-    for (int ns = 0; ns < NS; ++ns)
+    for (int m = 0; m < MS; ++m) {
+      const char* ar = cur + (m * 32 + j) * kPitch + hf * 64;
+      f16x8_t af[4];
 #pragma unroll
-      for (int p = 0; p < P; ++p) {
-        const _Float16 sc = __builtin_bit_cast(_Float16, bs[ns][p]);
-        const f16x2_t s2 = {sc, sc};
-        bf[ns][p][0] = q4_f16x8(bq[ns][p].x, s2);
-        bf[ns][p][1] = q4_f16x8(bq[ns][p].y, s2);
-        bf[ns][p][2] = q4_f16x8(bq[ns][p].z, s2);
-        bf[ns][p][3] = q4_f16x8(bq[ns][p].w, s2);
-      }
-    const bool more = ks + 1 < nks;
-    if (more) {
-      a_load(as, rowp, K, ks + 1);
-      b_load(ks + 1);
-    }
-    const char* cur = lds[ks & 1];
+      for (int d = 0; d < 4; ++d) af[d] = *reinterpret_cast<const f16x8_t*>(ar + 16 * d);
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      if (m < msub) {
-        const char* arow = cur + (m * 32 + j) * kPitch + hf * 64;
-        f16x8_t af[4];
-#pragma unroll
-        for (int d = 0; d < 4; ++d) af[d] = *reinterpret_cast<const f16x8_t*>(arow + 16 * d);
+      for (int d = 0; d < 4; ++d)
 #pragma unroll
         for (int ns = 0; ns < NS; ++ns)
 #pragma unroll
           for (int p = 0; p < P; ++p)
-#pragma unroll
-            for (int d = 0; d < 4; ++d)
-              acc[m][ns][p] =
-                  __builtin_amdgcn_mfma_f32_32x32x16_f16(af[d], bf[ns][p][d], acc[m][ns][p], 0, 0, 0);
-      }
+            acc[m][ns][p] =
+                __builtin_amdgcn_mfma_f32_32x32x16_f16(af[d], bf[ns][p][d], acc[m][ns][p], 0, 0, 0);
     }
-    if (more) a_store(as, lds[(ks + 1) & 1]);
+    __builtin_amdgcn_sched_barrier(0);
+    a_store(as[(u + 1) % DA], lds[(s + 1) & 1]);
     __syncthreads();
-  }
+  };
+
+  static_for<DB>([&](auto i) __attribute__((always_inline)) {
+    b_load(bs[decltype(i)::value], min((int)decltype(i)::value, n - 1));
+  });
+  static_for<DA>([&](auto i) __attribute__((always_inline)) {
+    a_load(as[decltype(i)::value], min((int)decltype(i)::value, n - 1));
+  });
+  a_store(as[0], lds[0]);
+  __syncthreads();
+  int s = 0;
+  for (; s + U <= n; s += U)
+    static_for<U>([&](auto i) __attribute__((always_inline)) { step(s + decltype(i)::value, i); });
+  if (s < n)
+    static_for<U>([&](auto i) __attribute__((always_inline)) {
+      if (s + decltype(i)::value < n) step(s + decltype(i)::value, i);
+    });
 
   // Epilogue.  Lane (j, hf) holds column col0 + ns*32 + j, rows
   // m*32 + 8*(v/4) + 4*hf + v%4 of the tile.
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    if (m >= msub) continue;
+  for (int m = 0; m < MS; ++m) {
 #pragma unroll
     for (int ns = 0; ns < NS; ++ns) {
       const int col = col0 + ns * 32 + j;
@@ -252,34 +296,148 @@ __global__ __launch_bounds__(256) void gemm_kernel(
           const float g = acc[m][ns][0][v], u = acc[m][ns][P - 1][v];
           const float hv = g / (1.0f + __expf(-g)) * u;
           const _Float16 hh = (_Float16)hv;
-          hout[(int64_t)(tv.row0 + i) * ldh + perm_col(col)] = __builtin_bit_cast(uint16_t, hh);
+          a.hout[(int64_t)(tv.row0 + i) * a.ldh + perm_col(col)] = __builtin_bit_cast(uint16_t, hh);
         } else {
-          unsafeAtomicAdd(&y[(int64_t)row_tok[i] * H + col], row_w[i] * acc[m][ns][0][v]);
+          unsafeAtomicAdd(&a.y[(int64_t)row_tok[i] * a.H + col], row_w[i] * acc[m][ns][0][v]);
         }
       }
     }
   }
 }
 
+}  // namespace
+
+// P planes (2 = gate and up, 1 = down), NS 32-column subtiles per wave.
+// MODE 0: gate/up -> h16 = fp16(silu(g) * u) at the tile's rows.
+// MODE 1: down    -> y[token] += weight * acc (fp32 atomics), K split over
+//                    blockIdx.z into a.ksplit ranges.
+template <int P, int NS, int MODE>
+__global__ __launch_bounds__(kThreads, MOE_GEMM_OCC) void gemm_kernel(Buckets b, GemmArgs a) {
+  TileView tv;
+  if (!tile_of(b, &tv)) return;
+
+  __shared__ __attribute__((aligned(16))) char lds[2][kBM * kPitch];
+  __shared__ int row_tok[kBM];
+  __shared__ float row_w[kBM];
+
+  // Destination token and combine weight of each tile row (down pass).
+  if (MODE == 1 && threadIdx.x < kBM) {
+    const int i = threadIdx.x;
+    int tok = 0;
+    float wt = 0.f;
+    if (i < tv.nrows) {
+      const int r = tv.row0 + i;
+      if (b.shared_T > 0) {
+        tok = r;
+        wt = a.gate_logit ? sigmoidf_acc(a.gate_logit[(int64_t)r * a.gate_ld]) : 1.0f;
+      } else {
+        const int s = b.sorted[r];
+        tok = s / b.k;
+        wt = a.w[s];
+      }
+    }
+    row_tok[i] = tok;
+    row_w[i] = wt;
+  }
+
+  // K range of this workgroup
+  const int nks = a.K / kKS;
+  int k0 = 0, k1 = nks;
+  if (MODE == 1) {
+    const int z = blockIdx.z, S = a.ksplit;
+    k0 = (int)((int64_t)nks * z / S);
+    k1 = (int)((int64_t)nks * (z + 1) / S);
+  }
+
+  // Source row of each activation chunk this thread loads; rows past the
+  // tile re-read its last row (their results are never stored).
+  auto src_row = [&](int i) -> const uint16_t* {
+    const int r = tv.row0 + min(i, tv.nrows - 1);
+    int64_t src = r;
+    if (MODE == 0 && b.shared_T == 0) src = b.sorted[r] / b.k;
+    return a.act + src * a.K;
+  };
+  const int r0 = threadIdx.x >> 3;
+  const int msub = (tv.nrows + 31) >> 5;
+  static_for<4>([&](auto c) __attribute__((always_inline)) {
+    constexpr int MS = decltype(c)::value + 1;
+    constexpr int NA = a_chunks<MS>();
+    if (msub == MS) {
+      const uint16_t* rows[NA];
+#pragma unroll
+      for (int i = 0; i < NA; ++i) rows[i] = src_row(r0 + kChunkRows * i);
+      gemm_tile<P, NS, MODE, MS>(tv, a, rows, lds, row_tok, row_w, k0, k1);
+    }
+  });
+}
+
+namespace {
+
+template <int P, int NS, int MODE>
+hipError_t launch_tiles(const Buckets& b, int max_tiles, int ncols, int ksplit, const GemmArgs& a0,
+                        const Launch& L) {
+  constexpr int BN = kWaves * 32 * NS;
+  GemmArgs a = a0;
+  a.ksplit = ksplit;
+  const int gx = (ncols + BN - 1) / BN;
+  MOE_LAUNCH(L, (gemm_kernel<P, NS, MODE>), dim3(gx, max_tiles, ksplit), dim3(kThreads), 0, b, a);
+  return hipGetLastError();
+}
+
+// K ranges for the down pass: enough workgroups to cover the chip twice
+// (from a lower estimate of the tile count), with at least 8 K steps each.
+int down_split(int64_t est_tiles, int gx, int nks) {
+  const int64_t blocks = std::max<int64_t>(1, est_tiles * gx);
+  int s = (int)std::min<int64_t>(64, (512 + blocks - 1) / blocks);
+  s = std::min(s, std::max(1, nks / 8));
+  return std::max(1, s);
+}
+
+}  // namespace
+
 hipError_t launch_gemm_gate_up(const Buckets& b, int max_tiles, const uint16_t* x16, int H,
                                int I, const uint8_t* gq, const uint16_t* gs,
                                const uint8_t* uq, const uint16_t* us, uint16_t* h16,
                                const Launch& L) {
-  constexpr int BN = 4 * 32 * 1;
-  dim3 grid((I + BN - 1) / BN, max_tiles);
-  MOE_LAUNCH(L, (gemm_kernel<2, 1, 0>), grid, dim3(256), 0, b, x16, H, I, gq, gs, uq, us,
-                     h16, nullptr, nullptr, 0, nullptr, H, I);
-  return hipGetLastError();
+  GemmArgs a{};
+  a.act = x16;
+  a.K = H;
+  a.N = I;
+  a.q[0] = gq;
+  a.s[0] = gs;
+  a.q[1] = uq;
+  a.s[1] = us;
+  a.hout = h16;
+  a.ldh = I;
+  a.H = H;
+  return launch_tiles<2, MOE_GEMM_GU_NS, 0>(b, max_tiles, I, 1, a, L);
 }
 
 hipError_t launch_gemm_down(const Buckets& b, int max_tiles, const uint16_t* h16, int H, int I,
                             const uint8_t* dq, const uint16_t* ds, const float* w,
                             const float* gate_logit, int gate_ld, float* y, const Launch& L) {
-  constexpr int BN = 4 * 32 * 2;
-  dim3 grid((H + BN - 1) / BN, max_tiles);
-  MOE_LAUNCH(L, (gemm_kernel<1, 2, 1>), grid, dim3(256), 0, b, h16, I, H, dq, ds, dq, ds,
-                     nullptr, w, gate_logit, gate_ld, y, H, 0);
-  return hipGetLastError();
+  GemmArgs a{};
+  a.act = h16;
+  a.K = I;
+  a.N = H;
+  a.q[0] = a.q[1] = dq;
+  a.s[0] = a.s[1] = ds;
+  a.w = w;
+  a.gate_logit = gate_logit;
+  a.gate_ld = gate_ld;
+  a.y = y;
+  a.H = H;
+  constexpr int BN = kWaves * 32 * MOE_GEMM_DN_NS;
+  const int gx = (H + BN - 1) / BN;
+  int64_t est;
+  if (b.shared_T > 0) {
+    est = (b.shared_T + kBM - 1) / kBM;
+  } else {
+    // at least ceil(slots/128) tiles; about half the experts add a short one
+    const int64_t slots = (int64_t)b.max_rows * b.k;
+    est = (slots + kBM - 1) / kBM + std::min<int64_t>(b.E, slots) / 2;
+  }
+  return launch_tiles<1, MOE_GEMM_DN_NS, 1>(b, max_tiles, H, down_split(est, gx, I / kKS), a, L);
 }
 
 }  // namespace moe

@@ -19,7 +19,7 @@ struct Launch {
 
 #define MOE_LAUNCH(L, kernel, grid, block, shmem, ...)                                    \
   do {                                                                                    \
-    if ((L).start)                                                                        \
+    if ((L).start || (L).stop)                                                            \
       hipExtLaunchKernelGGL(kernel, grid, block, shmem, (L).st, (L).start, (L).stop, 0,   \
                             __VA_ARGS__);                                                 \
     else                                                                                  \
@@ -31,6 +31,8 @@ struct Launch {
 //   [1] number of MFMA row tiles
 //   [4 .. 4+4E)            touched experts, ascending: {expert, first row, rows, 0}
 //   [tiles_offset(E) ..)   tiles, 4 ints each: {expert, first row, rows, 0}
+// An expert's rows are cut into tiles of kGemmTileRows; only its last tile can
+// be short.
 constexpr int kGemmTileRows = 128;  // rows (slots) per MFMA tile
 __host__ __device__ constexpr int sched_touched_offset() { return 4; }
 __host__ __device__ constexpr int sched_tiles_offset(int E) { return 4 + 4 * E; }
