@@ -83,24 +83,6 @@ struct TileView {
   int e, row0, nrows;
 };
 
-// Tile of this workgroup: blockIdx.y indexes the tile list (or, for the
-// shared expert, consecutive 128-row tiles of all tokens).
-__device__ __forceinline__ bool tile_of(const Buckets& b, TileView* v) {
-  const int u = blockIdx.y;
-  if (b.shared_T > 0) {
-    v->e = 0;
-    v->row0 = u * kBM;
-    v->nrows = min(kBM, b.shared_T - v->row0);
-    return v->nrows > 0;
-  }
-  if (u >= b.sched[1]) return false;
-  const int4 t = reinterpret_cast<const int4*>(b.sched + sched_tiles_offset(b.E))[u];
-  v->e = t.x;
-  v->row0 = t.y;
-  v->nrows = t.z;
-  return true;
-}
-
 // Row-major fp16 position of logical column j in the permuted-by-8 layout.
 __device__ __forceinline__ int perm_col(int j) { return (j & ~7) | perm8_pos(j & 7); }
 
@@ -119,20 +101,49 @@ struct AStage {
   u32x4_t v[NA];
 };
 
-struct GemmArgs {
-  const uint16_t* act;  // fp16 activations (perm-by-8 order), row stride K
-  int K, N;             // contraction depth and output columns of one plane
-  const uint8_t* q[2];  // weight planes: [E][N][K/2] nibbles
-  const uint16_t* s[2]; // and their [E][N][K/32] fp16 scales
-  uint16_t* hout;       // MODE 0 output, row stride ldh
-  int ldh;
-  const float* w;       // MODE 1 combine weights per slot
-  const float* gate_logit;
-  int gate_ld;
-  float* y;             // MODE 1 output [T][H]
-  int H;
-  int ksplit;           // MODE 1: K ranges over blockIdx.z
+// One source of tiles: the routed buckets or the shared expert.
+struct GemmSrc {
+  const uint16_t* act;   // fp16 activations (perm-by-8 order), row stride K
+  int K, N;              // contraction depth and output columns of one plane
+  const uint8_t* q[2];   // weight planes: [E][N][K/2] nibbles
+  const uint16_t* s[2];  // and their [E][N][K/32] fp16 scales
+  uint16_t* hout;        // MODE 0 output, row stride N
+  int ksplit;            // MODE 1: K ranges over blockIdx.z
 };
+
+struct GemmArgs {
+  GemmSrc src[2];        // [0] routed buckets, [1] shared expert
+  int shared_T;          // rows of the shared expert (0: none)
+  int shared_tiles;      // leading blockIdx.y values that hold shared tiles
+  const float* w;        // MODE 1 combine weights per slot
+  const float* gate_logit;  // MODE 1 shared-expert gate logits (nullable)
+  int gate_ld;
+  float* y;              // MODE 1 output [T][H]
+  int H;
+};
+
+// Tile of this workgroup.  The first a.shared_tiles values of blockIdx.y are
+// 128-row tiles of the shared expert (identity rows over all tokens); the
+// rest index the routed tile list.
+__device__ __forceinline__ bool tile_of(const Buckets& b, const GemmArgs& a, TileView* v,
+                                        int* src) {
+  int u = blockIdx.y;
+  if (u < a.shared_tiles) {
+    *src = 1;
+    v->e = 0;
+    v->row0 = u * kBM;
+    v->nrows = min(kBM, a.shared_T - v->row0);
+    return v->nrows > 0;
+  }
+  u -= a.shared_tiles;
+  *src = 0;
+  if (u >= b.sched[1]) return false;
+  const int4 t = reinterpret_cast<const int4*>(b.sched + sched_tiles_offset(b.E))[u];
+  v->e = t.x;
+  v->row0 = t.y;
+  v->nrows = t.z;
+  return true;
+}
 
 template <int MS>
 constexpr int a_chunks() {
@@ -152,7 +163,7 @@ constexpr int a_chunks() {
 // MFMAs.  Loads past the last step re-read the last step (their data is never
 // used), which keeps the loop free of branches around loads and accumulators.
 template <int P, int NS, int MODE, int MS>
-__device__ __forceinline__ void gemm_tile(const TileView& tv, const GemmArgs& a,
+__device__ __forceinline__ void gemm_tile(const TileView& tv, const GemmSrc& S, const GemmArgs& a,
                                           const uint16_t* const (&arow)[a_chunks<MS>()],
                                           char (*lds)[kBM * kPitch], const int* row_tok,
                                           const float* row_w, int k0, int k1) {
@@ -162,7 +173,7 @@ __device__ __forceinline__ void gemm_tile(const TileView& tv, const GemmArgs& a,
   constexpr int WN = 32 * NS;
   constexpr int BN = kWaves * WN;
   const int col0 = blockIdx.x * BN + wave * WN;
-  const int K = a.K, N = a.N;
+  const int K = S.K, N = S.N;
   const int n = k1 - k0;  // steps of this workgroup
 
   // weight row pointers of this lane (rows past N re-read row N-1; their
@@ -175,9 +186,9 @@ __device__ __forceinline__ void gemm_tile(const TileView& tv, const GemmArgs& a,
     const int row = min(col0 + ns * 32 + j, N - 1);
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-      bq_ptr[ns][p] = reinterpret_cast<const u32x4_t*>(a.q[p] + tv.e * plane + (int64_t)row * (K / 2)) +
+      bq_ptr[ns][p] = reinterpret_cast<const u32x4_t*>(S.q[p] + tv.e * plane + (int64_t)row * (K / 2)) +
                       hf + 2 * k0;
-      bs_ptr[ns][p] = a.s[p] + tv.e * splane + (int64_t)row * (K / 32) + hf + 2 * k0;
+      bs_ptr[ns][p] = S.s[p] + tv.e * splane + (int64_t)row * (K / 32) + hf + 2 * k0;
     }
   }
   auto b_load = [&](BStage<P, NS>& st, int s) __attribute__((always_inline)) {
@@ -296,7 +307,7 @@ __device__ __forceinline__ void gemm_tile(const TileView& tv, const GemmArgs& a,
           const float g = acc[m][ns][0][v], u = acc[m][ns][P - 1][v];
           const float hv = g / (1.0f + __expf(-g)) * u;
           const _Float16 hh = (_Float16)hv;
-          a.hout[(int64_t)(tv.row0 + i) * a.ldh + perm_col(col)] = __builtin_bit_cast(uint16_t, hh);
+          S.hout[(int64_t)(tv.row0 + i) * N + perm_col(col)] = __builtin_bit_cast(uint16_t, hh);
         } else {
           unsafeAtomicAdd(&a.y[(int64_t)row_tok[i] * a.H + col], row_w[i] * acc[m][ns][0][v]);
         }
@@ -314,7 +325,12 @@ __device__ __forceinline__ void gemm_tile(const TileView& tv, const GemmArgs& a,
 template <int P, int NS, int MODE>
 __global__ __launch_bounds__(kThreads, MOE_GEMM_OCC) void gemm_kernel(Buckets b, GemmArgs a) {
   TileView tv;
-  if (!tile_of(b, &tv)) return;
+  int src = 0;
+  if (!tile_of(b, a, &tv, &src)) return;
+  const GemmSrc S = src ? a.src[1] : a.src[0];
+  constexpr int BN = kWaves * 32 * NS;
+  if ((int)blockIdx.x * BN >= S.N) return;  // the other source is wider
+  if (MODE == 1 && (int)blockIdx.z >= S.ksplit) return;
 
   __shared__ __attribute__((aligned(16))) char lds[2][kBM * kPitch];
   __shared__ int row_tok[kBM];
@@ -327,7 +343,7 @@ __global__ __launch_bounds__(kThreads, MOE_GEMM_OCC) void gemm_kernel(Buckets b,
     float wt = 0.f;
     if (i < tv.nrows) {
       const int r = tv.row0 + i;
-      if (b.shared_T > 0) {
+      if (src) {
         tok = r;
         wt = a.gate_logit ? sigmoidf_acc(a.gate_logit[(int64_t)r * a.gate_ld]) : 1.0f;
       } else {
@@ -341,21 +357,21 @@ __global__ __launch_bounds__(kThreads, MOE_GEMM_OCC) void gemm_kernel(Buckets b,
   }
 
   // K range of this workgroup
-  const int nks = a.K / kKS;
+  const int nks = S.K / kKS;
   int k0 = 0, k1 = nks;
   if (MODE == 1) {
-    const int z = blockIdx.z, S = a.ksplit;
-    k0 = (int)((int64_t)nks * z / S);
-    k1 = (int)((int64_t)nks * (z + 1) / S);
+    const int z = blockIdx.z, ks = S.ksplit;
+    k0 = (int)((int64_t)nks * z / ks);
+    k1 = (int)((int64_t)nks * (z + 1) / ks);
   }
 
   // Source row of each activation chunk this thread loads; rows past the
   // tile re-read its last row (their results are never stored).
   auto src_row = [&](int i) -> const uint16_t* {
     const int r = tv.row0 + min(i, tv.nrows - 1);
-    int64_t src = r;
-    if (MODE == 0 && b.shared_T == 0) src = b.sorted[r] / b.k;
-    return a.act + src * a.K;
+    int64_t row = r;
+    if (MODE == 0 && !src) row = b.sorted[r] / b.k;
+    return S.act + row * S.K;
   };
   const int r0 = threadIdx.x >> 3;
   const int msub = (tv.nrows + 31) >> 5;
@@ -366,31 +382,40 @@ __global__ __launch_bounds__(kThreads, MOE_GEMM_OCC) void gemm_kernel(Buckets b,
       const uint16_t* rows[NA];
 #pragma unroll
       for (int i = 0; i < NA; ++i) rows[i] = src_row(r0 + kChunkRows * i);
-      gemm_tile<P, NS, MODE, MS>(tv, a, rows, lds, row_tok, row_w, k0, k1);
+      gemm_tile<P, NS, MODE, MS>(tv, S, a, rows, lds, row_tok, row_w, k0, k1);
     }
   });
 }
 
 namespace {
 
-template <int P, int NS, int MODE>
-hipError_t launch_tiles(const Buckets& b, int max_tiles, int ncols, int ksplit, const GemmArgs& a0,
-                        const Launch& L) {
-  constexpr int BN = kWaves * 32 * NS;
-  GemmArgs a = a0;
-  a.ksplit = ksplit;
-  const int gx = (ncols + BN - 1) / BN;
-  MOE_LAUNCH(L, (gemm_kernel<P, NS, MODE>), dim3(gx, max_tiles, ksplit), dim3(kThreads), 0, b, a);
-  return hipGetLastError();
+constexpr int kDownNS = MOE_GEMM_DN_NS;
+constexpr int kGateUpNS = MOE_GEMM_GU_NS;
+
+// K ranges for one source of the down pass: about equal work per workgroup,
+// enough workgroups to cover the chip twice, and at least 8 K steps each.
+int down_split(int nks, int64_t total_steps) {
+  const int64_t target = std::max<int64_t>(8, total_steps / 512);
+  int s = (int)((nks + target - 1) / target);
+  s = std::min(s, std::max(1, nks / 8));
+  return std::max(1, std::min(s, 64));
 }
 
-// K ranges for the down pass: enough workgroups to cover the chip twice
-// (from a lower estimate of the tile count), with at least 8 K steps each.
-int down_split(int64_t est_tiles, int gx, int nks) {
-  const int64_t blocks = std::max<int64_t>(1, est_tiles * gx);
-  int s = (int)std::min<int64_t>(64, (512 + blocks - 1) / blocks);
-  s = std::min(s, std::max(1, nks / 8));
-  return std::max(1, s);
+// At least ceil(slots/128) routed tiles; about half the experts add a short one.
+int64_t routed_tile_estimate(const Buckets& b) {
+  const int64_t slots = (int64_t)b.max_rows * b.k;
+  return (slots + kBM - 1) / kBM + std::min<int64_t>(b.E, slots) / 2;
+}
+
+template <int P, int NS, int MODE>
+hipError_t launch_tiles(const Buckets& b, int max_tiles, const GemmArgs& a, int gz,
+                        const Launch& L) {
+  constexpr int BN = kWaves * 32 * NS;
+  int gx = (a.src[0].N + BN - 1) / BN;
+  if (a.shared_tiles > 0) gx = std::max(gx, (a.src[1].N + BN - 1) / BN);
+  MOE_LAUNCH(L, (gemm_kernel<P, NS, MODE>), dim3(gx, a.shared_tiles + max_tiles, gz),
+             dim3(kThreads), 0, b, a);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -398,46 +423,73 @@ int down_split(int64_t est_tiles, int gx, int nks) {
 hipError_t launch_gemm_gate_up(const Buckets& b, int max_tiles, const uint16_t* x16, int H,
                                int I, const uint8_t* gq, const uint16_t* gs,
                                const uint8_t* uq, const uint16_t* us, uint16_t* h16,
-                               const Launch& L) {
+                               const SharedGemm* shared, const Launch& L) {
   GemmArgs a{};
-  a.act = x16;
-  a.K = H;
-  a.N = I;
-  a.q[0] = gq;
-  a.s[0] = gs;
-  a.q[1] = uq;
-  a.s[1] = us;
-  a.hout = h16;
-  a.ldh = I;
+  GemmSrc& r = a.src[0];
+  r.act = x16;
+  r.K = H;
+  r.N = I;
+  r.q[0] = gq;
+  r.s[0] = gs;
+  r.q[1] = uq;
+  r.s[1] = us;
+  r.hout = h16;
+  r.ksplit = 1;
+  if (shared) {
+    GemmSrc& sh = a.src[1];
+    sh.act = x16;
+    sh.K = H;
+    sh.N = shared->SI;
+    sh.q[0] = shared->q[0];
+    sh.s[0] = shared->s[0];
+    sh.q[1] = shared->q[1];
+    sh.s[1] = shared->s[1];
+    sh.hout = shared->h16;
+    sh.ksplit = 1;
+    a.shared_T = shared->T;
+    a.shared_tiles = (shared->T + kBM - 1) / kBM;
+  }
   a.H = H;
-  return launch_tiles<2, MOE_GEMM_GU_NS, 0>(b, max_tiles, I, 1, a, L);
+  return launch_tiles<2, kGateUpNS, 0>(b, max_tiles, a, 1, L);
 }
 
 hipError_t launch_gemm_down(const Buckets& b, int max_tiles, const uint16_t* h16, int H, int I,
-                            const uint8_t* dq, const uint16_t* ds, const float* w,
-                            const float* gate_logit, int gate_ld, float* y, const Launch& L) {
+                            const uint8_t* dq, const uint16_t* ds, const float* w, float* y,
+                            const SharedGemm* shared, const Launch& L) {
   GemmArgs a{};
-  a.act = h16;
-  a.K = I;
-  a.N = H;
-  a.q[0] = a.q[1] = dq;
-  a.s[0] = a.s[1] = ds;
+  GemmSrc& r = a.src[0];
+  r.act = h16;
+  r.K = I;
+  r.N = H;
+  r.q[0] = r.q[1] = dq;
+  r.s[0] = r.s[1] = ds;
   a.w = w;
-  a.gate_logit = gate_logit;
-  a.gate_ld = gate_ld;
   a.y = y;
   a.H = H;
-  constexpr int BN = kWaves * 32 * MOE_GEMM_DN_NS;
+  constexpr int BN = kWaves * 32 * kDownNS;
   const int gx = (H + BN - 1) / BN;
-  int64_t est;
-  if (b.shared_T > 0) {
-    est = (b.shared_T + kBM - 1) / kBM;
-  } else {
-    // at least ceil(slots/128) tiles; about half the experts add a short one
-    const int64_t slots = (int64_t)b.max_rows * b.k;
-    est = (slots + kBM - 1) / kBM + std::min<int64_t>(b.E, slots) / 2;
+  const int64_t est = routed_tile_estimate(b);
+  int64_t total = est * gx * (I / kKS);
+  if (shared) {
+    GemmSrc& sh = a.src[1];
+    sh.act = shared->h16;
+    sh.K = shared->SI;
+    sh.N = H;
+    sh.q[0] = sh.q[1] = shared->q[2];
+    sh.s[0] = sh.s[1] = shared->s[2];
+    a.shared_T = shared->T;
+    a.shared_tiles = (shared->T + kBM - 1) / kBM;
+    a.gate_logit = shared->gate_logit;
+    a.gate_ld = shared->gate_ld;
+    total += (int64_t)a.shared_tiles * gx * (shared->SI / kKS);
   }
-  return launch_tiles<1, MOE_GEMM_DN_NS, 1>(b, max_tiles, H, down_split(est, gx, I / kKS), a, L);
+  r.ksplit = down_split(I / kKS, total);
+  int gz = r.ksplit;
+  if (shared) {
+    a.src[1].ksplit = down_split(shared->SI / kKS, total);
+    gz = std::max(gz, a.src[1].ksplit);
+  }
+  return launch_tiles<1, kDownNS, 1>(b, max_tiles, a, gz, L);
 }
 
 }  // namespace moe

@@ -110,13 +110,26 @@ bool gemv_supported(int K);
 // Grouped MFMA GEMM (prefill), fp16 operands with fp32 accumulation.
 hipError_t launch_convert_x16(const uint16_t* x, int T, int H, uint16_t* x16, float* y_zero,
                               int64_t y_elems, const Launch& L);
+// The shared expert as extra tiles of the grouped-GEMM launches: identity
+// rows over all T tokens, planes gate/up/down, hidden rows h16 [T][SI], and
+// the down pass weighting row t by sigmoid(gate_logit[t * gate_ld]) (1 when
+// gate_logit is null).
+struct SharedGemm {
+  int T, SI;
+  const uint8_t* q[3];
+  const uint16_t* s[3];
+  uint16_t* h16;
+  const float* gate_logit;
+  int gate_ld;
+};
+
 hipError_t launch_gemm_gate_up(const Buckets& b, int max_tiles, const uint16_t* x16, int H,
                                int I, const uint8_t* gq, const uint16_t* gs,
                                const uint8_t* uq, const uint16_t* us, uint16_t* h16,
-                               const Launch& L);
+                               const SharedGemm* shared, const Launch& L);
 hipError_t launch_gemm_down(const Buckets& b, int max_tiles, const uint16_t* h16, int H, int I,
-                            const uint8_t* dq, const uint16_t* ds, const float* w,
-                            const float* gate_logit, int gate_ld, float* y, const Launch& L);
+                            const uint8_t* dq, const uint16_t* ds, const float* w, float* y,
+                            const SharedGemm* shared, const Launch& L);
 
 hipError_t launch_debug_dequant(const uint8_t* q, const uint16_t* s, int N, int K, int mode,
                                 float* out, const Launch& L);

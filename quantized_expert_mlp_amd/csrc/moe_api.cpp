@@ -160,29 +160,30 @@ int run_mlp(const moe_shape* sh, bool gemm, const Layout& L, void* ws, const uin
   uint16_t* h16 = at<uint16_t>(ws, L.h);
   uint16_t* hs16 = at<uint16_t>(ws, L.hs);
   const int max_tiles = (int)moe::sched_max_tiles(slots, E);
-  const int shared_tiles = (T + moe::kGemmTileRows - 1) / moe::kGemmTileRows;
+  // the shared expert rides in the routed launches as extra tiles
+  moe::SharedGemm sgm{};
+  if (shared) {
+    sgm.T = T;
+    sgm.SI = sh->SI;
+    for (int i = 0; i < 3; ++i) {
+      sgm.q[i] = shared[i].q;
+      sgm.s[i] = shared[i].s;
+    }
+    sgm.h16 = hs16;
+    sgm.gate_logit = gate_logit;
+    sgm.gate_ld = gate_ld;
+  }
+  const moe::SharedGemm* sgp = shared ? &sgm : nullptr;
   err = moe::launch_convert_x16(x, T, H, x16, y, y_elems, sg.at(MOE_STAGE_ACTIVATIONS));
   if (err != hipSuccess) return MOE_ERR_HIP;
   err = moe::launch_gemm_gate_up(routed, max_tiles, x16, H, I, gate.q, gate.s, up.q, up.s, h16,
-                                 sg.at(MOE_STAGE_GATE_UP));
+                                 sgp, sg.at(MOE_STAGE_GATE_UP));
   if (err != hipSuccess) return MOE_ERR_HIP;
-  if (shared) {
-    err = moe::launch_gemm_gate_up(sharedb, shared_tiles, x16, H, sh->SI, shared[0].q, shared[0].s,
-                                   shared[1].q, shared[1].s, hs16, sg.at(MOE_STAGE_SHARED_GATE_UP));
-    if (err != hipSuccess) return MOE_ERR_HIP;
-  } else if (!sg.skip(MOE_STAGE_SHARED_GATE_UP)) {
-    return MOE_ERR_HIP;
-  }
-  err = moe::launch_gemm_down(routed, max_tiles, h16, H, I, down.q, down.s, w, nullptr, 0, y,
+  if (!sg.skip(MOE_STAGE_SHARED_GATE_UP)) return MOE_ERR_HIP;
+  err = moe::launch_gemm_down(routed, max_tiles, h16, H, I, down.q, down.s, w, y, sgp,
                               sg.at(MOE_STAGE_DOWN));
   if (err != hipSuccess) return MOE_ERR_HIP;
-  if (shared) {
-    err = moe::launch_gemm_down(sharedb, shared_tiles, hs16, H, sh->SI, shared[2].q, shared[2].s,
-                                nullptr, gate_logit, gate_ld, y, sg.at(MOE_STAGE_SHARED_DOWN));
-    if (err != hipSuccess) return MOE_ERR_HIP;
-  } else if (!sg.skip(MOE_STAGE_SHARED_DOWN)) {
-    return MOE_ERR_HIP;
-  }
+  if (!sg.skip(MOE_STAGE_SHARED_DOWN)) return MOE_ERR_HIP;
   return MOE_OK;
 }
 
