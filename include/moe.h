@@ -170,10 +170,14 @@ enum moe_stage {
   MOE_STAGE_TOPK = 2,           /* softmax -> top-k -> renormalise           */
   MOE_STAGE_PERMUTE = 3,        /* permutation + expert schedule             */
   MOE_STAGE_ACTIVATIONS = 4,    /* fp16 activation copy (MFMA path only)     */
-  MOE_STAGE_GATE_UP = 5,        /* routed gate/up + SiLU*mul                 */
-  MOE_STAGE_SHARED_GATE_UP = 6, /* shared expert gate/up + SiLU*mul          */
-  MOE_STAGE_DOWN = 7,           /* routed down + weighted combine            */
-  MOE_STAGE_SHARED_DOWN = 8,    /* shared expert down + gated combine        */
+  MOE_STAGE_GATE_UP = 5,        /* routed gate/up + SiLU*mul (MFMA path: also
+                                   the shared expert's, and clearing y)     */
+  MOE_STAGE_SHARED_GATE_UP = 6, /* shared expert gate/up + SiLU*mul (GEMV
+                                   path only)                               */
+  MOE_STAGE_DOWN = 7,           /* routed down + weighted combine (MFMA path:
+                                   and the shared expert's gated combine)   */
+  MOE_STAGE_SHARED_DOWN = 8,    /* shared expert down + gated combine (GEMV
+                                   path only)                               */
   MOE_STAGE_COUNT = 9
 };
 int moe_layer_profiled(const moe_shape *shape, const uint16_t *x, const float *logits,

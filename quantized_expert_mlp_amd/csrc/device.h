@@ -156,6 +156,22 @@ __device__ __forceinline__ f16x8_t q4_f16x8(uint32_t w, f16x2_t s2) {
 // MFMA kernels' fp16 activation buffers (inverse of the order 0,4,1,5,2,6,3,7).
 __device__ __forceinline__ int perm8_pos(int i) { return ((i & 3) << 1) | (i >> 2); }
 
+// Eight bf16 activations (natural order, 16 bytes) -> eight fp16 in the MFMA
+// operand order 0,4,1,5,2,6,3,7: dword d of the result holds elements d and
+// d+4.  bf16 -> fp32 is exact; fp32 -> fp16 rounds to nearest even, which is
+// exact for |x| in [2^-14, 65504] and within 2^-25 below.
+__device__ __forceinline__ u32x4_t bf16x8_to_f16_perm8(u32x4_t v) {
+  u32x4_t r;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t lo = (v[d >> 1] >> (16 * (d & 1))) & 0xFFFFu;         // element d
+    const uint32_t hi = (v[(d + 4) >> 1] >> (16 * (d & 1))) & 0xFFFFu;   // element d + 4
+    const f16x2_t h = {(_Float16)bf16_to_f32(lo), (_Float16)bf16_to_f32(hi)};
+    r[d] = __builtin_bit_cast(uint32_t, h);
+  }
+  return r;
+}
+
 __device__ __forceinline__ float sigmoidf_acc(float z) { return 1.0f / (1.0f + expf(-z)); }
 
 }  // namespace moe

@@ -103,7 +103,8 @@ struct AStage {
 
 // One source of tiles: the routed buckets or the shared expert.
 struct GemmSrc {
-  const uint16_t* act;   // fp16 activations (perm-by-8 order), row stride K
+  const uint16_t* act;   // fp16 activations, row stride K, each block of 8 in
+                         // the operand order 0,4,1,5,2,6,3,7
   int K, N;              // contraction depth and output columns of one plane
   const uint8_t* q[2];   // weight planes: [E][N][K/2] nibbles
   const uint16_t* s[2];  // and their [E][N][K/32] fp16 scales
@@ -120,6 +121,8 @@ struct GemmArgs {
   int gate_ld;
   float* y;              // MODE 1 output [T][H]
   int H;
+  float* y_zero;         // MODE 0: output the launch clears for the down pass
+  int64_t y_elems;       // (a multiple of 4)
 };
 
 // Tile of this workgroup.  The first a.shared_tiles values of blockIdx.y are
@@ -324,6 +327,13 @@ __device__ __forceinline__ void gemm_tile(const TileView& tv, const GemmSrc& S, 
 //                    blockIdx.z into a.ksplit ranges.
 template <int P, int NS, int MODE>
 __global__ __launch_bounds__(kThreads, MOE_GEMM_OCC) void gemm_kernel(Buckets b, GemmArgs a) {
+  if (MODE == 0 && a.y_zero) {
+    // every workgroup of the launch, tile or not, clears its share of y
+    const int64_t nthr = (int64_t)gridDim.x * gridDim.y * kThreads;
+    const int64_t gid = ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * kThreads + threadIdx.x;
+    float4* y4 = reinterpret_cast<float4*>(a.y_zero);
+    for (int64_t i = gid; i < a.y_elems / 4; i += nthr) y4[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   TileView tv;
   int src = 0;
   if (!tile_of(b, a, &tv, &src)) return;
@@ -423,8 +433,11 @@ hipError_t launch_tiles(const Buckets& b, int max_tiles, const GemmArgs& a, int 
 hipError_t launch_gemm_gate_up(const Buckets& b, int max_tiles, const uint16_t* x16, int H,
                                int I, const uint8_t* gq, const uint16_t* gs,
                                const uint8_t* uq, const uint16_t* us, uint16_t* h16,
-                               const SharedGemm* shared, const Launch& L) {
+                               const SharedGemm* shared, float* y_zero, int64_t y_elems,
+                               const Launch& L) {
   GemmArgs a{};
+  a.y_zero = y_zero;
+  a.y_elems = y_elems;
   GemmSrc& r = a.src[0];
   r.act = x16;
   r.K = H;

@@ -70,8 +70,17 @@ hipError_t launch_route(const float* logits, int ld, int T, int E, int k, float 
                         int32_t* idx, float* w, int32_t* off, int32_t* sorted, int32_t* row_of,
                         int32_t* sched, const Launch& L);
 
+// Stable permutation (+ schedule when sched is given).  Up to
+// kPermuteOneBlockMax slots, or without scratch, one workgroup does it all;
+// beyond, three launches over blocks of 1024 slots use scratch
+// (permute_scratch_words ints).
+constexpr int kPermuteOneBlockMax = 4096;
+__host__ __device__ constexpr int64_t permute_scratch_words(int64_t slots, int E) {
+  return ((slots + 1023) / 1024) * E;
+}
 hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* off,
-                          int32_t* sorted, int32_t* row_of, int32_t* sched, const Launch& L);
+                          int32_t* sorted, int32_t* row_of, int32_t* sched, int32_t* scratch,
+                          const Launch& L);
 
 hipError_t launch_schedule_from_offsets(const int32_t* off, int E, int64_t slots, int32_t* sched,
                                         const Launch& L);
@@ -108,8 +117,9 @@ hipError_t launch_gemv_down(const Buckets& b, int max_buckets, const uint16_t* h
 bool gemv_supported(int K);
 
 // Grouped MFMA GEMM (prefill), fp16 operands with fp32 accumulation.
-hipError_t launch_convert_x16(const uint16_t* x, int T, int H, uint16_t* x16, float* y_zero,
-                              int64_t y_elems, const Launch& L);
+// bf16 x [T][H] -> fp16 copy with each block of 8 in the order 0,4,1,5,2,6,3,7.
+hipError_t launch_convert_x16(const uint16_t* x, int T, int H, uint16_t* x16, const Launch& L);
+
 // The shared expert as extra tiles of the grouped-GEMM launches: identity
 // rows over all T tokens, planes gate/up/down, hidden rows h16 [T][SI], and
 // the down pass weighting row t by sigmoid(gate_logit[t * gate_ld]) (1 when
@@ -123,10 +133,14 @@ struct SharedGemm {
   int gate_ld;
 };
 
+// x16: the activations in fp16, operand order (launch_convert_x16).  The
+// launch also clears y_zero[0 .. y_elems) (y_elems a multiple of 4) for the
+// down pass's atomic combine.
 hipError_t launch_gemm_gate_up(const Buckets& b, int max_tiles, const uint16_t* x16, int H,
                                int I, const uint8_t* gq, const uint16_t* gs,
                                const uint8_t* uq, const uint16_t* us, uint16_t* h16,
-                               const SharedGemm* shared, const Launch& L);
+                               const SharedGemm* shared, float* y_zero, int64_t y_elems,
+                               const Launch& L);
 hipError_t launch_gemm_down(const Buckets& b, int max_tiles, const uint16_t* h16, int H, int I,
                             const uint8_t* dq, const uint16_t* ds, const float* w, float* y,
                             const SharedGemm* shared, const Launch& L);

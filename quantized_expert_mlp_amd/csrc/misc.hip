@@ -6,40 +6,22 @@
 namespace moe {
 
 // x (bf16 [T][H]) -> fp16 [T][H] with every aligned block of 8 stored in the
-// MFMA operand order (element i at position perm8_pos(i)).  bf16 -> fp16 is
-// exact for |x| in [2^-14, 65504]; smaller magnitudes keep their value to
-// within 2^-25 (fp16 subnormal spacing).  Also zeroes y (grid-stride).
+// MFMA operand order 0,4,1,5,2,6,3,7 (bf16x8_to_f16_perm8).  Grid-stride.
 __global__ __launch_bounds__(256) void convert_x16_kernel(const uint16_t* __restrict__ x,
                                                           int64_t blocks8,
-                                                          uint16_t* __restrict__ x16,
-                                                          float* __restrict__ y_zero,
-                                                          int64_t y_elems) {
+                                                          uint16_t* __restrict__ x16) {
   const int64_t nthr = (int64_t)gridDim.x * blockDim.x;
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  for (int64_t i = gid; i < blocks8; i += nthr) {
-    const uint4 v = reinterpret_cast<const uint4*>(x)[i];
-    const uint32_t nat[4] = {v.x, v.y, v.z, v.w};
-    _Float16 out[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t b = (nat[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-      out[perm8_pos(j)] = (_Float16)bf16_to_f32(b);
-    }
-    reinterpret_cast<uint4*>(x16)[i] = __builtin_bit_cast(uint4, out);
-  }
-  if (y_zero)
-    for (int64_t i = gid; i < y_elems; i += nthr) y_zero[i] = 0.f;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < blocks8; i += nthr)
+    reinterpret_cast<u32x4_t*>(x16)[i] =
+        bf16x8_to_f16_perm8(reinterpret_cast<const u32x4_t*>(x)[i]);
 }
 
-hipError_t launch_convert_x16(const uint16_t* x, int T, int H, uint16_t* x16, float* y_zero,
-                              int64_t y_elems, const Launch& L) {
+hipError_t launch_convert_x16(const uint16_t* x, int T, int H, uint16_t* x16, const Launch& L) {
   const int64_t blocks8 = (int64_t)T * H / 8;
-  const int64_t work = blocks8 > y_elems ? blocks8 : y_elems;
-  int grid = (int)((work + 255) / 256);
+  int grid = (int)((blocks8 + 255) / 256);
   if (grid > 8192) grid = 8192;
   if (grid < 1) grid = 1;
-  MOE_LAUNCH(L, convert_x16_kernel, dim3(grid), dim3(256), 0, x, blocks8, x16, y_zero,
-                     y_elems);
+  MOE_LAUNCH(L, convert_x16_kernel, dim3(grid), dim3(256), 0, x, blocks8, x16);
   return hipGetLastError();
 }
 

@@ -54,7 +54,7 @@ int pick_gemm(const moe_shape* sh, bool* gemm) {
 }
 
 struct Layout {
-  size_t logits, gate, idx, w, off, sorted, row_of, sched, x16, h, hs, total;
+  size_t logits, gate, idx, w, off, sorted, row_of, sched, pscratch, x16, h, hs, total;
   int ld;  // logits row stride in the workspace (E, or E+1 with a gate column)
 };
 
@@ -76,8 +76,9 @@ Layout make_layout(const moe_shape* sh, bool gemm) {
   L.sorted = take(sizeof(int32_t) * slots);
   L.row_of = take(sizeof(int32_t) * slots);
   L.sched = take(sizeof(int32_t) * moe::sched_words(slots, (int)E));
-  const size_t act = 2;  // hidden rows are fp16 on both paths
+  L.pscratch = take(sizeof(int32_t) * moe::permute_scratch_words(slots, (int)E));
   L.x16 = take(gemm ? sizeof(uint16_t) * T * sh->H : 0);
+  const size_t act = 2;  // hidden rows are fp16 on both paths
   L.h = take(act * slots * sh->I);
   L.hs = take(act * T * sh->SI);
   L.total = p;
@@ -174,10 +175,10 @@ int run_mlp(const moe_shape* sh, bool gemm, const Layout& L, void* ws, const uin
     sgm.gate_ld = gate_ld;
   }
   const moe::SharedGemm* sgp = shared ? &sgm : nullptr;
-  err = moe::launch_convert_x16(x, T, H, x16, y, y_elems, sg.at(MOE_STAGE_ACTIVATIONS));
+  err = moe::launch_convert_x16(x, T, H, x16, sg.at(MOE_STAGE_ACTIVATIONS));
   if (err != hipSuccess) return MOE_ERR_HIP;
   err = moe::launch_gemm_gate_up(routed, max_tiles, x16, H, I, gate.q, gate.s, up.q, up.s, h16,
-                                 sgp, sg.at(MOE_STAGE_GATE_UP));
+                                 sgp, y, y_elems, sg.at(MOE_STAGE_GATE_UP));
   if (err != hipSuccess) return MOE_ERR_HIP;
   if (!sg.skip(MOE_STAGE_SHARED_GATE_UP)) return MOE_ERR_HIP;
   err = moe::launch_gemm_down(routed, max_tiles, h16, H, I, down.q, down.s, w, y, sgp,
@@ -225,7 +226,7 @@ int moe_permute(const int32_t* idx, int32_t T, int32_t k, int32_t E, int32_t* of
     return MOE_ERR_INVALID_ARG;
   if (E > 256) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)T * k >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
-  return hip_status(moe::launch_permute(idx, T, k, E, off, sorted, row_of, nullptr,
+  return hip_status(moe::launch_permute(idx, T, k, E, off, sorted, row_of, nullptr, nullptr,
                                         moe::Launch{reinterpret_cast<hipStream_t>(stream)}));
 }
 
@@ -341,7 +342,8 @@ static int layer_impl(const moe_shape* sh, const uint16_t* x, const float* logit
         hipSuccess)
       return MOE_ERR_HIP;
     if (moe::launch_permute(idx, T, k, E, off, sorted, at<int32_t>(ws, L.row_of),
-                            at<int32_t>(ws, L.sched), sg.at(MOE_STAGE_PERMUTE)) != hipSuccess)
+                            at<int32_t>(ws, L.sched), at<int32_t>(ws, L.pscratch),
+                            sg.at(MOE_STAGE_PERMUTE)) != hipSuccess)
       return MOE_ERR_HIP;
   }
 

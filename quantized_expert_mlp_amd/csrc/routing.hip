@@ -21,18 +21,20 @@ namespace moe {
 // ---------------------------------------------------------------------------
 // Logits L[t][e] = sum_h x[t][h] * Wr[e][h], plus column E = x[t] . g when a
 // gate row is given.  One workgroup computes a 16-token x 16-row tile with
-// v_mfma_f32_16x16x4_f32; its four waves split H in interleaved 16-wide
-// chunks and their partial tiles are added through LDS.  Within a chunk lane
-// (i, q) = (lane % 16, lane / 16) feeds A[i][q] = x[t0+i][c+4q+r] and
-// B[q][i] = Wr[e0+i][c+4q+r] to the r-th of four MFMAs, so the four MFMAs
-// together contract the 16 inputs c..c+15 (each lane reads 4 consecutive
-// inputs with one vector load).
+// v_mfma_f32_16x16x4_f32.  Its 16 waves each own one contiguous sixteenth of
+// H (in 16-wide chunks) and issue the loads of 8 chunks before their MFMAs,
+// so a wave waits about one memory latency per 8 chunks; the 16 partial tiles
+// are added through LDS.  Within a chunk lane (i, q) = (lane % 16, lane / 16)
+// feeds A[i][q] = x[t0+i][c+4q+r] and B[q][i] = Wr[e0+i][c+4q+r] to the r-th
+// of four MFMAs, so the four MFMAs together contract the 16 inputs c..c+15
+// (each lane reads 4 consecutive inputs with one vector load).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x,
-                                                            const float* __restrict__ wr,
-                                                            const float* __restrict__ gate_row,
-                                                            int T, int H, int E, float* out,
-                                                            int ld) {
+constexpr int kLogitWaves = 16;
+constexpr int kLogitBatch = 8;  // chunks whose loads are in flight together
+
+__global__ __launch_bounds__(64 * kLogitWaves) void router_logits_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ wr,
+    const float* __restrict__ gate_row, int T, int H, int E, float* out, int ld) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i = lane & 15, q = lane >> 4;
   const int t = blockIdx.x * 16 + i;
@@ -42,38 +44,45 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
   if (e < E) wrow = wr + (int64_t)e * H;
   else if (e == E && gate_row) wrow = gate_row;
 
+  const int nch = H / 16;
+  const int c0 = (int)((int64_t)nch * wave / kLogitWaves);
+  const int c1 = (int)((int64_t)nch * (wave + 1) / kLogitWaves);
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int c = wave * 16; c < H; c += 64) {
-    const int kk = c + 4 * q;
-    float a[4] = {0.f, 0.f, 0.f, 0.f}, b[4] = {0.f, 0.f, 0.f, 0.f};
-    if (xrow) {
-      const uint2 v = *reinterpret_cast<const uint2*>(xrow + kk);
-      a[0] = __uint_as_float(v.x << 16);
-      a[1] = __uint_as_float(v.x & 0xFFFF0000u);
-      a[2] = __uint_as_float(v.y << 16);
-      a[3] = __uint_as_float(v.y & 0xFFFF0000u);
-    }
-    if (wrow) {
-      const float4 v = *reinterpret_cast<const float4*>(wrow + kk);
-      b[0] = v.x; b[1] = v.y; b[2] = v.z; b[3] = v.w;
+  for (int cb = c0; cb < c1; cb += kLogitBatch) {
+    uint2 xv[kLogitBatch];
+    float4 wv[kLogitBatch];
+#pragma unroll
+    for (int u = 0; u < kLogitBatch; ++u) {
+      const int kk = 16 * min(cb + u, c1 - 1) + 4 * q;
+      xv[u] = xrow ? *reinterpret_cast<const uint2*>(xrow + kk) : make_uint2(0, 0);
+      wv[u] = wrow ? *reinterpret_cast<const float4*>(wrow + kk) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r], b[r], acc, 0, 0, 0);
+    for (int u = 0; u < kLogitBatch; ++u) {
+      if (cb + u < c1) {
+        const float a[4] = {__uint_as_float(xv[u].x << 16), __uint_as_float(xv[u].x & 0xFFFF0000u),
+                            __uint_as_float(xv[u].y << 16), __uint_as_float(xv[u].y & 0xFFFF0000u)};
+        const float bb[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r], bb[r], acc, 0, 0, 0);
+      }
+    }
   }
 
-  __shared__ f32x4_t part[4][64];
+  __shared__ f32x4_t part[kLogitWaves][64];
   part[wave][lane] = acc;
   __syncthreads();
   if (wave == 0) {
-    f32x4_t s = part[0][lane];
+    f32x4_t sum = part[0][lane];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) s += part[w][lane];
+    for (int w = 1; w < kLogitWaves; ++w) sum += part[w][lane];
     // D[4*(lane/16) + r][lane % 16]: row = token, column = router row.
     const int col = blockIdx.y * 16 + i;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = blockIdx.x * 16 + 4 * q + r;
-      if (row < T && col < ld) out[(int64_t)row * ld + col] = s[r];
+      if (row < T && col < ld) out[(int64_t)row * ld + col] = sum[r];
     }
   }
 }
@@ -81,8 +90,8 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
 hipError_t launch_router_logits(const uint16_t* x, const float* wr, const float* gate_row, int T,
                                 int H, int E, float* out, int ld, const Launch& L) {
   dim3 grid((T + 15) / 16, (ld + 15) / 16);
-  MOE_LAUNCH(L, router_logits_kernel, grid, dim3(256), 0, x, wr, gate_row, T, H, E, out,
-                     ld);
+  MOE_LAUNCH(L, router_logits_kernel, grid, dim3(64 * kLogitWaves), 0, x, wr, gate_row, T, H, E,
+             out, ld);
   return hipGetLastError();
 }
 
@@ -305,11 +314,114 @@ __global__ __launch_bounds__(256) void schedule_kernel(const int32_t* __restrict
   write_schedule(cnt, offs, E, max_tiles, sched, tmp);
 }
 
+// ---------------------------------------------------------------------------
+// Permutation over many workgroups (large slot counts).  Slots are cut into
+// blocks of kThreads; (1) each block counts its slots per expert, (2) one
+// workgroup turns the counts into bucket offsets, each block's first position
+// inside every bucket, and the tile schedule, (3) each block scatters its
+// slots, ranking equal experts in slot order exactly as the one-workgroup
+// version does, so the result is the same stable permutation.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void block_count_kernel(const int32_t* __restrict__ idx,
+                                                               int S, int E,
+                                                               int32_t* __restrict__ bcnt) {
+  __shared__ int cnt[kMaxE];
+  for (int i = threadIdx.x; i < kMaxE; i += kThreads) cnt[i] = 0;
+  __syncthreads();
+  const int s = blockIdx.x * kThreads + threadIdx.x;
+  if (s < S) {
+    const int e = idx[s];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kThreads) bcnt[(int64_t)blockIdx.x * E + e] = cnt[e];
+}
+
+__global__ __launch_bounds__(256) void block_offsets_kernel(int32_t* __restrict__ bcnt, int nblk,
+                                                            int E, int32_t* __restrict__ off,
+                                                            int32_t* __restrict__ sched,
+                                                            int max_tiles) {
+  __shared__ int cnt[kMaxE];
+  __shared__ int offs[kMaxE];
+  __shared__ int tmp[4];
+  const int e = threadIdx.x;
+  int run = 0;
+  if (e < E)
+    for (int b0 = 0; b0 < nblk; b0 += 8) {
+      int c[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) c[u] = (b0 + u < nblk) ? bcnt[(int64_t)(b0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (b0 + u < nblk) {
+          bcnt[(int64_t)(b0 + u) * E + e] = run;  // block's position inside bucket e
+          run += c[u];
+        }
+    }
+  int total;
+  const int pre = scan256(e < E ? run : 0, tmp, &total);
+  if (e < E) {
+    cnt[e] = run;
+    offs[e] = pre;
+    off[e] = pre;
+  }
+  if (e == 0) off[E] = total;
+  __syncthreads();
+  if (sched) write_schedule(cnt, offs, E, max_tiles, sched, tmp);
+}
+
+__global__ __launch_bounds__(kThreads) void block_scatter_kernel(const int32_t* __restrict__ idx,
+                                                                 int S, int E,
+                                                                 const int32_t* __restrict__ bpos,
+                                                                 const int32_t* __restrict__ off,
+                                                                 int32_t* __restrict__ sorted,
+                                                                 int32_t* __restrict__ row_of) {
+  __shared__ int wcnt[kWaves][kMaxE];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int s = blockIdx.x * kThreads + tid;
+  int e = (s < S) ? idx[s] : -1;
+  if (e >= E) e = -1;
+  for (int i = tid; i < kWaves * kMaxE; i += kThreads) (&wcnt[0][0])[i] = 0;
+  __syncthreads();
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int key = e + 1;
+  uint64_t peers = ~0ull;
+#pragma unroll
+  for (int bit = 0; bit < 9; ++bit) {
+    const uint64_t bal = __ballot((key >> bit) & 1);
+    peers &= ((key >> bit) & 1) ? bal : ~bal;
+  }
+  const int rank = __popcll(peers & lt_mask);
+  if (e >= 0 && rank == 0) wcnt[wave][e] = __popcll(peers);
+  __syncthreads();
+  if (e >= 0) {
+    int pos = off[e] + bpos[(int64_t)blockIdx.x * E + e] + rank;
+    for (int w = 0; w < wave; ++w) pos += wcnt[w][e];
+    sorted[pos] = s;
+    row_of[s] = pos;
+  } else if (s < S) {
+    row_of[s] = -1;
+  }
+}
+
 hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* off,
-                          int32_t* sorted, int32_t* row_of, int32_t* sched, const Launch& L) {
-  const int max_tiles = (int)sched_max_tiles((int64_t)T * k, E);
-  MOE_LAUNCH(L, permute_kernel, dim3(1), dim3(kThreads), 0, idx, T * k, E, off, sorted,
-                     row_of, sched, max_tiles);
+                          int32_t* sorted, int32_t* row_of, int32_t* sched, int32_t* scratch,
+                          const Launch& L) {
+  const int S = T * k;
+  const int max_tiles = (int)sched_max_tiles((int64_t)S, E);
+  if (!scratch || S <= kPermuteOneBlockMax) {
+    MOE_LAUNCH(L, permute_kernel, dim3(1), dim3(kThreads), 0, idx, S, E, off, sorted, row_of,
+               sched, max_tiles);
+    return hipGetLastError();
+  }
+  // the first launch carries the caller's start event, the last its stop
+  const int nblk = (S + kThreads - 1) / kThreads;
+  const Launch first{L.st, L.start, nullptr}, mid{L.st, nullptr, nullptr}, last{L.st, nullptr, L.stop};
+  MOE_LAUNCH(first, block_count_kernel, dim3(nblk), dim3(kThreads), 0, idx, S, E, scratch);
+  MOE_LAUNCH(mid, block_offsets_kernel, dim3(1), dim3(256), 0, scratch, nblk, E, off, sched,
+             max_tiles);
+  MOE_LAUNCH(last, block_scatter_kernel, dim3(nblk), dim3(kThreads), 0, idx, S, E, scratch, off,
+             sorted, row_of);
   return hipGetLastError();
 }
 
