@@ -95,25 +95,44 @@ def stage_work(wl, T, U, gemm):
     """Algorithmic bytes and flops of the gate/up and down launches of one call.
 
     Counted: the touched experts' packed nibbles and fp16 scales, activations
-    in, hidden rows out/in, y out.  Not counted: untouched experts."""
+    in, hidden rows (fp16) out/in, y out.  Not counted: untouched experts.  On
+    the MFMA path the shared expert's tiles run inside the routed launches, so
+    its work is added to theirs."""
     H, I, slots = wl.H, wl.I, T * wl.k
-    act = 2 if gemm else 4
+    act = 2
     gu_w = U * 2 * (I * H // 2 + I * (H // 32) * 2)
     dn_w = U * (H * I // 2 + H * (I // 32) * 2)
     sh_gu = sh_dn = 0
     if wl.SI:
         sh_gu = 2 * (wl.SI * H // 2 + wl.SI * (H // 32) * 2) + T * H * 2 + T * wl.SI * act
         sh_dn = (H * wl.SI // 2 + H * (wl.SI // 32) * 2) + T * wl.SI * act + T * H * 4
-    return {
+    work = {
         "gate_up": {"bytes": gu_w + T * H * 2 + slots * I * act, "flops": 4.0 * slots * H * I},
         "down": {"bytes": dn_w + slots * I * act + T * H * 4, "flops": 2.0 * slots * H * I},
         "shared_gate_up": {"bytes": sh_gu, "flops": 4.0 * T * H * wl.SI},
         "shared_down": {"bytes": sh_dn, "flops": 2.0 * T * H * wl.SI},
     }
+    if gemm:
+        for routed, shared in (("gate_up", "shared_gate_up"), ("down", "shared_down")):
+            for key in ("bytes", "flops"):
+                work[routed][key] += work[shared][key]
+                work[shared][key] = 0
+    return work
 
 
-def build_sets(wl, nsets, seed0=0):
+def build_sets(wl, nsets, seed0=0, tiled=False):
+    """Device-resident inputs; with tiled=True the planes are packed into the
+    tiled layout once, as at weight-load time."""
     import torch
+
+    import quantized_expert_mlp_amd as moe
+
+    def pack(plane, N, K):
+        q, s_ = plane
+        dq, ds = torch.empty_like(q), torch.empty_like(s_)
+        moe.moe_pack_weights((q, s_), q.numel() // (N * K // 2), N, K, (dq, ds))
+        torch.cuda.synchronize()
+        return dq, ds
 
     def dev(a):
         a = np.ascontiguousarray(a)
@@ -131,6 +150,12 @@ def build_sets(wl, nsets, seed0=0):
                 (dev(inp.shared[p][0]), dev(inp.shared[p][1])) for p in S.PLANES],
             "shared_gate": None if inp.shared_gate is None else dev(inp.shared_gate),
         }
+        if tiled:
+            dims = {"gate": (wl.I, wl.H), "up": (wl.I, wl.H), "down": (wl.H, wl.I)}
+            d["planes"] = {p: pack(pl, *dims[p]) for p, pl in d["planes"].items()}
+            if d["shared"] is not None:
+                sd = [(wl.SI, wl.H), (wl.SI, wl.H), (wl.H, wl.SI)]
+                d["shared"] = [pack(pl, *nk) for pl, nk in zip(d["shared"], sd)]
         sets.append(d)
         inp.planes = None  # host copies no longer needed
     return sets
@@ -170,6 +195,9 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="decode", choices=list(S.WORKLOADS))
+    ap.add_argument("--layout", default="rows", choices=["rows", "tiled"],
+                    help="weight plane layout (tiled: packed once with moe_pack_weights, "
+                         "served by the MFMA path)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -203,7 +231,8 @@ def main():
     nsets = WEIGHT_SETS.get(wl.name, 1)
     log("workload %s: %s; %d weight set(s)" % (wl.name, wl.description, nsets))
     t0 = time.perf_counter()
-    sets = build_sets(wl, nsets)
+    tiled = args.layout == "tiled"
+    sets = build_sets(wl, nsets, tiled=tiled)
     log("inputs resident in %.1f s" % (time.perf_counter() - t0))
 
     # per-step inputs: logits pool (given-logit workloads) or weight-set rotation
@@ -220,8 +249,9 @@ def main():
             touched.append(touched_experts(L, wl.k))
     nvar = len(pool) if pool is not None else len(sets)
 
-    sh = moe.make_shape(T, wl.H, wl.E, wl.k, wl.I, wl.SI)
-    gemm = (T * wl.k) >= 8 * wl.E  # the library's AUTO rule (MOE_PATH_AUTO)
+    sh = moe.make_shape(T, wl.H, wl.E, wl.k, wl.I, wl.SI,
+                        layout=moe.MOE_LAYOUT_TILED if tiled else moe.MOE_LAYOUT_ROWS)
+    gemm = tiled or (T * wl.k) >= 8 * wl.E  # the library's AUTO rule (MOE_PATH_AUTO)
     nbytes = moe.moe_workspace_bytes(sh)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     y = torch.empty((T, wl.H), dtype=torch.float32, device="cuda")
@@ -306,6 +336,7 @@ def main():
         "config": {"workload": wl.name, "description": wl.description, "T": T, "H": wl.H,
                    "E": wl.E, "k": wl.k, "I": wl.I, "SI": wl.SI,
                    "weights": "int4 offset-binary, fp16 scale per 32 inputs",
+                   "layout": args.layout,
                    "expert_path": "grouped fp16 MFMA GEMM" if gemm else "streaming int4 GEMV",
                    "input_rotation": ("%d logits rows" % nvar) if pool is not None
                    else ("%d weight sets" % nvar)},

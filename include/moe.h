@@ -34,6 +34,16 @@
  * with a plain copy, no repacking).  s = fp16 scale bits, uint16 [E][N][K/32],
  * one scale per 32 consecutive inputs along K.  Gate and up planes have N = I,
  * K = H; down planes have N = H, K = I.  q and s must be 16-byte aligned.
+ *
+ * Tiled planes (moe_shape.layout = MOE_LAYOUT_TILED, written by
+ * moe_pack_weights): the same bytes regrouped so that the grouped MFMA GEMM
+ * reads each weight block as one contiguous kilobyte.  Per expert, the block
+ * of rows 32*b .. 32*b+31 and inputs 64*c .. 64*c+63 is 1024 bytes at byte
+ * ((b*(K/64) + c) * 1024); inside it, the 16 bytes of row 32*b+j for scale
+ * group 2*c+h (inputs 64*c+32*h .. +31, same nibble order as above) sit at
+ * byte (32*h + j) * 16.  The scales of that block are 64 fp16 values at
+ * element ((b*(K/64) + c) * 64), the one of row 32*b+j, group 2*c+h at index
+ * 32*h + j.  Expert e's plane starts where it does in the row layout.
  */
 #ifndef MOE_H_
 #define MOE_H_
@@ -60,6 +70,10 @@ enum moe_status {
  * expert are few (decode) and the grouped MFMA GEMM otherwise (prefill). */
 enum moe_path { MOE_PATH_AUTO = 0, MOE_PATH_GEMV = 1, MOE_PATH_GEMM = 2 };
 
+/* Weight plane layout (see above).  TILED planes are served by the grouped
+ * MFMA GEMM only (path AUTO or GEMM); ROWS planes by both paths. */
+enum moe_layout { MOE_LAYOUT_ROWS = 0, MOE_LAYOUT_TILED = 1 };
+
 /* One int4 plane set: q [E][N][K/2] packed nibbles, s [E][N][K/32] fp16 bits. */
 typedef struct {
   const uint8_t *q;
@@ -68,7 +82,8 @@ typedef struct {
 
 /* Layer shape.  T tokens, H hidden, E experts, k picks per token, I expert
  * intermediate, SI shared-expert intermediate (0 = none), group must be 32,
- * route_scale multiplies the renormalised weights, path is a moe_path.
+ * route_scale multiplies the renormalised weights, path is a moe_path,
+ * layout a moe_layout (every plane of the call, shared ones included).
  * Served: 1 <= k <= min(E, 64), E <= 256, H % 64 == 0, I % 64 == 0,
  * SI % 64 == 0, T >= 1, T*k < 2^31. */
 typedef struct {
@@ -76,6 +91,7 @@ typedef struct {
   int32_t group;
   float route_scale;
   int32_t path;
+  int32_t layout;
 } moe_shape;
 
 /*
@@ -186,6 +202,20 @@ int moe_layer_profiled(const moe_shape *shape, const uint16_t *x, const float *l
                        int32_t *idx_out, float *w_out, float *logits_out, void *ws,
                        size_t ws_bytes, moe_stream_t stream, void *const *events,
                        int32_t n_events);
+
+/*
+ * Regroup E experts' int4 planes from the row layout into the tiled layout
+ * (see above), for the grouped MFMA GEMM's contiguous weight reads.  A pure
+ * byte permutation of q and of s; the values are unchanged.  Meant to run once
+ * when weights are loaded.
+ *   src    : row-layout planes, q [E][N][K/2], s [E][N][K/32].
+ *   dst    : tiled planes of the same sizes (caller-allocated, 16-byte
+ *            aligned, not overlapping src).
+ * Errors: INVALID_ARG (null, E < 1, N < 1, N % 32 != 0, K % 64 != 0,
+ *         misaligned, overlapping).
+ */
+int moe_pack_weights(moe_q4 src, int32_t E, int32_t N, int32_t K, moe_q4 dst,
+                     moe_stream_t stream);
 
 /* Scratch bytes moe_layer and moe_expert_mlp need for this shape (0 if the
  * shape is not served).  Host only; enqueues nothing. */

@@ -19,11 +19,12 @@ LIB_PATH = os.path.join(PKG, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_PATH_AUTO, MOE_PATH_GEMV, MOE_PATH_GEMM = range(3)
+MOE_LAYOUT_ROWS, MOE_LAYOUT_TILED = range(2)
 
 # Every symbol include/moe.h declares.
 EXPORTS = ("moe_router_topk", "moe_permute", "moe_expert_mlp", "moe_layer",
-           "moe_layer_profiled", "moe_workspace_bytes", "moe_status_string",
-           "moe_debug_dequant_int4")
+           "moe_layer_profiled", "moe_pack_weights", "moe_workspace_bytes",
+           "moe_status_string", "moe_debug_dequant_int4")
 STAGES = ("start", "logits", "topk", "permute", "activations", "gate_up", "shared_gate_up",
           "down", "shared_down")
 
@@ -42,7 +43,7 @@ class moe_shape(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("E", ctypes.c_int32),
                 ("k", ctypes.c_int32), ("I", ctypes.c_int32), ("SI", ctypes.c_int32),
                 ("group", ctypes.c_int32), ("route_scale", ctypes.c_float),
-                ("path", ctypes.c_int32)]
+                ("path", ctypes.c_int32), ("layout", ctypes.c_int32)]
 
 
 _lib = None
@@ -69,8 +70,9 @@ def lib() -> ctypes.CDLL:
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_debug_dequant_int4.argtypes = [moe_q4, i32, i32, i32, P, P]
+        L.moe_pack_weights.argtypes = [moe_q4, i32, i32, i32, moe_q4, P]
         for name in ("moe_router_topk", "moe_permute", "moe_expert_mlp", "moe_layer",
-                     "moe_layer_profiled", "moe_debug_dequant_int4"):
+                     "moe_layer_profiled", "moe_pack_weights", "moe_debug_dequant_int4"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -100,9 +102,10 @@ def _check(fn: str, rc: int) -> None:
         raise MoeError(fn, rc)
 
 
-def make_shape(T, H, E, k, I, SI=0, route_scale=1.0, path=MOE_PATH_AUTO, group=32) -> moe_shape:
+def make_shape(T, H, E, k, I, SI=0, route_scale=1.0, path=MOE_PATH_AUTO, group=32,
+               layout=MOE_LAYOUT_ROWS) -> moe_shape:
     return moe_shape(int(T), int(H), int(E), int(k), int(I), int(SI), int(group),
-                     float(route_scale), int(path))
+                     float(route_scale), int(path), int(layout))
 
 
 def q4(plane: Tuple) -> moe_q4:
@@ -158,6 +161,12 @@ def moe_layer_profiled(shape: moe_shape, x, logits, w_router, gate, up, down,
         ctypes.byref(shape), _ptr(x), _ptr(logits), _ptr(w_router), q4(gate), q4(up), q4(down),
         sh_arr, _ptr(shared_gate), _ptr(y), _ptr(idx_out), _ptr(w_out), _ptr(logits_out),
         _ptr(ws), int(ws_bytes), _stream(stream), ev, len(events)))
+
+
+def moe_pack_weights(src, E, N, K, dst, stream=None) -> None:
+    """Row-layout plane set (q, s) -> tiled layout into dst (q, s) of the same sizes."""
+    _check("moe_pack_weights", lib().moe_pack_weights(q4(src), E, N, K, q4(dst),
+                                                      _stream(stream)))
 
 
 def moe_debug_dequant_int4(plane, N, K, mode, out, stream=None) -> None:

@@ -110,6 +110,7 @@ struct GemmSrc {
   const uint16_t* s[2];  // and their [E][N][K/32] fp16 scales
   uint16_t* hout;        // MODE 0 output, row stride N
   int ksplit;            // MODE 1: K ranges over blockIdx.z
+  int tiled;             // planes in the tiled layout (1 KB per 32 rows x 64 k)
 };
 
 struct GemmArgs {
@@ -179,19 +180,28 @@ __device__ __forceinline__ void gemm_tile(const TileView& tv, const GemmSrc& S, 
   const int K = S.K, N = S.N;
   const int n = k1 - k0;  // steps of this workgroup
 
-  // weight row pointers of this lane (rows past N re-read row N-1; their
-  // columns are never stored)
+  // Weight pointers of this lane at step 0 (columns past N re-read valid
+  // rows; they are never stored).  Row layout: row col0+32*ns+j, group
+  // 2*step+hf, consecutive steps 2 groups apart.  Tiled layout: lane's 16
+  // bytes of the 1 KB block (subtile, step), consecutive steps 1 KB apart.
   const u32x4_t* bq_ptr[NS][P];
   const uint16_t* bs_ptr[NS][P];
   const int64_t plane = (int64_t)N * (K / 2), splane = (int64_t)N * (K / 32);
+  const int stride = S.tiled ? 64 : 2;  // per K step, in 16-byte / scale units
 #pragma unroll
   for (int ns = 0; ns < NS; ++ns) {
-    const int row = min(col0 + ns * 32 + j, N - 1);
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-      bq_ptr[ns][p] = reinterpret_cast<const u32x4_t*>(S.q[p] + tv.e * plane + (int64_t)row * (K / 2)) +
-                      hf + 2 * k0;
-      bs_ptr[ns][p] = S.s[p] + tv.e * splane + (int64_t)row * (K / 32) + hf + 2 * k0;
+      if (S.tiled) {
+        const int64_t blk = (int64_t)(min(col0 + ns * 32, N - 32) / 32) * (K / 64) + k0;
+        bq_ptr[ns][p] = reinterpret_cast<const u32x4_t*>(S.q[p] + tv.e * plane + blk * 1024) + lane;
+        bs_ptr[ns][p] = S.s[p] + tv.e * splane + blk * 64 + lane;
+      } else {
+        const int row = min(col0 + ns * 32 + j, N - 1);
+        bq_ptr[ns][p] = reinterpret_cast<const u32x4_t*>(S.q[p] + tv.e * plane + (int64_t)row * (K / 2)) +
+                        hf + 2 * k0;
+        bs_ptr[ns][p] = S.s[p] + tv.e * splane + (int64_t)row * (K / 32) + hf + 2 * k0;
+      }
     }
   }
   auto b_load = [&](BStage<P, NS>& st, int s) __attribute__((always_inline)) {
@@ -199,8 +209,8 @@ __device__ __forceinline__ void gemm_tile(const TileView& tv, const GemmSrc& S, 
     for (int ns = 0; ns < NS; ++ns)
 #pragma unroll
       for (int p = 0; p < P; ++p) {
-        st.q[ns][p] = bq_ptr[ns][p][2 * s];
-        st.s[ns][p] = bs_ptr[ns][p][2 * s];
+        st.q[ns][p] = bq_ptr[ns][p][stride * s];
+        st.s[ns][p] = bs_ptr[ns][p][stride * s];
       }
   };
   const int chunk = threadIdx.x & 7;
@@ -434,8 +444,9 @@ hipError_t launch_gemm_gate_up(const Buckets& b, int max_tiles, const uint16_t* 
                                int I, const uint8_t* gq, const uint16_t* gs,
                                const uint8_t* uq, const uint16_t* us, uint16_t* h16,
                                const SharedGemm* shared, float* y_zero, int64_t y_elems,
-                               const Launch& L) {
+                               bool tiled, const Launch& L) {
   GemmArgs a{};
+  a.src[0].tiled = a.src[1].tiled = tiled ? 1 : 0;
   a.y_zero = y_zero;
   a.y_elems = y_elems;
   GemmSrc& r = a.src[0];
@@ -468,8 +479,9 @@ hipError_t launch_gemm_gate_up(const Buckets& b, int max_tiles, const uint16_t* 
 
 hipError_t launch_gemm_down(const Buckets& b, int max_tiles, const uint16_t* h16, int H, int I,
                             const uint8_t* dq, const uint16_t* ds, const float* w, float* y,
-                            const SharedGemm* shared, const Launch& L) {
+                            const SharedGemm* shared, bool tiled, const Launch& L) {
   GemmArgs a{};
+  a.src[0].tiled = a.src[1].tiled = tiled ? 1 : 0;
   GemmSrc& r = a.src[0];
   r.act = h16;
   r.K = I;

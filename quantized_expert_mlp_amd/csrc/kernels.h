@@ -117,6 +117,10 @@ hipError_t launch_gemv_down(const Buckets& b, int max_buckets, const uint16_t* h
 bool gemv_supported(int K);
 
 // Grouped MFMA GEMM (prefill), fp16 operands with fp32 accumulation.
+// Row layout -> tiled layout of E experts' planes q [E][N][K/2], s [E][N][K/32].
+hipError_t launch_pack_weights(const uint8_t* sq, const uint16_t* ss, int E, int N, int K,
+                               uint8_t* dq, uint16_t* ds, const Launch& L);
+
 // bf16 x [T][H] -> fp16 copy with each block of 8 in the order 0,4,1,5,2,6,3,7.
 hipError_t launch_convert_x16(const uint16_t* x, int T, int H, uint16_t* x16, const Launch& L);
 
@@ -136,14 +140,15 @@ struct SharedGemm {
 // x16: the activations in fp16, operand order (launch_convert_x16).  The
 // launch also clears y_zero[0 .. y_elems) (y_elems a multiple of 4) for the
 // down pass's atomic combine.
+// tiled: every plane (shared ones included) is in the tiled layout.
 hipError_t launch_gemm_gate_up(const Buckets& b, int max_tiles, const uint16_t* x16, int H,
                                int I, const uint8_t* gq, const uint16_t* gs,
                                const uint8_t* uq, const uint16_t* us, uint16_t* h16,
                                const SharedGemm* shared, float* y_zero, int64_t y_elems,
-                               const Launch& L);
+                               bool tiled, const Launch& L);
 hipError_t launch_gemm_down(const Buckets& b, int max_tiles, const uint16_t* h16, int H, int I,
                             const uint8_t* dq, const uint16_t* ds, const float* w, float* y,
-                            const SharedGemm* shared, const Launch& L);
+                            const SharedGemm* shared, bool tiled, const Launch& L);
 
 hipError_t launch_debug_dequant(const uint8_t* q, const uint16_t* s, int N, int K, int mode,
                                 float* out, const Launch& L);

@@ -1,5 +1,5 @@
-// Small helper kernels: the fp16 activation copy for the MFMA path and the
-// int4 decode test hook.
+// Small helper kernels: the fp16 activation copy for the MFMA path, the
+// tiled weight packing and the int4 decode test hook.
 #include "device.h"
 #include "kernels.h"
 
@@ -22,6 +22,39 @@ hipError_t launch_convert_x16(const uint16_t* x, int T, int H, uint16_t* x16, co
   if (grid > 8192) grid = 8192;
   if (grid < 1) grid = 1;
   MOE_LAUNCH(L, convert_x16_kernel, dim3(grid), dim3(256), 0, x, blocks8, x16);
+  return hipGetLastError();
+}
+
+// Row layout -> tiled layout (see the moe_pack_weights contract): thread c
+// moves destination q chunk c (16 bytes) and destination scale c; per expert
+// both number N*K/32.
+__global__ __launch_bounds__(256) void pack_weights_kernel(const uint8_t* __restrict__ sq,
+                                                           const uint16_t* __restrict__ ss,
+                                                           int64_t total, int N, int K,
+                                                           uint8_t* __restrict__ dq,
+                                                           uint16_t* __restrict__ ds) {
+  const int64_t per = (int64_t)N * K / 32;
+  const int nc = K / 64;
+  const int64_t nthr = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < total; c += nthr) {
+    const int64_t e = c / per, r = c % per;
+    const int64_t tile = r / 64;
+    const int within = (int)(r % 64), h = within / 32, j = within % 32;
+    const int64_t b = tile / nc, cc = tile % nc;
+    const int64_t row = e * N + 32 * b + j;
+    reinterpret_cast<u32x4_t*>(dq)[c] =
+        *reinterpret_cast<const u32x4_t*>(sq + row * (K / 2) + 32 * cc + 16 * h);
+    ds[c] = ss[row * (K / 32) + 2 * cc + h];
+  }
+}
+
+hipError_t launch_pack_weights(const uint8_t* sq, const uint16_t* ss, int E, int N, int K,
+                               uint8_t* dq, uint16_t* ds, const Launch& L) {
+  const int64_t total = (int64_t)E * N * K / 32;
+  int64_t grid = (total + 255) / 256;
+  if (grid > 16384) grid = 16384;
+  MOE_LAUNCH(L, pack_weights_kernel, dim3((unsigned)grid), dim3(256), 0, sq, ss, total, N, K, dq,
+             ds);
   return hipGetLastError();
 }
 

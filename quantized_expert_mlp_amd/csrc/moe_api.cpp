@@ -23,6 +23,7 @@ int check_shape(const moe_shape* sh) {
   if (sh->k > sh->E) return MOE_ERR_INVALID_ARG;
   if (sh->group != 32) return MOE_ERR_UNSUPPORTED;
   if (sh->path < MOE_PATH_AUTO || sh->path > MOE_PATH_GEMM) return MOE_ERR_INVALID_ARG;
+  if (sh->layout != MOE_LAYOUT_ROWS && sh->layout != MOE_LAYOUT_TILED) return MOE_ERR_INVALID_ARG;
   if (sh->E > 256 || sh->k > 64) return MOE_ERR_UNSUPPORTED;
   if (sh->H % 64 || sh->I % 64 || sh->SI % 64) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)sh->T * sh->k >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
@@ -41,14 +42,14 @@ int pick_gemm(const moe_shape* sh, bool* gemm) {
   const int64_t slots = (int64_t)sh->T * sh->k;
   switch (sh->path) {
     case MOE_PATH_GEMV:
-      if (!gemv_ok(sh)) return MOE_ERR_UNSUPPORTED;
+      if (!gemv_ok(sh) || sh->layout == MOE_LAYOUT_TILED) return MOE_ERR_UNSUPPORTED;
       *gemm = false;
       return MOE_OK;
     case MOE_PATH_GEMM:
       *gemm = true;
       return MOE_OK;
     default:
-      *gemm = !gemv_ok(sh) || slots >= 8 * (int64_t)sh->E;
+      *gemm = sh->layout == MOE_LAYOUT_TILED || !gemv_ok(sh) || slots >= 8 * (int64_t)sh->E;
       return MOE_OK;
   }
 }
@@ -177,11 +178,12 @@ int run_mlp(const moe_shape* sh, bool gemm, const Layout& L, void* ws, const uin
   const moe::SharedGemm* sgp = shared ? &sgm : nullptr;
   err = moe::launch_convert_x16(x, T, H, x16, sg.at(MOE_STAGE_ACTIVATIONS));
   if (err != hipSuccess) return MOE_ERR_HIP;
+  const bool tiled = sh->layout == MOE_LAYOUT_TILED;
   err = moe::launch_gemm_gate_up(routed, max_tiles, x16, H, I, gate.q, gate.s, up.q, up.s, h16,
-                                 sgp, y, y_elems, sg.at(MOE_STAGE_GATE_UP));
+                                 sgp, y, y_elems, tiled, sg.at(MOE_STAGE_GATE_UP));
   if (err != hipSuccess) return MOE_ERR_HIP;
   if (!sg.skip(MOE_STAGE_SHARED_GATE_UP)) return MOE_ERR_HIP;
-  err = moe::launch_gemm_down(routed, max_tiles, h16, H, I, down.q, down.s, w, y, sgp,
+  err = moe::launch_gemm_down(routed, max_tiles, h16, H, I, down.q, down.s, w, y, sgp, tiled,
                               sg.at(MOE_STAGE_DOWN));
   if (err != hipSuccess) return MOE_ERR_HIP;
   if (!sg.skip(MOE_STAGE_SHARED_DOWN)) return MOE_ERR_HIP;
@@ -217,6 +219,23 @@ int moe_router_topk(const float* logits, int32_t T, int32_t E, int32_t k, float 
   if (E > 256 || k > 64) return MOE_ERR_UNSUPPORTED;
   return hip_status(moe::launch_topk(logits, E, T, E, k, route_scale, idx, w,
                                      moe::Launch{reinterpret_cast<hipStream_t>(stream)}));
+}
+
+int moe_pack_weights(moe_q4 src, int32_t E, int32_t N, int32_t K, moe_q4 dst,
+                     moe_stream_t stream) {
+  if (!plane_ok(src) || !plane_ok(dst)) return MOE_ERR_INVALID_ARG;
+  if (E < 1 || N < 1 || K < 64 || N % 32 || K % 64) return MOE_ERR_INVALID_ARG;
+  const uintptr_t qb = (uintptr_t)E * N * (K / 2), sb = (uintptr_t)E * N * (K / 32) * 2;
+  auto overlap = [](const void* a, uintptr_t na, const void* b, uintptr_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+  };
+  if (overlap(src.q, qb, dst.q, qb) || overlap(src.s, sb, dst.s, sb) ||
+      overlap(src.q, qb, dst.s, sb) || overlap(src.s, sb, dst.q, qb))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_pack_weights(src.q, src.s, E, N, K, const_cast<uint8_t*>(dst.q),
+                                             const_cast<uint16_t*>(dst.s),
+                                             moe::Launch{reinterpret_cast<hipStream_t>(stream)}));
 }
 
 int moe_permute(const int32_t* idx, int32_t T, int32_t k, int32_t E, int32_t* off,

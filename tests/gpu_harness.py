@@ -48,16 +48,53 @@ class DeviceLayer:
         self.shared = None
         if inp.shared is not None:
             self.shared = [(dev(inp.shared[p][0]), dev(inp.shared[p][1])) for p in S.PLANES]
+        self.layout = moe.MOE_LAYOUT_ROWS
+
+    def tiled(self) -> "DeviceLayer":
+        """A copy whose planes are packed into the tiled layout on the device."""
+        t = DeviceLayer.__new__(DeviceLayer)
+        t.__dict__.update(self.__dict__)
+        t.layout = moe.MOE_LAYOUT_TILED
+        wl = self.inp.wl
+        dims = {"gate": (wl.I, wl.H), "up": (wl.I, wl.H), "down": (wl.H, wl.I)}
+        t.planes = {p: pack_plane(self.planes[p], *dims[p]) for p in self.planes}
+        if self.shared is not None:
+            sd = [(wl.SI, wl.H), (wl.SI, wl.H), (wl.H, wl.SI)]
+            t.shared = [pack_plane(pl, *nk) for pl, nk in zip(self.shared, sd)]
+        torch.cuda.synchronize()
+        return t
+
+
+def pack_plane(plane, N, K):
+    """moe_pack_weights of one device plane set (E inferred from the sizes)."""
+    q, s = plane
+    E = q.numel() // (N * K // 2)
+    dq, ds = torch.empty_like(q), torch.empty_like(s)
+    moe.moe_pack_weights((q, s), E, N, K, (dq, ds))
+    return dq, ds
+
+
+def tiled_reference(q: np.ndarray, s: np.ndarray):
+    """The tiled layout written out with numpy index arithmetic: per expert,
+    block (b, c) of rows 32b..32b+31 and inputs 64c..64c+63 is 1 KB; within it
+    row 32b+j's 16 bytes of scale group 2c+h sit at (32h + j) * 16; its scales
+    at (b*(K/64) + c) * 64 + 32h + j."""
+    E, N, Kh = q.shape
+    K = 2 * Kh
+    qt = q.reshape(E, N // 32, 32, K // 64, 2, 16).transpose(0, 1, 3, 4, 2, 5)
+    st = s.reshape(E, N // 32, 32, K // 64, 2).transpose(0, 1, 3, 4, 2)
+    return np.ascontiguousarray(qt).reshape(E, N, Kh), np.ascontiguousarray(st).reshape(E, N, K // 32)
 
 
 def run_layer(d: DeviceLayer, logits=None, use_router=False, path=moe.MOE_PATH_AUTO,
               route_scale=1.0, ws_extra=0):
     """moe_layer through the C ABI.  logits: host array to feed (given logits),
-    else the inputs' own; use_router: compute logits from w_router."""
+    else the inputs' own; use_router: compute logits from w_router.  The
+    planes' layout is the DeviceLayer's."""
     wl = d.inp.wl
     T = d.inp.x.shape[0]
     sh = moe.make_shape(T, wl.H, wl.E, wl.k, wl.I, wl.SI if d.shared else 0,
-                        route_scale=route_scale, path=path)
+                        route_scale=route_scale, path=path, layout=d.layout)
     nbytes = moe.moe_workspace_bytes(sh)
     assert nbytes > 0
     ws = torch.empty(nbytes + ws_extra, dtype=torch.uint8, device="cuda")

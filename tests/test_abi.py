@@ -115,6 +115,28 @@ def test_expert_mlp_rejects(L):
     assert f(*args(shape=_shape(path=moe.MOE_PATH_GEMV, H=16384))) == moe.MOE_ERR_UNSUPPORTED
 
 
+def test_tiled_layout_shape_rules(L):
+    tiled = dict(layout=moe.MOE_LAYOUT_TILED)
+    assert moe.moe_workspace_bytes(_shape(**tiled)) > 0                      # AUTO -> MFMA path
+    assert moe.moe_workspace_bytes(_shape(path=moe.MOE_PATH_GEMM, **tiled)) > 0
+    assert moe.moe_workspace_bytes(_shape(path=moe.MOE_PATH_GEMV, **tiled)) == 0
+    assert moe.moe_workspace_bytes(_shape(layout=2)) == 0
+
+
+def test_pack_weights_rejects(L):
+    f = L.moe_pack_weights
+    src = moe.moe_q4(FAKE, FAKE + (1 << 24))
+    dst = moe.moe_q4(FAKE + (2 << 24), FAKE + (3 << 24))
+    assert f(moe.moe_q4(None, FAKE), 2, 64, 128, dst, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(src, 2, 64, 128, moe.moe_q4(FAKE + 8, FAKE), None) == moe.MOE_ERR_INVALID_ARG  # align
+    assert f(src, 0, 64, 128, dst, None) == moe.MOE_ERR_INVALID_ARG    # E
+    assert f(src, 2, 48, 128, dst, None) == moe.MOE_ERR_INVALID_ARG    # N % 32
+    assert f(src, 2, 64, 96, dst, None) == moe.MOE_ERR_INVALID_ARG     # K % 64
+    assert f(src, 2, 64, 128, src, None) == moe.MOE_ERR_INVALID_ARG    # in place
+    assert f(src, 2, 64, 128, moe.moe_q4(FAKE + 64, FAKE + (3 << 24)), None) == \
+        moe.MOE_ERR_INVALID_ARG                                        # overlapping q
+
+
 def test_debug_dequant_rejects(L):
     f = L.moe_debug_dequant_int4
     assert f(_q(), 4, 48, 0, FAKE, None) == moe.MOE_ERR_INVALID_ARG   # K % 32

@@ -1,0 +1,68 @@
+"""GPU tests of the tiled weight layout: moe_pack_weights against the layout's
+definition (bit-exact), and the whole layer on tiled planes against the CPU
+oracle, at mid sizes and at the full prefill sizes."""
+import numpy as np
+import pytest
+import torch
+
+import moe_synth as S
+import oracle
+import quantized_expert_mlp_amd as moe
+from gpu_harness import (DeviceLayer, assert_w_close, assert_y_close, dev, host, run_layer, say,
+                         tiled_reference)
+from test_gpu_parity import MID, SAMPLE_ROWS, _oracle_logits, _rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    moe.lib()
+
+
+@pytest.mark.parametrize("E,N,K", [(1, 32, 64), (3, 96, 192), (2, 64, 6144), (4, 1408, 128)])
+def test_pack_matches_layout_definition(E, N, K):
+    say("pack E=%d N=%d K=%d" % (E, N, K))
+    rng = np.random.default_rng([7, E, N, K])
+    q = rng.integers(0, 256, (E, N, K // 2), dtype=np.uint8)
+    s = rng.integers(0, 65536, (E, N, K // 32), dtype=np.uint16)
+    dq = torch.full((E, N, K // 2), 0x5A, dtype=torch.uint8, device="cuda")
+    ds = torch.full((E, N, K // 32), 0x1234, dtype=torch.int16, device="cuda")
+    moe.moe_pack_weights((dev(q), dev(s)), E, N, K, (dq, ds))
+    torch.cuda.synchronize()
+    q_ref, s_ref = tiled_reference(q, s)
+    assert np.array_equal(host(dq), q_ref)
+    assert np.array_equal(host(ds, np.uint16), s_ref)
+
+
+@pytest.mark.parametrize("wl", MID, ids=[w.name for w in MID])
+def test_layer_mid_tiled(wl):
+    say("tiled layer %s" % wl.name)
+    inp = S.make_layer_inputs(wl, seed=0)
+    d = DeviceLayer(inp).tiled()
+    L = _oracle_logits(inp)
+    y_ref, idx_ref, w_ref = oracle.layer(inp.x, L, wl.k, inp.planes, inp.shared, inp.shared_gate,
+                                         route_scale=0.75)
+    y, idx, w, lo = run_layer(d, logits=L, route_scale=0.75)
+    assert np.array_equal(idx, idx_ref)
+    assert_w_close(w, w_ref, wl.name)
+    assert_y_close(y, y_ref, "%s tiled" % wl.name)
+
+
+@pytest.mark.parametrize("name", ["prefill_shared", "prefill_skewed"])
+def test_layer_full_size_tiled(name):
+    wl = S.WORKLOADS[name]
+    say("full-size tiled layer %s (%s)" % (name, wl.description))
+    inp = S.make_layer_inputs(wl, seed=0)
+    d = DeviceLayer(inp).tiled()
+    L = _oracle_logits(inp)
+    rows = _rows(wl)
+    y, idx, w, _ = run_layer(d, logits=L)
+    idx_ref, w_ref, _ = oracle.router_topk(L, wl.k)
+    assert np.array_equal(idx, idx_ref)
+    assert_w_close(w, w_ref, name)
+    y_ref, _, _ = oracle.layer(inp.x, L, wl.k, inp.planes, inp.shared, inp.shared_gate, rows=rows)
+    sel = slice(None) if rows is None else rows
+    assert_y_close(y[sel], y_ref, name + " tiled")
