@@ -156,9 +156,8 @@ __device__ void small_route(const RouteArgs& ra, int k, SmallRoute& sr) {
   const bool publish = blockIdx.x == 0 && blockIdx.y == 0;
   const int S = ra.T * k;
   if (wave < ra.T)
-    topk_wave<V>(ra.logits + (int64_t)wave * ra.ld, ra.E, k, ra.route_scale,
-                 publish ? ra.idx + wave * k : nullptr, publish ? ra.w + wave * k : nullptr,
-                 sr.pick + wave * k, sr.wt + wave * k);
+    topk_group<V, 64>(ra.logits, ra.ld, ra.T, wave, ra.E, k, ra.route_scale,
+                      publish ? ra.idx : nullptr, publish ? ra.w : nullptr, sr.pick, sr.wt, 0);
   __syncthreads();
   int less = 0, rank = 0, first = 1, e = -1;
   if (tid < S) {

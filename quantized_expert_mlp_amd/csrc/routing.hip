@@ -16,6 +16,8 @@
 #include "kernels.h"
 #include "topk.h"
 
+#include <type_traits>
+
 namespace moe {
 
 // ---------------------------------------------------------------------------
@@ -95,28 +97,42 @@ hipError_t launch_router_logits(const uint16_t* x, const float* wr, const float*
   return hipGetLastError();
 }
 
-template <int V>
+// Four waves per workgroup, 64/G tokens per wave.
+template <int V, int G>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int ld,
                                                    int T, int E, int k, float route_scale,
                                                    int32_t* __restrict__ idx,
                                                    float* __restrict__ w) {
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  topk_wave<V>(logits + (int64_t)t * ld, E, k, route_scale, idx + (int64_t)t * k,
-               w + (int64_t)t * k, nullptr);
+  const int t0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * (64 / G);
+  if (t0 >= T) return;
+  topk_group<V, G>(logits, ld, T, t0, E, k, route_scale, idx, w);
+}
+
+// Calls f(integral_constant V, integral_constant G) for the (V, G) that serves (E, k).
+template <typename F>
+hipError_t topk_dispatch(int E, int k, F&& f) {
+  const int G = topk_group_lanes(E, k);
+  const int V = (E + G - 1) / G;
+  if (V < 1 || V > 4) return hipErrorInvalidValue;
+#define MOE_TOPK_CASE(VV, GG) \
+  if (V == VV && G == GG)       \
+    return f(std::integral_constant<int, VV>{}, std::integral_constant<int, GG>{});
+  MOE_TOPK_CASE(1, 16) MOE_TOPK_CASE(2, 16) MOE_TOPK_CASE(3, 16) MOE_TOPK_CASE(4, 16)
+  MOE_TOPK_CASE(1, 32) MOE_TOPK_CASE(2, 32) MOE_TOPK_CASE(3, 32) MOE_TOPK_CASE(4, 32)
+  MOE_TOPK_CASE(1, 64) MOE_TOPK_CASE(2, 64) MOE_TOPK_CASE(3, 64) MOE_TOPK_CASE(4, 64)
+#undef MOE_TOPK_CASE
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_topk(const float* logits, int ld, int T, int E, int k, float route_scale,
                        int32_t* idx, float* w, const Launch& L) {
-  dim3 grid((T + 3) / 4);
-  switch ((E + 63) / 64) {
-    case 1: MOE_LAUNCH(L, topk_kernel<1>, grid, dim3(256), 0, logits, ld, T, E, k, route_scale, idx, w); break;
-    case 2: MOE_LAUNCH(L, topk_kernel<2>, grid, dim3(256), 0, logits, ld, T, E, k, route_scale, idx, w); break;
-    case 3: MOE_LAUNCH(L, topk_kernel<3>, grid, dim3(256), 0, logits, ld, T, E, k, route_scale, idx, w); break;
-    case 4: MOE_LAUNCH(L, topk_kernel<4>, grid, dim3(256), 0, logits, ld, T, E, k, route_scale, idx, w); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  return topk_dispatch(E, k, [&](auto vc, auto gc) {
+    constexpr int V = decltype(vc)::value, G = decltype(gc)::value;
+    const int per_block = 4 * (64 / G);
+    MOE_LAUNCH(L, (topk_kernel<V, G>), dim3((T + per_block - 1) / per_block), dim3(256), 0,
+               logits, ld, T, E, k, route_scale, idx, w);
+    return hipGetLastError();
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -262,9 +278,9 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(const int32_t* __rest
 }
 
 // Fused routing for small batches: the workgroup's 16 waves run the top-k of
-// every token (wave w takes tokens w, w+16, ...), keep the picks in LDS, and
-// the same workgroup then builds the permutation and schedule from them.
-template <int V>
+// every token (64/G tokens per wave at a time), keep the picks in LDS, and the
+// same workgroup then builds the permutation and schedule from them.
+template <int V, int G>
 __global__ __launch_bounds__(kThreads) void route_kernel(const float* __restrict__ logits, int ld,
                                                          int T, int E, int k, float route_scale,
                                                          int32_t* __restrict__ idx,
@@ -276,9 +292,9 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const float* __restrict
                                                          int max_tiles) {
   __shared__ PermuteLds sm;
   __shared__ int32_t picks[kRouteMaxSlots];
-  for (int t = threadIdx.x >> 6; t < T; t += kWaves)
-    topk_wave<V>(logits + (int64_t)t * ld, E, k, route_scale, idx + (int64_t)t * k,
-                 w + (int64_t)t * k, picks + t * k);
+  constexpr int TPW = 64 / G;
+  for (int t0 = (threadIdx.x >> 6) * TPW; t0 < T; t0 += kWaves * TPW)
+    topk_group<V, G>(logits, ld, T, t0, E, k, route_scale, idx, w, picks, nullptr, 0);
   __syncthreads();
   permute_block(picks, T * k, E, off, sorted, row_of, sched, max_tiles, sm);
 }
@@ -287,14 +303,12 @@ hipError_t launch_route(const float* logits, int ld, int T, int E, int k, float 
                         int32_t* idx, float* w, int32_t* off, int32_t* sorted, int32_t* row_of,
                         int32_t* sched, const Launch& L) {
   const int max_tiles = (int)sched_max_tiles((int64_t)T * k, E);
-  switch ((E + 63) / 64) {
-    case 1: MOE_LAUNCH(L, route_kernel<1>, dim3(1), dim3(kThreads), 0, logits, ld, T, E, k, route_scale, idx, w, off, sorted, row_of, sched, max_tiles); break;
-    case 2: MOE_LAUNCH(L, route_kernel<2>, dim3(1), dim3(kThreads), 0, logits, ld, T, E, k, route_scale, idx, w, off, sorted, row_of, sched, max_tiles); break;
-    case 3: MOE_LAUNCH(L, route_kernel<3>, dim3(1), dim3(kThreads), 0, logits, ld, T, E, k, route_scale, idx, w, off, sorted, row_of, sched, max_tiles); break;
-    case 4: MOE_LAUNCH(L, route_kernel<4>, dim3(1), dim3(kThreads), 0, logits, ld, T, E, k, route_scale, idx, w, off, sorted, row_of, sched, max_tiles); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  return topk_dispatch(E, k, [&](auto vc, auto gc) {
+    constexpr int V = decltype(vc)::value, G = decltype(gc)::value;
+    MOE_LAUNCH(L, (route_kernel<V, G>), dim3(1), dim3(kThreads), 0, logits, ld, T, E, k,
+               route_scale, idx, w, off, sorted, row_of, sched, max_tiles);
+    return hipGetLastError();
+  });
 }
 
 // The schedule alone, from offsets written earlier (for callers that bring

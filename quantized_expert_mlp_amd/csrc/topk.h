@@ -11,98 +11,124 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// Top-k for one token on one wave.  Expert e lives in lane e % 64, register
-// e / 64 (V registers, E <= 64 V).  Each of the k rounds takes the arg-max of
-// what is left - larger logit first, lower expert index among equal logits -
-// by a lane-local scan, a DPP all-reduce inside each 16-lane row and a
-// 4-way pick across the rows' results (read as uniform values); because
-// (value desc, index asc) is a total order every lane agrees on the winner,
-// whose owning lane then masks it.  Pick j stays in lane j.  Weights are
-// exp(L_j - L_0) / sum_j' exp(L_j' - L_0) evaluated in fp64 (exact logit
-// differences, one rounding to fp32 at the end).
+// Top-k for 64/G tokens on one wave: token g of the wave owns the aligned
+// group of G lanes g*G .. g*G+G-1 (G = 16, 32 or 64); its expert e lives in
+// group lane e % G, register e / G (V registers, E <= G*V; k <= G).  Each of
+// the k rounds takes the arg-max of what is left - larger logit first, lower
+// expert index among equal logits - by a lane-local scan, a DPP all-reduce
+// inside each 16-lane row and, for G > 16, DPP row broadcasts that fold the
+// rows into the group's last lane, read back as a uniform value.  All
+// selects are branch-free.  Because (value desc, index asc) is a total order
+// every lane of a group agrees on the winner, whose owning lane retires it
+// (value -inf, index past every expert).  Pick j stays in group lane j.
+// Weights are exp(L_j - L_0) / sum_j' exp(L_j' - L_0) evaluated in fp64
+// (exact logit differences, one rounding to fp32 at the end).  Logits must be
+// finite (an out-of-range lane and a retired pick read as -inf).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
-  return bi < 0 || (i >= 0 && (v > bv || (v == bv && i < bi)));
+constexpr int kRetired = 0x7FFFFFFF;
+
+// (ov, oi) beats (bv, bi): larger value, or equal value and lower index.
+__device__ __forceinline__ bool beats(float ov, int oi, float bv, int bi) {
+  return (ov > bv) | ((ov == bv) & (oi < bi));
 }
 
-template <int CTRL>
+template <int CTRL, int ROW_MASK = 0xF>
 __device__ __forceinline__ void argmax_step(float& bv, int& bi) {
-  const float ov = dpp<CTRL>(bv);
-  const int oi = dpp_i<CTRL>(bi);
-  if (better(ov, oi, bv, bi)) {
-    bv = ov;
-    bi = oi;
-  }
+  // lanes outside ROW_MASK keep their own pair (update_dpp's old value)
+  const float ov = __int_as_float(
+      __builtin_amdgcn_update_dpp(__float_as_int(bv), __float_as_int(bv), CTRL, ROW_MASK, 0xF, false));
+  const int oi = __builtin_amdgcn_update_dpp(bi, bi, CTRL, ROW_MASK, 0xF, false);
+  const bool take = beats(ov, oi, bv, bi);
+  bv = take ? ov : bv;
+  bi = take ? oi : bi;
 }
 
 __device__ __forceinline__ float readlane_f(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
-// Writes idx[j], w[j] for j < k when those are non-null (global), and the
-// same into idx_lds[j], w_lds[j] when those are non-null (LDS).
-template <int V>
-__device__ __forceinline__ void topk_wave(const float* __restrict__ row, int E, int k,
-                                          float route_scale, int32_t* __restrict__ idx,
-                                          float* __restrict__ w, int32_t* idx_lds,
-                                          float* w_lds = nullptr) {
+// Tokens t0 .. t0 + 64/G - 1 (those below T) of a logits matrix with row
+// stride ld.  Writes idx[t*k + j], w[t*k + j] for j < k when those are
+// non-null (global), and the same into idx_lds / w_lds (indexed t*k + j, t
+// relative to lds_t0) when those are non-null (LDS).
+template <int V, int G>
+__device__ __forceinline__ void topk_group(const float* __restrict__ logits, int ld, int T, int t0,
+                                           int E, int k, float route_scale,
+                                           int32_t* __restrict__ idx, float* __restrict__ w,
+                                           int32_t* idx_lds = nullptr, float* w_lds = nullptr,
+                                           int lds_t0 = 0) {
+  static_assert(G == 16 || G == 32 || G == 64, "group size");
   const int lane = threadIdx.x & 63;
+  const int g = lane / G, gl = lane % G;
+  const int t = t0 + g;
+  const bool tok = t < T;
+  const float ninf = -__builtin_huge_valf();
   float val[V];
-  bool live[V];
+  int id[V];
 #pragma unroll
   for (int r = 0; r < V; ++r) {
-    const int e = lane + 64 * r;
-    live[r] = e < E;
-    val[r] = live[r] ? row[e] : 0.f;
+    const int e = gl + G * r;
+    const bool live = tok && e < E;
+    val[r] = live ? logits[(int64_t)t * ld + e] : ninf;
+    id[r] = live ? e : kRetired;
   }
   float my_val = 0.f;
   int my_idx = -1;
   for (int j = 0; j < k; ++j) {
-    float bv = 0.f;
-    int bi = -1;
+    float bv = val[0];
+    int bi = id[0];
 #pragma unroll
-    for (int r = 0; r < V; ++r)
-      if (live[r] && (bi < 0 || val[r] > bv)) {  // ascending index: strict > keeps ties low
-        bv = val[r];
-        bi = lane + 64 * r;
-      }
+    for (int r = 1; r < V; ++r) {
+      const bool take = beats(val[r], id[r], bv, bi);
+      bv = take ? val[r] : bv;
+      bi = take ? id[r] : bi;
+    }
     argmax_step<kDppXor1>(bv, bi);
     argmax_step<kDppXor2>(bv, bi);
     argmax_step<kDppHalfMirror>(bv, bi);
-    argmax_step<kDppMirror>(bv, bi);
-    float cv = readlane_f(bv, 0);
-    int ci = __builtin_amdgcn_readlane(bi, 0);
+    argmax_step<kDppMirror>(bv, bi);        // every lane of a row: the row's winner
+    if (G >= 32) argmax_step<kDppBcast15, 0xA>(bv, bi);  // rows 1, 3 also see rows 0, 2
+    if (G == 64) argmax_step<kDppBcast31, 0x8>(bv, bi);  // row 3 also sees rows 0-1
+    // the group's winner sits in its last lane; bring it to every lane
+    float cv = bv;
+    int ci = bi;
+    if (G == 64) {
+      cv = readlane_f(bv, 63);
+      ci = __builtin_amdgcn_readlane(bi, 63);
+    } else if (G == 32) {
+      const float c0 = readlane_f(bv, 31), c1 = readlane_f(bv, 63);
+      const int i0 = __builtin_amdgcn_readlane(bi, 31), i1 = __builtin_amdgcn_readlane(bi, 63);
+      cv = g ? c1 : c0;
+      ci = g ? i1 : i0;
+    }
 #pragma unroll
-    for (int rw = 1; rw < 4; ++rw) {
-      const float ov = readlane_f(bv, 16 * rw);
-      const int oi = __builtin_amdgcn_readlane(bi, 16 * rw);
-      if (better(ov, oi, cv, ci)) {
-        cv = ov;
-        ci = oi;
-      }
+    for (int r = 0; r < V; ++r) {
+      const bool mine = id[r] == ci;  // the winner's own register (ids are distinct)
+      val[r] = mine ? ninf : val[r];
+      id[r] = mine ? kRetired : id[r];
     }
-    if (ci >= 0 && (ci & 63) == lane) {
-#pragma unroll
-      for (int r = 0; r < V; ++r)
-        if (r == (ci >> 6)) live[r] = false;
-    }
-    if (lane == j) {
-      my_val = cv;
-      my_idx = ci;
-    }
+    my_val = gl == j ? cv : my_val;
+    my_idx = gl == j ? ci : my_idx;
   }
-  const double l0 = (double)readlane_f(my_val, 0);
-  const double ex = (lane < k) ? exp((double)my_val - l0) : 0.0;
+  // weights: group lane 0 holds the top logit
+  const double l0 = (double)__shfl(my_val, g * G, 64);
+  const double ex = (gl < k) ? exp((double)my_val - l0) : 0.0;
   double den = ex;
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) den += __shfl_xor(den, o, 64);
-  if (lane < k) {
+  for (int o = G / 2; o > 0; o >>= 1) den += __shfl_xor(den, o, 64);
+  if (tok && gl < k) {
     const float wv = (float)((double)route_scale * ex / den);
-    if (idx) idx[lane] = my_idx;
-    if (w) w[lane] = wv;
-    if (idx_lds) idx_lds[lane] = my_idx;
-    if (w_lds) w_lds[lane] = wv;
+    if (idx) idx[(int64_t)t * k + gl] = my_idx;
+    if (w) w[(int64_t)t * k + gl] = wv;
+    if (idx_lds) idx_lds[(t - lds_t0) * k + gl] = my_idx;
+    if (w_lds) w_lds[(t - lds_t0) * k + gl] = wv;
   }
+}
+
+// Lanes per token: the smallest group that holds the row in 4 registers and
+// the k picks in its lanes.
+__host__ __device__ constexpr int topk_group_lanes(int E, int k) {
+  return (E <= 64 && k <= 16) ? 16 : (E <= 128 && k <= 32) ? 32 : 64;
 }
 
 }  // namespace moe
