@@ -36,6 +36,9 @@
 #ifndef MOE_GEMV_WAVES
 #define MOE_GEMV_WAVES 2048
 #endif
+#ifndef MOE_GEMV_WAVES_DOWN1
+#define MOE_GEMV_WAVES_DOWN1 4096  // the down launch when buckets pass one token at a time
+#endif
 #ifndef MOE_GEMV_NT
 #define MOE_GEMV_NT 1
 #endif
@@ -573,9 +576,9 @@ constexpr int rb_for(int gpl) { return gpl == 1 ? 4 : gpl == 2 ? 2 : 1; }
 // Row iterations per wave: the launch is spread over about MOE_GEMV_WAVES
 // waves per token held in registers (more tokens, more VALU per byte, more
 // waves), every wave streaming a multiple of its batch.
-int rows_per_wave(int N, int rpi, int buckets, int rb, int mt) {
+int rows_per_wave(int N, int rpi, int buckets, int rb, int mt, int waves_per_token = MOE_GEMV_WAVES) {
   const int64_t row_iters = (int64_t)((N + rpi - 1) / rpi) * buckets;
-  const int64_t waves = (int64_t)MOE_GEMV_WAVES * mt;
+  const int64_t waves = (int64_t)waves_per_token * mt;
   int64_t nit = (row_iters + waves - 1) / waves;
   nit = (nit + rb - 1) / rb * rb;
   if (nit < rb) nit = rb;
@@ -654,7 +657,10 @@ hipError_t launch_gemv_down(const Buckets& b, int max_buckets, const uint16_t* h
   const GemvShape sh = pick_shape(I);
   const int mt = pow2_floor_min(b.max_rows, sh.gpl == 1 ? 4 : sh.gpl == 2 ? 2 : 1);
   const int buckets = b.shared_T > 0 ? 1 : max_buckets;
-  const int nit = rows_per_wave(H, 64 / sh.lpr, buckets, rb_for(sh.gpl), mt);
+  // down rows are short (K = I): with one token per pass, shorter waves keep
+  // more rows in flight
+  const int nit = rows_per_wave(H, 64 / sh.lpr, buckets, rb_for(sh.gpl), mt,
+                                mt == 1 ? MOE_GEMV_WAVES_DOWN1 : MOE_GEMV_WAVES);
   const int rpb = 4 * nit * (64 / sh.lpr);
   const bool slds = (I / 32) % 8 == 0;
   dim3 grid((H + rpb - 1) / rpb, buckets);
