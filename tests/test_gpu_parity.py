@@ -131,6 +131,8 @@ MID = [
     _mid("mid_dense", 23, 40, 128, 6, 6, 64),
     # single token through the decode GEMV with long rows and short down rows
     _mid("mid_decode", 24, 3, 4096, 64, 8, 320),
+    # 5600 slots: the permutation over many workgroups, a ragged last block
+    _mid("mid_many_slots", 26, 700, 256, 32, 8, 128),
 ]
 
 
