@@ -195,6 +195,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="decode", choices=list(S.WORKLOADS))
+    ap.add_argument("--path", default="auto", choices=["auto", "gemv", "gemm"],
+                    help="expert-MLP path (auto: the library's choice)")
     ap.add_argument("--layout", default="rows", choices=["rows", "tiled"],
                     help="weight plane layout (tiled: packed once with moe_pack_weights, "
                          "served by the MFMA path)")
@@ -249,9 +251,14 @@ def main():
             touched.append(touched_experts(L, wl.k))
     nvar = len(pool) if pool is not None else len(sets)
 
-    sh = moe.make_shape(T, wl.H, wl.E, wl.k, wl.I, wl.SI,
+    path = {"auto": moe.MOE_PATH_AUTO, "gemv": moe.MOE_PATH_GEMV, "gemm": moe.MOE_PATH_GEMM}[args.path]
+    sh = moe.make_shape(T, wl.H, wl.E, wl.k, wl.I, wl.SI, path=path,
                         layout=moe.MOE_LAYOUT_TILED if tiled else moe.MOE_LAYOUT_ROWS)
-    gemm = tiled or (T * wl.k) >= 8 * wl.E  # the library's AUTO rule (MOE_PATH_AUTO)
+    if moe.moe_workspace_bytes(sh) == 0:
+        sys.exit("bench.py: this workload is not served with --path %s --layout %s"
+                 % (args.path, args.layout))
+    # the library's AUTO rule (MOE_PATH_AUTO)
+    gemm = args.path == "gemm" or (args.path == "auto" and (tiled or (T * wl.k) >= 8 * wl.E))
     nbytes = moe.moe_workspace_bytes(sh)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     y = torch.empty((T, wl.H), dtype=torch.float32, device="cuda")
@@ -337,6 +344,7 @@ def main():
                    "E": wl.E, "k": wl.k, "I": wl.I, "SI": wl.SI,
                    "weights": "int4 offset-binary, fp16 scale per 32 inputs",
                    "layout": args.layout,
+                   "path": args.path,
                    "expert_path": "grouped fp16 MFMA GEMM" if gemm else "streaming int4 GEMV",
                    "input_rotation": ("%d logits rows" % nvar) if pool is not None
                    else ("%d weight sets" % nvar)},
