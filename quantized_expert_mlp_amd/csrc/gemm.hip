@@ -413,11 +413,13 @@ constexpr int kDownNS = MOE_GEMM_DN_NS;
 constexpr int kGateUpNS = MOE_GEMM_GU_NS;
 
 // K ranges for one source of the down pass: about equal work per workgroup,
-// enough workgroups to cover the chip twice, and at least 8 K steps each.
+// enough workgroups to cover the chip twice, and at least 16 K steps each
+// (shorter ranges spend more on the pipeline's ramp and the atomic epilogue
+// than they gain in parallelism).
 int down_split(int nks, int64_t total_steps) {
-  const int64_t target = std::max<int64_t>(8, total_steps / 512);
+  const int64_t target = std::max<int64_t>(16, total_steps / 512);
   int s = (int)((nks + target - 1) / target);
-  s = std::min(s, std::max(1, nks / 8));
+  s = std::min(s, std::max(1, nks / 16));
   return std::max(1, std::min(s, 64));
 }
 
