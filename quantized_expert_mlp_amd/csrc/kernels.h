@@ -56,8 +56,10 @@ struct Buckets {
   int32_t E;              // experts (locates the tile list in sched)
 };
 
+// x16 (nullable): also write the fp16 operand-order copy of x (as
+// launch_convert_x16 does).
 hipError_t launch_router_logits(const uint16_t* x, const float* wr, const float* gate_row, int T,
-                                int H, int E, float* out, int ld, const Launch& L);
+                                int H, int E, float* out, int ld, uint16_t* x16, const Launch& L);
 
 hipError_t launch_topk(const float* logits, int ld, int T, int E, int k, float route_scale,
                        int32_t* idx, float* w, const Launch& L);

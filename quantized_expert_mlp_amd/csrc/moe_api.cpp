@@ -119,10 +119,13 @@ bool plane_ok(const moe_q4& p) {
 }
 
 // Expert MLPs over the routed buckets (and the shared expert when given).
+// x16_ready: the MFMA path's fp16 activation copy was written already (by the
+// router logits launch).
 int run_mlp(const moe_shape* sh, bool gemm, const Layout& L, void* ws, const uint16_t* x,
             const int32_t* off, const int32_t* sorted, const float* w, moe_q4 gate, moe_q4 up,
             moe_q4 down, const moe_q4* shared, const float* gate_logit, int gate_ld, float* y,
-            hipStream_t st, const Stages& sg, const moe::RouteArgs* route = nullptr) {
+            hipStream_t st, const Stages& sg, const moe::RouteArgs* route = nullptr,
+            bool x16_ready = false) {
   const int T = sh->T, H = sh->H, I = sh->I, E = sh->E, k = sh->k;
   const int64_t slots = (int64_t)T * k;
   const int32_t* sched = at<int32_t>(ws, L.sched);
@@ -176,8 +179,12 @@ int run_mlp(const moe_shape* sh, bool gemm, const Layout& L, void* ws, const uin
     sgm.gate_ld = gate_ld;
   }
   const moe::SharedGemm* sgp = shared ? &sgm : nullptr;
-  err = moe::launch_convert_x16(x, T, H, x16, sg.at(MOE_STAGE_ACTIVATIONS));
-  if (err != hipSuccess) return MOE_ERR_HIP;
+  if (x16_ready) {
+    if (!sg.skip(MOE_STAGE_ACTIVATIONS)) return MOE_ERR_HIP;
+  } else {
+    err = moe::launch_convert_x16(x, T, H, x16, sg.at(MOE_STAGE_ACTIVATIONS));
+    if (err != hipSuccess) return MOE_ERR_HIP;
+  }
   const bool tiled = sh->layout == MOE_LAYOUT_TILED;
   err = moe::launch_gemm_gate_up(routed, max_tiles, x16, H, I, gate.q, gate.s, up.q, up.s, h16,
                                  sgp, y, y_elems, tiled, sg.at(MOE_STAGE_GATE_UP));
@@ -315,6 +322,7 @@ static int layer_impl(const moe_shape* sh, const uint16_t* x, const float* logit
     float* Lw = at<float>(ws, L.logits);
     const int ld = gated ? E + 1 : E;
     if (moe::launch_router_logits(x, w_router, gated ? shared_gate : nullptr, T, H, E, Lw, ld,
+                                  gemm ? at<uint16_t>(ws, L.x16) : nullptr,
                                   sg.at(MOE_STAGE_LOGITS)) != hipSuccess)
       return MOE_ERR_HIP;
     Lp = Lw;
@@ -326,6 +334,7 @@ static int layer_impl(const moe_shape* sh, const uint16_t* x, const float* logit
   } else if (gated) {
     float* gl = at<float>(ws, L.gate);
     if (moe::launch_router_logits(x, nullptr, shared_gate, T, H, 0, gl, 1,
+                                  gemm ? at<uint16_t>(ws, L.x16) : nullptr,
                                   sg.at(MOE_STAGE_LOGITS)) != hipSuccess)
       return MOE_ERR_HIP;
     gate_logit = gl;
@@ -367,8 +376,9 @@ static int layer_impl(const moe_shape* sh, const uint16_t* x, const float* logit
   }
 
   // 4.-5. expert MLPs with the fused combine
+  const bool x16_ready = gemm && (w_router || gated);
   return run_mlp(sh, gemm, L, ws, x, off, sorted, w, gate, up, down, shared, gate_logit, gate_ld,
-                 y, st, sg, fold ? &ra : nullptr);
+                 y, st, sg, fold ? &ra : nullptr, x16_ready);
 }
 
 int moe_layer(const moe_shape* sh, const uint16_t* x, const float* logits,

@@ -36,7 +36,17 @@ constexpr int kLogitBatch = 8;  // chunks whose loads are in flight together
 
 __global__ __launch_bounds__(64 * kLogitWaves) void router_logits_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ wr,
-    const float* __restrict__ gate_row, int T, int H, int E, float* out, int ld) {
+    const float* __restrict__ gate_row, int T, int H, int E, float* out, int ld,
+    uint16_t* __restrict__ x16) {
+  // The first column of tiles also writes the MFMA path's fp16 copy of its
+  // 16 token rows (it reads them anyway).
+  if (x16 && blockIdx.y == 0) {
+    const int t0 = blockIdx.x * 16, nt = min(16, T - t0);
+    const int64_t chunks = (int64_t)nt * H / 8;
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x + (int64_t)t0 * H);
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(x16 + (int64_t)t0 * H);
+    for (int64_t c = threadIdx.x; c < chunks; c += blockDim.x) dst[c] = bf16x8_to_f16_perm8(src[c]);
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i = lane & 15, q = lane >> 4;
   const int t = blockIdx.x * 16 + i;
@@ -90,10 +100,10 @@ __global__ __launch_bounds__(64 * kLogitWaves) void router_logits_kernel(
 }
 
 hipError_t launch_router_logits(const uint16_t* x, const float* wr, const float* gate_row, int T,
-                                int H, int E, float* out, int ld, const Launch& L) {
+                                int H, int E, float* out, int ld, uint16_t* x16, const Launch& L) {
   dim3 grid((T + 15) / 16, (ld + 15) / 16);
   MOE_LAUNCH(L, router_logits_kernel, grid, dim3(64 * kLogitWaves), 0, x, wr, gate_row, T, H, E,
-             out, ld);
+             out, ld, x16);
   return hipGetLastError();
 }
 
