@@ -220,3 +220,52 @@ def test_layer_full_size(name):
         check = [r for r in (range(wl.T) if rows is None else rows) if ok[r]]
         pos = [i for i, r in enumerate(range(wl.T) if rows is None else rows) if ok[r]]
         assert_y_close(y2[check], y_ref[pos], name + " (router logits)")
+
+
+# ------------------------------------------------- profiled entry point --
+
+@pytest.mark.parametrize("path", [moe.MOE_PATH_GEMV, moe.MOE_PATH_GEMM])
+def test_layer_profiled_matches_layer(path):
+    """moe_layer_profiled does the same work as moe_layer (same y, picks and
+    weights) and leaves every stage with a finished, non-negative interval."""
+    import ctypes
+    wl = MID[1]  # shared expert with a gate vector, router-computed logits
+    say("profiled layer %s path=%d" % (wl.name, path))
+    inp = S.make_layer_inputs(wl, seed=0)
+    d = DeviceLayer(inp)
+    sh = moe.make_shape(wl.T, wl.H, wl.E, wl.k, wl.I, wl.SI, path=path)
+    nb = moe.moe_workspace_bytes(sh)
+    outs = []
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    events = []
+    for _ in range(2 * len(moe.STAGES)):
+        e = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+        events.append(e.value)
+    for profiled in (False, True):
+        ws = torch.full((nb,), 0xAB, dtype=torch.uint8, device="cuda")
+        y = torch.full((wl.T, wl.H), float("nan"), device="cuda")
+        idx = torch.full((wl.T, wl.k), -1, dtype=torch.int32, device="cuda")
+        w = torch.full((wl.T, wl.k), float("nan"), device="cuda")
+        args = (sh, d.x, None, d.w_router, d.planes["gate"], d.planes["up"], d.planes["down"],
+                d.shared, d.shared_gate, y, idx, w, None, ws, nb)
+        if profiled:
+            moe.moe_layer_profiled(*args, events=events)
+        else:
+            moe.moe_layer(*args)
+        torch.cuda.synchronize()
+        outs.append((host(y), host(idx), host(w)))
+    assert np.array_equal(outs[0][1], outs[1][1])
+    assert np.array_equal(outs[0][2].view(np.uint32), outs[1][2].view(np.uint32))
+    # y: same kernels, but atomics add in no fixed order
+    assert_y_close(outs[1][0], outs[0][0], "profiled vs plain")
+    for i in range(len(moe.STAGES)):
+        ms = ctypes.c_float()
+        assert hip.hipEventElapsedTime(ctypes.byref(ms), events[2 * i], events[2 * i + 1]) == 0
+        assert ms.value >= 0.0, moe.STAGES[i]
+    for e in events:
+        hip.hipEventDestroy(e)
