@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the fused int4 MoE layer.
+"""Seeded synthetic inputs for the fused int4 / MXFP4 MoE layer.
 
 This module is shared by the CPU oracle's tests and by the GPU path's tests and
 benchmark.  It only draws random numbers and encodes them into the storage
@@ -24,6 +24,11 @@ Storage conventions (the boundary's):
   g        float32 [H]            N(0, 0.02)      (shared-expert gate vector)
   q        uint8 [E][N][K/2]      element kk in byte kk/2, low nibble = even kk
   s        uint16 [E][N][K/32]    fp16 bits, uniform[0.005, 0.02] rounded RNE
+MXFP4 planes (fmt "mxfp4") keep q's layout (uniform bytes: every e2m1 code)
+and replace s by
+  s        uint8 [E][N][K/32]     ue8m0 exponents, uniform on 119..122
+                                  (group scales 2^-8 .. 2^-5, so weights have
+                                  the int4 planes' magnitude)
 Gate/up planes have N = I, K = H; down planes have N = H, K = I.
 
 Every array is drawn from its own counter-style stream
@@ -138,6 +143,19 @@ def draw_plane(N: int, K: int, rng: np.random.Generator):
     return q, s
 
 
+MX_EXP_LO, MX_EXP_HI = 119, 122
+
+
+def draw_plane_mxfp4(N: int, K: int, rng: np.random.Generator):
+    """One MXFP4 plane: packed e2m1 nibbles [N][K/2] (uniform bytes) + ue8m0 bytes [N][K/32]."""
+    q = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    s = rng.integers(MX_EXP_LO, MX_EXP_HI + 1, size=(N, K // GROUP), dtype=np.uint8)
+    return q, s
+
+
+DRAW = {"int4": draw_plane, "mxfp4": draw_plane_mxfp4}
+SCALE_DTYPE = {"int4": np.uint16, "mxfp4": np.uint8}
+
 PLANES = ("gate", "up", "down")
 
 
@@ -146,18 +164,18 @@ def plane_shape(wl: Workload, plane: str, shared: bool = False):
     return (inter, wl.H) if plane in ("gate", "up") else (wl.H, inter)
 
 
-def draw_expert(wl: Workload, e: int, plane: str, seed: int = 0):
+def draw_expert(wl: Workload, e: int, plane: str, seed: int = 0, fmt: str = "int4"):
     N, K = plane_shape(wl, plane)
-    return draw_plane(N, K, _rng(seed, wl.wid, 10, e, PLANES.index(plane)))
+    return DRAW[fmt](N, K, _rng(seed, wl.wid, 10, e, PLANES.index(plane)))
 
 
-def draw_shared(wl: Workload, plane: str, seed: int = 0):
+def draw_shared(wl: Workload, plane: str, seed: int = 0, fmt: str = "int4"):
     N, K = plane_shape(wl, plane, shared=True)
-    return draw_plane(N, K, _rng(seed, wl.wid, 11, PLANES.index(plane)))
+    return DRAW[fmt](N, K, _rng(seed, wl.wid, 11, PLANES.index(plane)))
 
 
 def draw_all_experts(wl: Workload, plane: str, seed: int = 0,
-                     experts: Optional[Iterable[int]] = None):
+                     experts: Optional[Iterable[int]] = None, fmt: str = "int4"):
     """Stacked planes [E][N][K/2] and [E][N][K/32].
 
     Experts not listed in ``experts`` (when given) are left as zero bytes /
@@ -165,9 +183,9 @@ def draw_all_experts(wl: Workload, plane: str, seed: int = 0,
     """
     N, K = plane_shape(wl, plane)
     q = np.zeros((wl.E, N, K // 2), dtype=np.uint8)
-    s = np.zeros((wl.E, N, K // GROUP), dtype=np.uint16)
+    s = np.zeros((wl.E, N, K // GROUP), dtype=SCALE_DTYPE[fmt])
     for e in (range(wl.E) if experts is None else experts):
-        q[e], s[e] = draw_expert(wl, e, plane, seed)
+        q[e], s[e] = draw_expert(wl, e, plane, seed, fmt)
     return q, s
 
 
@@ -180,17 +198,18 @@ class LayerInputs:
     shared_gate: Optional[np.ndarray]
     planes: Dict[str, tuple]          # name -> (q [E][N][K/2], s [E][N][K/32])
     shared: Optional[Dict[str, tuple]]  # name -> (q [N][K/2], s [N][K/32])
+    fmt: str = "int4"                   # weight format of every plane
 
 
 def make_layer_inputs(wl: Workload, seed: int = 0, T: Optional[int] = None,
-                      experts: Optional[Iterable[int]] = None) -> LayerInputs:
+                      experts: Optional[Iterable[int]] = None, fmt: str = "int4") -> LayerInputs:
     x = draw_x(wl, seed, T)
     logits = draw_logits(wl, seed, T) if wl.logits in ("given", "zipf") else None
     w_router = draw_router(wl, seed) if wl.logits == "router" else None
     experts = None if experts is None else sorted(set(int(e) for e in experts))
-    planes = {p: draw_all_experts(wl, p, seed, experts) for p in PLANES}
+    planes = {p: draw_all_experts(wl, p, seed, experts, fmt) for p in PLANES}
     shared = shared_gate = None
     if wl.SI > 0:
-        shared = {p: draw_shared(wl, p, seed) for p in PLANES}
+        shared = {p: draw_shared(wl, p, seed, fmt) for p in PLANES}
         shared_gate = draw_shared_gate(wl, seed)
-    return LayerInputs(wl, x, logits, w_router, shared_gate, planes, shared)
+    return LayerInputs(wl, x, logits, w_router, shared_gate, planes, shared, fmt)

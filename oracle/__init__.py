@@ -45,10 +45,15 @@ def lib():
         L.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
         L.oracle_bf16_to_double.restype = ctypes.c_double
         L.oracle_dequant_int4.argtypes = [P, P, i64, i64, P]
+        L.oracle_dequant_mxfp4.argtypes = [P, P, i64, i64, P]
+        L.oracle_e2m1_to_double.argtypes = [ctypes.c_int]
+        L.oracle_e2m1_to_double.restype = ctypes.c_double
+        L.oracle_e8m0_to_double.argtypes = [ctypes.c_uint8]
+        L.oracle_e8m0_to_double.restype = ctypes.c_double
         L.oracle_router_logits.argtypes = [P, P, P, i64, i64, i64, P]
         L.oracle_router_topk.argtypes = [P, i64, i64, i64, ctypes.c_double, P, P, P]
         L.oracle_permute.argtypes = [P, i64, i64, i64, P, P, P]
-        L.oracle_expert_forward.argtypes = [P] * 6 + [i64, i64, P, P, P]
+        L.oracle_expert_forward.argtypes = [P] * 6 + [i64, i64, P, P, P, ctypes.c_int]
         L.oracle_layer.argtypes = [P] * 13 + [i64, P, P, P]
         _lib = L
     return _lib
@@ -57,7 +62,12 @@ def lib():
 class _Shape(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("H", ctypes.c_int64), ("E", ctypes.c_int64),
                 ("k", ctypes.c_int64), ("I", ctypes.c_int64), ("SI", ctypes.c_int64),
-                ("route_scale", ctypes.c_double)]
+                ("route_scale", ctypes.c_double), ("fmt", ctypes.c_int64)]
+
+
+# Weight formats: int4 nibble-8 with fp16 scale bits (uint16), MXFP4 e2m1 with
+# ue8m0 scale bytes (uint8); both one scale per 32 inputs.
+FORMATS = {"int4": (0, np.uint16), "mxfp4": (1, np.uint8)}
 
 
 def _p(a: Optional[np.ndarray]):
@@ -80,13 +90,23 @@ def bf16_to_double(b: int) -> float:
     return lib().oracle_bf16_to_double(int(b))
 
 
-def dequant(q: np.ndarray, s: np.ndarray) -> np.ndarray:
-    """Dense fp64 W[N][K] of one int4 plane (q [N][K/2] u8, s [N][K/32] fp16 bits)."""
+def e2m1_to_double(nib: int) -> float:
+    return lib().oracle_e2m1_to_double(int(nib))
+
+
+def e8m0_to_double(e: int) -> float:
+    return lib().oracle_e8m0_to_double(int(e))
+
+
+def dequant(q: np.ndarray, s: np.ndarray, fmt: str = "int4") -> np.ndarray:
+    """Dense fp64 W[N][K] of one plane: q [N][K/2] u8 and s [N][K/32], fp16 bits
+    (int4) or ue8m0 bytes (mxfp4)."""
     q = _c(q, np.uint8)
-    s = _c(s, np.uint16)
+    s = _c(s, FORMATS[fmt][1])
     N, K = q.shape[0], q.shape[1] * 2
     out = np.empty((N, K), dtype=np.float64)
-    lib().oracle_dequant_int4(_p(q), _p(s), N, K, _p(out))
+    f = lib().oracle_dequant_mxfp4 if fmt == "mxfp4" else lib().oracle_dequant_int4
+    f(_p(q), _p(s), N, K, _p(out))
     return out
 
 
@@ -124,42 +144,45 @@ def permute(idx: np.ndarray, E: int):
     return off, srt, row_of
 
 
-def expert_forward(gate, up, down, x64: np.ndarray):
+def expert_forward(gate, up, down, x64: np.ndarray, fmt: str = "int4"):
     """One expert on one fp64 row: returns (h fp64 [I], o fp64 [H]).
 
     gate/up/down are (q, s) pairs of single planes."""
-    (qg, sg), (qu, su), (qd, sd) = [(_c(q, np.uint8), _c(s, np.uint16)) for q, s in (gate, up, down)]
+    fid, st = FORMATS[fmt]
+    (qg, sg), (qu, su), (qd, sd) = [(_c(q, np.uint8), _c(s, st)) for q, s in (gate, up, down)]
     I, H = qg.shape[0], qg.shape[1] * 2
     x64 = _c(x64, np.float64)
     h = np.empty(I, dtype=np.float64)
     o = np.empty(H, dtype=np.float64)
     lib().oracle_expert_forward(_p(qg), _p(sg), _p(qu), _p(su), _p(qd), _p(sd), H, I,
-                                _p(x64), _p(h), _p(o))
+                                _p(x64), _p(h), _p(o), fid)
     return h, o
 
 
 def layer(x: np.ndarray, logits: np.ndarray, k: int, planes: Dict[str, tuple],
           shared: Optional[Dict[str, tuple]] = None, shared_gate: Optional[np.ndarray] = None,
-          rows: Optional[Sequence[int]] = None, route_scale: float = 1.0):
+          rows: Optional[Sequence[int]] = None, route_scale: float = 1.0, fmt: str = "int4"):
     """The whole layer on the token rows ``rows`` (default: all).
 
     planes: {"gate": (q [E][I][H/2], s [E][I][H/32]), "up": ..., "down": (q [E][H][I/2], s)}
     shared: same keys with single planes, or None.
+    fmt: "int4" (s = fp16 bits) or "mxfp4" (s = ue8m0 bytes) for every plane.
     Returns (y fp32 [n][H], idx int32 [n][k], w fp32 [n][k])."""
     x = _c(x, np.uint16)
     logits = _c(logits, np.float32)
     T, H = x.shape
     E = logits.shape[1]
-    gq, gs = [_c(a, t) for a, t in zip(planes["gate"], (np.uint8, np.uint16))]
-    uq, us = [_c(a, t) for a, t in zip(planes["up"], (np.uint8, np.uint16))]
-    dq, ds = [_c(a, t) for a, t in zip(planes["down"], (np.uint8, np.uint16))]
+    fid, st = FORMATS[fmt]
+    gq, gs = [_c(a, t) for a, t in zip(planes["gate"], (np.uint8, st))]
+    uq, us = [_c(a, t) for a, t in zip(planes["up"], (np.uint8, st))]
+    dq, ds = [_c(a, t) for a, t in zip(planes["down"], (np.uint8, st))]
     I = gq.shape[1]
     SI = 0
     keep = []
     sq_arr = ss_arr = None
     if shared is not None:
         sq = [_c(shared[p][0], np.uint8) for p in ("gate", "up", "down")]
-        ss = [_c(shared[p][1], np.uint16) for p in ("gate", "up", "down")]
+        ss = [_c(shared[p][1], st) for p in ("gate", "up", "down")]
         keep += sq + ss
         SI = sq[0].shape[0]
         sq_arr = (ctypes.c_void_p * 3)(*[a.ctypes.data for a in sq])
@@ -170,7 +193,7 @@ def layer(x: np.ndarray, logits: np.ndarray, k: int, planes: Dict[str, tuple],
     shared_gate = _c(shared_gate, np.float32)
     rows_a = None if rows is None else np.ascontiguousarray(rows, dtype=np.int32)
     n = T if rows_a is None else len(rows_a)
-    sh = _Shape(T, H, E, k, I, SI, float(route_scale))
+    sh = _Shape(T, H, E, k, I, SI, float(route_scale), fid)
     y = np.empty((n, H), dtype=np.float32)
     idx = np.empty((n, k), dtype=np.int32)
     w = np.empty((n, k), dtype=np.float32)

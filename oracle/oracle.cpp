@@ -1,4 +1,4 @@
-// CPU oracle for the fused int4 Mixture-of-Experts layer.
+// CPU oracle for the fused int4 / MXFP4 Mixture-of-Experts layer.
 //
 // TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
 // call this file: only the tests, the package's smoke check and the
@@ -23,6 +23,13 @@
 //   [vllmcpp]  vllm.cpp PR #481, "gate(#378): the first DEVICE run of the
 //              warp MoE router": the ungated softmax router with top-k, k
 //              passes of mask-and-reseed over the logit row.
+//   [colibri-mx] the same colibri PR, the later comment adding fmt=7: MXFP4
+//              expert weights, an e2m1 nibble per weight and one ue8m0
+//              exponent per 32-input group.  The two element formats are
+//              those of the OCP Microscaling (MX) v1.0 specification, which
+//              the pages name but do not define: e2m1 = 1 sign, 2 exponent
+//              (bias 1), 1 mantissa bit, no inf/NaN; ue8m0 = an unsigned
+//              8-bit biased exponent, 2^(e - 127), 0xFF = NaN.
 // Where the pages leave a step open, the reading taken is stated at the
 // function.
 //
@@ -70,10 +77,47 @@ double bf16_to_double(uint16_t b) {
 // Reading of the byte layout: element kk of a row sits in byte kk/2, the low
 // nibble holding the even element.  Scales run along the input (K) axis,
 // gs = 32.
-inline double weight(const uint8_t* q, const uint16_t* s, int64_t K, int64_t n, int64_t kk) {
+inline double weight_int4(const uint8_t* q, const uint16_t* s, int64_t K, int64_t n, int64_t kk) {
   const uint8_t byte = q[n * (K / 2) + kk / 2];
   const int nib = (kk & 1) ? (byte >> 4) : (byte & 0xf);
   return (double)(nib - 8) * half_to_double(s[n * (K / 32) + kk / 32]);
+}
+
+// e2m1 from its bit fields: bit 3 sign, bits 2..1 exponent (bias 1), bit 0
+// mantissa.  Exponent field 0 is subnormal: 0.m * 2^0 = m/2; otherwise
+// 1.m * 2^(E-1).  All 16 codes are finite.
+double e2m1_to_double(int nib) {
+  const int sign = (nib >> 3) & 1;
+  const int ex = (nib >> 1) & 3;
+  const int man = nib & 1;
+  const double v = (ex == 0) ? 0.5 * man : std::ldexp(1.0 + 0.5 * man, ex - 1);
+  return sign ? -v : v;
+}
+
+// ue8m0: the byte is a biased exponent, value 2^(e - 127); 0xFF is NaN.
+double e8m0_to_double(uint8_t e) { return e == 0xFF ? NAN : std::ldexp(1.0, (int)e - 127); }
+
+// MXFP4 ([colibri-mx]): same byte layout as the int4 planes (element kk in
+// byte kk/2, low nibble = even kk); element value e2m1(nibble) times the
+// group's 2^(e - 127), one ue8m0 byte per 32 consecutive inputs, scales
+// row-major [N][K/32] like the int4 fp16 scales.
+inline double weight_mxfp4(const uint8_t* q, const uint8_t* s, int64_t K, int64_t n, int64_t kk) {
+  const uint8_t byte = q[n * (K / 2) + kk / 2];
+  const int nib = (kk & 1) ? (byte >> 4) : (byte & 0xf);
+  return e2m1_to_double(nib) * e8m0_to_double(s[n * (K / 32) + kk / 32]);
+}
+
+// Weight formats: 0 = int4 with fp16 scales, 1 = MXFP4 with ue8m0 scales.
+// s points at the scale plane in its own element type.
+inline double weight(int fmt, const uint8_t* q, const void* s, int64_t K, int64_t n, int64_t kk) {
+  return fmt == 1 ? weight_mxfp4(q, static_cast<const uint8_t*>(s), K, n, kk)
+                  : weight_int4(q, static_cast<const uint16_t*>(s), K, n, kk);
+}
+
+// Bytes of one scale element.
+inline int64_t scale_bytes(int fmt) { return fmt == 1 ? 1 : 2; }
+inline const void* scale_at(int fmt, const void* s, int64_t elems) {
+  return static_cast<const char*>(s) + elems * scale_bytes(fmt);
 }
 
 double sigmoid(double z) { return 1.0 / (1.0 + std::exp(-z)); }
@@ -81,20 +125,20 @@ double sigmoid(double z) { return 1.0 / (1.0 + std::exp(-z)); }
 // One expert's SwiGLU MLP in fp64: g = Wg.x, u = Wu.x, h = silu(g)*u,
 // o = Wd.h ([colibri] Summary: the fused expert computes gate and up, the SiLU
 // product, then down; silu(z) = z*sigmoid(z) applied to the gate row).
-void expert_forward(const uint8_t* qg, const uint16_t* sg, const uint8_t* qu,
-                    const uint16_t* su, const uint8_t* qd, const uint16_t* sd,
+void expert_forward(int fmt, const uint8_t* qg, const void* sg, const uint8_t* qu,
+                    const void* su, const uint8_t* qd, const void* sd,
                     int64_t H, int64_t I, const double* x, double* h, double* o) {
   for (int64_t n = 0; n < I; ++n) {
     double g = 0.0, u = 0.0;
     for (int64_t kk = 0; kk < H; ++kk) {
-      g += weight(qg, sg, H, n, kk) * x[kk];
-      u += weight(qu, su, H, n, kk) * x[kk];
+      g += weight(fmt, qg, sg, H, n, kk) * x[kk];
+      u += weight(fmt, qu, su, H, n, kk) * x[kk];
     }
     h[n] = g * sigmoid(g) * u;
   }
   for (int64_t n = 0; n < H; ++n) {
     double acc = 0.0;
-    for (int64_t kk = 0; kk < I; ++kk) acc += weight(qd, sd, I, n, kk) * h[kk];
+    for (int64_t kk = 0; kk < I; ++kk) acc += weight(fmt, qd, sd, I, n, kk) * h[kk];
     o[n] = acc;
   }
 }
@@ -156,7 +200,17 @@ double oracle_bf16_to_double(uint16_t b) { return bf16_to_double(b); }
 // times an integer in [-8, 7] needs at most 15 significant bits).
 void oracle_dequant_int4(const uint8_t* q, const uint16_t* s, int64_t N, int64_t K, double* out) {
   for (int64_t n = 0; n < N; ++n)
-    for (int64_t kk = 0; kk < K; ++kk) out[n * K + kk] = weight(q, s, K, n, kk);
+    for (int64_t kk = 0; kk < K; ++kk) out[n * K + kk] = weight_int4(q, s, K, n, kk);
+}
+
+double oracle_e2m1_to_double(int nib) { return e2m1_to_double(nib); }
+double oracle_e8m0_to_double(uint8_t e) { return e8m0_to_double(e); }
+
+// W[n][kk] = e2m1(nibble) * 2^(e - 127) of one MXFP4 plane (q [N][K/2],
+// s [N][K/32] ue8m0 bytes), exact in fp64.
+void oracle_dequant_mxfp4(const uint8_t* q, const uint8_t* s, int64_t N, int64_t K, double* out) {
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t kk = 0; kk < K; ++kk) out[n * K + kk] = weight_mxfp4(q, s, K, n, kk);
 }
 
 // Router logits L[t][e] = sum_h x[t][h] * Wr[e][h] ([dasllama] routed-block
@@ -215,16 +269,19 @@ void oracle_permute(const int32_t* idx, int64_t T, int64_t k, int64_t E, int32_t
 }
 
 // One expert MLP on one activation row (fp64 in/out), for the tests.
-void oracle_expert_forward(const uint8_t* qg, const uint16_t* sg, const uint8_t* qu,
-                           const uint16_t* su, const uint8_t* qd, const uint16_t* sd,
-                           int64_t H, int64_t I, const double* x, double* h, double* o) {
+// fmt: 0 = int4 (fp16 scales), 1 = MXFP4 (ue8m0 scales).
+void oracle_expert_forward(const uint8_t* qg, const void* sg, const uint8_t* qu,
+                           const void* su, const uint8_t* qd, const void* sd,
+                           int64_t H, int64_t I, const double* x, double* h, double* o,
+                           int fmt) {
   std::vector<double> hh(I);
-  expert_forward(qg, sg, qu, su, qd, sd, H, I, x, h ? h : hh.data(), o);
+  expert_forward(fmt, qg, sg, qu, su, qd, sd, H, I, x, h ? h : hh.data(), o);
 }
 
 struct oracle_shape {
   int64_t T, H, E, k, I, SI;
   double route_scale;
+  int64_t fmt;  // weight format of every plane: 0 = int4, 1 = MXFP4
 };
 
 // The whole layer for the token rows listed in `rows` (all T rows when rows is
@@ -239,13 +296,15 @@ struct oracle_shape {
 // a null shared_gate means an ungated shared expert, added at weight one.
 // Planes are stacked [E][N][K/2] / [E][N][K/32] (gate, up: N=I, K=H; down:
 // N=H, K=I); shared planes are single [N][K/2] / [N][K/32] with I -> SI.
+// Scales are fp16 bits (int4) or ue8m0 bytes (MXFP4), per sh->fmt.
 // y is [nrows][H]; idx_out [nrows][k] and w_out [nrows][k] are nullable.
 void oracle_layer(const oracle_shape* sh, const uint16_t* x, const float* logits,
-                  const uint8_t* gq, const uint16_t* gs, const uint8_t* uq, const uint16_t* us,
-                  const uint8_t* dq, const uint16_t* ds, const uint8_t* const* shared_q,
-                  const uint16_t* const* shared_s, const float* shared_gate, const int32_t* rows,
+                  const uint8_t* gq, const void* gs, const uint8_t* uq, const void* us,
+                  const uint8_t* dq, const void* ds, const uint8_t* const* shared_q,
+                  const void* const* shared_s, const float* shared_gate, const int32_t* rows,
                   int64_t nrows, float* y, int32_t* idx_out, float* w_out) {
   const int64_t H = sh->H, E = sh->E, k = sh->k, I = sh->I, SI = sh->SI;
+  const int fmt = (int)sh->fmt;
   const bool has_shared = shared_q && shared_q[0];
   const int64_t gate_plane = I * (H / 2), gate_scales = I * (H / 32);
   const int64_t down_plane = H * (I / 2), down_scales = H * (I / 32);
@@ -265,14 +324,15 @@ void oracle_layer(const oracle_shape* sh, const uint16_t* x, const float* logits
         for (int64_t h = 0; h < H; ++h) a += xd[h] * (double)shared_gate[h];
         gw = sigmoid(a);
       }
-      expert_forward(shared_q[0], shared_s[0], shared_q[1], shared_s[1], shared_q[2],
+      expert_forward(fmt, shared_q[0], shared_s[0], shared_q[1], shared_s[1], shared_q[2],
                      shared_s[2], H, SI, xd.data(), hbuf.data(), o.data());
       for (int64_t h = 0; h < H; ++h) acc[h] += gw * o[h];
     }
     for (int64_t j = 0; j < k; ++j) {
       const int64_t e = idx[j];
-      expert_forward(gq + e * gate_plane, gs + e * gate_scales, uq + e * gate_plane,
-                     us + e * gate_scales, dq + e * down_plane, ds + e * down_scales, H, I,
+      expert_forward(fmt, gq + e * gate_plane, scale_at(fmt, gs, e * gate_scales),
+                     uq + e * gate_plane, scale_at(fmt, us, e * gate_scales),
+                     dq + e * down_plane, scale_at(fmt, ds, e * down_scales), H, I,
                      xd.data(), hbuf.data(), o.data());
       for (int64_t h = 0; h < H; ++h) acc[h] += w[j] * o[h];
     }

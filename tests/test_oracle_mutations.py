@@ -35,9 +35,25 @@ MUTATIONS = {
     "silu_dropped": ("h[n] = g * sigmoid(g) * u;", "h[n] = g * u;",
                      ["test_expert_closed_form_uniform_planes"]),
     "down_reads_gate_row_count": (
-        "acc += weight(qd, sd, I, n, kk) * h[kk];", "acc += weight(qd, sd, I, n, kk) * h[0];",
+        "acc += weight(fmt, qd, sd, I, n, kk) * h[kk];",
+        "acc += weight(fmt, qd, sd, I, n, kk) * h[0];",
         ["test_expert_down_plane_orientation"]),
     "shared_gate_ignored": ("gw = sigmoid(a);", "gw = 1.0;", ["test_layer_shared_expert_gate"]),
+    "e2m1_exponent_bias_zero": ("std::ldexp(1.0 + 0.5 * man, ex - 1)", "std::ldexp(1.0 + 0.5 * man, ex)",
+                                ["test_e2m1_golden", "test_dequant_mxfp4_golden"]),
+    "e2m1_subnormal_read_as_normal": ("(ex == 0) ? 0.5 * man", "(ex == 0) ? 1.0 * man",
+                                      ["test_e2m1_golden"]),
+    "e8m0_bias_128": ("std::ldexp(1.0, (int)e - 127)", "std::ldexp(1.0, (int)e - 128)",
+                      ["test_e8m0_matches_library"]),
+    "mxfp4_nibble_order_swapped": (
+        "(kk & 1) ? (byte >> 4) : (byte & 0xf);\n  return e2m1_to_double(nib)",
+        "(kk & 1) ? (byte & 0xf) : (byte >> 4);\n  return e2m1_to_double(nib)",
+        ["test_dequant_mxfp4_golden"]),
+    "mxfp4_scale_group_of_64": ("e8m0_to_double(s[n * (K / 32) + kk / 32])",
+                                "e8m0_to_double(s[n * (K / 32) + kk / 64])",
+                                ["test_dequant_mxfp4_golden"]),
+    "mxfp4_scale_stride_two_bytes": ("return fmt == 1 ? 1 : 2;", "return 2;",
+                                     ["test_layer_mxfp4_equals_dense_library_mixture"]),
     "combine_uses_first_weight": ("acc[h] += w[j] * o[h];", "acc[h] += w[0] * o[h];",
                                   ["test_layer_equals_dense_masked_mixture"]),
 }

@@ -56,9 +56,9 @@ def test_bf16_decode(orc):
 
 # ----------------------------------------------------------------- dequant --
 
-def _read_dequant_golden():
+def _read_dequant_golden(name="dequant_k64.txt", sdtype=np.uint16):
     rows = {}
-    for line in open(os.path.join(GOLDEN, "dequant_k64.txt")):
+    for line in open(os.path.join(GOLDEN, name)):
         if line.startswith("#") or not line.strip():
             continue
         tok = line.split()
@@ -73,7 +73,7 @@ def _read_dequant_golden():
                 else:
                     byts.append(int(b, 16))
             rows.setdefault(r, {})["q"] = np.array(byts, dtype=np.uint8)
-            rows[r]["s"] = np.array([int(v, 16) for v in tok[si + 1:]], dtype=np.uint16)
+            rows[r]["s"] = np.array([int(v, 16) for v in tok[si + 1:]], dtype=sdtype)
         else:
             rows.setdefault(r, {})["expect"] = np.array([float(v) for v in tok[3:]])
     n = len(rows)
@@ -109,6 +109,117 @@ def test_dequant_values_fit_fp32(orc):
     q, s = S.draw_plane(64, 256, np.random.default_rng(3))
     w = orc.dequant(q, s)
     assert np.array_equal(w.astype(np.float32).astype(np.float64), w)
+
+
+# ------------------------------------------------------------------ MXFP4 --
+
+def _read_e2m1_golden():
+    tab = {}
+    for line in open(os.path.join(GOLDEN, "e2m1_values.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        c, v = line.split()
+        tab[int(c, 16)] = float(v)
+    assert sorted(tab) == list(range(16))
+    return np.array([tab[c] for c in range(16)])
+
+
+def _e8m0_library(e):
+    """ue8m0 bytes -> fp64 through torch's float8_e8m0fnu conversion."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(e, dtype=np.uint8)).view(torch.float8_e8m0fnu)
+    return t.to(torch.float64).numpy()
+
+
+def _dequant_mxfp4_ref(q, s):
+    """Test-side MXFP4 dequant: the golden e2m1 table and the library's ue8m0."""
+    tab = _read_e2m1_golden()
+    q = np.asarray(q, np.uint8)
+    nib = np.stack([q & 0xF, q >> 4], axis=-1).reshape(q.shape[:-1] + (q.shape[-1] * 2,))
+    return tab[nib] * np.repeat(_e8m0_library(s), 32, axis=-1)
+
+
+def test_e2m1_golden(orc):
+    tab = _read_e2m1_golden()
+    for c in range(16):
+        got = orc.e2m1_to_double(c)
+        assert got == tab[c], (c, got, tab[c])
+        assert math.copysign(1.0, got) == math.copysign(1.0, tab[c]), c
+
+
+def test_e2m1_properties(orc):
+    v = [orc.e2m1_to_double(c) for c in range(16)]
+    assert all(v[c | 8] == -v[c] for c in range(8))          # bit 3 is the sign
+    assert all(v[c] < v[c + 1] for c in range(7))            # codes 0..7 ascend
+    assert all((2 * x).is_integer() for x in v) and max(v) == 6.0 and min(v) == -6.0
+
+
+def test_e8m0_matches_library(orc):
+    codes = np.arange(256, dtype=np.uint8)
+    ref = _e8m0_library(codes)
+    got = np.array([orc.e8m0_to_double(int(c)) for c in codes])
+    assert np.isnan(got[255]) and np.isnan(ref[255])
+    assert np.array_equal(got[:255], ref[:255])
+    assert orc.e8m0_to_double(127) == 1.0
+
+
+def test_dequant_mxfp4_golden(orc):
+    q, s, expect = _read_dequant_golden("dequant_mxfp4_k64.txt", np.uint8)
+    assert q.shape == (3, 32) and s.shape == (3, 2) and expect.shape == (3, 64)
+    assert np.array_equal(orc.dequant(q, s, "mxfp4"), expect)
+
+
+def test_dequant_mxfp4_matches_table_and_library(orc):
+    q, s = S.draw_plane_mxfp4(48, 256, np.random.default_rng(4))
+    s[0, :] = [0, 1, 126, 127, 128, 200, 253, 254]  # the exponent range's ends
+    assert np.array_equal(orc.dequant(q, s, "mxfp4"), _dequant_mxfp4_ref(q, s))
+
+
+def test_expert_mxfp4_matches_library_matmul(orc):
+    rng = np.random.default_rng(24)
+    H, I = 256, 96
+    gate, up, down = [S.draw_plane_mxfp4(*shape, rng) for shape in ((I, H), (I, H), (H, I))]
+    x = rng.standard_normal(H)
+    h, o = orc.expert_forward(gate, up, down, x, "mxfp4")
+    Wg, Wu, Wd = [_dequant_mxfp4_ref(*pl) for pl in (gate, up, down)]
+    g, u = Wg @ x, Wu @ x
+    href = g * scipy.special.expit(g) * u
+    assert np.allclose(h, href, rtol=1e-10, atol=1e-12)
+    assert np.allclose(o, Wd @ href, rtol=1e-9, atol=1e-10)
+
+
+def test_layer_mxfp4_equals_dense_library_mixture(orc):
+    """MXFP4 layer with a gated shared expert against numpy: test-side dequant,
+    brute-force top-k, scipy softmax weights, dense matmuls."""
+    rng = np.random.default_rng(25)
+    T, H, E, k, I, SI = 5, 64, 6, 2, 32, 64
+    x = S.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    planes = {}
+    for p, (N, K) in zip(S.PLANES, ((I, H), (I, H), (H, I))):
+        qs = [S.draw_plane_mxfp4(N, K, rng) for _ in range(E)]
+        planes[p] = (np.stack([a for a, _ in qs]), np.stack([b for _, b in qs]))
+    shared = {p: S.draw_plane_mxfp4(N, K, rng)
+              for p, (N, K) in zip(S.PLANES, ((SI, H), (SI, H), (H, SI)))}
+    gvec = rng.normal(0, 0.1, H).astype(np.float32)
+    y, idx, _ = orc.layer(x, logits, k, planes, shared, gvec, fmt="mxfp4")
+    xd = S.bf16_bits_to_f32(x).astype(np.float64)
+
+    def mlp(Wg, Wu, Wd, v):
+        g, u = Wg @ v, Wu @ v
+        return Wd @ (g * scipy.special.expit(g) * u)
+
+    Ws = [_dequant_mxfp4_ref(*shared[p]) for p in S.PLANES]
+    p_soft = scipy.special.softmax(logits.astype(np.float64), axis=1)
+    for t in range(T):
+        sel = _brute_topk(list(logits[t]), k)
+        assert sorted(idx[t]) == sorted(sel)
+        wsel = p_soft[t, sel] / p_soft[t, sel].sum()
+        ref = scipy.special.expit(xd[t] @ gvec.astype(np.float64)) * mlp(*Ws, xd[t])
+        for wj, e in zip(wsel, sel):
+            ref = ref + wj * mlp(*[_dequant_mxfp4_ref(planes[p][0][e], planes[p][1][e])
+                                   for p in S.PLANES], xd[t])
+        assert np.allclose(y[t], ref, rtol=1e-6, atol=1e-6 * np.abs(ref).max())
 
 
 # ---------------------------------------------------------- router: top-k --
