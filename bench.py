@@ -64,11 +64,13 @@ class Hip:
         return out.value
 
 
-def counted_traffic(kernel: str, workload: str, gemm: bool):
+def counted_traffic(kernel: str, workload: str, gemm: bool, fmt: str = "int4"):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summary (profiles/<workload>_gemv_hbm_counters.md), or None when there is
     none or the kernel sources changed since the counters were taken."""
     import hashlib
+    if fmt != "int4":
+        return None
     f = os.path.join(ROOT, "profiles", "%s_%s_hbm_counters.md" % (workload, "gemm" if gemm else "gemv"))
     if not os.path.exists(f):
         return None
@@ -91,21 +93,23 @@ def touched_experts(logits: np.ndarray, k: int) -> int:
     return len(np.unique(picks))
 
 
-def stage_work(wl, T, U, gemm):
+def stage_work(wl, T, U, gemm, fmt="int4"):
     """Algorithmic bytes and flops of the gate/up and down launches of one call.
 
-    Counted: the touched experts' packed nibbles and fp16 scales, activations
-    in, hidden rows (fp16) out/in, y out.  Not counted: untouched experts.  On
-    the MFMA path the shared expert's tiles run inside the routed launches, so
-    its work is added to theirs."""
+    Counted: the touched experts' packed nibbles and group scales (fp16 for
+    int4, one byte for MXFP4), activations in, hidden rows (fp16) out/in, y
+    out.  Not counted: untouched experts.  On the MFMA path the shared
+    expert's tiles run inside the routed launches, so its work is added to
+    theirs."""
     H, I, slots = wl.H, wl.I, T * wl.k
     act = 2
-    gu_w = U * 2 * (I * H // 2 + I * (H // 32) * 2)
-    dn_w = U * (H * I // 2 + H * (I // 32) * 2)
+    sb = 1 if fmt == "mxfp4" else 2
+    gu_w = U * 2 * (I * H // 2 + I * (H // 32) * sb)
+    dn_w = U * (H * I // 2 + H * (I // 32) * sb)
     sh_gu = sh_dn = 0
     if wl.SI:
-        sh_gu = 2 * (wl.SI * H // 2 + wl.SI * (H // 32) * 2) + T * H * 2 + T * wl.SI * act
-        sh_dn = (H * wl.SI // 2 + H * (wl.SI // 32) * 2) + T * wl.SI * act + T * H * 4
+        sh_gu = 2 * (wl.SI * H // 2 + wl.SI * (H // 32) * sb) + T * H * 2 + T * wl.SI * act
+        sh_dn = (H * wl.SI // 2 + H * (wl.SI // 32) * sb) + T * wl.SI * act + T * H * 4
     work = {
         "gate_up": {"bytes": gu_w + T * H * 2 + slots * I * act, "flops": 4.0 * slots * H * I},
         "down": {"bytes": dn_w + slots * I * act + T * H * 4, "flops": 2.0 * slots * H * I},
@@ -120,7 +124,7 @@ def stage_work(wl, T, U, gemm):
     return work
 
 
-def build_sets(wl, nsets, seed0=0, tiled=False):
+def build_sets(wl, nsets, seed0=0, tiled=False, fmt="int4"):
     """Device-resident inputs; with tiled=True the planes are packed into the
     tiled layout once, as at weight-load time."""
     import torch
@@ -140,7 +144,7 @@ def build_sets(wl, nsets, seed0=0, tiled=False):
 
     sets = []
     for r in range(nsets):
-        inp = S.make_layer_inputs(wl, seed=seed0 + r)
+        inp = S.make_layer_inputs(wl, seed=seed0 + r, fmt=fmt)
         d = {
             "inp": inp,
             "x": dev(inp.x),
@@ -161,11 +165,11 @@ def build_sets(wl, nsets, seed0=0, tiled=False):
     return sets
 
 
-def cpu_baseline(wl, seconds_hint: float):
+def cpu_baseline(wl, seconds_hint: float, fmt: str = "int4"):
     """The oracle as it stands, on a bounded sample of the workload's tokens."""
     import oracle
     threads = oracle.set_threads(min(16, os.cpu_count() or 1))
-    inp = S.make_layer_inputs(wl, seed=0)
+    inp = S.make_layer_inputs(wl, seed=0, fmt=fmt)
     if wl.logits == "router":
         logits = oracle.router_logits(inp.x, inp.w_router)
     else:
@@ -183,7 +187,7 @@ def cpu_baseline(wl, seconds_hint: float):
         rows = sorted(np.random.default_rng(7).choice(wl.T, n, replace=False).tolist())
         sample = "%d of %d token rows, %d threads" % (n, wl.T, threads)
     t0 = time.perf_counter()
-    oracle.layer(x, logits, wl.k, inp.planes, inp.shared, inp.shared_gate, rows=rows)
+    oracle.layer(x, logits, wl.k, inp.planes, inp.shared, inp.shared_gate, rows=rows, fmt=fmt)
     dt = time.perf_counter() - t0
     return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": sample, "seconds": round(dt, 2)}
@@ -200,6 +204,9 @@ def main():
     ap.add_argument("--layout", default="rows", choices=["rows", "tiled"],
                     help="weight plane layout (tiled: packed once with moe_pack_weights, "
                          "served by the MFMA path)")
+    ap.add_argument("--format", default="int4", choices=["int4", "mxfp4"],
+                    help="expert weight format (mxfp4: e2m1 nibbles, ue8m0 exponent per 32 "
+                         "inputs; served by the MFMA path with the row layout)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -234,7 +241,8 @@ def main():
     log("workload %s: %s; %d weight set(s)" % (wl.name, wl.description, nsets))
     t0 = time.perf_counter()
     tiled = args.layout == "tiled"
-    sets = build_sets(wl, nsets, tiled=tiled)
+    mx = args.format == "mxfp4"
+    sets = build_sets(wl, nsets, tiled=tiled, fmt=args.format)
     log("inputs resident in %.1f s" % (time.perf_counter() - t0))
 
     # per-step inputs: logits pool (given-logit workloads) or weight-set rotation
@@ -253,12 +261,13 @@ def main():
 
     path = {"auto": moe.MOE_PATH_AUTO, "gemv": moe.MOE_PATH_GEMV, "gemm": moe.MOE_PATH_GEMM}[args.path]
     sh = moe.make_shape(T, wl.H, wl.E, wl.k, wl.I, wl.SI, path=path,
-                        layout=moe.MOE_LAYOUT_TILED if tiled else moe.MOE_LAYOUT_ROWS)
+                        layout=moe.MOE_LAYOUT_TILED if tiled else moe.MOE_LAYOUT_ROWS,
+                        format=moe.MOE_FORMAT_MXFP4 if mx else moe.MOE_FORMAT_INT4)
     if moe.moe_workspace_bytes(sh) == 0:
-        sys.exit("bench.py: this workload is not served with --path %s --layout %s"
-                 % (args.path, args.layout))
+        sys.exit("bench.py: this workload is not served with --path %s --layout %s --format %s"
+                 % (args.path, args.layout, args.format))
     # the library's AUTO rule (MOE_PATH_AUTO)
-    gemm = args.path == "gemm" or (args.path == "auto" and (tiled or (T * wl.k) >= 8 * wl.E))
+    gemm = args.path == "gemm" or (args.path == "auto" and (tiled or mx or (T * wl.k) >= 8 * wl.E))
     nbytes = moe.moe_workspace_bytes(sh)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     y = torch.empty((T, wl.H), dtype=torch.float32, device="cuda")
@@ -300,7 +309,7 @@ def main():
     for k_ in stage_ms:
         stage_ms[k_] /= args.steps
     U = float(np.mean([touched[i % nvar] for i in range(args.steps)]))
-    work = stage_work(wl, T, U, gemm)
+    work = stage_work(wl, T, U, gemm, args.format)
     dom = max(("gate_up", "down", "shared_gate_up", "shared_down"), key=lambda s_: stage_ms[s_])
     dur_s = stage_ms[dom] * 1e-3
     if gemm:
@@ -312,7 +321,7 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
     roof["kernel"] = dom
-    roof["traffic"] = counted_traffic(dom, wl.name, gemm)
+    roof["traffic"] = counted_traffic(dom, wl.name, gemm, args.format)
     layer_bytes = sum(w_["bytes"] for w_ in work.values())
     layer_flops = sum(w_["flops"] for w_ in work.values())
     log("stage device time (us): " + ", ".join("%s %.2f" % (k_, v * 1e3)
@@ -324,7 +333,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, args.cpu_seconds)
+        cpu = cpu_baseline(wl, args.cpu_seconds, args.format)
         log("cpu oracle: %s" % cpu)
 
     out = {
@@ -342,7 +351,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "description": wl.description, "T": T, "H": wl.H,
                    "E": wl.E, "k": wl.k, "I": wl.I, "SI": wl.SI,
-                   "weights": "int4 offset-binary, fp16 scale per 32 inputs",
+                   "weights": ("mxfp4: e2m1, ue8m0 exponent per 32 inputs" if mx
+                               else "int4 offset-binary, fp16 scale per 32 inputs"),
                    "layout": args.layout,
                    "path": args.path,
                    "expert_path": "grouped fp16 MFMA GEMM" if gemm else "streaming int4 GEMV",

@@ -1,6 +1,6 @@
 /*
- * moe.h - C ABI of libmoe, a fused int4 Mixture-of-Experts layer for AMD
- * Instinct MI355X (gfx950, CDNA4).
+ * moe.h - C ABI of libmoe, a fused int4 / MXFP4 Mixture-of-Experts layer for
+ * AMD Instinct MI355X (gfx950, CDNA4).
  *
  * The layer (sources: the colibri Vulkan-backend PR #418, the dasLLAMA vulkan
  * PR #3988 and the vllm.cpp warp-router PR #481):
@@ -11,7 +11,9 @@
  *   4. per expert, the SwiGLU MLP on its bucket's rows:
  *        h = silu(Wg x) * (Wu x),   o = Wd h,
  *      with int4 weights: nibble n stands for (n - 8), times an fp16 scale per
- *      32 consecutive inputs;
+ *      32 consecutive inputs; or MXFP4 weights (the colibri PR's later fmt=7
+ *      comment): nibble n is an e2m1 value, times 2^(e - 127) for a ue8m0
+ *      byte e per 32 consecutive inputs;
  *   5. combine y[t] = sigma(x_t . g) * shared(x_t) + sum_j w[t][j] * o[t][j]
  *      (the shared expert optional; without a gate vector it adds at weight 1).
  *
@@ -34,6 +36,17 @@
  * with a plain copy, no repacking).  s = fp16 scale bits, uint16 [E][N][K/32],
  * one scale per 32 consecutive inputs along K.  Gate and up planes have N = I,
  * K = H; down planes have N = H, K = I.  q and s must be 16-byte aligned.
+ *
+ * MXFP4 planes (moe_shape.format = MOE_FORMAT_MXFP4): q as above, each
+ * nibble an OCP MX e2m1 code (bit 3 sign, bits 2..1 exponent with bias 1,
+ * bit 0 mantissa: 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives); s = ue8m0
+ * exponent bytes, uint8 [E][N][K/32], scale 2^(e - 127), e = 255 is NaN.  The
+ * kernels feed the MFMA the fp16 value e2m1 * 2^(e - 127) rounded to nearest
+ * even for 103 <= e <= 142 (the exact weight for 104 <= e <= 140; past 140 the
+ * larger codes overflow to +-inf).  Outside that range the scale itself is
+ * not an fp16 number: e <= 102 gives zero weights, 143 <= e <= 254 +-inf
+ * (NaN for a zero code), e = 255 NaN.  Served by the grouped MFMA GEMM with
+ * the row layout.
  *
  * Tiled planes (moe_shape.layout = MOE_LAYOUT_TILED, written by
  * moe_pack_weights): the same bytes regrouped so that the grouped MFMA GEMM
@@ -74,16 +87,22 @@ enum moe_path { MOE_PATH_AUTO = 0, MOE_PATH_GEMV = 1, MOE_PATH_GEMM = 2 };
  * MFMA GEMM only (path AUTO or GEMM); ROWS planes by both paths. */
 enum moe_layout { MOE_LAYOUT_ROWS = 0, MOE_LAYOUT_TILED = 1 };
 
-/* One int4 plane set: q [E][N][K/2] packed nibbles, s [E][N][K/32] fp16 bits. */
+/* Weight format (see above).  MXFP4 planes are served by the grouped MFMA
+ * GEMM with the row layout (path AUTO or GEMM, layout ROWS). */
+enum moe_format { MOE_FORMAT_INT4 = 0, MOE_FORMAT_MXFP4 = 1 };
+
+/* One 4-bit plane set: q [E][N][K/2] packed nibbles, s [E][N][K/32] group
+ * scales: fp16 bits (uint16) for int4, ue8m0 bytes (uint8) for MXFP4. */
 typedef struct {
   const uint8_t *q;
-  const uint16_t *s;
+  const void *s;
 } moe_q4;
 
 /* Layer shape.  T tokens, H hidden, E experts, k picks per token, I expert
  * intermediate, SI shared-expert intermediate (0 = none), group must be 32,
  * route_scale multiplies the renormalised weights, path is a moe_path,
- * layout a moe_layout (every plane of the call, shared ones included).
+ * layout a moe_layout and format a moe_format (both for every plane of the
+ * call, shared ones included).
  * Served: 1 <= k <= min(E, 64), E <= 256, H % 64 == 0, I % 64 == 0,
  * SI % 64 == 0, T >= 1, T*k < 2^31. */
 typedef struct {
@@ -92,6 +111,7 @@ typedef struct {
   float route_scale;
   int32_t path;
   int32_t layout;
+  int32_t format;
 } moe_shape;
 
 /*
@@ -129,17 +149,19 @@ int moe_permute(const int32_t *idx, int32_t T, int32_t k, int32_t E, int32_t *of
  * The routed experts' SwiGLU MLPs with the weighted combine fused into the
  * down projection's epilogue:
  *   y[t][:] = sum over slots s = t*k+j in the buckets of w[s] * MLP_e(x[t]).
- *   shape  : host pointer; T, H, E, k, I, group, path are used (SI ignored).
+ *   shape  : host pointer; T, H, E, k, I, group, path, layout, format are
+ *            used (SI ignored).
  *   x      : bf16 bits [T][H].
  *   off, sorted : as written by moe_permute.
  *   w      : fp32 [T][k] combine weights (from moe_router_topk).
- *   gate, up, down : int4 planes (see above).
+ *   gate, up, down : 4-bit planes in shape->format and shape->layout.
  *   y      : fp32 [T][H] out, OVERWRITTEN (not accumulated).
  *   ws     : device scratch of at least moe_workspace_bytes(shape) bytes,
  *            256-byte aligned; its contents on entry are ignored.
  * The order in which a token's k terms are added to y is not fixed (device
  * atomics); the result differs from an ordered sum only by fp32 rounding.
- * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.
+ * Errors: INVALID_ARG, UNSUPPORTED (also for path GEMV with TILED or MXFP4
+ *         planes, and for MXFP4 with TILED), WORKSPACE, HIP.
  */
 int moe_expert_mlp(const moe_shape *shape, const uint16_t *x, const int32_t *off,
                    const int32_t *sorted, const float *w, moe_q4 gate, moe_q4 up, moe_q4 down,
@@ -162,7 +184,7 @@ int moe_expert_mlp(const moe_shape *shape, const uint16_t *x, const int32_t *off
  *   w_out      : fp32 [T][k] out, or NULL.
  *   logits_out : fp32 [T][E] out (the logits used), or NULL.
  *   ws         : as for moe_expert_mlp.
- * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.
+ * Errors: as moe_expert_mlp.
  */
 int moe_layer(const moe_shape *shape, const uint16_t *x, const float *logits,
               const float *w_router, moe_q4 gate, moe_q4 up, moe_q4 down, const moe_q4 *shared,
@@ -207,7 +229,7 @@ int moe_layer_profiled(const moe_shape *shape, const uint16_t *x, const float *l
  * Regroup E experts' int4 planes from the row layout into the tiled layout
  * (see above), for the grouped MFMA GEMM's contiguous weight reads.  A pure
  * byte permutation of q and of s; the values are unchanged.  Meant to run once
- * when weights are loaded.
+ * when weights are loaded.  int4 planes (fp16 scales) only.
  *   src    : row-layout planes, q [E][N][K/2], s [E][N][K/32].
  *   dst    : tiled planes of the same sizes (caller-allocated, 16-byte
  *            aligned, not overlapping src).
@@ -235,6 +257,15 @@ const char *moe_status_string(int status);
  */
 int moe_debug_dequant_int4(moe_q4 plane, int32_t N, int32_t K, int32_t mode, float *out,
                            moe_stream_t stream);
+
+/*
+ * Test hook: the MFMA kernels' MXFP4 decode of one plane (q [N][K/2] e2m1
+ * nibbles, s [N][K/32] ue8m0 bytes), written as fp32 [N][K]: the fp16
+ * operand e2m1 * 2^(e - 127) rounded to nearest even, widened to fp32.
+ * Errors: INVALID_ARG (null, N < 1, K % 32 != 0, misaligned).
+ */
+int moe_debug_dequant_mxfp4(moe_q4 plane, int32_t N, int32_t K, float *out,
+                            moe_stream_t stream);
 
 #ifdef __cplusplus
 }

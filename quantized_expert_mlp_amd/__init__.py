@@ -20,11 +20,12 @@ LIB_PATH = os.path.join(PKG, "libmoe.so")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_PATH_AUTO, MOE_PATH_GEMV, MOE_PATH_GEMM = range(3)
 MOE_LAYOUT_ROWS, MOE_LAYOUT_TILED = range(2)
+MOE_FORMAT_INT4, MOE_FORMAT_MXFP4 = range(2)
 
 # Every symbol include/moe.h declares.
 EXPORTS = ("moe_router_topk", "moe_permute", "moe_expert_mlp", "moe_layer",
            "moe_layer_profiled", "moe_pack_weights", "moe_workspace_bytes",
-           "moe_status_string", "moe_debug_dequant_int4")
+           "moe_status_string", "moe_debug_dequant_int4", "moe_debug_dequant_mxfp4")
 STAGES = ("start", "logits", "topk", "permute", "activations", "gate_up", "shared_gate_up",
           "down", "shared_down")
 
@@ -43,7 +44,8 @@ class moe_shape(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("E", ctypes.c_int32),
                 ("k", ctypes.c_int32), ("I", ctypes.c_int32), ("SI", ctypes.c_int32),
                 ("group", ctypes.c_int32), ("route_scale", ctypes.c_float),
-                ("path", ctypes.c_int32), ("layout", ctypes.c_int32)]
+                ("path", ctypes.c_int32), ("layout", ctypes.c_int32),
+                ("format", ctypes.c_int32)]
 
 
 _lib = None
@@ -70,9 +72,11 @@ def lib() -> ctypes.CDLL:
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_debug_dequant_int4.argtypes = [moe_q4, i32, i32, i32, P, P]
+        L.moe_debug_dequant_mxfp4.argtypes = [moe_q4, i32, i32, P, P]
         L.moe_pack_weights.argtypes = [moe_q4, i32, i32, i32, moe_q4, P]
         for name in ("moe_router_topk", "moe_permute", "moe_expert_mlp", "moe_layer",
-                     "moe_layer_profiled", "moe_pack_weights", "moe_debug_dequant_int4"):
+                     "moe_layer_profiled", "moe_pack_weights", "moe_debug_dequant_int4",
+                     "moe_debug_dequant_mxfp4"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -103,9 +107,9 @@ def _check(fn: str, rc: int) -> None:
 
 
 def make_shape(T, H, E, k, I, SI=0, route_scale=1.0, path=MOE_PATH_AUTO, group=32,
-               layout=MOE_LAYOUT_ROWS) -> moe_shape:
+               layout=MOE_LAYOUT_ROWS, format=MOE_FORMAT_INT4) -> moe_shape:
     return moe_shape(int(T), int(H), int(E), int(k), int(I), int(SI), int(group),
-                     float(route_scale), int(path), int(layout))
+                     float(route_scale), int(path), int(layout), int(format))
 
 
 def q4(plane: Tuple) -> moe_q4:
@@ -172,3 +176,8 @@ def moe_pack_weights(src, E, N, K, dst, stream=None) -> None:
 def moe_debug_dequant_int4(plane, N, K, mode, out, stream=None) -> None:
     _check("moe_debug_dequant_int4", lib().moe_debug_dequant_int4(
         q4(plane), N, K, mode, _ptr(out), _stream(stream)))
+
+
+def moe_debug_dequant_mxfp4(plane, N, K, out, stream=None) -> None:
+    _check("moe_debug_dequant_mxfp4", lib().moe_debug_dequant_mxfp4(
+        q4(plane), N, K, _ptr(out), _stream(stream)))

@@ -152,6 +152,49 @@ __device__ __forceinline__ f16x8_t q4_f16x8(uint32_t w, f16x2_t s2) {
   return r;
 }
 
+// ---------------------------------------------------------------------------
+// MXFP4 decode, fp16 form (MFMA kernels).  The nibbles are e2m1 codes (bit 3
+// sign, bits 2..1 exponent with bias 1, bit 0 mantissa) whose eight
+// magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 are fp16 values with a zero low
+// byte.  One v_perm_b32 looks up the high bytes of four codes at once (its
+// byte selectors 0..7 index the 8-byte table below), the sign bit moves to
+// bit 7 of each byte, and the same pairing as the int4 decode spreads the
+// high bytes into fp16 pairs [e0,e4], [e1,e5], [e2,e6], [e3,e7].  One packed
+// multiply by the group scale [s, s] rounds the exact product once, so the
+// vector holds the 8 elements in the order 0,4,1,5,2,6,3,7 like q4_f16x8.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kE2m1Lo = 0x3E3C3800u;  // fp16 high bytes of codes 3, 2, 1, 0
+constexpr uint32_t kE2m1Hi = 0x46444240u;  // codes 7, 6, 5, 4
+constexpr uint32_t kSelPairLo = 0x02040004u;  // [0, b0, 0, b2] (src0 = 0 gives the zero bytes)
+constexpr uint32_t kSelPairHi = 0x03040104u;  // [0, b1, 0, b3]
+
+__device__ __forceinline__ uint32_t e2m1_hi_bytes(uint32_t nibbles) {
+  const uint32_t mag = __builtin_amdgcn_perm(kE2m1Hi, kE2m1Lo, nibbles & 0x07070707u);
+  return mag | ((nibbles << 4) & 0x80808080u);
+}
+
+__device__ __forceinline__ f16x8_t mx4_f16x8(uint32_t w, f16x2_t s2) {
+  const uint32_t ht = e2m1_hi_bytes(w & 0x0F0F0F0Fu);         // codes of e0, e2, e4, e6
+  const uint32_t hu = e2m1_hi_bytes((w >> 4) & 0x0F0F0F0Fu);  // codes of e1, e3, e5, e7
+  const f16x2_t a = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0u, ht, kSelPairLo)) * s2;
+  const f16x2_t b = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0u, hu, kSelPairLo)) * s2;
+  const f16x2_t c = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0u, ht, kSelPairHi)) * s2;
+  const f16x2_t d = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0u, hu, kSelPairHi)) * s2;
+  f16x8_t r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
+// ue8m0 group exponent e -> the fp16 scale 2^(e - 127), rounded to nearest
+// even from the exact fp32 power of two: exact for 103 <= e <= 142 (fp16
+// subnormals included), zero below, +inf from 143 to 254; e = 255 (NaN in
+// the MX format) gives NaN.
+__device__ __forceinline__ _Float16 e8m0_f16(uint32_t e) {
+  const float f = e == 255u ? __builtin_nanf("") : __uint_as_float(e << 23);
+  return (_Float16)f;
+}
+
 // Position, within an aligned block of 8, at which element i is stored in the
 // MFMA kernels' fp16 activation buffers (inverse of the order 0,4,1,5,2,6,3,7).
 __device__ __forceinline__ int perm8_pos(int i) { return ((i & 3) << 1) | (i >> 2); }

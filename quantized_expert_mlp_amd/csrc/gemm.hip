@@ -1,12 +1,13 @@
-// Grouped int4 GEMM on fp16 MFMA for prefill-sized buckets.
+// Grouped 4-bit (int4 or MXFP4) GEMM on fp16 MFMA for prefill-sized buckets.
 //
 // Sources: the dasLLAMA vulkan PR #3988 routed block (bucket rows gathered
 // through the slot map into expert tiles, an upper-bound dispatch whose
 // surplus workgroups return at once, the act step between gate/up and down,
 // the combine reading each slot's row through the map; the shared expert as
 // one more region over every row with an identity map, weighted by the
-// sigmoid of its gate logit) and the colibri PR #418 int4 format (nibble - 8,
-// one fp16 scale per 32 inputs).
+// sigmoid of its gate logit) and the colibri PR #418 weight formats: int4
+// (nibble - 8, one fp16 scale per 32 inputs) and, from its later fmt=7
+// comment, MXFP4 (e2m1 nibbles, one ue8m0 exponent per 32 inputs).
 //
 // gfx950 design.  A workgroup of kWaves waves (one per SIMD; two workgroups
 // share a CU) owns one row tile of up to 128 bucket rows and a block of output columns.  Waves
@@ -18,8 +19,8 @@
 //   A (32 rows x 16 k)  lane l: row l%32, k 8*(l/32)..+7  (activations)
 //   B (16 k x 32 cols)  lane l: col l%32, k 8*(l/32)..+7  (weights)
 //   D (32 x 32, fp32)   lane l: col l%32, rows 8*(v/4) + 4*(l/32) + v%4.
-// The weight operand is the exact dequantised value (nibble-8)*scale rounded
-// once to fp16; fp16 and bf16 MFMA have the same peak on gfx950, and fp16's
+// The weight operand is the exact dequantised value ((nibble-8)*scale, or
+// e2m1(nibble)*2^(e-127)) rounded once to fp16; fp16 and bf16 MFMA have the same peak on gfx950, and fp16's
 // 11-bit significand keeps the layer within its tolerance where bf16 would
 // not.  Activations are fp16 copies stored with each block of 8 in the order
 // 0,4,1,5,2,6,3,7, matching the nibble pairing of the decode.
@@ -54,6 +55,7 @@
 #endif
 
 #include <algorithm>
+#include <type_traits>
 #include <utility>
 
 namespace moe {
@@ -87,7 +89,8 @@ struct TileView {
 __device__ __forceinline__ int perm_col(int j) { return (j & ~7) | perm8_pos(j & 7); }
 
 // Raw weight operands of one K step for one lane: the 16 bytes of scale
-// group 2*step + hf of each (subtile, plane) weight row, and its fp16 scale.
+// group 2*step + hf of each (subtile, plane) weight row, and its scale (fp16
+// bits or a ue8m0 byte).
 template <int P, int NS>
 struct BStage {
   u32x4_t q[NS][P];
@@ -107,7 +110,7 @@ struct GemmSrc {
                          // the operand order 0,4,1,5,2,6,3,7
   int K, N;              // contraction depth and output columns of one plane
   const uint8_t* q[2];   // weight planes: [E][N][K/2] nibbles
-  const uint16_t* s[2];  // and their [E][N][K/32] fp16 scales
+  const void* s[2];      // and their [E][N][K/32] scales (fp16 bits or ue8m0 bytes)
   uint16_t* hout;        // MODE 0 output, row stride N
   int ksplit;            // MODE 1: K ranges over blockIdx.z
   int tiled;             // planes in the tiled layout (1 KB per 32 rows x 64 k)
@@ -156,7 +159,7 @@ constexpr int a_chunks() {
 
 // One tile: MS row subtiles of 32 (compile-time, so the accumulators stay in
 // fixed registers), NS column subtiles of 32 per wave, P weight planes, K
-// steps [k0, k1).
+// steps [k0, k1), weights in format FMT.
 //
 // Pipeline (one barrier per K step, two LDS buffers, register rings of DA
 // activation and DB weight stages): at step s a wave decodes B(s), issues the
@@ -166,7 +169,7 @@ constexpr int a_chunks() {
 // Scheduling barriers keep the compiler from sinking the loads below the
 // MFMAs.  Loads past the last step re-read the last step (their data is never
 // used), which keeps the loop free of branches around loads and accumulators.
-template <int P, int NS, int MODE, int MS>
+template <int P, int NS, int MODE, int MS, int FMT>
 __device__ __forceinline__ void gemm_tile(const TileView& tv, const GemmSrc& S, const GemmArgs& a,
                                           const uint16_t* const (&arow)[a_chunks<MS>()],
                                           char (*lds)[kBM * kPitch], const int* row_tok,
@@ -184,8 +187,9 @@ __device__ __forceinline__ void gemm_tile(const TileView& tv, const GemmSrc& S, 
   // rows; they are never stored).  Row layout: row col0+32*ns+j, group
   // 2*step+hf, consecutive steps 2 groups apart.  Tiled layout: lane's 16
   // bytes of the 1 KB block (subtile, step), consecutive steps 1 KB apart.
+  using SElem = std::conditional_t<FMT == kFmtMxfp4, uint8_t, uint16_t>;
   const u32x4_t* bq_ptr[NS][P];
-  const uint16_t* bs_ptr[NS][P];
+  const SElem* bs_ptr[NS][P];
   const int64_t plane = (int64_t)N * (K / 2), splane = (int64_t)N * (K / 32);
   const int stride = S.tiled ? 64 : 2;  // per K step, in 16-byte / scale units
 #pragma unroll
@@ -195,12 +199,13 @@ __device__ __forceinline__ void gemm_tile(const TileView& tv, const GemmSrc& S, 
       if (S.tiled) {
         const int64_t blk = (int64_t)(min(col0 + ns * 32, N - 32) / 32) * (K / 64) + k0;
         bq_ptr[ns][p] = reinterpret_cast<const u32x4_t*>(S.q[p] + tv.e * plane + blk * 1024) + lane;
-        bs_ptr[ns][p] = S.s[p] + tv.e * splane + blk * 64 + lane;
+        bs_ptr[ns][p] = static_cast<const SElem*>(S.s[p]) + tv.e * splane + blk * 64 + lane;
       } else {
         const int row = min(col0 + ns * 32 + j, N - 1);
         bq_ptr[ns][p] = reinterpret_cast<const u32x4_t*>(S.q[p] + tv.e * plane + (int64_t)row * (K / 2)) +
                         hf + 2 * k0;
-        bs_ptr[ns][p] = S.s[p] + tv.e * splane + (int64_t)row * (K / 32) + hf + 2 * k0;
+        bs_ptr[ns][p] = static_cast<const SElem*>(S.s[p]) + tv.e * splane + (int64_t)row * (K / 32) +
+                        hf + 2 * k0;
       }
     }
   }
@@ -244,10 +249,17 @@ __device__ __forceinline__ void gemm_tile(const TileView& tv, const GemmSrc& S, 
     for (int ns = 0; ns < NS; ++ns)
 #pragma unroll
       for (int p = 0; p < P; ++p) {
-        const _Float16 sc = __builtin_bit_cast(_Float16, (uint16_t)st.s[ns][p]);
-        const f16x2_t s2 = {sc, sc};
+        if constexpr (FMT == kFmtMxfp4) {
+          const _Float16 sc = e8m0_f16(st.s[ns][p]);
+          const f16x2_t s2 = {sc, sc};
 #pragma unroll
-        for (int d = 0; d < 4; ++d) bf[ns][p][d] = q4_f16x8(st.q[ns][p][d], s2);
+          for (int d = 0; d < 4; ++d) bf[ns][p][d] = mx4_f16x8(st.q[ns][p][d], s2);
+        } else {
+          const _Float16 sc = __builtin_bit_cast(_Float16, (uint16_t)st.s[ns][p]);
+          const f16x2_t s2 = {sc, sc};
+#pragma unroll
+          for (int d = 0; d < 4; ++d) bf[ns][p][d] = q4_f16x8(st.q[ns][p][d], s2);
+        }
       }
   };
 
@@ -331,11 +343,12 @@ __device__ __forceinline__ void gemm_tile(const TileView& tv, const GemmSrc& S, 
 
 }  // namespace
 
-// P planes (2 = gate and up, 1 = down), NS 32-column subtiles per wave.
+// P planes (2 = gate and up, 1 = down), NS 32-column subtiles per wave, FMT
+// the weight format.
 // MODE 0: gate/up -> h16 = fp16(silu(g) * u) at the tile's rows.
 // MODE 1: down    -> y[token] += weight * acc (fp32 atomics), K split over
 //                    blockIdx.z into a.ksplit ranges.
-template <int P, int NS, int MODE>
+template <int P, int NS, int MODE, int FMT>
 __global__ __launch_bounds__(kThreads, MOE_GEMM_OCC) void gemm_kernel(Buckets b, GemmArgs a) {
   if (MODE == 0 && a.y_zero) {
     // every workgroup of the launch, tile or not, clears its share of y
@@ -402,7 +415,7 @@ __global__ __launch_bounds__(kThreads, MOE_GEMM_OCC) void gemm_kernel(Buckets b,
       const uint16_t* rows[NA];
 #pragma unroll
       for (int i = 0; i < NA; ++i) rows[i] = src_row(r0 + kChunkRows * i);
-      gemm_tile<P, NS, MODE, MS>(tv, S, a, rows, lds, row_tok, row_w, k0, k1);
+      gemm_tile<P, NS, MODE, MS, FMT>(tv, S, a, rows, lds, row_tok, row_w, k0, k1);
     }
   });
 }
@@ -430,23 +443,26 @@ int64_t routed_tile_estimate(const Buckets& b) {
 }
 
 template <int P, int NS, int MODE>
-hipError_t launch_tiles(const Buckets& b, int max_tiles, const GemmArgs& a, int gz,
+hipError_t launch_tiles(const Buckets& b, int max_tiles, const GemmArgs& a, int gz, int fmt,
                         const Launch& L) {
   constexpr int BN = kWaves * 32 * NS;
   int gx = (a.src[0].N + BN - 1) / BN;
   if (a.shared_tiles > 0) gx = std::max(gx, (a.src[1].N + BN - 1) / BN);
-  MOE_LAUNCH(L, (gemm_kernel<P, NS, MODE>), dim3(gx, a.shared_tiles + max_tiles, gz),
-             dim3(kThreads), 0, b, a);
+  const dim3 grid(gx, a.shared_tiles + max_tiles, gz);
+  if (fmt == kFmtMxfp4)
+    MOE_LAUNCH(L, (gemm_kernel<P, NS, MODE, kFmtMxfp4>), grid, dim3(kThreads), 0, b, a);
+  else
+    MOE_LAUNCH(L, (gemm_kernel<P, NS, MODE, kFmtInt4>), grid, dim3(kThreads), 0, b, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_gemm_gate_up(const Buckets& b, int max_tiles, const uint16_t* x16, int H,
-                               int I, const uint8_t* gq, const uint16_t* gs,
-                               const uint8_t* uq, const uint16_t* us, uint16_t* h16,
+                               int I, const uint8_t* gq, const void* gs,
+                               const uint8_t* uq, const void* us, uint16_t* h16,
                                const SharedGemm* shared, float* y_zero, int64_t y_elems,
-                               bool tiled, const Launch& L) {
+                               bool tiled, int fmt, const Launch& L) {
   GemmArgs a{};
   a.src[0].tiled = a.src[1].tiled = tiled ? 1 : 0;
   a.y_zero = y_zero;
@@ -476,12 +492,12 @@ hipError_t launch_gemm_gate_up(const Buckets& b, int max_tiles, const uint16_t* 
     a.shared_tiles = (shared->T + kBM - 1) / kBM;
   }
   a.H = H;
-  return launch_tiles<2, kGateUpNS, 0>(b, max_tiles, a, 1, L);
+  return launch_tiles<2, kGateUpNS, 0>(b, max_tiles, a, 1, fmt, L);
 }
 
 hipError_t launch_gemm_down(const Buckets& b, int max_tiles, const uint16_t* h16, int H, int I,
-                            const uint8_t* dq, const uint16_t* ds, const float* w, float* y,
-                            const SharedGemm* shared, bool tiled, const Launch& L) {
+                            const uint8_t* dq, const void* ds, const float* w, float* y,
+                            const SharedGemm* shared, bool tiled, int fmt, const Launch& L) {
   GemmArgs a{};
   a.src[0].tiled = a.src[1].tiled = tiled ? 1 : 0;
   GemmSrc& r = a.src[0];
@@ -516,7 +532,7 @@ hipError_t launch_gemm_down(const Buckets& b, int max_tiles, const uint16_t* h16
     a.src[1].ksplit = down_split(shared->SI / kKS, total);
     gz = std::max(gz, a.src[1].ksplit);
   }
-  return launch_tiles<1, kDownNS, 1>(b, max_tiles, a, gz, L);
+  return launch_tiles<1, kDownNS, 1>(b, max_tiles, a, gz, fmt, L);
 }
 
 }  // namespace moe

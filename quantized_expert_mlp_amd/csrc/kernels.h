@@ -133,7 +133,7 @@ hipError_t launch_convert_x16(const uint16_t* x, int T, int H, uint16_t* x16, co
 struct SharedGemm {
   int T, SI;
   const uint8_t* q[3];
-  const uint16_t* s[3];
+  const void* s[3];  // scales in the call's weight format
   uint16_t* h16;
   const float* gate_logit;
   int gate_ld;
@@ -143,16 +143,21 @@ struct SharedGemm {
 // launch also clears y_zero[0 .. y_elems) (y_elems a multiple of 4) for the
 // down pass's atomic combine.
 // tiled: every plane (shared ones included) is in the tiled layout.
+// fmt: the weight format of every plane; the scale pointers hold fp16 bits
+// (kFmtInt4) or ue8m0 bytes (kFmtMxfp4).
+enum WeightFormat : int { kFmtInt4 = 0, kFmtMxfp4 = 1 };
 hipError_t launch_gemm_gate_up(const Buckets& b, int max_tiles, const uint16_t* x16, int H,
-                               int I, const uint8_t* gq, const uint16_t* gs,
-                               const uint8_t* uq, const uint16_t* us, uint16_t* h16,
+                               int I, const uint8_t* gq, const void* gs,
+                               const uint8_t* uq, const void* us, uint16_t* h16,
                                const SharedGemm* shared, float* y_zero, int64_t y_elems,
-                               bool tiled, const Launch& L);
+                               bool tiled, int fmt, const Launch& L);
 hipError_t launch_gemm_down(const Buckets& b, int max_tiles, const uint16_t* h16, int H, int I,
-                            const uint8_t* dq, const uint16_t* ds, const float* w, float* y,
-                            const SharedGemm* shared, bool tiled, const Launch& L);
+                            const uint8_t* dq, const void* ds, const float* w, float* y,
+                            const SharedGemm* shared, bool tiled, int fmt, const Launch& L);
 
-hipError_t launch_debug_dequant(const uint8_t* q, const uint16_t* s, int N, int K, int mode,
+// mode 0: int4 GEMV decode; 1: int4 MFMA operand; 2: MXFP4 MFMA operand (s
+// holds ue8m0 bytes).
+hipError_t launch_debug_dequant(const uint8_t* q, const void* s, int N, int K, int mode,
                                 float* out, const Launch& L);
 
 }  // namespace moe

@@ -61,7 +61,7 @@ hipError_t launch_pack_weights(const uint8_t* sq, const uint16_t* ss, int E, int
 // Decode one plane with the kernels' own routines.  One thread per packed
 // 32-bit word (8 nibbles).
 __global__ __launch_bounds__(256) void debug_dequant_kernel(const uint8_t* __restrict__ q,
-                                                            const uint16_t* __restrict__ s,
+                                                            const void* __restrict__ s,
                                                             int N, int K, int mode,
                                                             float* __restrict__ out) {
   const int64_t words = (int64_t)N * K / 8;
@@ -70,8 +70,17 @@ __global__ __launch_bounds__(256) void debug_dequant_kernel(const uint8_t* __res
   const int64_t n = i / (K / 8);
   const int kk0 = (int)(i % (K / 8)) * 8;
   const uint32_t wv = reinterpret_cast<const uint32_t*>(q)[i];
-  const uint16_t sb = s[n * (K / 32) + kk0 / 32];
+  const int64_t g = n * (K / 32) + kk0 / 32;
   float* o = out + n * K + kk0;
+  if (mode == 2) {
+    const _Float16 sh = e8m0_f16(static_cast<const uint8_t*>(s)[g]);
+    const f16x2_t s2 = {sh, sh};
+    const f16x8_t v = mx4_f16x8(wv, s2);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j] = (float)v[perm8_pos(j)];
+    return;
+  }
+  const uint16_t sb = static_cast<const uint16_t*>(s)[g];
   if (mode == 0) {
     // bf16 offset form: pair j holds elements j and j+4 as 128 + nibble.
     const Q4Pairs p = q4_bf16_pairs(wv);
@@ -92,7 +101,7 @@ __global__ __launch_bounds__(256) void debug_dequant_kernel(const uint8_t* __res
   }
 }
 
-hipError_t launch_debug_dequant(const uint8_t* q, const uint16_t* s, int N, int K, int mode,
+hipError_t launch_debug_dequant(const uint8_t* q, const void* s, int N, int K, int mode,
                                 float* out, const Launch& L) {
   const int64_t words = (int64_t)N * K / 8;
   MOE_LAUNCH(L, debug_dequant_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0,

@@ -24,6 +24,8 @@ int check_shape(const moe_shape* sh) {
   if (sh->group != 32) return MOE_ERR_UNSUPPORTED;
   if (sh->path < MOE_PATH_AUTO || sh->path > MOE_PATH_GEMM) return MOE_ERR_INVALID_ARG;
   if (sh->layout != MOE_LAYOUT_ROWS && sh->layout != MOE_LAYOUT_TILED) return MOE_ERR_INVALID_ARG;
+  if (sh->format != MOE_FORMAT_INT4 && sh->format != MOE_FORMAT_MXFP4) return MOE_ERR_INVALID_ARG;
+  if (sh->format == MOE_FORMAT_MXFP4 && sh->layout == MOE_LAYOUT_TILED) return MOE_ERR_UNSUPPORTED;
   if (sh->E > 256 || sh->k > 64) return MOE_ERR_UNSUPPORTED;
   if (sh->H % 64 || sh->I % 64 || sh->SI % 64) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)sh->T * sh->k >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
@@ -37,19 +39,22 @@ bool gemv_ok(const moe_shape* sh) {
 }
 
 // The grouped MFMA GEMM is taken when an expert's bucket is expected to hold
-// at least 8 rows (slots / E >= 8), or when the GEMV cannot serve the shape.
+// at least 8 rows (slots / E >= 8), or when the GEMV cannot serve the shape
+// (tiled or MXFP4 planes included).
 int pick_gemm(const moe_shape* sh, bool* gemm) {
   const int64_t slots = (int64_t)sh->T * sh->k;
   switch (sh->path) {
     case MOE_PATH_GEMV:
-      if (!gemv_ok(sh) || sh->layout == MOE_LAYOUT_TILED) return MOE_ERR_UNSUPPORTED;
+      if (!gemv_ok(sh) || sh->layout == MOE_LAYOUT_TILED || sh->format == MOE_FORMAT_MXFP4)
+        return MOE_ERR_UNSUPPORTED;
       *gemm = false;
       return MOE_OK;
     case MOE_PATH_GEMM:
       *gemm = true;
       return MOE_OK;
     default:
-      *gemm = sh->layout == MOE_LAYOUT_TILED || !gemv_ok(sh) || slots >= 8 * (int64_t)sh->E;
+      *gemm = sh->layout == MOE_LAYOUT_TILED || sh->format == MOE_FORMAT_MXFP4 || !gemv_ok(sh) ||
+              slots >= 8 * (int64_t)sh->E;
       return MOE_OK;
   }
 }
@@ -114,6 +119,9 @@ struct Stages {
   }
 };
 
+// int4 scale plane (fp16 bits) of a moe_q4.
+const uint16_t* s16(const void* s) { return static_cast<const uint16_t*>(s); }
+
 bool plane_ok(const moe_q4& p) {
   return p.q && p.s && aligned(p.q, 16) && aligned(p.s, 16);
 }
@@ -138,23 +146,23 @@ int run_mlp(const moe_shape* sh, bool gemm, const Layout& L, void* ws, const uin
     uint16_t* hs = at<uint16_t>(ws, L.hs);
     const int max_buckets = (int)(slots < E ? slots : E);
     if (!sg.skip(MOE_STAGE_ACTIVATIONS)) return MOE_ERR_HIP;
-    err = moe::launch_gemv_gate_up(routed, max_buckets, x, H, I, gate.q, gate.s, up.q, up.s, h, y,
-                                   y_elems, sg.at(MOE_STAGE_GATE_UP), route);
+    err = moe::launch_gemv_gate_up(routed, max_buckets, x, H, I, gate.q, s16(gate.s), up.q,
+                                   s16(up.s), h, y, y_elems, sg.at(MOE_STAGE_GATE_UP), route);
     if (err != hipSuccess) return MOE_ERR_HIP;
     if (shared) {
-      err = moe::launch_gemv_gate_up(sharedb, 1, x, H, sh->SI, shared[0].q, shared[0].s,
-                                     shared[1].q, shared[1].s, hs, nullptr, 0,
+      err = moe::launch_gemv_gate_up(sharedb, 1, x, H, sh->SI, shared[0].q, s16(shared[0].s),
+                                     shared[1].q, s16(shared[1].s), hs, nullptr, 0,
                                      sg.at(MOE_STAGE_SHARED_GATE_UP));
       if (err != hipSuccess) return MOE_ERR_HIP;
     } else if (!sg.skip(MOE_STAGE_SHARED_GATE_UP)) {
       return MOE_ERR_HIP;
     }
-    err = moe::launch_gemv_down(routed, max_buckets, h, H, I, down.q, down.s, w, nullptr, 0, y,
-                                sg.at(MOE_STAGE_DOWN));
+    err = moe::launch_gemv_down(routed, max_buckets, h, H, I, down.q, s16(down.s), w, nullptr, 0,
+                                y, sg.at(MOE_STAGE_DOWN));
     if (err != hipSuccess) return MOE_ERR_HIP;
     if (shared) {
-      err = moe::launch_gemv_down(sharedb, 1, hs, H, sh->SI, shared[2].q, shared[2].s, nullptr,
-                                  gate_logit, gate_ld, y, sg.at(MOE_STAGE_SHARED_DOWN));
+      err = moe::launch_gemv_down(sharedb, 1, hs, H, sh->SI, shared[2].q, s16(shared[2].s),
+                                  nullptr, gate_logit, gate_ld, y, sg.at(MOE_STAGE_SHARED_DOWN));
       if (err != hipSuccess) return MOE_ERR_HIP;
     } else if (!sg.skip(MOE_STAGE_SHARED_DOWN)) {
       return MOE_ERR_HIP;
@@ -186,12 +194,13 @@ int run_mlp(const moe_shape* sh, bool gemm, const Layout& L, void* ws, const uin
     if (err != hipSuccess) return MOE_ERR_HIP;
   }
   const bool tiled = sh->layout == MOE_LAYOUT_TILED;
+  const int fmt = sh->format == MOE_FORMAT_MXFP4 ? moe::kFmtMxfp4 : moe::kFmtInt4;
   err = moe::launch_gemm_gate_up(routed, max_tiles, x16, H, I, gate.q, gate.s, up.q, up.s, h16,
-                                 sgp, y, y_elems, tiled, sg.at(MOE_STAGE_GATE_UP));
+                                 sgp, y, y_elems, tiled, fmt, sg.at(MOE_STAGE_GATE_UP));
   if (err != hipSuccess) return MOE_ERR_HIP;
   if (!sg.skip(MOE_STAGE_SHARED_GATE_UP)) return MOE_ERR_HIP;
   err = moe::launch_gemm_down(routed, max_tiles, h16, H, I, down.q, down.s, w, y, sgp, tiled,
-                              sg.at(MOE_STAGE_DOWN));
+                              fmt, sg.at(MOE_STAGE_DOWN));
   if (err != hipSuccess) return MOE_ERR_HIP;
   if (!sg.skip(MOE_STAGE_SHARED_DOWN)) return MOE_ERR_HIP;
   return MOE_OK;
@@ -240,8 +249,9 @@ int moe_pack_weights(moe_q4 src, int32_t E, int32_t N, int32_t K, moe_q4 dst,
   if (overlap(src.q, qb, dst.q, qb) || overlap(src.s, sb, dst.s, sb) ||
       overlap(src.q, qb, dst.s, sb) || overlap(src.s, sb, dst.q, qb))
     return MOE_ERR_INVALID_ARG;
-  return hip_status(moe::launch_pack_weights(src.q, src.s, E, N, K, const_cast<uint8_t*>(dst.q),
-                                             const_cast<uint16_t*>(dst.s),
+  return hip_status(moe::launch_pack_weights(src.q, static_cast<const uint16_t*>(src.s), E, N, K,
+                                             const_cast<uint8_t*>(dst.q),
+                                             static_cast<uint16_t*>(const_cast<void*>(dst.s)),
                                              moe::Launch{reinterpret_cast<hipStream_t>(stream)}));
 }
 
@@ -409,6 +419,12 @@ int moe_debug_dequant_int4(moe_q4 plane, int32_t N, int32_t K, int32_t mode, flo
   if (!plane_ok(plane) || !out || N < 1 || K < 32 || K % 32 || (mode != 0 && mode != 1))
     return MOE_ERR_INVALID_ARG;
   return hip_status(moe::launch_debug_dequant(plane.q, plane.s, N, K, mode, out,
+                                              moe::Launch{reinterpret_cast<hipStream_t>(stream)}));
+}
+
+int moe_debug_dequant_mxfp4(moe_q4 plane, int32_t N, int32_t K, float* out, moe_stream_t stream) {
+  if (!plane_ok(plane) || !out || N < 1 || K < 32 || K % 32) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_debug_dequant(plane.q, plane.s, N, K, 2, out,
                                               moe::Launch{reinterpret_cast<hipStream_t>(stream)}));
 }
 

@@ -49,6 +49,7 @@ class DeviceLayer:
         if inp.shared is not None:
             self.shared = [(dev(inp.shared[p][0]), dev(inp.shared[p][1])) for p in S.PLANES]
         self.layout = moe.MOE_LAYOUT_ROWS
+        self.format = moe.MOE_FORMAT_MXFP4 if inp.fmt == "mxfp4" else moe.MOE_FORMAT_INT4
 
     def tiled(self) -> "DeviceLayer":
         """A copy whose planes are packed into the tiled layout on the device."""
@@ -90,11 +91,11 @@ def run_layer(d: DeviceLayer, logits=None, use_router=False, path=moe.MOE_PATH_A
               route_scale=1.0, ws_extra=0):
     """moe_layer through the C ABI.  logits: host array to feed (given logits),
     else the inputs' own; use_router: compute logits from w_router.  The
-    planes' layout is the DeviceLayer's."""
+    planes' layout and format are the DeviceLayer's."""
     wl = d.inp.wl
     T = d.inp.x.shape[0]
     sh = moe.make_shape(T, wl.H, wl.E, wl.k, wl.I, wl.SI if d.shared else 0,
-                        route_scale=route_scale, path=path, layout=d.layout)
+                        route_scale=route_scale, path=path, layout=d.layout, format=d.format)
     nbytes = moe.moe_workspace_bytes(sh)
     assert nbytes > 0
     ws = torch.empty(nbytes + ws_extra, dtype=torch.uint8, device="cuda")

@@ -123,6 +123,19 @@ def test_tiled_layout_shape_rules(L):
     assert moe.moe_workspace_bytes(_shape(layout=2)) == 0
 
 
+def test_mxfp4_format_shape_rules(L):
+    mx = dict(format=moe.MOE_FORMAT_MXFP4)
+    assert moe.moe_workspace_bytes(_shape(**mx)) > 0                        # AUTO -> MFMA path
+    assert moe.moe_workspace_bytes(_shape(path=moe.MOE_PATH_GEMM, **mx)) > 0
+    assert moe.moe_workspace_bytes(_shape(path=moe.MOE_PATH_GEMV, **mx)) == 0
+    assert moe.moe_workspace_bytes(_shape(layout=moe.MOE_LAYOUT_TILED, **mx)) == 0
+    assert moe.moe_workspace_bytes(_shape(format=2)) == 0
+    # a decode-sized MXFP4 shape also takes the MFMA path: its workspace holds
+    # the fp16 activation copy the GEMV path does not need
+    dec = dict(T=1, H=6144, E=256, k=8, I=2048)
+    assert moe.moe_workspace_bytes(_shape(**dec, **mx)) > moe.moe_workspace_bytes(_shape(**dec))
+
+
 def test_pack_weights_rejects(L):
     f = L.moe_pack_weights
     src = moe.moe_q4(FAKE, FAKE + (1 << 24))
@@ -143,6 +156,11 @@ def test_debug_dequant_rejects(L):
     assert f(_q(), 4, 64, 2, FAKE, None) == moe.MOE_ERR_INVALID_ARG   # mode
     assert f(_q(), 0, 64, 0, FAKE, None) == moe.MOE_ERR_INVALID_ARG
     assert f(_q(False), 4, 64, 0, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    g = L.moe_debug_dequant_mxfp4
+    assert g(_q(), 4, 48, FAKE, None) == moe.MOE_ERR_INVALID_ARG      # K % 32
+    assert g(_q(), 0, 64, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert g(_q(False), 4, 64, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert g(_q(), 4, 64, None, None) == moe.MOE_ERR_INVALID_ARG
 
 
 def test_product_path_has_no_oracle_dependency():
