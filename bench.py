@@ -206,7 +206,7 @@ def main():
                          "served by the MFMA path)")
     ap.add_argument("--format", default="int4", choices=["int4", "mxfp4"],
                     help="expert weight format (mxfp4: e2m1 nibbles, ue8m0 exponent per 32 "
-                         "inputs; served by the MFMA path with the row layout)")
+                         "inputs; row layout only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -267,7 +267,7 @@ def main():
         sys.exit("bench.py: this workload is not served with --path %s --layout %s --format %s"
                  % (args.path, args.layout, args.format))
     # the library's AUTO rule (MOE_PATH_AUTO)
-    gemm = args.path == "gemm" or (args.path == "auto" and (tiled or mx or (T * wl.k) >= 8 * wl.E))
+    gemm = args.path == "gemm" or (args.path == "auto" and (tiled or (T * wl.k) >= 8 * wl.E))
     nbytes = moe.moe_workspace_bytes(sh)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     y = torch.empty((T, wl.H), dtype=torch.float32, device="cuda")
@@ -347,7 +347,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16" if gemm else "bf16",
+        "dtype": "f16" if gemm or mx else "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "description": wl.description, "T": T, "H": wl.H,
                    "E": wl.E, "k": wl.k, "I": wl.I, "SI": wl.SI,
@@ -355,7 +355,8 @@ def main():
                                else "int4 offset-binary, fp16 scale per 32 inputs"),
                    "layout": args.layout,
                    "path": args.path,
-                   "expert_path": "grouped fp16 MFMA GEMM" if gemm else "streaming int4 GEMV",
+                   "expert_path": "grouped fp16 MFMA GEMM" if gemm else
+                   "streaming %s GEMV" % args.format,
                    "input_rotation": ("%d logits rows" % nvar) if pool is not None
                    else ("%d weight sets" % nvar)},
         "roofline": roof,

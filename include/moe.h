@@ -41,12 +41,13 @@
  * nibble an OCP MX e2m1 code (bit 3 sign, bits 2..1 exponent with bias 1,
  * bit 0 mantissa: 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives); s = ue8m0
  * exponent bytes, uint8 [E][N][K/32], scale 2^(e - 127), e = 255 is NaN.  The
- * kernels feed the MFMA the fp16 value e2m1 * 2^(e - 127) rounded to nearest
- * even for 103 <= e <= 142 (the exact weight for 104 <= e <= 140; past 140 the
+ * MFMA path feeds the fp16 value e2m1 * 2^(e - 127) rounded to nearest even
+ * for 103 <= e <= 142 (the exact weight for 104 <= e <= 140; past 140 the
  * larger codes overflow to +-inf).  Outside that range the scale itself is
  * not an fp16 number: e <= 102 gives zero weights, 143 <= e <= 254 +-inf
- * (NaN for a zero code), e = 255 NaN.  Served by the grouped MFMA GEMM with
- * the row layout.
+ * (NaN for a zero code), e = 255 NaN.  The GEMV path dots the exact e2m1
+ * values with fp16 activations and scales each group's fp32 partial by
+ * 2^(e - 127) in fp32.  Both paths serve MXFP4 with the row layout.
  *
  * Tiled planes (moe_shape.layout = MOE_LAYOUT_TILED, written by
  * moe_pack_weights): the same bytes regrouped so that the grouped MFMA GEMM
@@ -87,8 +88,8 @@ enum moe_path { MOE_PATH_AUTO = 0, MOE_PATH_GEMV = 1, MOE_PATH_GEMM = 2 };
  * MFMA GEMM only (path AUTO or GEMM); ROWS planes by both paths. */
 enum moe_layout { MOE_LAYOUT_ROWS = 0, MOE_LAYOUT_TILED = 1 };
 
-/* Weight format (see above).  MXFP4 planes are served by the grouped MFMA
- * GEMM with the row layout (path AUTO or GEMM, layout ROWS). */
+/* Weight format (see above).  MXFP4 planes are served with the row layout
+ * (layout ROWS) on either path. */
 enum moe_format { MOE_FORMAT_INT4 = 0, MOE_FORMAT_MXFP4 = 1 };
 
 /* One 4-bit plane set: q [E][N][K/2] packed nibbles, s [E][N][K/32] group
@@ -160,8 +161,8 @@ int moe_permute(const int32_t *idx, int32_t T, int32_t k, int32_t E, int32_t *of
  *            256-byte aligned; its contents on entry are ignored.
  * The order in which a token's k terms are added to y is not fixed (device
  * atomics); the result differs from an ordered sum only by fp32 rounding.
- * Errors: INVALID_ARG, UNSUPPORTED (also for path GEMV with TILED or MXFP4
- *         planes, and for MXFP4 with TILED), WORKSPACE, HIP.
+ * Errors: INVALID_ARG, UNSUPPORTED (also for path GEMV with TILED planes and
+ *         for MXFP4 with TILED), WORKSPACE, HIP.
  */
 int moe_expert_mlp(const moe_shape *shape, const uint16_t *x, const int32_t *off,
                    const int32_t *sorted, const float *w, moe_q4 gate, moe_q4 up, moe_q4 down,

@@ -106,16 +106,20 @@ struct RouteArgs {
   int32_t* sched;   // schedule words
 };
 
-// Streaming int4 GEMV (decode).  gate/up: h[row][I] = fp16(silu(Wg x)*(Wu x));
+// Weight formats: the scale pointers hold fp16 bits (kFmtInt4) or ue8m0
+// bytes (kFmtMxfp4).
+enum WeightFormat : int { kFmtInt4 = 0, kFmtMxfp4 = 1 };
+
+// Streaming 4-bit GEMV (decode).  gate/up: h[row][I] = fp16(silu(Wg x)*(Wu x));
 // down: y[token] += weight * (Wd h[row]).  The gate/up launch also zeroes y.
 hipError_t launch_gemv_gate_up(const Buckets& b, int max_buckets, const uint16_t* x, int H,
-                               int I, const uint8_t* gq, const uint16_t* gs,
-                               const uint8_t* uq, const uint16_t* us, uint16_t* h,
-                               float* y_zero, int64_t y_elems, const Launch& L,
-                               const RouteArgs* route = nullptr);
+                               int I, const uint8_t* gq, const void* gs, const uint8_t* uq,
+                               const void* us, uint16_t* h, float* y_zero, int64_t y_elems,
+                               int fmt, const Launch& L, const RouteArgs* route = nullptr);
 hipError_t launch_gemv_down(const Buckets& b, int max_buckets, const uint16_t* h, int H, int I,
-                            const uint8_t* dq, const uint16_t* ds, const float* w,
-                            const float* gate_logit, int gate_ld, float* y, const Launch& L);
+                            const uint8_t* dq, const void* ds, const float* w,
+                            const float* gate_logit, int gate_ld, float* y, int fmt,
+                            const Launch& L);
 bool gemv_supported(int K);
 
 // Grouped MFMA GEMM (prefill), fp16 operands with fp32 accumulation.
@@ -143,9 +147,7 @@ struct SharedGemm {
 // launch also clears y_zero[0 .. y_elems) (y_elems a multiple of 4) for the
 // down pass's atomic combine.
 // tiled: every plane (shared ones included) is in the tiled layout.
-// fmt: the weight format of every plane; the scale pointers hold fp16 bits
-// (kFmtInt4) or ue8m0 bytes (kFmtMxfp4).
-enum WeightFormat : int { kFmtInt4 = 0, kFmtMxfp4 = 1 };
+// fmt: the weight format of every plane (WeightFormat).
 hipError_t launch_gemm_gate_up(const Buckets& b, int max_tiles, const uint16_t* x16, int H,
                                int I, const uint8_t* gq, const void* gs,
                                const uint8_t* uq, const void* us, uint16_t* h16,

@@ -40,21 +40,19 @@ bool gemv_ok(const moe_shape* sh) {
 
 // The grouped MFMA GEMM is taken when an expert's bucket is expected to hold
 // at least 8 rows (slots / E >= 8), or when the GEMV cannot serve the shape
-// (tiled or MXFP4 planes included).
+// (tiled planes included).
 int pick_gemm(const moe_shape* sh, bool* gemm) {
   const int64_t slots = (int64_t)sh->T * sh->k;
   switch (sh->path) {
     case MOE_PATH_GEMV:
-      if (!gemv_ok(sh) || sh->layout == MOE_LAYOUT_TILED || sh->format == MOE_FORMAT_MXFP4)
-        return MOE_ERR_UNSUPPORTED;
+      if (!gemv_ok(sh) || sh->layout == MOE_LAYOUT_TILED) return MOE_ERR_UNSUPPORTED;
       *gemm = false;
       return MOE_OK;
     case MOE_PATH_GEMM:
       *gemm = true;
       return MOE_OK;
     default:
-      *gemm = sh->layout == MOE_LAYOUT_TILED || sh->format == MOE_FORMAT_MXFP4 || !gemv_ok(sh) ||
-              slots >= 8 * (int64_t)sh->E;
+      *gemm = sh->layout == MOE_LAYOUT_TILED || !gemv_ok(sh) || slots >= 8 * (int64_t)sh->E;
       return MOE_OK;
   }
 }
@@ -119,9 +117,6 @@ struct Stages {
   }
 };
 
-// int4 scale plane (fp16 bits) of a moe_q4.
-const uint16_t* s16(const void* s) { return static_cast<const uint16_t*>(s); }
-
 bool plane_ok(const moe_q4& p) {
   return p.q && p.s && aligned(p.q, 16) && aligned(p.s, 16);
 }
@@ -140,29 +135,30 @@ int run_mlp(const moe_shape* sh, bool gemm, const Layout& L, void* ws, const uin
   Buckets routed{off, sorted, sched, k, 0, T, E};
   Buckets sharedb{nullptr, nullptr, nullptr, 1, T, T, 1};
   const int64_t y_elems = (int64_t)T * H;
+  const int fmt = sh->format == MOE_FORMAT_MXFP4 ? moe::kFmtMxfp4 : moe::kFmtInt4;
   hipError_t err;
   if (!gemm) {
     uint16_t* h = at<uint16_t>(ws, L.h);
     uint16_t* hs = at<uint16_t>(ws, L.hs);
     const int max_buckets = (int)(slots < E ? slots : E);
     if (!sg.skip(MOE_STAGE_ACTIVATIONS)) return MOE_ERR_HIP;
-    err = moe::launch_gemv_gate_up(routed, max_buckets, x, H, I, gate.q, s16(gate.s), up.q,
-                                   s16(up.s), h, y, y_elems, sg.at(MOE_STAGE_GATE_UP), route);
+    err = moe::launch_gemv_gate_up(routed, max_buckets, x, H, I, gate.q, gate.s, up.q, up.s, h, y,
+                                   y_elems, fmt, sg.at(MOE_STAGE_GATE_UP), route);
     if (err != hipSuccess) return MOE_ERR_HIP;
     if (shared) {
-      err = moe::launch_gemv_gate_up(sharedb, 1, x, H, sh->SI, shared[0].q, s16(shared[0].s),
-                                     shared[1].q, s16(shared[1].s), hs, nullptr, 0,
+      err = moe::launch_gemv_gate_up(sharedb, 1, x, H, sh->SI, shared[0].q, shared[0].s,
+                                     shared[1].q, shared[1].s, hs, nullptr, 0, fmt,
                                      sg.at(MOE_STAGE_SHARED_GATE_UP));
       if (err != hipSuccess) return MOE_ERR_HIP;
     } else if (!sg.skip(MOE_STAGE_SHARED_GATE_UP)) {
       return MOE_ERR_HIP;
     }
-    err = moe::launch_gemv_down(routed, max_buckets, h, H, I, down.q, s16(down.s), w, nullptr, 0,
-                                y, sg.at(MOE_STAGE_DOWN));
+    err = moe::launch_gemv_down(routed, max_buckets, h, H, I, down.q, down.s, w, nullptr, 0, y,
+                                fmt, sg.at(MOE_STAGE_DOWN));
     if (err != hipSuccess) return MOE_ERR_HIP;
     if (shared) {
-      err = moe::launch_gemv_down(sharedb, 1, hs, H, sh->SI, shared[2].q, s16(shared[2].s),
-                                  nullptr, gate_logit, gate_ld, y, sg.at(MOE_STAGE_SHARED_DOWN));
+      err = moe::launch_gemv_down(sharedb, 1, hs, H, sh->SI, shared[2].q, shared[2].s, nullptr,
+                                  gate_logit, gate_ld, y, fmt, sg.at(MOE_STAGE_SHARED_DOWN));
       if (err != hipSuccess) return MOE_ERR_HIP;
     } else if (!sg.skip(MOE_STAGE_SHARED_DOWN)) {
       return MOE_ERR_HIP;
@@ -194,7 +190,6 @@ int run_mlp(const moe_shape* sh, bool gemm, const Layout& L, void* ws, const uin
     if (err != hipSuccess) return MOE_ERR_HIP;
   }
   const bool tiled = sh->layout == MOE_LAYOUT_TILED;
-  const int fmt = sh->format == MOE_FORMAT_MXFP4 ? moe::kFmtMxfp4 : moe::kFmtInt4;
   err = moe::launch_gemm_gate_up(routed, max_tiles, x16, H, I, gate.q, gate.s, up.q, up.s, h16,
                                  sgp, y, y_elems, tiled, fmt, sg.at(MOE_STAGE_GATE_UP));
   if (err != hipSuccess) return MOE_ERR_HIP;

@@ -127,13 +127,17 @@ def test_mxfp4_format_shape_rules(L):
     mx = dict(format=moe.MOE_FORMAT_MXFP4)
     assert moe.moe_workspace_bytes(_shape(**mx)) > 0                        # AUTO -> MFMA path
     assert moe.moe_workspace_bytes(_shape(path=moe.MOE_PATH_GEMM, **mx)) > 0
-    assert moe.moe_workspace_bytes(_shape(path=moe.MOE_PATH_GEMV, **mx)) == 0
+    assert moe.moe_workspace_bytes(_shape(path=moe.MOE_PATH_GEMV, **mx)) > 0
     assert moe.moe_workspace_bytes(_shape(layout=moe.MOE_LAYOUT_TILED, **mx)) == 0
     assert moe.moe_workspace_bytes(_shape(format=2)) == 0
-    # a decode-sized MXFP4 shape also takes the MFMA path: its workspace holds
-    # the fp16 activation copy the GEMV path does not need
+    assert moe.moe_workspace_bytes(_shape(format=-1)) == 0
+    # the AUTO rule does not depend on the format: decode takes the GEMV path
+    # (no fp16 activation copy in its workspace), prefill the MFMA path
+    for dims in (dict(T=1, H=6144, E=256, k=8, I=2048), dict(T=2048, H=6144, E=256, k=8, I=2048)):
+        assert moe.moe_workspace_bytes(_shape(**dims, **mx)) == moe.moe_workspace_bytes(_shape(**dims))
     dec = dict(T=1, H=6144, E=256, k=8, I=2048)
-    assert moe.moe_workspace_bytes(_shape(**dec, **mx)) > moe.moe_workspace_bytes(_shape(**dec))
+    assert moe.moe_workspace_bytes(_shape(path=moe.MOE_PATH_GEMM, **dec, **mx)) > \
+        moe.moe_workspace_bytes(_shape(**dec, **mx))
 
 
 def test_pack_weights_rejects(L):

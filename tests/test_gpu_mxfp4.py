@@ -1,7 +1,7 @@
 """GPU tests of MXFP4 expert weights (e2m1 nibbles, one ue8m0 exponent per 32
 inputs): the MFMA kernels' decode against the oracle's exact weights rounded
 to fp16 (bit-exact), and the whole layer on MXFP4 planes against the CPU
-oracle at mid sizes and at every full workload size."""
+oracle at mid sizes on both expert paths and at every full workload size."""
 import numpy as np
 import pytest
 import torch
@@ -63,7 +63,7 @@ def test_debug_dequant_mxfp4_scale_range_ends():
     assert np.all(got[~nan] == 0.0)
 
 
-@pytest.mark.parametrize("path", [moe.MOE_PATH_AUTO, moe.MOE_PATH_GEMM])
+@pytest.mark.parametrize("path", [moe.MOE_PATH_GEMV, moe.MOE_PATH_GEMM])
 @pytest.mark.parametrize("wl", MID, ids=[w.name for w in MID])
 def test_layer_mid_mxfp4(wl, path):
     say("mxfp4 layer %s path=%d" % (wl.name, path))
@@ -94,3 +94,18 @@ def test_layer_full_size_mxfp4(name):
                                fmt="mxfp4")
     sel = slice(None) if rows is None else rows
     assert_y_close(y[sel], y_ref, name + " mxfp4")
+
+
+@pytest.mark.parametrize("name", ["decode", "decode_batch"])
+def test_layer_full_size_mxfp4_mfma_path(name):
+    """The decode sizes through the MFMA path as well (AUTO takes the GEMV)."""
+    wl = S.WORKLOADS[name]
+    say("full-size mxfp4 layer %s on the MFMA path" % name)
+    inp = S.make_layer_inputs(wl, seed=1, fmt="mxfp4")
+    d = DeviceLayer(inp)
+    L = _oracle_logits(inp)
+    y, idx, w, _ = run_layer(d, logits=L, path=moe.MOE_PATH_GEMM)
+    y_ref, idx_ref, _ = oracle.layer(inp.x, L, wl.k, inp.planes, inp.shared, inp.shared_gate,
+                                     fmt="mxfp4")
+    assert np.array_equal(idx, idx_ref)
+    assert_y_close(y, y_ref, name + " mxfp4 mfma")
