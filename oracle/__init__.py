@@ -55,6 +55,9 @@ def lib():
         L.oracle_permute.argtypes = [P, i64, i64, i64, P, P, P]
         L.oracle_expert_forward.argtypes = [P] * 6 + [i64, i64, P, P, P, ctypes.c_int]
         L.oracle_layer.argtypes = [P] * 13 + [i64, P, P, P]
+        L.oracle_add_rmsnorm.argtypes = [P, P, P, i64, i64, ctypes.c_double, P, P]
+        L.oracle_double_to_bf16.argtypes = [ctypes.c_double]
+        L.oracle_double_to_bf16.restype = ctypes.c_uint16
         _lib = L
     return _lib
 
@@ -201,3 +204,20 @@ def layer(x: np.ndarray, logits: np.ndarray, k: int, planes: Dict[str, tuple],
                        _p(dq), _p(ds), sq_arr, ss_arr, _p(shared_gate), _p(rows_a), n,
                        _p(y), _p(idx), _p(w))
     return y, idx, w
+
+
+def double_to_bf16(v: float) -> int:
+    return lib().oracle_double_to_bf16(float(v))
+
+
+def add_rmsnorm(r: np.ndarray, y: np.ndarray, g: np.ndarray, eps: float):
+    """The combine folded into the residual step: (r + y as fp32 [T][H],
+    bf16 bits [T][H] of the RMS-normed row times g)."""
+    r = _c(r, np.float32)
+    y = _c(y, np.float32)
+    g = _c(g, np.float32)
+    T, H = r.shape
+    r_out = np.empty((T, H), dtype=np.float32)
+    n_out = np.empty((T, H), dtype=np.uint16)
+    lib().oracle_add_rmsnorm(_p(r), _p(y), _p(g), T, H, float(eps), _p(r_out), _p(n_out))
+    return r_out, n_out

@@ -20,6 +20,10 @@
 //              more router row) and on the combine folded into add+rms (the
 //              FFN row summed as gated shared row first, then the slots in
 //              order).
+//   [dasllama-fold] the same dasLLAMA PR's commit folding the combine into the
+//              residual step: the add+rms after the routed block adds the FFN
+//              row (gated shared row, then the slots in order) to the
+//              residual and norms the row for the next layer.
 //   [vllmcpp]  vllm.cpp PR #481, "gate(#378): the first DEVICE run of the
 //              warp MoE router": the ungated softmax router with top-k, k
 //              passes of mask-and-reseed over the logit row.
@@ -121,6 +125,29 @@ inline const void* scale_at(int fmt, const void* s, int64_t elems) {
 }
 
 double sigmoid(double z) { return 1.0 / (1.0 + std::exp(-z)); }
+
+// fp64 -> bf16 bits, rounded once to nearest with ties to even.  bf16 keeps 8
+// significant bits and fp32's exponent range: normal values are rounded to 8
+// significant bits, values below 2^-126 to a multiple of 2^-133 (subnormal
+// spacing); magnitudes past the largest bf16 after rounding are +-inf.
+uint16_t double_to_bf16(double v) {
+  if (std::isnan(v)) return 0x7FC0;
+  const double a = std::fabs(v);
+  double r;
+  if (a == 0.0 || std::isinf(a)) {
+    r = a;
+  } else {
+    int e;
+    std::frexp(a, &e);                      // a = m * 2^e, 0.5 <= m < 1
+    const int q = std::max(e - 8, -133);    // weight of the last kept bit
+    r = std::ldexp(std::nearbyint(std::ldexp(a, -q)), q);
+  }
+  const double kMax = std::ldexp(255.0, 120);  // (2 - 2^-7) * 2^127
+  float f = r > kMax ? INFINITY : (float)r;    // r has <= 8 significant bits: exact
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  return (uint16_t)((u >> 16) | (std::signbit(v) ? 0x8000u : 0u));
+}
 
 // One expert's SwiGLU MLP in fp64: g = Wg.x, u = Wu.x, h = silu(g)*u,
 // o = Wd.h ([colibri] Summary: the fused expert computes gate and up, the SiLU
@@ -277,6 +304,31 @@ void oracle_expert_forward(const uint8_t* qg, const void* sg, const uint8_t* qu,
   std::vector<double> hh(I);
   expert_forward(fmt, qg, sg, qu, su, qd, sd, H, I, x, h ? h : hh.data(), o);
 }
+
+// The combine folded into the residual step ([dasllama-fold]), for T rows:
+//   r_out[t] = fp32(r[t] + y[t])                      (fp64 add, one rounding)
+//   n_out[t] = bf16(r_out[t] * g / sqrt(mean_h r_out[t][h]^2 + eps))
+// with y the layer's FFN row (shared row and slots already summed in order).
+// Reading of the norm (the pages name it add+rms): RMS normalisation over
+// the H features of the stored fp32 residual row, eps inside the square
+// root, then the elementwise weight g of the next layer; computed in fp64
+// and rounded once to bf16, the layer's activation format.  r_out may alias r.
+void oracle_add_rmsnorm(const float* r, const float* y, const float* g, int64_t T, int64_t H,
+                        double eps, float* r_out, uint16_t* n_out) {
+  for (int64_t t = 0; t < T; ++t) {
+    double ss = 0.0;
+    for (int64_t h = 0; h < H; ++h) {
+      const float v = (float)((double)r[t * H + h] + (double)y[t * H + h]);
+      r_out[t * H + h] = v;
+      ss += (double)v * (double)v;
+    }
+    const double inv = 1.0 / std::sqrt(ss / (double)H + eps);
+    for (int64_t h = 0; h < H; ++h)
+      n_out[t * H + h] = double_to_bf16((double)r_out[t * H + h] * inv * (double)g[h]);
+  }
+}
+
+uint16_t oracle_double_to_bf16(double v) { return double_to_bf16(v); }
 
 struct oracle_shape {
   int64_t T, H, E, k, I, SI;

@@ -54,6 +54,17 @@ MUTATIONS = {
                                 ["test_dequant_mxfp4_golden"]),
     "mxfp4_scale_stride_two_bytes": ("return fmt == 1 ? 1 : 2;", "return 2;",
                                      ["test_layer_mxfp4_equals_dense_library_mixture"]),
+    "bf16_rounded_through_fp32": ("const double a = std::fabs(v);",
+                                  "const double a = (double)(float)std::fabs(v);",
+                                  ["test_bf16_rounding_golden"]),
+    "bf16_truncates": ("std::nearbyint(std::ldexp(a, -q))", "std::trunc(std::ldexp(a, -q))",
+                       ["test_bf16_rounding_golden"]),
+    "rms_eps_outside_root": ("std::sqrt(ss / (double)H + eps)", "(std::sqrt(ss / (double)H) + eps)",
+                             ["test_add_rmsnorm_special_cases"]),
+    "rms_mean_over_h_plus_one": ("std::sqrt(ss / (double)H + eps)",
+                                 "std::sqrt(ss / (double)(H + 1) + eps)",
+                                 ["test_add_rmsnorm_matches_library_rms_norm"]),
+    "rms_weight_dropped": ("* inv * (double)g[h]", "* inv", ["test_add_rmsnorm_matches_library_rms_norm"]),
     "combine_uses_first_weight": ("acc[h] += w[j] * o[h];", "acc[h] += w[0] * o[h];",
                                   ["test_layer_equals_dense_masked_mixture"]),
 }

@@ -499,3 +499,68 @@ def test_layer_shared_expert_gate(orc):
     y_routed, _, _ = orc.layer(x, logits, 2, planes)
     assert np.allclose(y_full, y_routed.astype(np.float64) + y_g, rtol=1e-5,
                        atol=1e-5 * np.abs(y_full).max())
+
+
+# ------------------------------------------------- combine folded: add+rms --
+
+def test_bf16_rounding_golden(orc):
+    n = 0
+    for line in open(os.path.join(GOLDEN, "bf16_rounding.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        m, e, bits = line.split()[:3]
+        v = math.ldexp(int(m), int(e))
+        assert orc.double_to_bf16(v) == int(bits, 16), line
+        n += 1
+    assert n == 11
+
+
+def test_bf16_rounding_matches_library_on_fp32_values(orc):
+    """For values already in fp32 one rounding is the library's fp32 -> bf16."""
+    import torch
+    rng = np.random.default_rng(30)
+    f = np.concatenate([rng.standard_normal(3000).astype(np.float32),
+                        (rng.standard_normal(500) * 1e-38).astype(np.float32),
+                        np.float32([3.3e38, -3.39e38, 1.0, 0.0])])
+    ref = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([orc.double_to_bf16(float(v)) for v in f], dtype=np.uint16)
+    assert np.array_equal(got, ref)
+
+
+def test_add_rmsnorm_matches_library_rms_norm(orc):
+    import torch
+    rng = np.random.default_rng(31)
+    T, H, eps = 5, 384, 1e-6
+    r = rng.standard_normal((T, H)).astype(np.float32)
+    y = (0.1 * rng.standard_normal((T, H))).astype(np.float32)
+    g = (1.0 + 0.2 * rng.standard_normal(H)).astype(np.float32)
+    r_out, n_out = orc.add_rmsnorm(r, y, g, eps)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(r_out.astype(np.float64)), (H,),
+                                       torch.from_numpy(g.astype(np.float64)), eps).numpy()
+    want = np.array([orc.double_to_bf16(v) for v in ref.ravel()], dtype=np.uint16).reshape(T, H)
+    assert np.array_equal(n_out, want)
+
+
+def test_add_rmsnorm_special_cases(orc):
+    H = 64
+    g = np.ones(H, np.float32)
+    c = np.full((2, H), 3.0, np.float32)
+    c[1] = -0.25
+    z = np.zeros_like(c)
+    # y = 0 leaves the residual; a constant row normalises to its sign (eps = 0)
+    r_out, n_out = orc.add_rmsnorm(c, z, g, 0.0)
+    assert np.array_equal(r_out, c)
+    assert np.all(n_out[0] == 0x3F80) and np.all(n_out[1] == 0xBF80)
+    # eps = c^2 halves the mean square's weight: 1/sqrt(2)
+    _, n_eps = orc.add_rmsnorm(c[:1], z[:1], g, 9.0)
+    assert np.all(n_eps == orc.double_to_bf16(1.0 / math.sqrt(2.0)))
+    # r = 0 passes y through; the weight scales the normed row elementwise
+    g2 = np.arange(1, H + 1, dtype=np.float32)
+    r_out, n_out = orc.add_rmsnorm(z[:1], c[:1], g2, 0.0)
+    assert np.array_equal(r_out, c[:1])
+    assert np.array_equal(n_out[0], [orc.double_to_bf16(float(v)) for v in g2])
+    # the add is one rounding of the exact sum: 1 + 2^-24 + 2^-40 rounds up
+    r1 = np.ones((1, H), np.float32)
+    y1 = np.full((1, H), np.float32(2.0 ** -24 + 2.0 ** -40), np.float32)
+    r_out, _ = orc.add_rmsnorm(r1, y1, g, 0.0)
+    assert np.all(r_out == np.float32(1.0 + 2.0 ** -23))
