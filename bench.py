@@ -207,6 +207,9 @@ def main():
     ap.add_argument("--format", default="int4", choices=["int4", "mxfp4"],
                     help="expert weight format (mxfp4: e2m1 nibbles, ue8m0 exponent per 32 "
                          "inputs; row layout only)")
+    ap.add_argument("--fold", action="store_true",
+                    help="time the layer with its combine folded into the residual add + "
+                         "RMSnorm (moe_layer_residual_rmsnorm) instead of moe_layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -271,11 +274,21 @@ def main():
     nbytes = moe.moe_workspace_bytes(sh)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     y = torch.empty((T, wl.H), dtype=torch.float32, device="cuda")
+    if args.fold:
+        residual = torch.from_numpy(S.draw_residual(wl)).cuda()
+        norm_w = torch.from_numpy(S.draw_norm_weight(wl)).cuda()
+        x_next = torch.empty((T, wl.H), dtype=torch.int16, device="cuda")
 
     def call(i, events=None):
         s = sets[i % len(sets)] if pool is None else sets[0]
         lg = pool[i % len(pool)] if pool is not None else None
         wr = s["w_router"] if pool is None else None
+        if args.fold and events is None:
+            moe.moe_layer_residual_rmsnorm(sh, s["x"], lg, wr, s["planes"]["gate"],
+                                           s["planes"]["up"], s["planes"]["down"], s["shared"],
+                                           s["shared_gate"], residual, norm_w, 1e-6, x_next,
+                                           None, None, ws, nbytes)
+            return
         args_ = (sh, s["x"], lg, wr, s["planes"]["gate"], s["planes"]["up"], s["planes"]["down"],
                  s["shared"], s["shared_gate"], y, None, None, None, ws, nbytes)
         if events is None:
@@ -297,7 +310,9 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     tokens_per_s = T * args.steps / wall
 
-    # ---- per-stage device time (HIP events on the launch stream)
+    # ---- per-stage device time (HIP events on the launch stream); with --fold
+    # these come from moe_layer_profiled, whose kernels are the folded step's
+    # except the final norm launch
     ev = [[hip.event() for _ in range(2 * len(moe.STAGES))] for _ in range(args.steps)]
     for i in range(args.steps):
         call(i, ev[i])
@@ -355,6 +370,8 @@ def main():
                                else "int4 offset-binary, fp16 scale per 32 inputs"),
                    "layout": args.layout,
                    "path": args.path,
+                   "step": ("layer + residual add + RMSnorm (moe_layer_residual_rmsnorm)"
+                            if args.fold else "layer (moe_layer)"),
                    "expert_path": "grouped fp16 MFMA GEMM" if gemm else
                    "streaming %s GEMV" % args.format,
                    "input_rotation": ("%d logits rows" % nvar) if pool is not None

@@ -193,6 +193,35 @@ int moe_layer(const moe_shape *shape, const uint16_t *x, const float *logits,
               float *logits_out, void *ws, size_t ws_bytes, moe_stream_t stream);
 
 /*
+ * The layer with its combine folded into the residual step (the dasLLAMA
+ * PR's fold: the add+rms after the routed block adds the gated shared row and
+ * the k weighted expert rows straight into the residual, then norms the row
+ * for the next layer):
+ *   residual[t] += sigma(x_t . g) * shared(x_t) + sum_j w[t][j] * o[t][j]
+ *   x_next[t]    = bf16( residual[t] * norm_w / sqrt(mean_h residual[t][h]^2 + eps) )
+ * The down pass adds into `residual` directly (no separate FFN output), and
+ * one more launch writes the normed row in the layer's activation format, so
+ * x_next can be the next layer's x.
+ *   residual : fp32 [T][H], in/out, 16-byte aligned; must not overlap any
+ *              other argument.
+ *   norm_w   : fp32 [H], the next layer's norm weight, 16-byte aligned.
+ *   eps      : >= 0, added to the mean square inside the root.
+ *   x_next   : bf16 bits [T][H] out, 16-byte aligned; may be x itself (x is
+ *              no longer read when it is written).
+ *   the rest : as for moe_layer (no logits_out).
+ * The order of the terms added into a residual element is not fixed (device
+ * atomics); the result differs from an ordered sum by fp32 rounding only.
+ * Errors: as moe_layer, plus INVALID_ARG for a null or misaligned residual,
+ *         norm_w or x_next, or a negative or NaN eps.
+ */
+int moe_layer_residual_rmsnorm(const moe_shape *shape, const uint16_t *x, const float *logits,
+                               const float *w_router, moe_q4 gate, moe_q4 up, moe_q4 down,
+                               const moe_q4 *shared, const float *shared_gate, float *residual,
+                               const float *norm_w, float eps, uint16_t *x_next,
+                               int32_t *idx_out, float *w_out, void *ws, size_t ws_bytes,
+                               moe_stream_t stream);
+
+/*
  * Profiling twin of moe_layer: the same work, with stage i's kernel launched
  * through hipExtLaunchKernelGGL so that events[2i] and events[2i+1]
  * (hipEvent_t handles created by the caller) are recorded at that kernel's

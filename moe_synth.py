@@ -21,6 +21,8 @@ Storage conventions (the boundary's):
   x        uint16 [T][H]          bf16 bits, round-to-nearest-even from N(0,1)
   logits   float32 [T][E]         N(0,1) (given-logits workloads)
   w_router float32 [E][H]         N(0, 0.02)      (router-logits workloads)
+  residual float32 [T][H]         N(0, 1)         (folded residual step)
+  norm_w   float32 [H]            1 + N(0, 0.1)   (its next-layer RMSnorm weight)
   g        float32 [H]            N(0, 0.02)      (shared-expert gate vector)
   q        uint8 [E][N][K/2]      element kk in byte kk/2, low nibble = even kk
   s        uint16 [E][N][K/32]    fp16 bits, uniform[0.005, 0.02] rounded RNE
@@ -133,6 +135,17 @@ def draw_router(wl: Workload, seed: int = 0) -> np.ndarray:
 
 def draw_shared_gate(wl: Workload, seed: int = 0) -> np.ndarray:
     return _rng(seed, wl.wid, 4).normal(0.0, 0.02, (wl.H,)).astype(np.float32)
+
+
+def draw_residual(wl: Workload, seed: int = 0, T: Optional[int] = None) -> np.ndarray:
+    """fp32 residual stream [T][H] for the folded residual step, N(0, 1)."""
+    T = wl.T if T is None else T
+    return _rng(seed, wl.wid, 5).standard_normal((T, wl.H), dtype=np.float32)
+
+
+def draw_norm_weight(wl: Workload, seed: int = 0) -> np.ndarray:
+    """fp32 RMSnorm weight [H] of the next layer, 1 + N(0, 0.1)."""
+    return (1.0 + 0.1 * _rng(seed, wl.wid, 6).standard_normal(wl.H)).astype(np.float32)
 
 
 def draw_plane(N: int, K: int, rng: np.random.Generator):

@@ -25,7 +25,8 @@ MOE_FORMAT_INT4, MOE_FORMAT_MXFP4 = range(2)
 # Every symbol include/moe.h declares.
 EXPORTS = ("moe_router_topk", "moe_permute", "moe_expert_mlp", "moe_layer",
            "moe_layer_profiled", "moe_pack_weights", "moe_workspace_bytes",
-           "moe_status_string", "moe_debug_dequant_int4", "moe_debug_dequant_mxfp4")
+           "moe_status_string", "moe_debug_dequant_int4", "moe_debug_dequant_mxfp4",
+           "moe_layer_residual_rmsnorm")
 STAGES = ("start", "logits", "topk", "permute", "activations", "gate_up", "shared_gate_up",
           "down", "shared_down")
 
@@ -67,6 +68,9 @@ def lib() -> ctypes.CDLL:
                                 ctypes.POINTER(moe_q4), P, P, P, P, P, P, ctypes.c_size_t, P]
         L.moe_layer_profiled.argtypes = L.moe_layer.argtypes + [ctypes.POINTER(ctypes.c_void_p),
                                                                 i32]
+        L.moe_layer_residual_rmsnorm.argtypes = [
+            ctypes.POINTER(moe_shape), P, P, P, moe_q4, moe_q4, moe_q4, ctypes.POINTER(moe_q4), P,
+            P, P, ctypes.c_float, P, P, P, P, ctypes.c_size_t, P]
         L.moe_workspace_bytes.argtypes = [ctypes.POINTER(moe_shape)]
         L.moe_workspace_bytes.restype = ctypes.c_size_t
         L.moe_status_string.argtypes = [ctypes.c_int]
@@ -76,7 +80,7 @@ def lib() -> ctypes.CDLL:
         L.moe_pack_weights.argtypes = [moe_q4, i32, i32, i32, moe_q4, P]
         for name in ("moe_router_topk", "moe_permute", "moe_expert_mlp", "moe_layer",
                      "moe_layer_profiled", "moe_pack_weights", "moe_debug_dequant_int4",
-                     "moe_debug_dequant_mxfp4"):
+                     "moe_debug_dequant_mxfp4", "moe_layer_residual_rmsnorm"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -150,6 +154,20 @@ def moe_layer(shape: moe_shape, x, logits, w_router, gate, up, down,
         ctypes.byref(shape), _ptr(x), _ptr(logits), _ptr(w_router), q4(gate), q4(up), q4(down),
         sh_arr, _ptr(shared_gate), _ptr(y), _ptr(idx_out), _ptr(w_out), _ptr(logits_out),
         _ptr(ws), int(ws_bytes), _stream(stream)))
+
+
+def moe_layer_residual_rmsnorm(shape: moe_shape, x, logits, w_router, gate, up, down,
+                               shared: Optional[Sequence[Tuple]], shared_gate, residual, norm_w,
+                               eps, x_next, idx_out, w_out, ws, ws_bytes, stream=None) -> None:
+    """moe_layer whose combine adds into `residual` (fp32, in/out), followed by
+    x_next = bf16(RMSnorm(residual) * norm_w)."""
+    sh_arr = None
+    if shared is not None:
+        sh_arr = (moe_q4 * 3)(*[q4(p) for p in shared])
+    _check("moe_layer_residual_rmsnorm", lib().moe_layer_residual_rmsnorm(
+        ctypes.byref(shape), _ptr(x), _ptr(logits), _ptr(w_router), q4(gate), q4(up), q4(down),
+        sh_arr, _ptr(shared_gate), _ptr(residual), _ptr(norm_w), float(eps), _ptr(x_next),
+        _ptr(idx_out), _ptr(w_out), _ptr(ws), int(ws_bytes), _stream(stream)))
 
 
 def moe_layer_profiled(shape: moe_shape, x, logits, w_router, gate, up, down,

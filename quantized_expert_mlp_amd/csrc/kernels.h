@@ -127,6 +127,10 @@ bool gemv_supported(int K);
 hipError_t launch_pack_weights(const uint8_t* sq, const uint16_t* ss, int E, int N, int K,
                                uint8_t* dq, uint16_t* ds, const Launch& L);
 
+// n[t] = bf16(r[t] * g / sqrt(mean(r[t]^2) + eps)) for T rows of H (H % 4 == 0).
+hipError_t launch_rmsnorm(const float* r, const float* g, int T, int H, float eps, uint16_t* out,
+                          const Launch& L);
+
 // bf16 x [T][H] -> fp16 copy with each block of 8 in the order 0,4,1,5,2,6,3,7.
 hipError_t launch_convert_x16(const uint16_t* x, int T, int H, uint16_t* x16, const Launch& L);
 

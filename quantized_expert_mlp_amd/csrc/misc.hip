@@ -25,6 +25,46 @@ hipError_t launch_convert_x16(const uint16_t* x, int T, int H, uint16_t* x16, co
   return hipGetLastError();
 }
 
+// The residual step after the layer (the dasLLAMA PR's combine folded into
+// add+rms): the down pass has already added the FFN row into the fp32
+// residual r; this writes the next layer's input n = bf16(r * g / rms(r)),
+// rms(r) = sqrt(mean(r^2) + eps).  One workgroup per row: four float4 per
+// thread per pass, the sum of squares in fp32 (wave DPP sums, then LDS across
+// the 4 waves), one IEEE divide and square root per row, then a second pass
+// over the row (L2-resident) for the products, rounded to nearest even.
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ r,
+                                                      const float* __restrict__ g, int H,
+                                                      float eps, uint16_t* __restrict__ out) {
+  __shared__ float part[4];
+  const int64_t row = blockIdx.x;
+  const float4* r4 = reinterpret_cast<const float4*>(r + row * H);
+  const float4* g4 = reinterpret_cast<const float4*>(g);
+  const int n4 = H / 4;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < n4; i += 256) {
+    const float4 v = r4[i];
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  ss = group_sum<64>(ss);
+  if ((threadIdx.x & 63) == 63) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = (part[0] + part[1]) + (part[2] + part[3]);
+  const float inv = 1.0f / sqrtf(tot / (float)H + eps);
+  uint2* o4 = reinterpret_cast<uint2*>(out + row * H);
+  for (int i = threadIdx.x; i < n4; i += 256) {
+    const float4 v = r4[i], w = g4[i];
+    const uint32_t b0 = f32_to_bf16_rne(v.x * inv * w.x), b1 = f32_to_bf16_rne(v.y * inv * w.y);
+    const uint32_t b2 = f32_to_bf16_rne(v.z * inv * w.z), b3 = f32_to_bf16_rne(v.w * inv * w.w);
+    o4[i] = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+  }
+}
+
+hipError_t launch_rmsnorm(const float* r, const float* g, int T, int H, float eps, uint16_t* out,
+                          const Launch& L) {
+  MOE_LAUNCH(L, rmsnorm_kernel, dim3(T), dim3(256), 0, r, g, H, eps, out);
+  return hipGetLastError();
+}
+
 // Row layout -> tiled layout (see the moe_pack_weights contract): thread c
 // moves destination q chunk c (16 bytes) and destination scale c; per expert
 // both number N*K/32.

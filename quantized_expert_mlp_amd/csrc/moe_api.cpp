@@ -123,18 +123,20 @@ bool plane_ok(const moe_q4& p) {
 
 // Expert MLPs over the routed buckets (and the shared expert when given).
 // x16_ready: the MFMA path's fp16 activation copy was written already (by the
-// router logits launch).
+// router logits launch).  accumulate: add into y as it is (the residual)
+// instead of clearing it first.
 int run_mlp(const moe_shape* sh, bool gemm, const Layout& L, void* ws, const uint16_t* x,
             const int32_t* off, const int32_t* sorted, const float* w, moe_q4 gate, moe_q4 up,
             moe_q4 down, const moe_q4* shared, const float* gate_logit, int gate_ld, float* y,
             hipStream_t st, const Stages& sg, const moe::RouteArgs* route = nullptr,
-            bool x16_ready = false) {
+            bool x16_ready = false, bool accumulate = false) {
   const int T = sh->T, H = sh->H, I = sh->I, E = sh->E, k = sh->k;
   const int64_t slots = (int64_t)T * k;
   const int32_t* sched = at<int32_t>(ws, L.sched);
   Buckets routed{off, sorted, sched, k, 0, T, E};
   Buckets sharedb{nullptr, nullptr, nullptr, 1, T, T, 1};
   const int64_t y_elems = (int64_t)T * H;
+  float* y_zero = accumulate ? nullptr : y;
   const int fmt = sh->format == MOE_FORMAT_MXFP4 ? moe::kFmtMxfp4 : moe::kFmtInt4;
   hipError_t err;
   if (!gemm) {
@@ -142,8 +144,8 @@ int run_mlp(const moe_shape* sh, bool gemm, const Layout& L, void* ws, const uin
     uint16_t* hs = at<uint16_t>(ws, L.hs);
     const int max_buckets = (int)(slots < E ? slots : E);
     if (!sg.skip(MOE_STAGE_ACTIVATIONS)) return MOE_ERR_HIP;
-    err = moe::launch_gemv_gate_up(routed, max_buckets, x, H, I, gate.q, gate.s, up.q, up.s, h, y,
-                                   y_elems, fmt, sg.at(MOE_STAGE_GATE_UP), route);
+    err = moe::launch_gemv_gate_up(routed, max_buckets, x, H, I, gate.q, gate.s, up.q, up.s, h,
+                                   y_zero, y_elems, fmt, sg.at(MOE_STAGE_GATE_UP), route);
     if (err != hipSuccess) return MOE_ERR_HIP;
     if (shared) {
       err = moe::launch_gemv_gate_up(sharedb, 1, x, H, sh->SI, shared[0].q, shared[0].s,
@@ -191,7 +193,7 @@ int run_mlp(const moe_shape* sh, bool gemm, const Layout& L, void* ws, const uin
   }
   const bool tiled = sh->layout == MOE_LAYOUT_TILED;
   err = moe::launch_gemm_gate_up(routed, max_tiles, x16, H, I, gate.q, gate.s, up.q, up.s, h16,
-                                 sgp, y, y_elems, tiled, fmt, sg.at(MOE_STAGE_GATE_UP));
+                                 sgp, y_zero, y_elems, tiled, fmt, sg.at(MOE_STAGE_GATE_UP));
   if (err != hipSuccess) return MOE_ERR_HIP;
   if (!sg.skip(MOE_STAGE_SHARED_GATE_UP)) return MOE_ERR_HIP;
   err = moe::launch_gemm_down(routed, max_tiles, h16, H, I, down.q, down.s, w, y, sgp, tiled,
@@ -287,7 +289,7 @@ static int layer_impl(const moe_shape* sh, const uint16_t* x, const float* logit
                       const float* w_router, moe_q4 gate, moe_q4 up, moe_q4 down,
                       const moe_q4* shared, const float* shared_gate, float* y, int32_t* idx_out,
                       float* w_out, float* logits_out, void* ws, size_t ws_bytes,
-                      moe_stream_t stream, void* const* events) {
+                      moe_stream_t stream, void* const* events, bool accumulate = false) {
   int rc = check_shape(sh);
   if (rc != MOE_OK) return rc;
   if (!x || !y || !ws) return MOE_ERR_INVALID_ARG;
@@ -383,7 +385,7 @@ static int layer_impl(const moe_shape* sh, const uint16_t* x, const float* logit
   // 4.-5. expert MLPs with the fused combine
   const bool x16_ready = gemm && (w_router || gated);
   return run_mlp(sh, gemm, L, ws, x, off, sorted, w, gate, up, down, shared, gate_logit, gate_ld,
-                 y, st, sg, fold ? &ra : nullptr, x16_ready);
+                 y, st, sg, fold ? &ra : nullptr, x16_ready, accumulate);
 }
 
 int moe_layer(const moe_shape* sh, const uint16_t* x, const float* logits,
@@ -392,6 +394,24 @@ int moe_layer(const moe_shape* sh, const uint16_t* x, const float* logits,
               float* logits_out, void* ws, size_t ws_bytes, moe_stream_t stream) {
   return layer_impl(sh, x, logits, w_router, gate, up, down, shared, shared_gate, y, idx_out,
                     w_out, logits_out, ws, ws_bytes, stream, nullptr);
+}
+
+int moe_layer_residual_rmsnorm(const moe_shape* sh, const uint16_t* x, const float* logits,
+                               const float* w_router, moe_q4 gate, moe_q4 up, moe_q4 down,
+                               const moe_q4* shared, const float* shared_gate, float* residual,
+                               const float* norm_w, float eps, uint16_t* x_next,
+                               int32_t* idx_out, float* w_out, void* ws, size_t ws_bytes,
+                               moe_stream_t stream) {
+  if (!residual || !norm_w || !x_next || !aligned(residual, 16) || !aligned(norm_w, 16) ||
+      !aligned(x_next, 16) || !(eps >= 0.0f))
+    return MOE_ERR_INVALID_ARG;
+  if (sh && sh->H % 4) return MOE_ERR_UNSUPPORTED;
+  const int rc = layer_impl(sh, x, logits, w_router, gate, up, down, shared, shared_gate,
+                            residual, idx_out, w_out, nullptr, ws, ws_bytes, stream, nullptr,
+                            true);
+  if (rc != MOE_OK) return rc;
+  return hip_status(moe::launch_rmsnorm(residual, norm_w, sh->T, sh->H, eps, x_next,
+                                        moe::Launch{reinterpret_cast<hipStream_t>(stream)}));
 }
 
 int moe_layer_profiled(const moe_shape* sh, const uint16_t* x, const float* logits,

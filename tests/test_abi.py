@@ -103,6 +103,25 @@ def test_layer_rejects(L):
     assert call(shape=_shape(k=0)) == moe.MOE_ERR_INVALID_ARG
 
 
+def test_residual_rmsnorm_rejects(L):
+    sh = _shape()
+    need = moe.moe_workspace_bytes(sh)
+    f = L.moe_layer_residual_rmsnorm
+
+    def call(residual=FAKE, norm_w=FAKE, eps=1e-6, x_next=FAKE, shape=sh):
+        return f(ctypes.byref(shape), FAKE, FAKE, None, _q(), _q(), _q(), None, None, residual,
+                 norm_w, eps, x_next, None, None, FAKE, need, None)
+
+    assert call(residual=None) == moe.MOE_ERR_INVALID_ARG
+    assert call(norm_w=None) == moe.MOE_ERR_INVALID_ARG
+    assert call(x_next=None) == moe.MOE_ERR_INVALID_ARG
+    assert call(residual=FAKE + 4) == moe.MOE_ERR_INVALID_ARG       # misaligned
+    assert call(x_next=FAKE + 2) == moe.MOE_ERR_INVALID_ARG
+    assert call(eps=-1.0) == moe.MOE_ERR_INVALID_ARG
+    assert call(eps=float("nan")) == moe.MOE_ERR_INVALID_ARG
+    assert call(shape=_shape(H=96)) == moe.MOE_ERR_UNSUPPORTED
+
+
 def test_expert_mlp_rejects(L):
     sh = _shape()
     need = moe.moe_workspace_bytes(sh)

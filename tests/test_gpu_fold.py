@@ -1,0 +1,111 @@
+"""GPU tests of the layer with its combine folded into the residual step
+(moe_layer_residual_rmsnorm): the residual's increment against the oracle's
+FFN row, and the normed bf16 row against the oracle's add+rms applied to the
+kernel's own residual (at most one bf16 unit in the last place apart: the
+kernel sums squares and scales in fp32, the oracle in fp64, and both round
+once to bf16)."""
+import numpy as np
+import pytest
+import torch
+
+import moe_synth as S
+import oracle
+import quantized_expert_mlp_amd as moe
+from gpu_harness import DeviceLayer, Y_TOL, dev, host, say
+from test_gpu_parity import MID, _oracle_logits, _rows
+
+pytestmark = pytest.mark.gpu
+
+EPS = 1e-6
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    moe.lib()
+
+
+def _run_fold(d, L, r, g, path=moe.MOE_PATH_AUTO, alias_x=False):
+    """The oracle's logits L go in as given logits (the router itself is
+    checked elsewhere), so both sides pick the same experts."""
+    wl = d.inp.wl
+    T = d.inp.x.shape[0]
+    sh = moe.make_shape(T, wl.H, wl.E, wl.k, wl.I, wl.SI if d.shared else 0, path=path,
+                        layout=d.layout, format=d.format)
+    nbytes = moe.moe_workspace_bytes(sh)
+    assert nbytes > 0
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    ws.fill_(0xFF)
+    res = dev(r)
+    gd = dev(g)
+    x = d.x.clone() if alias_x else d.x
+    xn = x if alias_x else torch.full((T, wl.H), 0x7FC0, dtype=torch.int16, device="cuda")
+    moe.moe_layer_residual_rmsnorm(sh, x, dev(L), None, d.planes["gate"], d.planes["up"],
+                                   d.planes["down"], d.shared, d.shared_gate, res, gd, EPS, xn,
+                                   None, None, ws, nbytes)
+    torch.cuda.synchronize()
+    return host(res), host(xn, np.uint16)
+
+
+def _check(r, r_out, n_out, y_ref, g, what):
+    """Increment within the layer's bar (plus fp32 rounding at the residual's
+    magnitude); normed row within one bf16 ulp of the oracle's norm of r_out."""
+    inc = r_out.astype(np.float64) - r.astype(np.float64)
+    err = np.max(np.abs(inc - y_ref), axis=1)
+    bar = Y_TOL * np.max(np.abs(y_ref), axis=1) + 16 * 2.0 ** -24 * np.max(np.abs(r_out), axis=1)
+    say("  %s: worst increment error %.3e of its bar" % (what, float(np.max(err / bar))))
+    assert np.all(err <= bar), "%s: row %d" % (what, int(np.argmax(err / bar)))
+    _, n_ref = oracle.add_rmsnorm(r_out, np.zeros_like(r_out), g, EPS)
+    mag = lambda b: (b & 0x7FFF).astype(np.int32)
+    sign_ok = ((n_out ^ n_ref) & 0x8000) == 0
+    ulps = np.abs(mag(n_out) - mag(n_ref))
+    assert np.all(sign_ok | ((mag(n_out) == 0) & (mag(n_ref) == 0))), what + ": sign"
+    say("  %s: normed row max %d ulp, %.4f%% not bit-equal" % (what, int(ulps.max()),
+                                                               100.0 * np.mean(ulps > 0)))
+    assert ulps.max() <= 1, what
+
+
+@pytest.mark.parametrize("path", [moe.MOE_PATH_GEMV, moe.MOE_PATH_GEMM])
+@pytest.mark.parametrize("wl", MID, ids=[w.name for w in MID])
+def test_fold_mid(wl, path):
+    say("fold %s path=%d" % (wl.name, path))
+    inp = S.make_layer_inputs(wl, seed=0)
+    d = DeviceLayer(inp)
+    L = _oracle_logits(inp)
+    r = S.draw_residual(wl, T=inp.x.shape[0])
+    g = S.draw_norm_weight(wl)
+    r_out, n_out = _run_fold(d, L, r, g, path=path)
+    y_ref, _, _ = oracle.layer(inp.x, L, wl.k, inp.planes, inp.shared, inp.shared_gate)
+    _check(r, r_out, n_out, y_ref, g, wl.name)
+
+
+@pytest.mark.parametrize("name,fmt", [("decode", "int4"), ("decode", "mxfp4"),
+                                      ("prefill_shared", "int4")])
+def test_fold_full_size(name, fmt):
+    wl = S.WORKLOADS[name]
+    say("fold full-size %s %s" % (name, fmt))
+    inp = S.make_layer_inputs(wl, seed=0, fmt=fmt)
+    d = DeviceLayer(inp)
+    L = _oracle_logits(inp)
+    r = S.draw_residual(wl)
+    g = S.draw_norm_weight(wl)
+    r_out, n_out = _run_fold(d, L, r, g)
+    rows = _rows(wl)
+    y_ref, _, _ = oracle.layer(inp.x, L, wl.k, inp.planes, inp.shared, inp.shared_gate,
+                               rows=rows, fmt=fmt)
+    sel = slice(None) if rows is None else rows
+    _check(r[sel], r_out[sel], n_out[sel], y_ref, g, name)
+
+
+def test_fold_x_next_in_place():
+    """x_next may be x itself: the normed row overwrites the layer's input."""
+    wl = MID[1]  # a gated shared expert: x is read by the gate logit and the MLPs
+    inp = S.make_layer_inputs(wl, seed=3)
+    d = DeviceLayer(inp)
+    L = _oracle_logits(inp)
+    r = S.draw_residual(wl, seed=3, T=inp.x.shape[0])
+    g = S.draw_norm_weight(wl, seed=3)
+    r_out, n_out = _run_fold(d, L, r, g, alias_x=True)
+    y_ref, _, _ = oracle.layer(inp.x, L, wl.k, inp.planes, inp.shared, inp.shared_gate)
+    _check(r, r_out, n_out, y_ref, g, wl.name + " in place")
