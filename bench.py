@@ -134,7 +134,8 @@ def build_sets(wl, nsets, seed0=0, tiled=False, fmt="int4"):
     def pack(plane, N, K):
         q, s_ = plane
         dq, ds = torch.empty_like(q), torch.empty_like(s_)
-        moe.moe_pack_weights((q, s_), q.numel() // (N * K // 2), N, K, (dq, ds))
+        moe.moe_pack_weights((q, s_), q.numel() // (N * K // 2), N, K, (dq, ds),
+                             format=moe.MOE_FORMAT_MXFP4 if fmt == "mxfp4" else moe.MOE_FORMAT_INT4)
         torch.cuda.synchronize()
         return dq, ds
 
@@ -206,7 +207,7 @@ def main():
                          "served by the MFMA path)")
     ap.add_argument("--format", default="int4", choices=["int4", "mxfp4"],
                     help="expert weight format (mxfp4: e2m1 nibbles, ue8m0 exponent per 32 "
-                         "inputs; row layout only)")
+                         "inputs)")
     ap.add_argument("--fold", action="store_true",
                     help="time the layer with its combine folded into the residual add + "
                          "RMSnorm (moe_layer_residual_rmsnorm) instead of moe_layer")

@@ -47,7 +47,7 @@
  * not an fp16 number: e <= 102 gives zero weights, 143 <= e <= 254 +-inf
  * (NaN for a zero code), e = 255 NaN.  The GEMV path dots the exact e2m1
  * values with fp16 activations and scales each group's fp32 partial by
- * 2^(e - 127) in fp32.  Both paths serve MXFP4 with the row layout.
+ * 2^(e - 127) in fp32.
  *
  * Tiled planes (moe_shape.layout = MOE_LAYOUT_TILED, written by
  * moe_pack_weights): the same bytes regrouped so that the grouped MFMA GEMM
@@ -55,9 +55,10 @@
  * of rows 32*b .. 32*b+31 and inputs 64*c .. 64*c+63 is 1024 bytes at byte
  * ((b*(K/64) + c) * 1024); inside it, the 16 bytes of row 32*b+j for scale
  * group 2*c+h (inputs 64*c+32*h .. +31, same nibble order as above) sit at
- * byte (32*h + j) * 16.  The scales of that block are 64 fp16 values at
- * element ((b*(K/64) + c) * 64), the one of row 32*b+j, group 2*c+h at index
- * 32*h + j.  Expert e's plane starts where it does in the row layout.
+ * byte (32*h + j) * 16.  The scales of that block are 64 scale elements
+ * (fp16 for int4, ue8m0 bytes for MXFP4) at element ((b*(K/64) + c) * 64),
+ * the one of row 32*b+j, group 2*c+h at index 32*h + j.  Expert e's plane
+ * starts where it does in the row layout.
  */
 #ifndef MOE_H_
 #define MOE_H_
@@ -88,8 +89,7 @@ enum moe_path { MOE_PATH_AUTO = 0, MOE_PATH_GEMV = 1, MOE_PATH_GEMM = 2 };
  * MFMA GEMM only (path AUTO or GEMM); ROWS planes by both paths. */
 enum moe_layout { MOE_LAYOUT_ROWS = 0, MOE_LAYOUT_TILED = 1 };
 
-/* Weight format (see above).  MXFP4 planes are served with the row layout
- * (layout ROWS) on either path. */
+/* Weight format (see above), for every plane of a call. */
 enum moe_format { MOE_FORMAT_INT4 = 0, MOE_FORMAT_MXFP4 = 1 };
 
 /* One 4-bit plane set: q [E][N][K/2] packed nibbles, s [E][N][K/32] group
@@ -161,8 +161,8 @@ int moe_permute(const int32_t *idx, int32_t T, int32_t k, int32_t E, int32_t *of
  *            256-byte aligned; its contents on entry are ignored.
  * The order in which a token's k terms are added to y is not fixed (device
  * atomics); the result differs from an ordered sum only by fp32 rounding.
- * Errors: INVALID_ARG, UNSUPPORTED (also for path GEMV with TILED planes and
- *         for MXFP4 with TILED), WORKSPACE, HIP.
+ * Errors: INVALID_ARG, UNSUPPORTED (also for path GEMV with TILED planes),
+ *         WORKSPACE, HIP.
  */
 int moe_expert_mlp(const moe_shape *shape, const uint16_t *x, const int32_t *off,
                    const int32_t *sorted, const float *w, moe_q4 gate, moe_q4 up, moe_q4 down,
@@ -256,17 +256,18 @@ int moe_layer_profiled(const moe_shape *shape, const uint16_t *x, const float *l
                        int32_t n_events);
 
 /*
- * Regroup E experts' int4 planes from the row layout into the tiled layout
+ * Regroup E experts' 4-bit planes from the row layout into the tiled layout
  * (see above), for the grouped MFMA GEMM's contiguous weight reads.  A pure
  * byte permutation of q and of s; the values are unchanged.  Meant to run once
- * when weights are loaded.  int4 planes (fp16 scales) only.
+ * when weights are loaded.
  *   src    : row-layout planes, q [E][N][K/2], s [E][N][K/32].
+ *   format : a moe_format; it sets the scale element size (2 or 1 bytes).
  *   dst    : tiled planes of the same sizes (caller-allocated, 16-byte
  *            aligned, not overlapping src).
- * Errors: INVALID_ARG (null, E < 1, N < 1, N % 32 != 0, K % 64 != 0,
- *         misaligned, overlapping).
+ * Errors: INVALID_ARG (null, E < 1, N < 1, N % 32 != 0, K % 64 != 0, bad
+ *         format, misaligned, overlapping).
  */
-int moe_pack_weights(moe_q4 src, int32_t E, int32_t N, int32_t K, moe_q4 dst,
+int moe_pack_weights(moe_q4 src, int32_t E, int32_t N, int32_t K, int32_t format, moe_q4 dst,
                      moe_stream_t stream);
 
 /* Scratch bytes moe_layer and moe_expert_mlp need for this shape (0 if the

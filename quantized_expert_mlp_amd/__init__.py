@@ -77,7 +77,7 @@ def lib() -> ctypes.CDLL:
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_debug_dequant_int4.argtypes = [moe_q4, i32, i32, i32, P, P]
         L.moe_debug_dequant_mxfp4.argtypes = [moe_q4, i32, i32, P, P]
-        L.moe_pack_weights.argtypes = [moe_q4, i32, i32, i32, moe_q4, P]
+        L.moe_pack_weights.argtypes = [moe_q4, i32, i32, i32, i32, moe_q4, P]
         for name in ("moe_router_topk", "moe_permute", "moe_expert_mlp", "moe_layer",
                      "moe_layer_profiled", "moe_pack_weights", "moe_debug_dequant_int4",
                      "moe_debug_dequant_mxfp4", "moe_layer_residual_rmsnorm"):
@@ -185,9 +185,9 @@ def moe_layer_profiled(shape: moe_shape, x, logits, w_router, gate, up, down,
         _ptr(ws), int(ws_bytes), _stream(stream), ev, len(events)))
 
 
-def moe_pack_weights(src, E, N, K, dst, stream=None) -> None:
+def moe_pack_weights(src, E, N, K, dst, stream=None, format=MOE_FORMAT_INT4) -> None:
     """Row-layout plane set (q, s) -> tiled layout into dst (q, s) of the same sizes."""
-    _check("moe_pack_weights", lib().moe_pack_weights(q4(src), E, N, K, q4(dst),
+    _check("moe_pack_weights", lib().moe_pack_weights(q4(src), E, N, K, int(format), q4(dst),
                                                       _stream(stream)))
 
 

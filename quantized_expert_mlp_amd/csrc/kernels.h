@@ -123,9 +123,10 @@ hipError_t launch_gemv_down(const Buckets& b, int max_buckets, const uint16_t* h
 bool gemv_supported(int K);
 
 // Grouped MFMA GEMM (prefill), fp16 operands with fp32 accumulation.
-// Row layout -> tiled layout of E experts' planes q [E][N][K/2], s [E][N][K/32].
-hipError_t launch_pack_weights(const uint8_t* sq, const uint16_t* ss, int E, int N, int K,
-                               uint8_t* dq, uint16_t* ds, const Launch& L);
+// Row layout -> tiled layout of E experts' planes q [E][N][K/2], s [E][N][K/32]
+// (scale elements of the format fmt).
+hipError_t launch_pack_weights(const uint8_t* sq, const void* ss, int E, int N, int K,
+                               uint8_t* dq, void* ds, int fmt, const Launch& L);
 
 // n[t] = bf16(r[t] * g / sqrt(mean(r[t]^2) + eps)) for T rows of H (H % 4 == 0).
 hipError_t launch_rmsnorm(const float* r, const float* g, int T, int H, float eps, uint16_t* out,

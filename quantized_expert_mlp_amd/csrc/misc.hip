@@ -66,13 +66,14 @@ hipError_t launch_rmsnorm(const float* r, const float* g, int T, int H, float ep
 }
 
 // Row layout -> tiled layout (see the moe_pack_weights contract): thread c
-// moves destination q chunk c (16 bytes) and destination scale c; per expert
-// both number N*K/32.
+// moves destination q chunk c (16 bytes) and destination scale c (an fp16 or
+// a ue8m0 byte, SE); per expert both number N*K/32.
+template <typename SE>
 __global__ __launch_bounds__(256) void pack_weights_kernel(const uint8_t* __restrict__ sq,
-                                                           const uint16_t* __restrict__ ss,
+                                                           const SE* __restrict__ ss,
                                                            int64_t total, int N, int K,
                                                            uint8_t* __restrict__ dq,
-                                                           uint16_t* __restrict__ ds) {
+                                                           SE* __restrict__ ds) {
   const int64_t per = (int64_t)N * K / 32;
   const int nc = K / 64;
   const int64_t nthr = (int64_t)gridDim.x * blockDim.x;
@@ -88,13 +89,17 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const uint8_t* __rest
   }
 }
 
-hipError_t launch_pack_weights(const uint8_t* sq, const uint16_t* ss, int E, int N, int K,
-                               uint8_t* dq, uint16_t* ds, const Launch& L) {
+hipError_t launch_pack_weights(const uint8_t* sq, const void* ss, int E, int N, int K,
+                               uint8_t* dq, void* ds, int fmt, const Launch& L) {
   const int64_t total = (int64_t)E * N * K / 32;
   int64_t grid = (total + 255) / 256;
   if (grid > 16384) grid = 16384;
-  MOE_LAUNCH(L, pack_weights_kernel, dim3((unsigned)grid), dim3(256), 0, sq, ss, total, N, K, dq,
-             ds);
+  if (fmt == kFmtMxfp4)
+    MOE_LAUNCH(L, pack_weights_kernel<uint8_t>, dim3((unsigned)grid), dim3(256), 0, sq,
+               static_cast<const uint8_t*>(ss), total, N, K, dq, static_cast<uint8_t*>(ds));
+  else
+    MOE_LAUNCH(L, pack_weights_kernel<uint16_t>, dim3((unsigned)grid), dim3(256), 0, sq,
+               static_cast<const uint16_t*>(ss), total, N, K, dq, static_cast<uint16_t*>(ds));
   return hipGetLastError();
 }
 

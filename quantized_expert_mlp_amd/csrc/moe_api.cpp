@@ -25,7 +25,6 @@ int check_shape(const moe_shape* sh) {
   if (sh->path < MOE_PATH_AUTO || sh->path > MOE_PATH_GEMM) return MOE_ERR_INVALID_ARG;
   if (sh->layout != MOE_LAYOUT_ROWS && sh->layout != MOE_LAYOUT_TILED) return MOE_ERR_INVALID_ARG;
   if (sh->format != MOE_FORMAT_INT4 && sh->format != MOE_FORMAT_MXFP4) return MOE_ERR_INVALID_ARG;
-  if (sh->format == MOE_FORMAT_MXFP4 && sh->layout == MOE_LAYOUT_TILED) return MOE_ERR_UNSUPPORTED;
   if (sh->E > 256 || sh->k > 64) return MOE_ERR_UNSUPPORTED;
   if (sh->H % 64 || sh->I % 64 || sh->SI % 64) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)sh->T * sh->k >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
@@ -234,11 +233,13 @@ int moe_router_topk(const float* logits, int32_t T, int32_t E, int32_t k, float 
                                      moe::Launch{reinterpret_cast<hipStream_t>(stream)}));
 }
 
-int moe_pack_weights(moe_q4 src, int32_t E, int32_t N, int32_t K, moe_q4 dst,
+int moe_pack_weights(moe_q4 src, int32_t E, int32_t N, int32_t K, int32_t format, moe_q4 dst,
                      moe_stream_t stream) {
   if (!plane_ok(src) || !plane_ok(dst)) return MOE_ERR_INVALID_ARG;
   if (E < 1 || N < 1 || K < 64 || N % 32 || K % 64) return MOE_ERR_INVALID_ARG;
-  const uintptr_t qb = (uintptr_t)E * N * (K / 2), sb = (uintptr_t)E * N * (K / 32) * 2;
+  if (format != MOE_FORMAT_INT4 && format != MOE_FORMAT_MXFP4) return MOE_ERR_INVALID_ARG;
+  const bool mx = format == MOE_FORMAT_MXFP4;
+  const uintptr_t qb = (uintptr_t)E * N * (K / 2), sb = (uintptr_t)E * N * (K / 32) * (mx ? 1 : 2);
   auto overlap = [](const void* a, uintptr_t na, const void* b, uintptr_t nb) {
     const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
     return x < y + nb && y < x + na;
@@ -246,9 +247,9 @@ int moe_pack_weights(moe_q4 src, int32_t E, int32_t N, int32_t K, moe_q4 dst,
   if (overlap(src.q, qb, dst.q, qb) || overlap(src.s, sb, dst.s, sb) ||
       overlap(src.q, qb, dst.s, sb) || overlap(src.s, sb, dst.q, qb))
     return MOE_ERR_INVALID_ARG;
-  return hip_status(moe::launch_pack_weights(src.q, static_cast<const uint16_t*>(src.s), E, N, K,
-                                             const_cast<uint8_t*>(dst.q),
-                                             static_cast<uint16_t*>(const_cast<void*>(dst.s)),
+  return hip_status(moe::launch_pack_weights(src.q, src.s, E, N, K, const_cast<uint8_t*>(dst.q),
+                                             const_cast<void*>(dst.s),
+                                             mx ? moe::kFmtMxfp4 : moe::kFmtInt4,
                                              moe::Launch{reinterpret_cast<hipStream_t>(stream)}));
 }
 

@@ -58,20 +58,20 @@ class DeviceLayer:
         t.layout = moe.MOE_LAYOUT_TILED
         wl = self.inp.wl
         dims = {"gate": (wl.I, wl.H), "up": (wl.I, wl.H), "down": (wl.H, wl.I)}
-        t.planes = {p: pack_plane(self.planes[p], *dims[p]) for p in self.planes}
+        t.planes = {p: pack_plane(self.planes[p], *dims[p], self.format) for p in self.planes}
         if self.shared is not None:
             sd = [(wl.SI, wl.H), (wl.SI, wl.H), (wl.H, wl.SI)]
-            t.shared = [pack_plane(pl, *nk) for pl, nk in zip(self.shared, sd)]
+            t.shared = [pack_plane(pl, *nk, self.format) for pl, nk in zip(self.shared, sd)]
         torch.cuda.synchronize()
         return t
 
 
-def pack_plane(plane, N, K):
+def pack_plane(plane, N, K, fmt=moe.MOE_FORMAT_INT4):
     """moe_pack_weights of one device plane set (E inferred from the sizes)."""
     q, s = plane
     E = q.numel() // (N * K // 2)
     dq, ds = torch.empty_like(q), torch.empty_like(s)
-    moe.moe_pack_weights((q, s), E, N, K, (dq, ds))
+    moe.moe_pack_weights((q, s), E, N, K, (dq, ds), format=fmt)
     return dq, ds
 
 

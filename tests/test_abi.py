@@ -147,7 +147,9 @@ def test_mxfp4_format_shape_rules(L):
     assert moe.moe_workspace_bytes(_shape(**mx)) > 0                        # AUTO -> MFMA path
     assert moe.moe_workspace_bytes(_shape(path=moe.MOE_PATH_GEMM, **mx)) > 0
     assert moe.moe_workspace_bytes(_shape(path=moe.MOE_PATH_GEMV, **mx)) > 0
-    assert moe.moe_workspace_bytes(_shape(layout=moe.MOE_LAYOUT_TILED, **mx)) == 0
+    assert moe.moe_workspace_bytes(_shape(layout=moe.MOE_LAYOUT_TILED, **mx)) > 0
+    assert moe.moe_workspace_bytes(_shape(layout=moe.MOE_LAYOUT_TILED, path=moe.MOE_PATH_GEMV,
+                                          **mx)) == 0
     assert moe.moe_workspace_bytes(_shape(format=2)) == 0
     assert moe.moe_workspace_bytes(_shape(format=-1)) == 0
     # the AUTO rule does not depend on the format: decode takes the GEMV path
@@ -163,14 +165,19 @@ def test_pack_weights_rejects(L):
     f = L.moe_pack_weights
     src = moe.moe_q4(FAKE, FAKE + (1 << 24))
     dst = moe.moe_q4(FAKE + (2 << 24), FAKE + (3 << 24))
-    assert f(moe.moe_q4(None, FAKE), 2, 64, 128, dst, None) == moe.MOE_ERR_INVALID_ARG
-    assert f(src, 2, 64, 128, moe.moe_q4(FAKE + 8, FAKE), None) == moe.MOE_ERR_INVALID_ARG  # align
-    assert f(src, 0, 64, 128, dst, None) == moe.MOE_ERR_INVALID_ARG    # E
-    assert f(src, 2, 48, 128, dst, None) == moe.MOE_ERR_INVALID_ARG    # N % 32
-    assert f(src, 2, 64, 96, dst, None) == moe.MOE_ERR_INVALID_ARG     # K % 64
-    assert f(src, 2, 64, 128, src, None) == moe.MOE_ERR_INVALID_ARG    # in place
-    assert f(src, 2, 64, 128, moe.moe_q4(FAKE + 64, FAKE + (3 << 24)), None) == \
+    I4, MX = moe.MOE_FORMAT_INT4, moe.MOE_FORMAT_MXFP4
+    assert f(moe.moe_q4(None, FAKE), 2, 64, 128, I4, dst, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(src, 2, 64, 128, I4, moe.moe_q4(FAKE + 8, FAKE), None) == moe.MOE_ERR_INVALID_ARG
+    assert f(src, 0, 64, 128, I4, dst, None) == moe.MOE_ERR_INVALID_ARG    # E
+    assert f(src, 2, 48, 128, I4, dst, None) == moe.MOE_ERR_INVALID_ARG    # N % 32
+    assert f(src, 2, 64, 96, I4, dst, None) == moe.MOE_ERR_INVALID_ARG     # K % 64
+    assert f(src, 2, 64, 128, 2, dst, None) == moe.MOE_ERR_INVALID_ARG     # format
+    assert f(src, 2, 64, 128, MX, src, None) == moe.MOE_ERR_INVALID_ARG    # in place
+    assert f(src, 2, 64, 128, I4, moe.moe_q4(FAKE + 64, FAKE + (3 << 24)), None) == \
         moe.MOE_ERR_INVALID_ARG                                        # overlapping q
+    # scales overlap by their byte size: 2*64*4 fp16 scales = 1 KiB, ue8m0 = 512 B
+    near = moe.moe_q4(FAKE + (2 << 24), FAKE + (1 << 24) + 768)
+    assert f(src, 2, 64, 128, I4, near, None) == moe.MOE_ERR_INVALID_ARG
 
 
 def test_debug_dequant_rejects(L):

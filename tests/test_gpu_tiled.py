@@ -1,6 +1,7 @@
 """GPU tests of the tiled weight layout: moe_pack_weights against the layout's
-definition (bit-exact), and the whole layer on tiled planes against the CPU
-oracle, at mid sizes and at the full prefill sizes."""
+definition (bit-exact, both scale sizes), and the whole layer on tiled int4
+and MXFP4 planes against the CPU oracle, at mid sizes and at the full prefill
+sizes."""
 import numpy as np
 import pytest
 import torch
@@ -22,19 +23,24 @@ def _gpu():
     moe.lib()
 
 
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
 @pytest.mark.parametrize("E,N,K", [(1, 32, 64), (3, 96, 192), (2, 64, 6144), (4, 1408, 128)])
-def test_pack_matches_layout_definition(E, N, K):
-    say("pack E=%d N=%d K=%d" % (E, N, K))
+def test_pack_matches_layout_definition(E, N, K, fmt):
+    say("pack E=%d N=%d K=%d %s" % (E, N, K, fmt))
     rng = np.random.default_rng([7, E, N, K])
     q = rng.integers(0, 256, (E, N, K // 2), dtype=np.uint8)
-    s = rng.integers(0, 65536, (E, N, K // 32), dtype=np.uint16)
+    mx = fmt == "mxfp4"
+    st = np.uint8 if mx else np.uint16
+    s = rng.integers(0, 256 if mx else 65536, (E, N, K // 32), dtype=st)
     dq = torch.full((E, N, K // 2), 0x5A, dtype=torch.uint8, device="cuda")
-    ds = torch.full((E, N, K // 32), 0x1234, dtype=torch.int16, device="cuda")
-    moe.moe_pack_weights((dev(q), dev(s)), E, N, K, (dq, ds))
+    ds = (torch.full((E, N, K // 32), 0x77, dtype=torch.uint8, device="cuda") if mx else
+          torch.full((E, N, K // 32), 0x1234, dtype=torch.int16, device="cuda"))
+    moe.moe_pack_weights((dev(q), dev(s)), E, N, K, (dq, ds),
+                         format=moe.MOE_FORMAT_MXFP4 if mx else moe.MOE_FORMAT_INT4)
     torch.cuda.synchronize()
     q_ref, s_ref = tiled_reference(q, s)
     assert np.array_equal(host(dq), q_ref)
-    assert np.array_equal(host(ds, np.uint16), s_ref)
+    assert np.array_equal(host(ds, st), s_ref)
 
 
 @pytest.mark.parametrize("wl", MID, ids=[w.name for w in MID])
@@ -51,11 +57,25 @@ def test_layer_mid_tiled(wl):
     assert_y_close(y, y_ref, "%s tiled" % wl.name)
 
 
-@pytest.mark.parametrize("name", ["prefill_shared", "prefill_skewed"])
-def test_layer_full_size_tiled(name):
+@pytest.mark.parametrize("wl", MID, ids=[w.name for w in MID])
+def test_layer_mid_tiled_mxfp4(wl):
+    say("tiled mxfp4 layer %s" % wl.name)
+    inp = S.make_layer_inputs(wl, seed=0, fmt="mxfp4")
+    d = DeviceLayer(inp).tiled()
+    L = _oracle_logits(inp)
+    y_ref, idx_ref, _ = oracle.layer(inp.x, L, wl.k, inp.planes, inp.shared, inp.shared_gate,
+                                     fmt="mxfp4")
+    y, idx, _, _ = run_layer(d, logits=L)
+    assert np.array_equal(idx, idx_ref)
+    assert_y_close(y, y_ref, "%s tiled mxfp4" % wl.name)
+
+
+@pytest.mark.parametrize("name,fmt", [("prefill_shared", "int4"), ("prefill_skewed", "int4"),
+                                      ("prefill_skewed", "mxfp4")])
+def test_layer_full_size_tiled(name, fmt):
     wl = S.WORKLOADS[name]
-    say("full-size tiled layer %s (%s)" % (name, wl.description))
-    inp = S.make_layer_inputs(wl, seed=0)
+    say("full-size tiled layer %s %s (%s)" % (name, fmt, wl.description))
+    inp = S.make_layer_inputs(wl, seed=0, fmt=fmt)
     d = DeviceLayer(inp).tiled()
     L = _oracle_logits(inp)
     rows = _rows(wl)
@@ -63,6 +83,7 @@ def test_layer_full_size_tiled(name):
     idx_ref, w_ref, _ = oracle.router_topk(L, wl.k)
     assert np.array_equal(idx, idx_ref)
     assert_w_close(w, w_ref, name)
-    y_ref, _, _ = oracle.layer(inp.x, L, wl.k, inp.planes, inp.shared, inp.shared_gate, rows=rows)
+    y_ref, _, _ = oracle.layer(inp.x, L, wl.k, inp.planes, inp.shared, inp.shared_gate, rows=rows,
+                               fmt=fmt)
     sel = slice(None) if rows is None else rows
-    assert_y_close(y[sel], y_ref, name + " tiled")
+    assert_y_close(y[sel], y_ref, name + " tiled " + fmt)
