@@ -80,7 +80,8 @@ def counted_traffic(kernel: str, workload: str, gemm: bool, fmt: str = "int4"):
             k_, v_ = line.split(":", 1)
             kv[k_.strip()] = v_.strip()
     h = hashlib.sha256()
-    for src in ("device.h", "kernels.h", "gemm.hip" if gemm else "gemv.hip"):
+    srcs = ("gemm.hip",) if gemm else ("topk.h", "gemv_impl.h", "gemv.hip")
+    for src in ("device.h", "kernels.h") + srcs:
         h.update(open(os.path.join(ROOT, "quantized_expert_mlp_amd", "csrc", src), "rb").read())
     if kv.get("kernel") != kernel or kv.get("source_sha256") != h.hexdigest()[:16]:
         return None
