@@ -168,14 +168,23 @@ constexpr uint32_t kE2m1Hi = 0x46444240u;  // codes 7, 6, 5, 4
 constexpr uint32_t kSelPairLo = 0x02040004u;  // [0, b0, 0, b2] (src0 = 0 gives the zero bytes)
 constexpr uint32_t kSelPairHi = 0x03040104u;  // [0, b1, 0, b3]
 
-__device__ __forceinline__ uint32_t e2m1_hi_bytes(uint32_t nibbles) {
-  const uint32_t mag = __builtin_amdgcn_perm(kE2m1Hi, kE2m1Lo, nibbles & 0x07070707u);
-  return mag | ((nibbles << 4) & 0x80808080u);
+// fp16 high bytes of the 8 codes of one packed word: ht for the even
+// elements e0, e2, e4, e6 (low nibbles), hu for the odd ones (high nibbles).
+// The odd codes' sign bits already sit at bit 7 of each byte of w; the even
+// codes' sit four bits lower.
+struct E2m1Hi {
+  uint32_t ht, hu;
+};
+__device__ __forceinline__ E2m1Hi e2m1_hi_bytes(uint32_t w) {
+  E2m1Hi r;
+  r.ht = __builtin_amdgcn_perm(kE2m1Hi, kE2m1Lo, w & 0x07070707u) | ((w << 4) & 0x80808080u);
+  r.hu = __builtin_amdgcn_perm(kE2m1Hi, kE2m1Lo, (w >> 4) & 0x07070707u) | (w & 0x80808080u);
+  return r;
 }
 
 __device__ __forceinline__ f16x8_t mx4_f16x8(uint32_t w, f16x2_t s2) {
-  const uint32_t ht = e2m1_hi_bytes(w & 0x0F0F0F0Fu);         // codes of e0, e2, e4, e6
-  const uint32_t hu = e2m1_hi_bytes((w >> 4) & 0x0F0F0F0Fu);  // codes of e1, e3, e5, e7
+  const E2m1Hi hb = e2m1_hi_bytes(w);
+  const uint32_t ht = hb.ht, hu = hb.hu;
   const f16x2_t a = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0u, ht, kSelPairLo)) * s2;
   const f16x2_t b = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0u, hu, kSelPairLo)) * s2;
   const f16x2_t c = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0u, ht, kSelPairHi)) * s2;

@@ -134,8 +134,8 @@ __device__ __forceinline__ float dot_group_mx(uint4 w, const uint32_t* a) {
   float s = 0.f;
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
-    const uint32_t ht = e2m1_hi_bytes(ws[d] & 0x0F0F0F0Fu);
-    const uint32_t hu = e2m1_hi_bytes((ws[d] >> 4) & 0x0F0F0F0Fu);
+    const E2m1Hi hb = e2m1_hi_bytes(ws[d]);
+    const uint32_t ht = hb.ht, hu = hb.hu;
     s = dot2_f16(__builtin_amdgcn_perm(0u, ht, kSelPairLo), a[4 * d + 0], s);
     s = dot2_f16(__builtin_amdgcn_perm(0u, hu, kSelPairLo), a[4 * d + 1], s);
     s = dot2_f16(__builtin_amdgcn_perm(0u, ht, kSelPairHi), a[4 * d + 2], s);
