@@ -204,6 +204,41 @@ void weights_row(const float* L, const int32_t* idx, int64_t k, double scale, do
   for (int64_t j = 0; j < k; ++j) w[j] = scale * std::exp((double)L[idx[j]] - l0) / den;
 }
 
+// Expert top-p ([colibri] Measured performance: its end-to-end decode runs
+// with "expert-routing top-p 0.7"; the page names the setting but does not
+// define it).  Reading: after the top-k selection, the picks are taken in
+// rank order while the full-softmax probability of the picks ranked above
+// them is still below p (the first pick is always kept); the rest are dropped
+// (index -1, weight 0) and the weights are renormalised over the kept picks,
+// times the routed scale.  p outside (0, 1) keeps all k.  Probabilities are
+// exp(L_j - L_0) / sum_e exp(L_e - L_0) over all E experts, in fp64.
+// Returns the number of kept picks.
+int64_t top_p_row(const float* L, int64_t E, int64_t k, double top_p, double scale, int32_t* idx,
+                  double* w) {
+  if (!(top_p > 0.0 && top_p < 1.0)) return k;
+  const double l0 = (double)L[idx[0]];
+  double all = 0.0;
+  for (int64_t e = 0; e < E; ++e) all += std::exp((double)L[e] - l0);
+  double above = 0.0, kept_den = 0.0;
+  int64_t kept = 0;
+  for (int64_t j = 0; j < k; ++j) {
+    if (!(above / all < top_p)) break;
+    const double ex = std::exp((double)L[idx[j]] - l0);
+    above += ex;
+    kept_den += ex;
+    ++kept;
+  }
+  for (int64_t j = 0; j < k; ++j) {
+    if (j < kept) {
+      w[j] = scale * std::exp((double)L[idx[j]] - l0) / kept_den;
+    } else {
+      idx[j] = -1;
+      w[j] = 0.0;
+    }
+  }
+  return kept;
+}
+
 }  // namespace
 
 extern "C" {
@@ -259,15 +294,17 @@ void oracle_router_logits(const uint16_t* x, const float* wr, const float* gate_
   }
 }
 
-// Softmax -> top-k -> renormalise for every token row.  idx [T][k]
-// position-major in rank order, w [T][k] rounded to fp32; w64 (nullable)
-// receives the unrounded fp64 weights.
+// Softmax -> top-k -> renormalise for every token row, then the optional
+// expert top-p (top_p_row; top_p outside (0, 1) = off).  idx [T][k]
+// position-major in rank order (-1 for a pick top-p drops), w [T][k] rounded
+// to fp32; w64 (nullable) receives the unrounded fp64 weights.
 void oracle_router_topk(const float* logits, int64_t T, int64_t E, int64_t k, double route_scale,
-                        int32_t* idx, float* w, double* w64) {
+                        double top_p, int32_t* idx, float* w, double* w64) {
   std::vector<double> wr(k);
   for (int64_t t = 0; t < T; ++t) {
     select_row(logits + t * E, E, k, idx + t * k);
     weights_row(logits + t * E, idx + t * k, k, route_scale, wr.data());
+    top_p_row(logits + t * E, E, k, top_p, route_scale, idx + t * k, wr.data());
     for (int64_t j = 0; j < k; ++j) {
       w[t * k + j] = (float)wr[j];
       if (w64) w64[t * k + j] = wr[j];
@@ -333,7 +370,8 @@ uint16_t oracle_double_to_bf16(double v) { return double_to_bf16(v); }
 struct oracle_shape {
   int64_t T, H, E, k, I, SI;
   double route_scale;
-  int64_t fmt;  // weight format of every plane: 0 = int4, 1 = MXFP4
+  int64_t fmt;   // weight format of every plane: 0 = int4, 1 = MXFP4
+  double top_p;  // expert top-p after the top-k (outside (0, 1) = off)
 };
 
 // The whole layer for the token rows listed in `rows` (all T rows when rows is
@@ -369,6 +407,8 @@ void oracle_layer(const oracle_shape* sh, const uint16_t* x, const float* logits
     std::vector<double> w(k);
     select_row(logits + t * E, E, k, idx.data());
     weights_row(logits + t * E, idx.data(), k, sh->route_scale, w.data());
+    const int64_t kept = top_p_row(logits + t * E, E, k, sh->top_p, sh->route_scale, idx.data(),
+                                   w.data());
     if (has_shared) {
       double gw = 1.0;
       if (shared_gate) {
@@ -380,7 +420,7 @@ void oracle_layer(const oracle_shape* sh, const uint16_t* x, const float* logits
                      shared_s[2], H, SI, xd.data(), hbuf.data(), o.data());
       for (int64_t h = 0; h < H; ++h) acc[h] += gw * o[h];
     }
-    for (int64_t j = 0; j < k; ++j) {
+    for (int64_t j = 0; j < kept; ++j) {
       const int64_t e = idx[j];
       expert_forward(fmt, gq + e * gate_plane, scale_at(fmt, gs, e * gate_scales),
                      uq + e * gate_plane, scale_at(fmt, us, e * gate_scales),

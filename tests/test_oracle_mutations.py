@@ -65,6 +65,16 @@ MUTATIONS = {
                                  "std::sqrt(ss / (double)(H + 1) + eps)",
                                  ["test_add_rmsnorm_matches_library_rms_norm"]),
     "rms_weight_dropped": ("* inv * (double)g[h]", "* inv", ["test_add_rmsnorm_matches_library_rms_norm"]),
+    "top_p_counts_the_pick_itself": (
+        "    if (!(above / all < top_p)) break;\n    const double ex = std::exp((double)L[idx[j]] - l0);\n    above += ex;",
+        "    const double ex = std::exp((double)L[idx[j]] - l0);\n    above += ex;\n    if (!(above / all < top_p)) break;",
+        ["test_top_p_closed_form"]),
+    "top_p_mass_over_picks_only": ("all += std::exp((double)L[e] - l0);",
+                                   "all += (e < k) ? std::exp((double)L[idx[e]] - l0) : 0.0;",
+                                   ["test_top_p_closed_form", "test_top_p_prefix_property"]),
+    "top_p_weights_not_renormalised": ("w[j] = scale * std::exp((double)L[idx[j]] - l0) / kept_den;",
+                                       "w[j] = scale * std::exp((double)L[idx[j]] - l0) / all;",
+                                       ["test_top_p_closed_form"]),
     "combine_uses_first_weight": ("acc[h] += w[j] * o[h];", "acc[h] += w[0] * o[h];",
                                   ["test_layer_equals_dense_masked_mixture"]),
 }

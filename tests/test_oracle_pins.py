@@ -564,3 +564,74 @@ def test_add_rmsnorm_special_cases(orc):
     y1 = np.full((1, H), np.float32(2.0 ** -24 + 2.0 ** -40), np.float32)
     r_out, _ = orc.add_rmsnorm(r1, y1, g, 0.0)
     assert np.all(r_out == np.float32(1.0 + 2.0 ** -23))
+
+
+# --------------------------------------------------------- expert top-p --
+
+def _log_row(probs):
+    return np.log(np.asarray([probs], dtype=np.float64)).astype(np.float32)
+
+
+def test_top_p_closed_form(orc):
+    """Probabilities 1/2, 1/4, 1/8, 1/8: p = 0.7 keeps two picks (1/2 < 0.7,
+    3/4 >= 0.7), p = 0.76 three, p = 0.1 one; weights renormalise over them."""
+    L = _log_row([4, 2, 1, 1])
+    idx, w, _ = orc.router_topk(L, 4, 1.0, 0.7)
+    assert list(idx[0]) == [0, 1, -1, -1]
+    assert np.allclose(w[0], [2 / 3, 1 / 3, 0, 0], rtol=1e-6, atol=0)
+    idx, w, _ = orc.router_topk(L, 4, 2.0, 0.76)
+    assert list(idx[0]) == [0, 1, 2, -1]
+    assert np.allclose(w[0], [8 / 7, 4 / 7, 2 / 7, 0], rtol=1e-6, atol=0)
+    idx, w, _ = orc.router_topk(L, 4, 1.5, 0.1)
+    assert list(idx[0]) == [0, -1, -1, -1] and list(w[0]) == [1.5, 0, 0, 0]
+    # the mass of unpicked experts counts: probabilities 8, 4, 2, 2, 1, 1, 1, 1
+    # over 20; p = 0.45 keeps two picks (0.4 < 0.45 <= 0.6), where a mass over
+    # the four picks alone (0.5 >= 0.45) would keep one
+    L2 = _log_row([8, 4, 2, 2, 1, 1, 1, 1])
+    idx, w, _ = orc.router_topk(L2, 4, 1.0, 0.45)
+    assert list(idx[0]) == [0, 1, -1, -1]
+
+
+def test_top_p_off_values_keep_all(orc):
+    rng = np.random.default_rng(40)
+    L = rng.standard_normal((20, 32)).astype(np.float32)
+    ref = orc.router_topk(L, 6, 1.25)
+    for p in (0.0, 1.0, 1.5, -0.3):
+        got = orc.router_topk(L, 6, 1.25, p)
+        assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1])
+
+
+def test_top_p_prefix_property(orc):
+    """Against the library softmax: the kept picks are the shortest rank-order
+    prefix of the top-k whose probability reaches p (or all k), and their
+    weights are the renormalised softmax times the scale."""
+    rng = np.random.default_rng(41)
+    T, E, k, p, scale = 200, 64, 8, 0.6, 1.5
+    L = (2.0 * rng.standard_normal((T, E))).astype(np.float32)
+    idx_all, _, _ = orc.router_topk(L, k, scale)
+    idx, w, w64 = orc.router_topk(L, k, scale, p)
+    P = scipy.special.softmax(L.astype(np.float64), axis=1)
+    for t in range(T):
+        pr = P[t, idx_all[t]]
+        cum = np.concatenate([[0.0], np.cumsum(pr)])
+        kept = int(np.sum(idx[t] >= 0))
+        assert np.array_equal(idx[t][:kept], idx_all[t][:kept]) and np.all(idx[t][kept:] == -1)
+        assert cum[kept - 1] < p and (kept == k or cum[kept] >= p)
+        assert np.allclose(w64[t][:kept], scale * pr[:kept] / pr[:kept].sum(), rtol=1e-12)
+        assert np.all(w[t][kept:] == 0.0)
+
+
+def test_layer_top_p_is_mixture_over_kept_picks(orc):
+    x, logits, planes, _ = _tiny_layer_inputs(seed=42, E=6)
+    T, E, k, p = x.shape[0], 6, 4, 0.55
+    y, idx, w = orc.layer(x, logits, k, planes, top_p=p)
+    dense = _expert_outputs(orc, x, planes, E)
+    P = scipy.special.softmax(logits.astype(np.float64), axis=1)
+    for t in range(T):
+        order = _brute_topk(list(logits[t]), k)
+        cum = np.concatenate([[0.0], np.cumsum(P[t, order])])
+        kept = next((j for j in range(1, k + 1) if j == k or cum[j] >= p), k)
+        sel = order[:kept]
+        ref = (P[t, sel][:, None] * dense[t, sel]).sum(0) / P[t, sel].sum()
+        assert np.allclose(y[t], ref, rtol=1e-6, atol=1e-6 * np.abs(ref).max())
+        assert list(idx[t][:kept]) == list(sel) and np.all(idx[t][kept:] == -1)
