@@ -103,7 +103,8 @@ typedef struct {
  * intermediate, SI shared-expert intermediate (0 = none), group must be 32,
  * route_scale multiplies the renormalised weights, path is a moe_path,
  * layout a moe_layout and format a moe_format (both for every plane of the
- * call, shared ones included).
+ * call, shared ones included), top_p the expert top-p applied after the
+ * top-k (see moe_router_topk; 0, the zero-initialised value, keeps all k).
  * Served: 1 <= k <= min(E, 64), E <= 256, H % 64 == 0, I % 64 == 0,
  * SI % 64 == 0, T >= 1, T*k < 2^31. */
 typedef struct {
@@ -113,6 +114,7 @@ typedef struct {
   int32_t path;
   int32_t layout;
   int32_t format;
+  float top_p;
 } moe_shape;
 
 /*
@@ -124,11 +126,20 @@ typedef struct {
  *            the lower index first among equal logits).
  *   w      : fp32 [T][k] out, w[t][j] = route_scale * exp(L_j - L_0) /
  *            sum_j' exp(L_j' - L_0), evaluated in fp64 and rounded once.
+ *   top_p  : expert top-p after the top-k (the "expert-routing top-p" setting
+ *            of the colibri PR's measured decode, which the page does not
+ *            define; read as): with 0 < top_p < 1, pick j is kept while the
+ *            full-softmax probability of the picks ranked above it,
+ *            sum_{i<j} exp(L_i - L_0) / sum_e exp(L_e - L_0), is below top_p
+ *            (the first pick is always kept); a dropped pick is written as
+ *            idx -1, w 0, and the sums over j' above run over the kept picks.
+ *            Any other value (0, >= 1, negative, NaN) keeps all k.  Dropped
+ *            picks are skipped by moe_permute and by the layer.
  * Errors: INVALID_ARG (null pointer, T < 1, k < 1, k > E);
  *         UNSUPPORTED (E > 256, k > 64).
  */
 int moe_router_topk(const float *logits, int32_t T, int32_t E, int32_t k, float route_scale,
-                    int32_t *idx, float *w, moe_stream_t stream);
+                    float top_p, int32_t *idx, float *w, moe_stream_t stream);
 
 /*
  * Token-to-expert permutation (the bucket schedule of the dasLLAMA PR's routed

@@ -46,7 +46,7 @@ class moe_shape(ctypes.Structure):
                 ("k", ctypes.c_int32), ("I", ctypes.c_int32), ("SI", ctypes.c_int32),
                 ("group", ctypes.c_int32), ("route_scale", ctypes.c_float),
                 ("path", ctypes.c_int32), ("layout", ctypes.c_int32),
-                ("format", ctypes.c_int32)]
+                ("format", ctypes.c_int32), ("top_p", ctypes.c_float)]
 
 
 _lib = None
@@ -60,7 +60,7 @@ def lib() -> ctypes.CDLL:
             raise RuntimeError("libmoe.so is not built: run python -m quantized_expert_mlp_amd.build")
         L = ctypes.CDLL(LIB_PATH)
         P, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
-        L.moe_router_topk.argtypes = [P, i32, i32, i32, f32, P, P, P]
+        L.moe_router_topk.argtypes = [P, i32, i32, i32, f32, f32, P, P, P]
         L.moe_permute.argtypes = [P, i32, i32, i32, P, P, P, P]
         L.moe_expert_mlp.argtypes = [ctypes.POINTER(moe_shape), P, P, P, P, moe_q4, moe_q4,
                                      moe_q4, P, P, ctypes.c_size_t, P]
@@ -111,9 +111,9 @@ def _check(fn: str, rc: int) -> None:
 
 
 def make_shape(T, H, E, k, I, SI=0, route_scale=1.0, path=MOE_PATH_AUTO, group=32,
-               layout=MOE_LAYOUT_ROWS, format=MOE_FORMAT_INT4) -> moe_shape:
+               layout=MOE_LAYOUT_ROWS, format=MOE_FORMAT_INT4, top_p=0.0) -> moe_shape:
     return moe_shape(int(T), int(H), int(E), int(k), int(I), int(SI), int(group),
-                     float(route_scale), int(path), int(layout), int(format))
+                     float(route_scale), int(path), int(layout), int(format), float(top_p))
 
 
 def q4(plane: Tuple) -> moe_q4:
@@ -127,8 +127,8 @@ def moe_workspace_bytes(shape: moe_shape) -> int:
     return lib().moe_workspace_bytes(ctypes.byref(shape))
 
 
-def moe_router_topk(logits, T, E, k, route_scale, idx, w, stream=None) -> None:
-    _check("moe_router_topk", lib().moe_router_topk(_ptr(logits), T, E, k, route_scale,
+def moe_router_topk(logits, T, E, k, route_scale, idx, w, stream=None, top_p=0.0) -> None:
+    _check("moe_router_topk", lib().moe_router_topk(_ptr(logits), T, E, k, route_scale, top_p,
                                                     _ptr(idx), _ptr(w), _stream(stream)))
 
 

@@ -202,39 +202,50 @@ struct SmallRoute {
 // Waves t < T take token t's top-k; then slot s (thread s) finds its row in
 // the expert-major, slot-ascending order - #slots with a smaller expert plus
 // #earlier slots with the same expert - exactly the permutation of the
-// standalone kernels.  Every thread of the workgroup must call this.
+// standalone kernels, which also drop a pick outside [0, E) (top-p's -1):
+// it gets no row (row_of -1) and no bucket.  Every thread of the workgroup
+// must call this.
 template <int V>
 __device__ void small_route(const RouteArgs& ra, int k, SmallRoute& sr) {
   const int tid = threadIdx.x, wave = tid >> 6;
   const bool publish = blockIdx.x == 0 && blockIdx.y == 0;
   const int S = ra.T * k;
   if (wave < ra.T)
-    topk_group<V, 64>(ra.logits, ra.ld, ra.T, wave, ra.E, k, ra.route_scale,
+    topk_group<V, 64>(ra.logits, ra.ld, ra.T, wave, ra.E, k, ra.route_scale, ra.top_p,
                       publish ? ra.idx : nullptr, publish ? ra.w : nullptr, sr.pick, sr.wt, 0);
   __syncthreads();
-  int less = 0, rank = 0, first = 1, e = -1;
+  auto valid = [&](int e2) { return e2 >= 0 && e2 < ra.E; };
+  int less = 0, rank = 0, first = 0, e = -1;
   if (tid < S) {
     e = sr.pick[tid];
-    for (int s2 = 0; s2 < S; ++s2) {
-      const int e2 = sr.pick[s2];
-      less += e2 < e;
-      if (s2 < tid && e2 == e) {
-        ++rank;
-        first = 0;
+    if (valid(e)) {
+      first = 1;
+      for (int s2 = 0; s2 < S; ++s2) {
+        const int e2 = sr.pick[s2];
+        less += valid(e2) && e2 < e;
+        if (s2 < tid && e2 == e) {
+          ++rank;
+          first = 0;
+        }
       }
+      sr.sorted[less + rank] = tid;
+      if (publish) {
+        ra.sorted[less + rank] = tid;
+        ra.row_of[tid] = less + rank;
+      }
+    } else if (publish) {
+      ra.row_of[tid] = -1;
     }
-    sr.sorted[less + rank] = tid;
     sr.first[tid] = first;
-    if (publish) {
-      ra.sorted[less + rank] = tid;
-      ra.row_of[tid] = less + rank;
-    }
   }
   if (publish && tid < ra.E) {
-    int o = 0;
-    for (int s2 = 0; s2 < S; ++s2) o += sr.pick[s2] < tid;
+    int o = 0, nv = 0;
+    for (int s2 = 0; s2 < S; ++s2) {
+      o += valid(sr.pick[s2]) && sr.pick[s2] < tid;
+      nv += valid(sr.pick[s2]);
+    }
     ra.off[tid] = o;
-    if (tid == 0) ra.off[ra.E] = S;
+    if (tid == 0) ra.off[ra.E] = nv;  // the valid slots
   }
   __syncthreads();
   if (tid < S && first) {

@@ -61,16 +61,18 @@ struct Buckets {
 hipError_t launch_router_logits(const uint16_t* x, const float* wr, const float* gate_row, int T,
                                 int H, int E, float* out, int ld, uint16_t* x16, const Launch& L);
 
+// top_p: expert top-p after the top-k (0 < top_p < 1; other values keep all
+// k); a dropped pick is written as index -1, weight 0.
 hipError_t launch_topk(const float* logits, int ld, int T, int E, int k, float route_scale,
-                       int32_t* idx, float* w, const Launch& L);
+                       float top_p, int32_t* idx, float* w, const Launch& L);
 
 // Fused top-k + permutation in one workgroup, for up to kRouteMaxSlots slots
 // and kRouteMaxT tokens (4 tokens per wave of the 16).
 constexpr int kRouteMaxSlots = 4096;
 constexpr int kRouteMaxT = 64;
 hipError_t launch_route(const float* logits, int ld, int T, int E, int k, float route_scale,
-                        int32_t* idx, float* w, int32_t* off, int32_t* sorted, int32_t* row_of,
-                        int32_t* sched, const Launch& L);
+                        float top_p, int32_t* idx, float* w, int32_t* off, int32_t* sorted,
+                        int32_t* row_of, int32_t* sched, const Launch& L);
 
 // Stable permutation (+ schedule when sched is given).  Up to
 // kPermuteOneBlockMax slots, or without scratch, one workgroup does it all;
@@ -98,6 +100,7 @@ struct RouteArgs {
   const float* logits;  // [T][ld]
   int ld, E, T;
   float route_scale;
+  float top_p;
   int32_t* idx;     // [T][k]
   float* w;         // [T][k]
   int32_t* off;     // [E+1]

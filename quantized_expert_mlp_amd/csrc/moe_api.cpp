@@ -225,11 +225,11 @@ size_t moe_workspace_bytes(const moe_shape* sh) {
 }
 
 int moe_router_topk(const float* logits, int32_t T, int32_t E, int32_t k, float route_scale,
-                    int32_t* idx, float* w, moe_stream_t stream) {
+                    float top_p, int32_t* idx, float* w, moe_stream_t stream) {
   if (!logits || !idx || !w || T < 1 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID_ARG;
   if (!aligned(logits, 4) || !aligned(idx, 4) || !aligned(w, 4)) return MOE_ERR_INVALID_ARG;
   if (E > 256 || k > 64) return MOE_ERR_UNSUPPORTED;
-  return hip_status(moe::launch_topk(logits, E, T, E, k, route_scale, idx, w,
+  return hip_status(moe::launch_topk(logits, E, T, E, k, route_scale, top_p, idx, w,
                                      moe::Launch{reinterpret_cast<hipStream_t>(stream)}));
 }
 
@@ -363,19 +363,19 @@ static int layer_impl(const moe_shape* sh, const uint16_t* x, const float* logit
   int32_t* off = at<int32_t>(ws, L.off);
   int32_t* sorted = at<int32_t>(ws, L.sorted);
   const bool fold = !gemm && T <= moe::kFusedRouteMaxT && T * k <= moe::kFusedRouteMaxSlots;
-  moe::RouteArgs ra{Lp, ldL, E, T, sh->route_scale, idx, w, off, sorted,
+  moe::RouteArgs ra{Lp, ldL, E, T, sh->route_scale, sh->top_p, idx, w, off, sorted,
                     at<int32_t>(ws, L.row_of), at<int32_t>(ws, L.sched)};
   if (fold) {
     if (!sg.skip(MOE_STAGE_TOPK) || !sg.skip(MOE_STAGE_PERMUTE)) return MOE_ERR_HIP;
   } else if ((int64_t)T * k <= moe::kRouteMaxSlots && T <= moe::kRouteMaxT) {
-    if (moe::launch_route(Lp, ldL, T, E, k, sh->route_scale, idx, w, off, sorted,
+    if (moe::launch_route(Lp, ldL, T, E, k, sh->route_scale, sh->top_p, idx, w, off, sorted,
                           at<int32_t>(ws, L.row_of), at<int32_t>(ws, L.sched),
                           sg.at(MOE_STAGE_TOPK)) != hipSuccess ||
         !sg.skip(MOE_STAGE_PERMUTE))
       return MOE_ERR_HIP;
   } else {
-    if (moe::launch_topk(Lp, ldL, T, E, k, sh->route_scale, idx, w, sg.at(MOE_STAGE_TOPK)) !=
-        hipSuccess)
+    if (moe::launch_topk(Lp, ldL, T, E, k, sh->route_scale, sh->top_p, idx, w,
+                         sg.at(MOE_STAGE_TOPK)) != hipSuccess)
       return MOE_ERR_HIP;
     if (moe::launch_permute(idx, T, k, E, off, sorted, at<int32_t>(ws, L.row_of),
                             at<int32_t>(ws, L.sched), at<int32_t>(ws, L.pscratch),

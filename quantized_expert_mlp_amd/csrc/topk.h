@@ -51,9 +51,15 @@ __device__ __forceinline__ float readlane_f(float v, int l) {
 // stride ld.  Writes idx[t*k + j], w[t*k + j] for j < k when those are
 // non-null (global), and the same into idx_lds / w_lds (indexed t*k + j, t
 // relative to lds_t0) when those are non-null (LDS).
+//
+// Expert top-p (0 < top_p < 1; other values keep all k): pick j stays while
+// the full-softmax probability of the picks ranked above it is below top_p;
+// the others are written as index -1, weight 0, and the weights renormalise
+// over the kept picks.  The full softmax mass is the picks' terms plus the
+// logits still in the registers (selection retires picks to -inf), in fp64.
 template <int V, int G>
 __device__ __forceinline__ void topk_group(const float* __restrict__ logits, int ld, int T, int t0,
-                                           int E, int k, float route_scale,
+                                           int E, int k, float route_scale, float top_p,
                                            int32_t* __restrict__ idx, float* __restrict__ w,
                                            int32_t* idx_lds = nullptr, float* w_lds = nullptr,
                                            int lds_t0 = 0) {
@@ -112,15 +118,35 @@ __device__ __forceinline__ void topk_group(const float* __restrict__ logits, int
   }
   // weights: group lane 0 holds the top logit
   const double l0 = (double)__shfl(my_val, g * G, 64);
-  const double ex = (gl < k) ? exp((double)my_val - l0) : 0.0;
+  double ex = (gl < k) ? exp((double)my_val - l0) : 0.0;
+  bool keep = gl < k;
+  if (top_p > 0.f && top_p < 1.f) {
+    double all = ex;
+#pragma unroll
+    for (int r = 0; r < V; ++r) all += exp((double)val[r] - l0);  // retired: exp(-inf) = 0
+#pragma unroll
+    for (int o = G / 2; o > 0; o >>= 1) all += __shfl_xor(all, o, 64);
+    // inclusive prefix of the picks' terms over the group's lanes
+    double cum = ex;
+#pragma unroll
+    for (int o = 1; o < G; o <<= 1) {
+      const double v = __shfl_up(cum, o, G);
+      cum += gl >= o ? v : 0.0;
+    }
+    double above = __shfl_up(cum, 1, G);
+    above = gl == 0 ? 0.0 : above;
+    keep = keep && above / all < (double)top_p;
+    ex = keep ? ex : 0.0;
+  }
   double den = ex;
 #pragma unroll
   for (int o = G / 2; o > 0; o >>= 1) den += __shfl_xor(den, o, 64);
   if (tok && gl < k) {
-    const float wv = (float)((double)route_scale * ex / den);
-    if (idx) idx[(int64_t)t * k + gl] = my_idx;
+    const float wv = keep ? (float)((double)route_scale * ex / den) : 0.0f;
+    const int32_t iv = keep ? my_idx : -1;
+    if (idx) idx[(int64_t)t * k + gl] = iv;
     if (w) w[(int64_t)t * k + gl] = wv;
-    if (idx_lds) idx_lds[(t - lds_t0) * k + gl] = my_idx;
+    if (idx_lds) idx_lds[(t - lds_t0) * k + gl] = iv;
     if (w_lds) w_lds[(t - lds_t0) * k + gl] = wv;
   }
 }

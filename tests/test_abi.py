@@ -59,13 +59,13 @@ FAKE = 1 << 20  # a non-null, 256-aligned address; never dereferenced by these c
 
 def test_router_topk_rejects(L):
     f = L.moe_router_topk
-    assert f(None, 4, 8, 2, 1.0, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
-    assert f(FAKE, 0, 8, 2, 1.0, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
-    assert f(FAKE, 4, 8, 9, 1.0, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
-    assert f(FAKE, 4, 8, 0, 1.0, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
-    assert f(FAKE + 2, 4, 8, 2, 1.0, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
-    assert f(FAKE, 4, 257, 2, 1.0, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
-    assert f(FAKE, 4, 256, 65, 1.0, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert f(None, 4, 8, 2, 1.0, 0.0, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(FAKE, 0, 8, 2, 1.0, 0.0, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(FAKE, 4, 8, 9, 1.0, 0.0, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(FAKE, 4, 8, 0, 1.0, 0.0, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(FAKE + 2, 4, 8, 2, 1.0, 0.0, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(FAKE, 4, 257, 2, 1.0, 0.0, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert f(FAKE, 4, 256, 65, 1.0, 0.7, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
 
 
 def test_permute_rejects(L):
