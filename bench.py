@@ -88,13 +88,22 @@ def counted_traffic(kernel: str, workload: str, gemm: bool, fmt: str = "int4"):
     return int(kv["traffic_bytes_per_launch"])
 
 
-def touched_experts(logits: np.ndarray, k: int) -> int:
-    """Distinct experts among the top-k picks of every row (byte accounting)."""
-    picks = np.argpartition(-logits, k - 1, axis=1)[:, :k]
-    return len(np.unique(picks))
+def routing_counts(logits: np.ndarray, k: int, top_p: float = 0.0):
+    """(distinct experts, slots) among the top-k picks of every row, for the
+    byte and flop accounting; with 0 < top_p < 1, among the picks expert
+    top-p keeps."""
+    order = np.argsort(-logits, axis=1, kind="stable")[:, :k]
+    if not 0.0 < top_p < 1.0:
+        return len(np.unique(order)), order.size
+    z = logits.astype(np.float64)
+    P = np.exp(z - z.max(axis=1, keepdims=True))
+    P /= P.sum(axis=1, keepdims=True)
+    pk = np.take_along_axis(P, order, axis=1)
+    kept = order[(np.cumsum(pk, axis=1) - pk) < top_p]
+    return len(np.unique(kept)), kept.size
 
 
-def stage_work(wl, T, U, gemm, fmt="int4"):
+def stage_work(wl, T, U, gemm, fmt="int4", slots=None):
     """Algorithmic bytes and flops of the gate/up and down launches of one call.
 
     Counted: the touched experts' packed nibbles and group scales (fp16 for
@@ -102,7 +111,8 @@ def stage_work(wl, T, U, gemm, fmt="int4"):
     out.  Not counted: untouched experts.  On the MFMA path the shared
     expert's tiles run inside the routed launches, so its work is added to
     theirs."""
-    H, I, slots = wl.H, wl.I, T * wl.k
+    H, I = wl.H, wl.I
+    slots = T * wl.k if slots is None else slots
     act = 2
     sb = 1 if fmt == "mxfp4" else 2
     gu_w = U * 2 * (I * H // 2 + I * (H // 32) * sb)
@@ -212,6 +222,8 @@ def main():
     ap.add_argument("--fold", action="store_true",
                     help="time the layer with its combine folded into the residual add + "
                          "RMSnorm (moe_layer_residual_rmsnorm) instead of moe_layer")
+    ap.add_argument("--top-p", type=float, default=0.0,
+                    help="expert top-p after the top-k (0 < p < 1; default off)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -255,19 +267,21 @@ def main():
         pool_np = [S.draw_logits(wl, seed=100 + i) for i in range(LOGIT_POOL)] \
             if wl.T == 1 else [S.draw_logits(wl, seed=100 + i) for i in range(4)]
         pool = [torch.from_numpy(p).cuda() for p in pool_np]
-        touched = [touched_experts(p, wl.k) for p in pool_np]
+        counts = [routing_counts(p, wl.k, args.top_p) for p in pool_np]
     else:
         pool_np, pool = None, None
-        touched = []
+        counts = []
         for s in sets:  # byte accounting only: which experts the router picks
             L = S.bf16_bits_to_f32(s["inp"].x) @ s["inp"].w_router.T
-            touched.append(touched_experts(L, wl.k))
+            counts.append(routing_counts(L, wl.k, args.top_p))
+    touched = [c[0] for c in counts]
     nvar = len(pool) if pool is not None else len(sets)
 
     path = {"auto": moe.MOE_PATH_AUTO, "gemv": moe.MOE_PATH_GEMV, "gemm": moe.MOE_PATH_GEMM}[args.path]
     sh = moe.make_shape(T, wl.H, wl.E, wl.k, wl.I, wl.SI, path=path,
                         layout=moe.MOE_LAYOUT_TILED if tiled else moe.MOE_LAYOUT_ROWS,
-                        format=moe.MOE_FORMAT_MXFP4 if mx else moe.MOE_FORMAT_INT4)
+                        format=moe.MOE_FORMAT_MXFP4 if mx else moe.MOE_FORMAT_INT4,
+                        top_p=args.top_p)
     if moe.moe_workspace_bytes(sh) == 0:
         sys.exit("bench.py: this workload is not served with --path %s --layout %s --format %s"
                  % (args.path, args.layout, args.format))
@@ -326,7 +340,8 @@ def main():
     for k_ in stage_ms:
         stage_ms[k_] /= args.steps
     U = float(np.mean([touched[i % nvar] for i in range(args.steps)]))
-    work = stage_work(wl, T, U, gemm, args.format)
+    kept_slots = float(np.mean([counts[i % nvar][1] for i in range(args.steps)]))
+    work = stage_work(wl, T, U, gemm, args.format, kept_slots)
     dom = max(("gate_up", "down", "shared_gate_up", "shared_down"), key=lambda s_: stage_ms[s_])
     dur_s = stage_ms[dom] * 1e-3
     if gemm:
@@ -372,6 +387,7 @@ def main():
                                else "int4 offset-binary, fp16 scale per 32 inputs"),
                    "layout": args.layout,
                    "path": args.path,
+                   "top_p": args.top_p if 0.0 < args.top_p < 1.0 else None,
                    "step": ("layer + residual add + RMSnorm (moe_layer_residual_rmsnorm)"
                             if args.fold else "layer (moe_layer)"),
                    "expert_path": "grouped fp16 MFMA GEMM" if gemm else
