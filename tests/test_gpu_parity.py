@@ -133,6 +133,10 @@ MID = [
     _mid("mid_decode", 24, 3, 4096, 64, 8, 320),
     # 5600 slots: the permutation over many workgroups, a ragged last block
     _mid("mid_many_slots", 26, 700, 256, 32, 8, 128),
+    # the largest router served: E = 256, k = 64 (1280 slots, most experts touched)
+    _mid("mid_max_k", 27, 20, 256, 256, 64, 128),
+    # one token with k = 64: the GEMV's fused routing at its 64-slot limit
+    _mid("mid_one_token_max_k", 28, 1, 512, 256, 64, 192),
 ]
 
 
