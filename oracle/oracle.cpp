@@ -239,6 +239,59 @@ int64_t top_p_row(const float* L, int64_t E, int64_t k, double top_p, double sca
   return kept;
 }
 
+// Router variants that [dasllama]'s MoE seat lists as declined shapes (a
+// non-softmax gate, a router or selection bias) without defining them.
+// Reading: the published DeepSeek-V3 routing without expert groups -
+//   score s_e = softmax(L)_e (gate 0) or sigmoid(L_e) (gate 1),
+//   selection key s_e + b_e (b the selection bias, zero when absent), the
+//   top-k keys in rank order, the lower index winning a tie,
+//   weights from the unbiased scores of the picks, renormalised to sum to
+//   one, times the routed scale: w_j = scale * s_j / sum_j' s_j'.
+// For the softmax gate the full denominator cancels in the weights, so they
+// are exp(L_j - m) / sum_j' exp(L_j' - m) with m the largest picked logit.
+// Everything in fp64.
+void variant_row(const float* L, int64_t E, int64_t k, int gate, const float* bias, double scale,
+                 int32_t* idx, double* w) {
+  std::vector<double> s(E), key(E);
+  if (gate == 1) {
+    for (int64_t e = 0; e < E; ++e) s[e] = sigmoid((double)L[e]);
+  } else {
+    double m = (double)L[0];
+    for (int64_t e = 1; e < E; ++e) m = std::max(m, (double)L[e]);
+    double den = 0.0;
+    for (int64_t e = 0; e < E; ++e) den += std::exp((double)L[e] - m);
+    for (int64_t e = 0; e < E; ++e) s[e] = std::exp((double)L[e] - m) / den;
+  }
+  for (int64_t e = 0; e < E; ++e) key[e] = s[e] + (bias ? (double)bias[e] : 0.0);
+  std::vector<char> taken(E, 0);
+  for (int64_t j = 0; j < k; ++j) {
+    int64_t best = -1;
+    for (int64_t e = 0; e < E; ++e) {
+      if (taken[e]) continue;
+      if (best < 0 || key[e] > key[best]) best = e;
+    }
+    taken[best] = 1;
+    idx[j] = (int32_t)best;
+  }
+  double den = 0.0;
+  for (int64_t j = 0; j < k; ++j) den += s[idx[j]];
+  for (int64_t j = 0; j < k; ++j) w[j] = scale * s[idx[j]] / den;
+}
+
+// One token row's routing: the plain softmax router (select_row,
+// weights_row, then the optional top-p), or a variant (variant_row; top-p is
+// not defined for variants and is ignored).  Returns the kept picks.
+int64_t route_row(const float* L, int64_t E, int64_t k, double scale, double top_p, int gate,
+                  const float* bias, int32_t* idx, double* w) {
+  if (gate == 0 && !bias) {
+    select_row(L, E, k, idx);
+    weights_row(L, idx, k, scale, w);
+    return top_p_row(L, E, k, top_p, scale, idx, w);
+  }
+  variant_row(L, E, k, gate, bias, scale, idx, w);
+  return k;
+}
+
 }  // namespace
 
 extern "C" {
@@ -295,16 +348,16 @@ void oracle_router_logits(const uint16_t* x, const float* wr, const float* gate_
 }
 
 // Softmax -> top-k -> renormalise for every token row, then the optional
-// expert top-p (top_p_row; top_p outside (0, 1) = off).  idx [T][k]
+// expert top-p (top_p_row; top_p outside (0, 1) = off); or a router variant
+// (gate 1 = sigmoid, bias [E] nullable: variant_row).  idx [T][k]
 // position-major in rank order (-1 for a pick top-p drops), w [T][k] rounded
 // to fp32; w64 (nullable) receives the unrounded fp64 weights.
 void oracle_router_topk(const float* logits, int64_t T, int64_t E, int64_t k, double route_scale,
-                        double top_p, int32_t* idx, float* w, double* w64) {
+                        double top_p, int gate, const float* bias, int32_t* idx, float* w,
+                        double* w64) {
   std::vector<double> wr(k);
   for (int64_t t = 0; t < T; ++t) {
-    select_row(logits + t * E, E, k, idx + t * k);
-    weights_row(logits + t * E, idx + t * k, k, route_scale, wr.data());
-    top_p_row(logits + t * E, E, k, top_p, route_scale, idx + t * k, wr.data());
+    route_row(logits + t * E, E, k, route_scale, top_p, gate, bias, idx + t * k, wr.data());
     for (int64_t j = 0; j < k; ++j) {
       w[t * k + j] = (float)wr[j];
       if (w64) w64[t * k + j] = wr[j];
@@ -372,6 +425,8 @@ struct oracle_shape {
   double route_scale;
   int64_t fmt;   // weight format of every plane: 0 = int4, 1 = MXFP4
   double top_p;  // expert top-p after the top-k (outside (0, 1) = off)
+  int64_t gate;  // router score: 0 = softmax, 1 = sigmoid
+  const float* bias;  // selection bias [E], or null
 };
 
 // The whole layer for the token rows listed in `rows` (all T rows when rows is
@@ -405,10 +460,8 @@ void oracle_layer(const oracle_shape* sh, const uint16_t* x, const float* logits
     for (int64_t h = 0; h < H; ++h) xd[h] = bf16_to_double(x[t * H + h]);
     std::vector<int32_t> idx(k);
     std::vector<double> w(k);
-    select_row(logits + t * E, E, k, idx.data());
-    weights_row(logits + t * E, idx.data(), k, sh->route_scale, w.data());
-    const int64_t kept = top_p_row(logits + t * E, E, k, sh->top_p, sh->route_scale, idx.data(),
-                                   w.data());
+    const int64_t kept = route_row(logits + t * E, E, k, sh->route_scale, sh->top_p,
+                                   (int)sh->gate, sh->bias, idx.data(), w.data());
     if (has_shared) {
       double gw = 1.0;
       if (shared_gate) {

@@ -75,6 +75,14 @@ MUTATIONS = {
     "top_p_weights_not_renormalised": ("w[j] = scale * std::exp((double)L[idx[j]] - l0) / kept_den;",
                                        "w[j] = scale * std::exp((double)L[idx[j]] - l0) / all;",
                                        ["test_top_p_closed_form"]),
+    "variant_weights_from_keys": ("for (int64_t j = 0; j < k; ++j) den += s[idx[j]];\n  for (int64_t j = 0; j < k; ++j) w[j] = scale * s[idx[j]] / den;",
+                                  "for (int64_t j = 0; j < k; ++j) den += key[idx[j]];\n  for (int64_t j = 0; j < k; ++j) w[j] = scale * key[idx[j]] / den;",
+                                  ["test_sigmoid_gate_and_bias_closed_form"]),
+    "sigmoid_of_negated_logit": ("s[e] = sigmoid((double)L[e]);", "s[e] = sigmoid(-(double)L[e]);",
+                                 ["test_sigmoid_gate_and_bias_closed_form"]),
+    "variant_tie_to_higher_index": ("if (best < 0 || key[e] > key[best]) best = e;",
+                                    "if (best < 0 || key[e] >= key[best]) best = e;",
+                                    ["test_variant_ties_lower_index"]),
     "combine_uses_first_weight": ("acc[h] += w[j] * o[h];", "acc[h] += w[0] * o[h];",
                                   ["test_layer_equals_dense_masked_mixture"]),
 }

@@ -635,3 +635,63 @@ def test_layer_top_p_is_mixture_over_kept_picks(orc):
         ref = (P[t, sel][:, None] * dense[t, sel]).sum(0) / P[t, sel].sum()
         assert np.allclose(y[t], ref, rtol=1e-6, atol=1e-6 * np.abs(ref).max())
         assert list(idx[t][:kept]) == list(sel) and np.all(idx[t][kept:] == -1)
+
+
+# ------------------------------------------- router variants (gate, bias) --
+
+def test_sigmoid_gate_and_bias_closed_form(orc):
+    """sigma(0) = 1/2, sigma(ln 3) = 3/4, sigma(-ln 3) = 1/4."""
+    L = np.array([[0.0, math.log(3.0), -math.log(3.0), -5.0]], dtype=np.float32)
+    idx, w, _ = orc.router_topk(L, 2, 1.0, gate="sigmoid")
+    assert list(idx[0]) == [1, 0] and np.allclose(w[0], [0.6, 0.4], rtol=1e-6)
+    # a selection bias of 0.6 lifts expert 2's key to 0.85: it is picked first,
+    # but its weight comes from its unbiased score 1/4
+    b = np.array([0.0, 0.0, 0.6, 0.0], np.float32)
+    idx, w, _ = orc.router_topk(L, 2, 2.0, gate="sigmoid", bias=b)
+    assert list(idx[0]) == [2, 1] and np.allclose(w[0], [0.5, 1.5], rtol=1e-6)
+    # softmax gate with a bias: probabilities of [0, ln 3] alone are 1/4, 3/4
+    L2 = np.array([[0.0, math.log(3.0)]], dtype=np.float32)
+    idx, w, _ = orc.router_topk(L2, 1, 1.0, bias=np.array([0.6, 0.0], np.float32))
+    assert list(idx[0]) == [0] and w[0][0] == 1.0
+
+
+def test_variant_reductions(orc):
+    rng = np.random.default_rng(50)
+    T, E, k = 30, 40, 6
+    L = (1.5 * rng.standard_normal((T, E))).astype(np.float32)
+    plain = orc.router_topk(L, k, 1.25)
+    zero_bias = orc.router_topk(L, k, 1.25, bias=np.zeros(E, np.float32))
+    assert np.array_equal(plain[0], zero_bias[0])
+    assert np.allclose(plain[2], zero_bias[2], rtol=1e-12)
+    # sigmoid gate, k = E: weights are sigma(L) renormalised (library expit)
+    idx, _, w64 = orc.router_topk(L, E, 1.0, gate="sigmoid")
+    s = scipy.special.expit(L.astype(np.float64))
+    for t in range(T):
+        assert np.allclose(w64[t], s[t, idx[t]] / s[t].sum(), rtol=1e-12)
+        assert list(idx[t]) == sorted(range(E), key=lambda e: (-s[t, e], e))
+    # a dominant bias picks its experts first, in bias order
+    b = np.zeros(E, np.float32)
+    b[[7, 3, 21]] = [30.0, 20.0, 10.0]
+    idx, _, _ = orc.router_topk(L, 3, 1.0, gate="sigmoid", bias=b)
+    assert np.all(idx == [7, 3, 21])
+
+
+def test_variant_ties_lower_index(orc):
+    L = np.zeros((1, 8), np.float32)
+    b = np.array([0, 1, 0, 1, 0, 1, 0, 1], np.float32)
+    idx, w, _ = orc.router_topk(L, 5, 1.0, gate="sigmoid", bias=b)
+    assert list(idx[0]) == [1, 3, 5, 7, 0] and np.allclose(w[0], 0.2, rtol=1e-12)
+
+
+def test_layer_variant_is_mixture_over_picks(orc):
+    x, logits, planes, _ = _tiny_layer_inputs(seed=51, E=6)
+    T, E, k = x.shape[0], 6, 3
+    b = np.random.default_rng(52).normal(0, 0.3, E).astype(np.float32)
+    y, idx, w = orc.layer(x, logits, k, planes, gate="sigmoid", bias=b)
+    dense = _expert_outputs(orc, x, planes, E)
+    s = scipy.special.expit(logits.astype(np.float64))
+    for t in range(T):
+        sel = sorted(range(E), key=lambda e: (-(s[t, e] + float(b[e])), e))[:k]
+        ref = (s[t, sel][:, None] * dense[t, sel]).sum(0) / s[t, sel].sum()
+        assert list(idx[t]) == sel
+        assert np.allclose(y[t], ref, rtol=1e-6, atol=1e-6 * np.abs(ref).max())
