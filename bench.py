@@ -88,10 +88,31 @@ def counted_traffic(kernel: str, workload: str, gemm: bool, fmt: str = "int4"):
     return int(kv["traffic_bytes_per_launch"])
 
 
-def routing_counts(logits: np.ndarray, k: int, top_p: float = 0.0):
+def router_bias(router: str, E: int):
+    """Selection bias of the variant routers (None without one): N(0, 0.05)
+    beside sigmoid scores, N(0, 1/E) beside softmax probabilities."""
+    if not router.endswith("-bias"):
+        return None
+    sd = 0.05 if router.startswith("sigmoid") else 1.0 / E
+    return (np.random.default_rng([E, 77]).standard_normal(E) * sd).astype(np.float32)
+
+
+def routing_counts(logits: np.ndarray, k: int, top_p: float = 0.0, router: str = "softmax",
+                   bias=None):
     """(distinct experts, slots) among the top-k picks of every row, for the
     byte and flop accounting; with 0 < top_p < 1, among the picks expert
-    top-p keeps."""
+    top-p keeps; for a variant router, the picks of its selection keys."""
+    if router != "softmax":
+        z = logits.astype(np.float64)
+        if router.startswith("sigmoid"):
+            key = 1.0 / (1.0 + np.exp(-z))
+        else:
+            key = np.exp(z - z.max(axis=1, keepdims=True))
+            key /= key.sum(axis=1, keepdims=True)
+        if bias is not None:
+            key = key + bias.astype(np.float64)
+        order = np.argsort(-key, axis=1, kind="stable")[:, :k]
+        return len(np.unique(order)), order.size
     order = np.argsort(-logits, axis=1, kind="stable")[:, :k]
     if not 0.0 < top_p < 1.0:
         return len(np.unique(order)), order.size
@@ -177,7 +198,7 @@ def build_sets(wl, nsets, seed0=0, tiled=False, fmt="int4"):
     return sets
 
 
-def cpu_baseline(wl, seconds_hint: float, fmt: str = "int4"):
+def cpu_baseline(wl, seconds_hint: float, fmt: str = "int4", router: str = "softmax", bias=None):
     """The oracle as it stands, on a bounded sample of the workload's tokens."""
     import oracle
     threads = oracle.set_threads(min(16, os.cpu_count() or 1))
@@ -199,7 +220,8 @@ def cpu_baseline(wl, seconds_hint: float, fmt: str = "int4"):
         rows = sorted(np.random.default_rng(7).choice(wl.T, n, replace=False).tolist())
         sample = "%d of %d token rows, %d threads" % (n, wl.T, threads)
     t0 = time.perf_counter()
-    oracle.layer(x, logits, wl.k, inp.planes, inp.shared, inp.shared_gate, rows=rows, fmt=fmt)
+    oracle.layer(x, logits, wl.k, inp.planes, inp.shared, inp.shared_gate, rows=rows, fmt=fmt,
+                 gate="sigmoid" if router.startswith("sigmoid") else "softmax", bias=bias)
     dt = time.perf_counter() - t0
     return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": sample, "seconds": round(dt, 2)}
@@ -224,6 +246,10 @@ def main():
                          "RMSnorm (moe_layer_residual_rmsnorm) instead of moe_layer")
     ap.add_argument("--top-p", type=float, default=0.0,
                     help="expert top-p after the top-k (0 < p < 1; default off)")
+    ap.add_argument("--router", default="softmax",
+                    choices=["softmax", "sigmoid", "softmax-bias", "sigmoid-bias"],
+                    help="router: the plain softmax top-k, or a variant (sigmoid scores "
+                         "and/or a seeded selection bias)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -262,18 +288,24 @@ def main():
     sets = build_sets(wl, nsets, tiled=tiled, fmt=args.format)
     log("inputs resident in %.1f s" % (time.perf_counter() - t0))
 
+    if args.router != "softmax" and 0.0 < args.top_p < 1.0:
+        sys.exit("bench.py: --top-p applies to the plain softmax router only")
+    bias_np = router_bias(args.router, wl.E)
+    bias = None if bias_np is None else torch.from_numpy(bias_np).cuda()
+    rc = dict(top_p=args.top_p, router=args.router, bias=bias_np)
+
     # per-step inputs: logits pool (given-logit workloads) or weight-set rotation
     if wl.logits in ("given", "zipf"):
         pool_np = [S.draw_logits(wl, seed=100 + i) for i in range(LOGIT_POOL)] \
             if wl.T == 1 else [S.draw_logits(wl, seed=100 + i) for i in range(4)]
         pool = [torch.from_numpy(p).cuda() for p in pool_np]
-        counts = [routing_counts(p, wl.k, args.top_p) for p in pool_np]
+        counts = [routing_counts(p, wl.k, **rc) for p in pool_np]
     else:
         pool_np, pool = None, None
         counts = []
         for s in sets:  # byte accounting only: which experts the router picks
             L = S.bf16_bits_to_f32(s["inp"].x) @ s["inp"].w_router.T
-            counts.append(routing_counts(L, wl.k, args.top_p))
+            counts.append(routing_counts(L, wl.k, **rc))
     touched = [c[0] for c in counts]
     nvar = len(pool) if pool is not None else len(sets)
 
@@ -281,7 +313,9 @@ def main():
     sh = moe.make_shape(T, wl.H, wl.E, wl.k, wl.I, wl.SI, path=path,
                         layout=moe.MOE_LAYOUT_TILED if tiled else moe.MOE_LAYOUT_ROWS,
                         format=moe.MOE_FORMAT_MXFP4 if mx else moe.MOE_FORMAT_INT4,
-                        top_p=args.top_p)
+                        top_p=args.top_p,
+                        score=moe.MOE_SCORE_SIGMOID if args.router.startswith("sigmoid")
+                        else moe.MOE_SCORE_SOFTMAX, select_bias=bias)
     if moe.moe_workspace_bytes(sh) == 0:
         sys.exit("bench.py: this workload is not served with --path %s --layout %s --format %s"
                  % (args.path, args.layout, args.format))
@@ -365,7 +399,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, args.cpu_seconds, args.format)
+        cpu = cpu_baseline(wl, args.cpu_seconds, args.format, args.router, bias_np)
         log("cpu oracle: %s" % cpu)
 
     out = {
@@ -388,6 +422,7 @@ def main():
                    "layout": args.layout,
                    "path": args.path,
                    "top_p": args.top_p if 0.0 < args.top_p < 1.0 else None,
+                   "router": args.router,
                    "step": ("layer + residual add + RMSnorm (moe_layer_residual_rmsnorm)"
                             if args.fold else "layer (moe_layer)"),
                    "expert_path": "grouped fp16 MFMA GEMM" if gemm else

@@ -6,7 +6,8 @@
  * PR #3988 and the vllm.cpp warp-router PR #481):
  *   1. router logits L = x . W_router^T (fp32), unless the caller gives L;
  *   2. softmax over the E experts -> top-k (the lower index wins a tie) ->
- *      renormalise over the k picks, times route_scale;
+ *      renormalise over the k picks, times route_scale (or a router variant:
+ *      sigmoid scores, a selection bias; see moe_router_topk);
  *   3. token-to-expert permutation: per-expert buckets of slots, slot s = t*k+j;
  *   4. per expert, the SwiGLU MLP on its bucket's rows:
  *        h = silu(Wg x) * (Wu x),   o = Wd h,
@@ -92,6 +93,10 @@ enum moe_layout { MOE_LAYOUT_ROWS = 0, MOE_LAYOUT_TILED = 1 };
 /* Weight format (see above), for every plane of a call. */
 enum moe_format { MOE_FORMAT_INT4 = 0, MOE_FORMAT_MXFP4 = 1 };
 
+/* Router score function (see moe_router_topk): the softmax probability over
+ * the E experts, or the sigmoid of each logit on its own. */
+enum moe_score { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 };
+
 /* One 4-bit plane set: q [E][N][K/2] packed nibbles, s [E][N][K/32] group
  * scales: fp16 bits (uint16) for int4, ue8m0 bytes (uint8) for MXFP4. */
 typedef struct {
@@ -104,7 +109,10 @@ typedef struct {
  * route_scale multiplies the renormalised weights, path is a moe_path,
  * layout a moe_layout and format a moe_format (both for every plane of the
  * call, shared ones included), top_p the expert top-p applied after the
- * top-k (see moe_router_topk; 0, the zero-initialised value, keeps all k).
+ * top-k (see moe_router_topk; 0, the zero-initialised value, keeps all k),
+ * score a moe_score and select_bias a DEVICE pointer to fp32 [E] or NULL
+ * (the router variant of moe_router_topk; zero-initialised = the plain
+ * softmax router).
  * Served: 1 <= k <= min(E, 64), E <= 256, H % 64 == 0, I % 64 == 0,
  * SI % 64 == 0, T >= 1, T*k < 2^31. */
 typedef struct {
@@ -115,6 +123,8 @@ typedef struct {
   int32_t layout;
   int32_t format;
   float top_p;
+  int32_t score;
+  const float *select_bias;
 } moe_shape;
 
 /*
@@ -135,11 +145,26 @@ typedef struct {
  *            idx -1, w 0, and the sums over j' above run over the kept picks.
  *            Any other value (0, >= 1, negative, NaN) keeps all k.  Dropped
  *            picks are skipped by moe_permute and by the layer.
- * Errors: INVALID_ARG (null pointer, T < 1, k < 1, k > E);
- *         UNSUPPORTED (E > 256, k > 64).
+ *   score, select_bias : router variant (the dasLLAMA PR's MoE seat lists a
+ *            non-softmax gate and a router or selection bias among the shapes
+ *            it declines, without defining them; read as the published
+ *            DeepSeek-V3 routing without expert groups).  With score =
+ *            MOE_SCORE_SOFTMAX and select_bias = NULL the plain router above
+ *            runs.  Otherwise each expert gets a score s_e in fp64 -
+ *            softmax(L)_e (MOE_SCORE_SOFTMAX) or 1 / (1 + exp(-L_e))
+ *            (MOE_SCORE_SIGMOID) - the picks are the k largest keys s_e + b_e
+ *            in rank order (b = select_bias, device fp32 [E], zero when NULL;
+ *            the lower index wins a tie), and w[t][j] = route_scale * s_j /
+ *            sum_j' s_j' over the picks (the bias steers the selection only).
+ *            Top-p is not defined for variants: 0 < top_p < 1 with a variant
+ *            is UNSUPPORTED.
+ * Errors: INVALID_ARG (null pointer, T < 1, k < 1, k > E, unknown score,
+ *         misaligned select_bias); UNSUPPORTED (E > 256, k > 64, top-p with a
+ *         variant).
  */
 int moe_router_topk(const float *logits, int32_t T, int32_t E, int32_t k, float route_scale,
-                    float top_p, int32_t *idx, float *w, moe_stream_t stream);
+                    float top_p, int32_t score, const float *select_bias, int32_t *idx, float *w,
+                    moe_stream_t stream);
 
 /*
  * Token-to-expert permutation (the bucket schedule of the dasLLAMA PR's routed

@@ -21,6 +21,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_PATH_AUTO, MOE_PATH_GEMV, MOE_PATH_GEMM = range(3)
 MOE_LAYOUT_ROWS, MOE_LAYOUT_TILED = range(2)
 MOE_FORMAT_INT4, MOE_FORMAT_MXFP4 = range(2)
+MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = range(2)
 
 # Every symbol include/moe.h declares.
 EXPORTS = ("moe_router_topk", "moe_permute", "moe_expert_mlp", "moe_layer",
@@ -46,7 +47,8 @@ class moe_shape(ctypes.Structure):
                 ("k", ctypes.c_int32), ("I", ctypes.c_int32), ("SI", ctypes.c_int32),
                 ("group", ctypes.c_int32), ("route_scale", ctypes.c_float),
                 ("path", ctypes.c_int32), ("layout", ctypes.c_int32),
-                ("format", ctypes.c_int32), ("top_p", ctypes.c_float)]
+                ("format", ctypes.c_int32), ("top_p", ctypes.c_float),
+                ("score", ctypes.c_int32), ("select_bias", ctypes.c_void_p)]
 
 
 _lib = None
@@ -60,7 +62,7 @@ def lib() -> ctypes.CDLL:
             raise RuntimeError("libmoe.so is not built: run python -m quantized_expert_mlp_amd.build")
         L = ctypes.CDLL(LIB_PATH)
         P, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
-        L.moe_router_topk.argtypes = [P, i32, i32, i32, f32, f32, P, P, P]
+        L.moe_router_topk.argtypes = [P, i32, i32, i32, f32, f32, i32, P, P, P, P]
         L.moe_permute.argtypes = [P, i32, i32, i32, P, P, P, P]
         L.moe_expert_mlp.argtypes = [ctypes.POINTER(moe_shape), P, P, P, P, moe_q4, moe_q4,
                                      moe_q4, P, P, ctypes.c_size_t, P]
@@ -111,9 +113,13 @@ def _check(fn: str, rc: int) -> None:
 
 
 def make_shape(T, H, E, k, I, SI=0, route_scale=1.0, path=MOE_PATH_AUTO, group=32,
-               layout=MOE_LAYOUT_ROWS, format=MOE_FORMAT_INT4, top_p=0.0) -> moe_shape:
+               layout=MOE_LAYOUT_ROWS, format=MOE_FORMAT_INT4, top_p=0.0,
+               score=MOE_SCORE_SOFTMAX, select_bias=None) -> moe_shape:
+    """select_bias: a device tensor fp32 [E] (or a raw pointer); the caller
+    keeps it alive for as long as the shape is used."""
     return moe_shape(int(T), int(H), int(E), int(k), int(I), int(SI), int(group),
-                     float(route_scale), int(path), int(layout), int(format), float(top_p))
+                     float(route_scale), int(path), int(layout), int(format), float(top_p),
+                     int(score), _ptr(select_bias))
 
 
 def q4(plane: Tuple) -> moe_q4:
@@ -127,9 +133,11 @@ def moe_workspace_bytes(shape: moe_shape) -> int:
     return lib().moe_workspace_bytes(ctypes.byref(shape))
 
 
-def moe_router_topk(logits, T, E, k, route_scale, idx, w, stream=None, top_p=0.0) -> None:
+def moe_router_topk(logits, T, E, k, route_scale, idx, w, stream=None, top_p=0.0,
+                    score=MOE_SCORE_SOFTMAX, select_bias=None) -> None:
     _check("moe_router_topk", lib().moe_router_topk(_ptr(logits), T, E, k, route_scale, top_p,
-                                                    _ptr(idx), _ptr(w), _stream(stream)))
+                                                    int(score), _ptr(select_bias), _ptr(idx),
+                                                    _ptr(w), _stream(stream)))
 
 
 def moe_permute(idx, T, k, E, off, sorted_, row_of, stream=None) -> None:

@@ -211,7 +211,7 @@ __device__ void small_route(const RouteArgs& ra, int k, SmallRoute& sr) {
   const bool publish = blockIdx.x == 0 && blockIdx.y == 0;
   const int S = ra.T * k;
   if (wave < ra.T)
-    topk_group<V, 64>(ra.logits, ra.ld, ra.T, wave, ra.E, k, ra.route_scale, ra.top_p,
+    topk_group<V, 64>(ra.logits, ra.ld, ra.T, wave, ra.E, k, ra.rs,
                       publish ? ra.idx : nullptr, publish ? ra.w : nullptr, sr.pick, sr.wt, 0);
   __syncthreads();
   auto valid = [&](int e2) { return e2 >= 0 && e2 < ra.E; };

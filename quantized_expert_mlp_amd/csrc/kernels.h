@@ -61,17 +61,32 @@ struct Buckets {
 hipError_t launch_router_logits(const uint16_t* x, const float* wr, const float* gate_row, int T,
                                 int H, int E, float* out, int ld, uint16_t* x16, const Launch& L);
 
-// top_p: expert top-p after the top-k (0 < top_p < 1; other values keep all
-// k); a dropped pick is written as index -1, weight 0.
-hipError_t launch_topk(const float* logits, int ld, int T, int E, int k, float route_scale,
-                       float top_p, int32_t* idx, float* w, const Launch& L);
+// How a token's picks and weights are formed.
+//   route_scale : multiplies the renormalised weights.
+//   top_p       : expert top-p after the top-k (0 < top_p < 1; other values
+//                 keep all k); a dropped pick is written as index -1, weight 0.
+//                 Plain softmax router only.
+//   score, bias : router variant.  score 0 = softmax probability, 1 = sigmoid
+//                 of the logit; bias (nullable, fp32 [E]) is added to the
+//                 score for the selection only.  With score 0 and no bias the
+//                 plain router runs (selection on the logits themselves).
+struct RouterSpec {
+  float route_scale;
+  float top_p;
+  int score;
+  const float* bias;
+  __host__ __device__ bool variant() const { return score != 0 || bias != nullptr; }
+};
+
+hipError_t launch_topk(const float* logits, int ld, int T, int E, int k, const RouterSpec& rs,
+                       int32_t* idx, float* w, const Launch& L);
 
 // Fused top-k + permutation in one workgroup, for up to kRouteMaxSlots slots
 // and kRouteMaxT tokens (4 tokens per wave of the 16).
 constexpr int kRouteMaxSlots = 4096;
 constexpr int kRouteMaxT = 64;
-hipError_t launch_route(const float* logits, int ld, int T, int E, int k, float route_scale,
-                        float top_p, int32_t* idx, float* w, int32_t* off, int32_t* sorted,
+hipError_t launch_route(const float* logits, int ld, int T, int E, int k, const RouterSpec& rs,
+                        int32_t* idx, float* w, int32_t* off, int32_t* sorted,
                         int32_t* row_of, int32_t* sched, const Launch& L);
 
 // Stable permutation (+ schedule when sched is given).  Up to
@@ -99,8 +114,7 @@ constexpr int kFusedRouteMaxSlots = 64;
 struct RouteArgs {
   const float* logits;  // [T][ld]
   int ld, E, T;
-  float route_scale;
-  float top_p;
+  RouterSpec rs;
   int32_t* idx;     // [T][k]
   float* w;         // [T][k]
   int32_t* off;     // [E+1]

@@ -15,6 +15,20 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Router variant checks: a known score function, an aligned bias, and top-p
+// only with the plain softmax router.
+int check_router(int32_t score, const float* bias, float top_p) {
+  if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
+  if (bias && !aligned(bias, 4)) return MOE_ERR_INVALID_ARG;
+  const bool variant = score != MOE_SCORE_SOFTMAX || bias != nullptr;
+  if (variant && top_p > 0.0f && top_p < 1.0f) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe::RouterSpec router_spec(const moe_shape* sh) {
+  return moe::RouterSpec{sh->route_scale, sh->top_p, sh->score, sh->select_bias};
+}
+
 // Shape checks shared by every entry point that takes a moe_shape.
 int check_shape(const moe_shape* sh) {
   if (!sh) return MOE_ERR_INVALID_ARG;
@@ -29,7 +43,7 @@ int check_shape(const moe_shape* sh) {
   if (sh->H % 64 || sh->I % 64 || sh->SI % 64) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)sh->T * sh->k >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)sh->T * sh->H >= (int64_t)1 << 40) return MOE_ERR_UNSUPPORTED;
-  return MOE_OK;
+  return check_router(sh->score, sh->select_bias, sh->top_p);
 }
 
 bool gemv_ok(const moe_shape* sh) {
@@ -225,12 +239,16 @@ size_t moe_workspace_bytes(const moe_shape* sh) {
 }
 
 int moe_router_topk(const float* logits, int32_t T, int32_t E, int32_t k, float route_scale,
-                    float top_p, int32_t* idx, float* w, moe_stream_t stream) {
+                    float top_p, int32_t score, const float* select_bias, int32_t* idx, float* w,
+                    moe_stream_t stream) {
   if (!logits || !idx || !w || T < 1 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID_ARG;
   if (!aligned(logits, 4) || !aligned(idx, 4) || !aligned(w, 4)) return MOE_ERR_INVALID_ARG;
+  const int rc = check_router(score, select_bias, top_p);
+  if (rc != MOE_OK) return rc;
   if (E > 256 || k > 64) return MOE_ERR_UNSUPPORTED;
-  return hip_status(moe::launch_topk(logits, E, T, E, k, route_scale, top_p, idx, w,
-                                     moe::Launch{reinterpret_cast<hipStream_t>(stream)}));
+  return hip_status(moe::launch_topk(logits, E, T, E, k,
+                                     moe::RouterSpec{route_scale, top_p, score, select_bias},
+                                     idx, w, moe::Launch{reinterpret_cast<hipStream_t>(stream)}));
 }
 
 int moe_pack_weights(moe_q4 src, int32_t E, int32_t N, int32_t K, int32_t format, moe_q4 dst,
@@ -363,18 +381,18 @@ static int layer_impl(const moe_shape* sh, const uint16_t* x, const float* logit
   int32_t* off = at<int32_t>(ws, L.off);
   int32_t* sorted = at<int32_t>(ws, L.sorted);
   const bool fold = !gemm && T <= moe::kFusedRouteMaxT && T * k <= moe::kFusedRouteMaxSlots;
-  moe::RouteArgs ra{Lp, ldL, E, T, sh->route_scale, sh->top_p, idx, w, off, sorted,
+  moe::RouteArgs ra{Lp, ldL, E, T, router_spec(sh), idx, w, off, sorted,
                     at<int32_t>(ws, L.row_of), at<int32_t>(ws, L.sched)};
   if (fold) {
     if (!sg.skip(MOE_STAGE_TOPK) || !sg.skip(MOE_STAGE_PERMUTE)) return MOE_ERR_HIP;
   } else if ((int64_t)T * k <= moe::kRouteMaxSlots && T <= moe::kRouteMaxT) {
-    if (moe::launch_route(Lp, ldL, T, E, k, sh->route_scale, sh->top_p, idx, w, off, sorted,
+    if (moe::launch_route(Lp, ldL, T, E, k, router_spec(sh), idx, w, off, sorted,
                           at<int32_t>(ws, L.row_of), at<int32_t>(ws, L.sched),
                           sg.at(MOE_STAGE_TOPK)) != hipSuccess ||
         !sg.skip(MOE_STAGE_PERMUTE))
       return MOE_ERR_HIP;
   } else {
-    if (moe::launch_topk(Lp, ldL, T, E, k, sh->route_scale, sh->top_p, idx, w,
+    if (moe::launch_topk(Lp, ldL, T, E, k, router_spec(sh), idx, w,
                          sg.at(MOE_STAGE_TOPK)) != hipSuccess)
       return MOE_ERR_HIP;
     if (moe::launch_permute(idx, T, k, E, off, sorted, at<int32_t>(ws, L.row_of),

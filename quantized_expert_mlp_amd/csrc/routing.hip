@@ -110,12 +110,12 @@ hipError_t launch_router_logits(const uint16_t* x, const float* wr, const float*
 // Four waves per workgroup, 64/G tokens per wave.
 template <int V, int G>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int ld,
-                                                   int T, int E, int k, float route_scale,
-                                                   float top_p, int32_t* __restrict__ idx,
+                                                   int T, int E, int k, RouterSpec rs,
+                                                   int32_t* __restrict__ idx,
                                                    float* __restrict__ w) {
   const int t0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * (64 / G);
   if (t0 >= T) return;
-  topk_group<V, G>(logits, ld, T, t0, E, k, route_scale, top_p, idx, w);
+  topk_group<V, G>(logits, ld, T, t0, E, k, rs, idx, w);
 }
 
 // Calls f(integral_constant V, integral_constant G) for the (V, G) that serves (E, k).
@@ -134,13 +134,13 @@ hipError_t topk_dispatch(int E, int k, F&& f) {
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_topk(const float* logits, int ld, int T, int E, int k, float route_scale,
-                       float top_p, int32_t* idx, float* w, const Launch& L) {
+hipError_t launch_topk(const float* logits, int ld, int T, int E, int k, const RouterSpec& rs,
+                       int32_t* idx, float* w, const Launch& L) {
   return topk_dispatch(E, k, [&](auto vc, auto gc) {
     constexpr int V = decltype(vc)::value, G = decltype(gc)::value;
     const int per_block = 4 * (64 / G);
     MOE_LAUNCH(L, (topk_kernel<V, G>), dim3((T + per_block - 1) / per_block), dim3(256), 0,
-               logits, ld, T, E, k, route_scale, top_p, idx, w);
+               logits, ld, T, E, k, rs, idx, w);
     return hipGetLastError();
   });
 }
@@ -292,8 +292,7 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(const int32_t* __rest
 // same workgroup then builds the permutation and schedule from them.
 template <int V, int G>
 __global__ __launch_bounds__(kThreads) void route_kernel(const float* __restrict__ logits, int ld,
-                                                         int T, int E, int k, float route_scale,
-                                                         float top_p,
+                                                         int T, int E, int k, RouterSpec rs,
                                                          int32_t* __restrict__ idx,
                                                          float* __restrict__ w,
                                                          int32_t* __restrict__ off,
@@ -305,19 +304,19 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const float* __restrict
   __shared__ int32_t picks[kRouteMaxSlots];
   constexpr int TPW = 64 / G;
   for (int t0 = (threadIdx.x >> 6) * TPW; t0 < T; t0 += kWaves * TPW)
-    topk_group<V, G>(logits, ld, T, t0, E, k, route_scale, top_p, idx, w, picks, nullptr, 0);
+    topk_group<V, G>(logits, ld, T, t0, E, k, rs, idx, w, picks, nullptr, 0);
   __syncthreads();
   permute_block(picks, T * k, E, off, sorted, row_of, sched, max_tiles, sm);
 }
 
-hipError_t launch_route(const float* logits, int ld, int T, int E, int k, float route_scale,
-                        float top_p, int32_t* idx, float* w, int32_t* off, int32_t* sorted,
+hipError_t launch_route(const float* logits, int ld, int T, int E, int k, const RouterSpec& rs,
+                        int32_t* idx, float* w, int32_t* off, int32_t* sorted,
                         int32_t* row_of, int32_t* sched, const Launch& L) {
   const int max_tiles = (int)sched_max_tiles((int64_t)T * k, E);
   return topk_dispatch(E, k, [&](auto vc, auto gc) {
     constexpr int V = decltype(vc)::value, G = decltype(gc)::value;
     MOE_LAUNCH(L, (route_kernel<V, G>), dim3(1), dim3(kThreads), 0, logits, ld, T, E, k,
-               route_scale, top_p, idx, w, off, sorted, row_of, sched, max_tiles);
+               rs, idx, w, off, sorted, row_of, sched, max_tiles);
     return hipGetLastError();
   });
 }

@@ -7,6 +7,7 @@
 #pragma once
 
 #include "device.h"
+#include "kernels.h"
 
 namespace moe {
 
@@ -58,12 +59,23 @@ __device__ __forceinline__ float readlane_f(float v, int l) {
 // over the kept picks.  The full softmax mass is the picks' terms plus the
 // logits still in the registers (selection retires picks to -inf), in fp64.
 template <int V, int G>
+__device__ void topk_group_variant(const float* __restrict__ logits, int ld, int T, int t0, int E,
+                                   int k, const RouterSpec& rs, int32_t* __restrict__ idx,
+                                   float* __restrict__ w, int32_t* idx_lds, float* w_lds,
+                                   int lds_t0);
+
+template <int V, int G>
 __device__ __forceinline__ void topk_group(const float* __restrict__ logits, int ld, int T, int t0,
-                                           int E, int k, float route_scale, float top_p,
+                                           int E, int k, const RouterSpec& rs,
                                            int32_t* __restrict__ idx, float* __restrict__ w,
                                            int32_t* idx_lds = nullptr, float* w_lds = nullptr,
                                            int lds_t0 = 0) {
   static_assert(G == 16 || G == 32 || G == 64, "group size");
+  if (rs.variant()) {  // uniform over the launch
+    topk_group_variant<V, G>(logits, ld, T, t0, E, k, rs, idx, w, idx_lds, w_lds, lds_t0);
+    return;
+  }
+  const float route_scale = rs.route_scale, top_p = rs.top_p;
   const int lane = threadIdx.x & 63;
   const int g = lane / G, gl = lane % G;
   const int t = t0 + g;
@@ -147,6 +159,112 @@ __device__ __forceinline__ void topk_group(const float* __restrict__ logits, int
     if (idx) idx[(int64_t)t * k + gl] = iv;
     if (w) w[(int64_t)t * k + gl] = wv;
     if (idx_lds) idx_lds[(t - lds_t0) * k + gl] = iv;
+    if (w_lds) w_lds[(t - lds_t0) * k + gl] = wv;
+  }
+}
+
+// Router variants (the dasLLAMA PR's MoE seat lists a non-softmax gate and a
+// router or selection bias among the shapes it declines, without defining
+// them; read as the published DeepSeek-V3 routing without expert groups):
+// score s_e = softmax(L)_e (rs.score 0) or sigmoid(L_e) (rs.score 1) in fp64,
+// selection key s_e + b_e (b = rs.bias, zero when null), the k largest keys
+// in rank order with the lower index winning a tie, and weights from the
+// picks' unbiased scores renormalised, times route_scale:
+//   w_j = route_scale * s_j / sum_j' s_j'.
+// Same lane mapping as topk_group; the keys are fp64, so each round's
+// arg-max is a xor butterfly of (key, index, score) over the group's lanes.
+// Top-p does not apply.
+__device__ __forceinline__ bool beats_d(double ov, int oi, double bv, int bi) {
+  return (ov > bv) | ((ov == bv) & (oi < bi));
+}
+
+template <int V, int G>
+__device__ void topk_group_variant(const float* __restrict__ logits, int ld, int T, int t0, int E,
+                                   int k, const RouterSpec& rs, int32_t* __restrict__ idx,
+                                   float* __restrict__ w, int32_t* idx_lds, float* w_lds,
+                                   int lds_t0) {
+  const int lane = threadIdx.x & 63;
+  const int gl = lane % G;
+  const int t = t0 + lane / G;
+  const bool tok = t < T;
+  const double ninf = -__builtin_huge_val();
+  float lg[V];
+  bool live[V];
+#pragma unroll
+  for (int r = 0; r < V; ++r) {
+    const int e = gl + G * r;
+    live[r] = tok && e < E;
+    lg[r] = live[r] ? logits[(int64_t)t * ld + e] : 0.f;
+  }
+  double sc[V];
+  if (rs.score == 1) {
+#pragma unroll
+    for (int r = 0; r < V; ++r) sc[r] = live[r] ? 1.0 / (1.0 + exp(-(double)lg[r])) : 0.0;
+  } else {
+    // softmax over the row: max (exact in fp32), then the fp64 sum of exp
+    float m = -__builtin_huge_valf();
+#pragma unroll
+    for (int r = 0; r < V; ++r) m = live[r] ? fmaxf(m, lg[r]) : m;
+#pragma unroll
+    for (int o = G / 2; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    double den = 0.0;
+#pragma unroll
+    for (int r = 0; r < V; ++r) {
+      sc[r] = live[r] ? exp((double)lg[r] - (double)m) : 0.0;
+      den += sc[r];
+    }
+#pragma unroll
+    for (int o = G / 2; o > 0; o >>= 1) den += __shfl_xor(den, o, 64);
+    den = tok ? den : 1.0;
+#pragma unroll
+    for (int r = 0; r < V; ++r) sc[r] /= den;
+  }
+  double key[V];
+  int id[V];
+#pragma unroll
+  for (int r = 0; r < V; ++r) {
+    const int e = gl + G * r;
+    key[r] = live[r] ? sc[r] + (rs.bias ? (double)rs.bias[e] : 0.0) : ninf;
+    id[r] = live[r] ? e : kRetired;
+  }
+  int my_idx = -1;
+  double my_s = 0.0;
+  for (int j = 0; j < k; ++j) {
+    double bv = key[0], bs = sc[0];
+    int bi = id[0];
+#pragma unroll
+    for (int r = 1; r < V; ++r) {
+      const bool take = beats_d(key[r], id[r], bv, bi);
+      bv = take ? key[r] : bv;
+      bi = take ? id[r] : bi;
+      bs = take ? sc[r] : bs;
+    }
+#pragma unroll
+    for (int o = G / 2; o > 0; o >>= 1) {
+      const double ov = __shfl_xor(bv, o, 64), os = __shfl_xor(bs, o, 64);
+      const int oi = __shfl_xor(bi, o, 64);
+      const bool take = beats_d(ov, oi, bv, bi);
+      bv = take ? ov : bv;
+      bi = take ? oi : bi;
+      bs = take ? os : bs;
+    }
+#pragma unroll
+    for (int r = 0; r < V; ++r) {
+      const bool mine = id[r] == bi;  // every lane of the group holds the winner
+      key[r] = mine ? ninf : key[r];
+      id[r] = mine ? kRetired : id[r];
+    }
+    my_idx = gl == j ? bi : my_idx;
+    my_s = gl == j ? bs : my_s;
+  }
+  double den = gl < k ? my_s : 0.0;
+#pragma unroll
+  for (int o = G / 2; o > 0; o >>= 1) den += __shfl_xor(den, o, 64);
+  if (tok && gl < k) {
+    const float wv = (float)((double)rs.route_scale * my_s / den);
+    if (idx) idx[(int64_t)t * k + gl] = my_idx;
+    if (w) w[(int64_t)t * k + gl] = wv;
+    if (idx_lds) idx_lds[(t - lds_t0) * k + gl] = my_idx;
     if (w_lds) w_lds[(t - lds_t0) * k + gl] = wv;
   }
 }

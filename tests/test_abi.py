@@ -52,6 +52,12 @@ def test_workspace_bytes_valid_and_invalid(L):
                 dict(I=96), dict(SI=32), dict(group=64)]:
         assert moe.moe_workspace_bytes(_shape(**bad)) == 0, bad
     assert moe.moe_workspace_bytes(_shape(path=3)) == 0
+    # router variants in the shape: unknown score, misaligned bias, top-p with a variant
+    assert moe.moe_workspace_bytes(_shape(score=moe.MOE_SCORE_SIGMOID)) > 0
+    assert moe.moe_workspace_bytes(_shape(select_bias=FAKE)) > 0
+    for bad in [dict(score=2), dict(select_bias=FAKE + 2), dict(score=1, top_p=0.5),
+                dict(select_bias=FAKE, top_p=0.9)]:
+        assert moe.moe_workspace_bytes(_shape(**bad)) == 0, bad
 
 
 FAKE = 1 << 20  # a non-null, 256-aligned address; never dereferenced by these cases
@@ -59,13 +65,19 @@ FAKE = 1 << 20  # a non-null, 256-aligned address; never dereferenced by these c
 
 def test_router_topk_rejects(L):
     f = L.moe_router_topk
-    assert f(None, 4, 8, 2, 1.0, 0.0, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
-    assert f(FAKE, 0, 8, 2, 1.0, 0.0, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
-    assert f(FAKE, 4, 8, 9, 1.0, 0.0, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
-    assert f(FAKE, 4, 8, 0, 1.0, 0.0, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
-    assert f(FAKE + 2, 4, 8, 2, 1.0, 0.0, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
-    assert f(FAKE, 4, 257, 2, 1.0, 0.0, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
-    assert f(FAKE, 4, 256, 65, 1.0, 0.7, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert f(None, 4, 8, 2, 1.0, 0.0, 0, None, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(FAKE, 0, 8, 2, 1.0, 0.0, 0, None, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(FAKE, 4, 8, 9, 1.0, 0.0, 0, None, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(FAKE, 4, 8, 0, 1.0, 0.0, 0, None, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(FAKE + 2, 4, 8, 2, 1.0, 0.0, 0, None, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(FAKE, 4, 257, 2, 1.0, 0.0, 0, None, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert f(FAKE, 4, 256, 65, 1.0, 0.7, 0, None, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    # router variants: unknown score, misaligned bias, top-p with a variant
+    assert f(FAKE, 4, 8, 2, 1.0, 0.0, 2, None, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(FAKE, 4, 8, 2, 1.0, 0.0, -1, None, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(FAKE, 4, 8, 2, 1.0, 0.0, 0, FAKE + 2, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(FAKE, 4, 8, 2, 1.0, 0.5, 1, None, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert f(FAKE, 4, 8, 2, 1.0, 0.5, 0, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
 
 
 def test_permute_rejects(L):
