@@ -41,6 +41,9 @@
 #ifndef MOE_GEMM_DB
 #define MOE_GEMM_DB 2  // weight register stages
 #endif
+#ifndef MOE_GEMM_DOWN_THIN_FIRST
+#define MOE_GEMM_DOWN_THIN_FIRST 1  // down pass: thin experts' tiles first
+#endif
 #ifndef MOE_GEMM_OCC
 #define MOE_GEMM_OCC 2  // workgroups per CU
 #endif
@@ -133,7 +136,7 @@ struct GemmArgs {
 // 128-row tiles of the shared expert (identity rows over all tokens); the
 // rest index the routed tile list.
 __device__ __forceinline__ bool tile_of(const Buckets& b, const GemmArgs& a, TileView* v,
-                                        int* src) {
+                                        int* src, bool thin_first) {
   int u = blockIdx.y;
   if (u < a.shared_tiles) {
     *src = 1;
@@ -144,7 +147,12 @@ __device__ __forceinline__ bool tile_of(const Buckets& b, const GemmArgs& a, Til
   }
   u -= a.shared_tiles;
   *src = 0;
-  if (u >= b.sched[1]) return false;
+  const int n_tiles = b.sched[1];
+  if (u >= n_tiles) return false;
+  if (thin_first) {  // start with the thin experts' tiles, which end the list
+    u += b.sched[2];
+    if (u >= n_tiles) u -= n_tiles;
+  }
   const int4 t = reinterpret_cast<const int4*>(b.sched + sched_tiles_offset(b.E))[u];
   v->e = t.x;
   v->row0 = t.y;
@@ -359,7 +367,7 @@ __global__ __launch_bounds__(kThreads, MOE_GEMM_OCC) void gemm_kernel(Buckets b,
   }
   TileView tv;
   int src = 0;
-  if (!tile_of(b, a, &tv, &src)) return;
+  if (!tile_of(b, a, &tv, &src, MODE == 1 && MOE_GEMM_DOWN_THIN_FIRST)) return;
   const GemmSrc S = src ? a.src[1] : a.src[0];
   constexpr int BN = kWaves * 32 * NS;
   if ((int)blockIdx.x * BN >= S.N) return;  // the other source is wider

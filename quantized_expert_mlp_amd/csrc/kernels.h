@@ -29,6 +29,8 @@ struct Launch {
 // Schedule words written by the permutation kernels, read by the expert MLPs:
 //   [0] number of experts with at least one slot (touched experts)
 //   [1] number of MFMA row tiles
+//   [2] how many of them, at the end of the list, belong to the one-tile
+//       experts of at most 32 rows (the list's other tiles are in expert order)
 //   [4 .. 4+4E)            touched experts, ascending: {expert, first row, rows, 0}
 //   [tiles_offset(E) ..)   tiles, 4 ints each: {expert, first row, rows, 0}
 // An expert's rows are cut into tiles of kGemmTileRows; only its last tile can

@@ -180,6 +180,10 @@ __device__ int scan256(int v, int* tmp, int* total) {
 }
 
 // Schedule words from the per-expert counts and offsets held in LDS.
+// Touched experts in ascending order.  MFMA tiles: first every tile of the
+// experts with more than 32 rows, in expert order (an expert's tiles stay
+// adjacent, so they run together and share its weights in L2), then the
+// one-tile experts of at most 32 rows, which fill the launch's tail.
 // At most max_tiles tiles are written (the schedule buffer's capacity).
 __device__ void write_schedule(const int* cnt, const int* offs, int E, int max_tiles,
                                int32_t* sched, int* tmp) {
@@ -187,9 +191,12 @@ __device__ void write_schedule(const int* cnt, const int* offs, int E, int max_t
   const int c = (e < E) ? cnt[e] : 0;
   const int touched = c > 0 ? 1 : 0;
   const int ntile = (c + kGemmTileRows - 1) / kGemmTileRows;
-  int n_touched, n_tiles;
+  const bool thin = touched && c <= 32;
+  int n_touched, n_wide, n_thin;
   const int tpos = scan256(touched, tmp, &n_touched);
-  const int tilepos = scan256(ntile, tmp, &n_tiles);
+  const int wpos = scan256(thin ? 0 : ntile, tmp, &n_wide);
+  const int npos = scan256(thin ? 1 : 0, tmp, &n_thin);
+  const int tilepos = thin ? n_wide + npos : wpos;
   if (e < E) {
     if (touched)
       reinterpret_cast<int4*>(sched + sched_touched_offset())[tpos] = make_int4(e, offs[e], c, 0);
@@ -201,7 +208,8 @@ __device__ void write_schedule(const int* cnt, const int* offs, int E, int max_t
   }
   if (threadIdx.x == 0) {
     sched[0] = n_touched;
-    sched[1] = min(n_tiles, max_tiles);
+    sched[1] = min(n_wide + n_thin, max_tiles);
+    sched[2] = n_thin;  // the list's last n_thin tiles are the one-tile thin experts'
   }
 }
 
