@@ -122,7 +122,8 @@ struct GemmSrc {
 struct GemmArgs {
   GemmSrc src[2];        // [0] routed buckets, [1] shared expert
   int shared_T;          // rows of the shared expert (0: none)
-  int shared_tiles;      // leading blockIdx.y values that hold shared tiles
+  int shared_tiles;      // 128-row tiles of the shared expert
+  int gx[2];             // column blocks of one tile: [0] routed, [1] shared
   const float* w;        // MODE 1 combine weights per slot
   const float* gate_logit;  // MODE 1 shared-expert gate logits (nullable)
   int gate_ld;
@@ -132,20 +133,27 @@ struct GemmArgs {
   int64_t y_elems;       // (a multiple of 4)
 };
 
-// Tile of this workgroup.  The first a.shared_tiles values of blockIdx.y are
-// 128-row tiles of the shared expert (identity rows over all tokens); the
-// rest index the routed tile list.
+// Tile and column block of this workgroup.  blockIdx.x runs first over the
+// shared expert's tiles (identity rows over all tokens), a.gx[1] column
+// blocks each, then over the routed tile list, a.gx[0] column blocks each
+// (consecutive workgroups share a tile), so each source's grid is exactly
+// its own width.
 __device__ __forceinline__ bool tile_of(const Buckets& b, const GemmArgs& a, TileView* v,
-                                        int* src, bool thin_first) {
-  int u = blockIdx.y;
-  if (u < a.shared_tiles) {
+                                        int* src, int* cblk, bool thin_first) {
+  int wg = blockIdx.x;
+  const int shared_wgs = a.shared_tiles * a.gx[1];
+  if (wg < shared_wgs) {
+    const int u = wg / a.gx[1];
+    *cblk = wg - u * a.gx[1];
     *src = 1;
     v->e = 0;
     v->row0 = u * kBM;
     v->nrows = min(kBM, a.shared_T - v->row0);
     return v->nrows > 0;
   }
-  u -= a.shared_tiles;
+  wg -= shared_wgs;
+  int u = wg / a.gx[0];
+  *cblk = wg - u * a.gx[0];
   *src = 0;
   const int n_tiles = b.sched[1];
   if (u >= n_tiles) return false;
@@ -181,13 +189,13 @@ template <int P, int NS, int MODE, int MS, int FMT>
 __device__ __forceinline__ void gemm_tile(const TileView& tv, const GemmSrc& S, const GemmArgs& a,
                                           const uint16_t* const (&arow)[a_chunks<MS>()],
                                           char (*lds)[kBM * kPitch], const int* row_tok,
-                                          const float* row_w, int k0, int k1) {
+                                          const float* row_w, int cblk, int k0, int k1) {
   constexpr int NA = a_chunks<MS>();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = lane & 31, hf = lane >> 5;
   constexpr int WN = 32 * NS;
   constexpr int BN = kWaves * WN;
-  const int col0 = blockIdx.x * BN + wave * WN;
+  const int col0 = cblk * BN + wave * WN;
   const int K = S.K, N = S.N;
   const int n = k1 - k0;  // steps of this workgroup
 
@@ -366,11 +374,9 @@ __global__ __launch_bounds__(kThreads, MOE_GEMM_OCC) void gemm_kernel(Buckets b,
     for (int64_t i = gid; i < a.y_elems / 4; i += nthr) y4[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
   TileView tv;
-  int src = 0;
-  if (!tile_of(b, a, &tv, &src, MODE == 1 && MOE_GEMM_DOWN_THIN_FIRST)) return;
+  int src = 0, cblk = 0;
+  if (!tile_of(b, a, &tv, &src, &cblk, MODE == 1 && MOE_GEMM_DOWN_THIN_FIRST)) return;
   const GemmSrc S = src ? a.src[1] : a.src[0];
-  constexpr int BN = kWaves * 32 * NS;
-  if ((int)blockIdx.x * BN >= S.N) return;  // the other source is wider
   if (MODE == 1 && (int)blockIdx.z >= S.ksplit) return;
 
   __shared__ __attribute__((aligned(16))) char lds[2][kBM * kPitch];
@@ -423,7 +429,7 @@ __global__ __launch_bounds__(kThreads, MOE_GEMM_OCC) void gemm_kernel(Buckets b,
       const uint16_t* rows[NA];
 #pragma unroll
       for (int i = 0; i < NA; ++i) rows[i] = src_row(r0 + kChunkRows * i);
-      gemm_tile<P, NS, MODE, MS, FMT>(tv, S, a, rows, lds, row_tok, row_w, k0, k1);
+      gemm_tile<P, NS, MODE, MS, FMT>(tv, S, a, rows, lds, row_tok, row_w, cblk, k0, k1);
     }
   });
 }
@@ -451,12 +457,14 @@ int64_t routed_tile_estimate(const Buckets& b) {
 }
 
 template <int P, int NS, int MODE>
-hipError_t launch_tiles(const Buckets& b, int max_tiles, const GemmArgs& a, int gz, int fmt,
+hipError_t launch_tiles(const Buckets& b, int max_tiles, GemmArgs a, int gz, int fmt,
                         const Launch& L) {
   constexpr int BN = kWaves * 32 * NS;
-  int gx = (a.src[0].N + BN - 1) / BN;
-  if (a.shared_tiles > 0) gx = std::max(gx, (a.src[1].N + BN - 1) / BN);
-  const dim3 grid(gx, a.shared_tiles + max_tiles, gz);
+  a.gx[0] = (a.src[0].N + BN - 1) / BN;
+  a.gx[1] = a.shared_tiles > 0 ? (a.src[1].N + BN - 1) / BN : 1;
+  const int64_t wgs = (int64_t)a.shared_tiles * a.gx[1] + (int64_t)max_tiles * a.gx[0];
+  if (wgs < 1 || wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)wgs, 1, gz);
   if (fmt == kFmtMxfp4)
     MOE_LAUNCH(L, (gemm_kernel<P, NS, MODE, kFmtMxfp4>), grid, dim3(kThreads), 0, b, a);
   else
