@@ -158,7 +158,9 @@ constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 
 // Exclusive scan of v over the workgroup's first 256 threads (the others must
-// pass 0).  Every thread of the workgroup must call it.  tmp: >= kWaves ints.
+// pass 0, so only the first four waves' totals can be non-zero; their results
+// are meaningless).  Every thread of the workgroup (256 or more threads) must
+// call it.  tmp: >= 4 ints.
 __device__ int scan256(int v, int* tmp, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int inc = v;
@@ -167,12 +169,14 @@ __device__ int scan256(int v, int* tmp, int* total) {
     const int n = __shfl_up(inc, o, 64);
     if (lane >= o) inc += n;
   }
-  if (lane == 63) tmp[wave] = inc;
+  if (lane == 63 && wave < 4) tmp[wave] = inc;
   __syncthreads();
   int pre = 0, tot = 0;
-  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
-    if (w < wave) pre += tmp[w];
-    tot += tmp[w];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {  // four independent LDS reads
+    const int tw = tmp[w];
+    pre += w < wave ? tw : 0;
+    tot += tw;
   }
   *total = tot;
   __syncthreads();
@@ -267,7 +271,8 @@ __device__ void permute_block(const int32_t* idx, int S, int E, int32_t* __restr
     __syncthreads();
     if (e >= 0) {
       int pos = sm.cursor[e] + rank;
-      for (int w = 0; w < wave; ++w) pos += sm.wcnt[w][e];
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) pos += w < wave ? sm.wcnt[w][e] : 0;
       sorted[pos] = s;
       row_of[s] = pos;
     } else if (s < S) {

@@ -226,6 +226,40 @@ def test_layer_full_size(name):
         assert_y_close(y2[check], y_ref[pos], name + " (router logits)")
 
 
+# ------------------------------------------------ router-computed logits --
+
+ROUTER_SHAPES = [
+    # ragged 16-token tiles and the gate row of a shared expert as column E
+    _mid("router_small_gated", 30, 37, 256, 12, 2, 128, 192, "router"),
+    # three tokens: the GEMV's fused routing reading the computed logits
+    _mid("router_tiny", 31, 3, 512, 16, 4, 128, 0, "router"),
+    # several token tiles, a ragged last one
+    _mid("router_tiles", 32, 70, 256, 12, 2, 128, 192, "router"),
+]
+
+
+@pytest.mark.parametrize("path", [moe.MOE_PATH_GEMV, moe.MOE_PATH_GEMM])
+@pytest.mark.parametrize("wl", ROUTER_SHAPES, ids=[w.name for w in ROUTER_SHAPES])
+def test_layer_router_logits(wl, path):
+    """Logits computed on the device: within the fp32 forward-error bound of
+    the fp64 oracle; the device's own fp32 logits then feed the oracle's
+    top-k (indices bit-exact, weights 1e-6) and layer (y on every row), which
+    also covers the fp16 activation copy the logits launch writes for the
+    MFMA path and the shared gate's logit column."""
+    say("router logits %s path=%d" % (wl.name, path))
+    inp = S.make_layer_inputs(wl, seed=3)
+    d = DeviceLayer(inp)
+    y, idx, w, lo = run_layer(d, use_router=True, path=path)
+    L = oracle.router_logits(inp.x, inp.w_router)
+    bound = logits_bound(inp.x, inp.w_router)
+    assert np.all(np.abs(lo.astype(np.float64) - L.astype(np.float64)) <= bound + 1e-30)
+    idx_ref, w_ref, _ = oracle.router_topk(lo, wl.k)
+    assert np.array_equal(idx, idx_ref)
+    assert_w_close(w, w_ref, wl.name)
+    y_ref, _, _ = oracle.layer(inp.x, lo, wl.k, inp.planes, inp.shared, inp.shared_gate)
+    assert_y_close(y, y_ref, "%s path %d (router logits)" % (wl.name, path))
+
+
 # ------------------------------------------------- profiled entry point --
 
 @pytest.mark.parametrize("path", [moe.MOE_PATH_GEMV, moe.MOE_PATH_GEMM])
