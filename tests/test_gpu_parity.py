@@ -137,6 +137,9 @@ MID = [
     _mid("mid_max_k", 27, 20, 256, 256, 64, 128),
     # one token with k = 64: the GEMV's fused routing at its 64-slot limit
     _mid("mid_one_token_max_k", 28, 1, 512, 256, 64, 192),
+    # the widest rows the GEMV serves (256 scale groups, four per lane) on
+    # both gate/up (K = H) and down (K = I)
+    _mid("mid_widest_rows", 29, 2, 8192, 2, 1, 8192),
 ]
 
 
