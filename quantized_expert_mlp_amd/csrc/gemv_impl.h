@@ -192,14 +192,15 @@ __device__ __forceinline__ bool bucket_of(const Buckets& b, BucketView* v) {
 // Bucket build of the fused small-batch routing (see RouteArgs), in LDS.
 struct SmallRoute {
   int32_t pick[kFusedRouteMaxSlots];
-  float wt[kFusedRouteMaxSlots];
   int32_t sorted[kFusedRouteMaxSlots];
   int32_t first[kFusedRouteMaxSlots];
   int4 bucket[kFusedRouteMaxSlots];
   int n_touched;
 };
 
-// Waves t < T take token t's top-k; then slot s (thread s) finds its row in
+// Waves t < T take token t's top-k (the routing weights only in workgroup
+// (0,0), which publishes them for the down launch; the others need the picks
+// alone); then slot s (thread s) finds its row in
 // the expert-major, slot-ascending order - #slots with a smaller expert plus
 // #earlier slots with the same expert - exactly the permutation of the
 // standalone kernels, which also drop a pick outside [0, E) (top-p's -1):
@@ -212,7 +213,8 @@ __device__ void small_route(const RouteArgs& ra, int k, SmallRoute& sr) {
   const int S = ra.T * k;
   if (wave < ra.T)
     topk_group<V, 64>(ra.logits, ra.ld, ra.T, wave, ra.E, k, ra.rs,
-                      publish ? ra.idx : nullptr, publish ? ra.w : nullptr, sr.pick, sr.wt, 0);
+                      publish ? ra.idx : nullptr, publish ? ra.w : nullptr, sr.pick, nullptr, 0,
+                      publish);
   __syncthreads();
   auto valid = [&](int e2) { return e2 >= 0 && e2 < ra.E; };
   int less = 0, rank = 0, first = 0, e = -1;

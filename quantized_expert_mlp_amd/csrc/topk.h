@@ -64,12 +64,15 @@ __device__ void topk_group_variant(const float* __restrict__ logits, int ld, int
                                    float* __restrict__ w, int32_t* idx_lds, float* w_lds,
                                    int lds_t0);
 
+// need_w = false: the caller uses the picks only (w and w_lds are not
+// written); with expert top-p on, the weights decide the picks and are
+// formed anyway.
 template <int V, int G>
 __device__ __forceinline__ void topk_group(const float* __restrict__ logits, int ld, int T, int t0,
                                            int E, int k, const RouterSpec& rs,
                                            int32_t* __restrict__ idx, float* __restrict__ w,
                                            int32_t* idx_lds = nullptr, float* w_lds = nullptr,
-                                           int lds_t0 = 0) {
+                                           int lds_t0 = 0, bool need_w = true) {
   static_assert(G == 16 || G == 32 || G == 64, "group size");
   if (rs.variant()) {  // uniform over the launch
     topk_group_variant<V, G>(logits, ld, T, t0, E, k, rs, idx, w, idx_lds, w_lds, lds_t0);
@@ -127,6 +130,13 @@ __device__ __forceinline__ void topk_group(const float* __restrict__ logits, int
     }
     my_val = gl == j ? cv : my_val;
     my_idx = gl == j ? ci : my_idx;
+  }
+  if (!need_w && !(top_p > 0.f && top_p < 1.f)) {
+    if (tok && gl < k) {
+      if (idx) idx[(int64_t)t * k + gl] = my_idx;
+      if (idx_lds) idx_lds[(t - lds_t0) * k + gl] = my_idx;
+    }
+    return;
   }
   // weights: group lane 0 holds the top logit
   const double l0 = (double)__shfl(my_val, g * G, 64);
