@@ -26,8 +26,9 @@
 // decodes to exact fp16 (1024 + e) pairs and dots them with the fp16 hidden
 // row (v_dot2_f32_f16).  A per-group constant removes the offset.
 // MXFP4 (the colibri PR's later fmt=7 comment: e2m1 nibbles, one ue8m0
-// exponent per 32 inputs): the nibbles decode to their exact fp16 e2m1 values
-// and dot with fp16 activations (gate/up: the bf16 row converted once in the
+// exponent per 32 inputs): each byte's two nibbles convert to their exact
+// fp16 e2m1 pair with one packed fp4 conversion and dot with natural-order
+// fp16 activation pairs (gate/up: the bf16 row converted once in the
 // prologue); no offset.  Each group's fp32 partial is scaled once (fp16 scale,
 // or 2^(e - 127) exactly in fp32); the LPR-lane fold is a DPP add tree.
 // Gate/up rows are processed in pairs so SiLU(g)*u is formed in registers and
@@ -126,20 +127,27 @@ __device__ __forceinline__ float dot_group_f16(uint4 w, const uint32_t* a) {
   return s;
 }
 
+// The two e2m1 codes of byte B of w (low nibble first) as an fp16 pair, by
+// gfx950's packed fp4 conversion with unit scale: every e2m1 value is an
+// fp16 number, so the pair is exact.
+template <int B>
+__device__ __forceinline__ uint32_t e2m1_pair(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, B));
+}
+
 // sum_i e2m1(e_i) a_i over one 32-input group (4 packed words) of MXFP4
-// nibbles against fp16 activation pairs in the decode's operand order: the
-// fp16 e2m1 values are exact, so the products are exact in fp32.
+// nibbles against fp16 activation pairs in natural order (a[j] holds inputs
+// 2j, 2j+1): the fp16 e2m1 values are exact, so the products are exact in
+// fp32.
 __device__ __forceinline__ float dot_group_mx(uint4 w, const uint32_t* a) {
   const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
   float s = 0.f;
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
-    const E2m1Hi hb = e2m1_hi_bytes(ws[d]);
-    const uint32_t ht = hb.ht, hu = hb.hu;
-    s = dot2_f16(__builtin_amdgcn_perm(0u, ht, kSelPairLo), a[4 * d + 0], s);
-    s = dot2_f16(__builtin_amdgcn_perm(0u, hu, kSelPairLo), a[4 * d + 1], s);
-    s = dot2_f16(__builtin_amdgcn_perm(0u, ht, kSelPairHi), a[4 * d + 2], s);
-    s = dot2_f16(__builtin_amdgcn_perm(0u, hu, kSelPairHi), a[4 * d + 3], s);
+    s = dot2_f16(e2m1_pair<0>(ws[d]), a[4 * d + 0], s);
+    s = dot2_f16(e2m1_pair<1>(ws[d]), a[4 * d + 1], s);
+    s = dot2_f16(e2m1_pair<2>(ws[d]), a[4 * d + 2], s);
+    s = dot2_f16(e2m1_pair<3>(ws[d]), a[4 * d + 3], s);
   }
   return s;
 }
@@ -416,15 +424,15 @@ __global__ __launch_bounds__(256) void gemv_gate_up_kernel(
           for (int c = 0; c < 16; ++c) nat[c] = 0;
         }
         float sum = 0.f;
+        if constexpr (FMT == kFmtMxfp4) {
+          // natural-order fp16 pairs (the MXFP4 decode yields natural pairs)
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-          pair_block(nat[4 * blk], nat[4 * blk + 1], nat[4 * blk + 2], nat[4 * blk + 3],
-                     &xa[t][gi][4 * blk]);
-          if constexpr (FMT == kFmtMxfp4) {
+          for (int c = 0; c < 16; ++c) xa[t][gi][c] = bf16x2_to_f16x2(nat[c]);
+        } else {
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-              xa[t][gi][4 * blk + c] = bf16x2_to_f16x2(xa[t][gi][4 * blk + c]);
-          } else {
+          for (int blk = 0; blk < 4; ++blk) {
+            pair_block(nat[4 * blk], nat[4 * blk + 1], nat[4 * blk + 2], nat[4 * blk + 3],
+                       &xa[t][gi][4 * blk]);
             sum += sum8_bf16(nat[4 * blk], nat[4 * blk + 1], nat[4 * blk + 2], nat[4 * blk + 3]);
           }
         }
@@ -575,12 +583,16 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(
           for (int c = 0; c < 16; ++c) nat[c] = 0;
         }
         float sum = 0.f;
+        if constexpr (FMT == kFmtMxfp4) {
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-          pair_block(nat[4 * blk], nat[4 * blk + 1], nat[4 * blk + 2], nat[4 * blk + 3],
-                     &xa[t][gi][4 * blk]);
-          if constexpr (FMT != kFmtMxfp4)
+          for (int c = 0; c < 16; ++c) xa[t][gi][c] = nat[c];  // natural-order fp16 pairs
+        } else {
+#pragma unroll
+          for (int blk = 0; blk < 4; ++blk) {
+            pair_block(nat[4 * blk], nat[4 * blk + 1], nat[4 * blk + 2], nat[4 * blk + 3],
+                       &xa[t][gi][4 * blk]);
             sum += sum8_f16(nat[4 * blk], nat[4 * blk + 1], nat[4 * blk + 2], nat[4 * blk + 3]);
+          }
         }
         corr[t][gi] = 1032.0f * sum;
       }
