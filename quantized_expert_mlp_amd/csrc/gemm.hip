@@ -168,6 +168,30 @@ __device__ __forceinline__ bool tile_of(const Buckets& b, const GemmArgs& a, Til
   return true;
 }
 
+// MXFP4 operands of one packed word for one-subtile tiles, where the decode
+// VALU outweighs the MFMA work of a K step: gfx950's packed fp4 conversion at
+// unit scale gives the exact fp16 pairs [e0,e1], [e2,e3], [e4,e5], [e6,e7]
+// (one per byte, low nibble first), one v_perm_b32 per pair regroups them
+// into the operand order of mx4_f16x8, and the packed multiply by [s, s]
+// rounds the exact product once: the same operands as mx4_f16x8, with fewer
+// instructions.  (Beside the MFMA work of wider tiles the table decode of
+// mx4_f16x8 measured faster.)
+__device__ __forceinline__ f16x8_t mx4_f16x8_cvt(uint32_t w, f16x2_t s2) {
+  constexpr uint32_t kLo = 0x05040100u, kHi = 0x07060302u;  // [src1, src0] low / high halves
+  const uint32_t p01 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0));
+  const uint32_t p23 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1));
+  const uint32_t p45 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2));
+  const uint32_t p67 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3));
+  const f16x2_t a = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(p45, p01, kLo)) * s2;
+  const f16x2_t b = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(p45, p01, kHi)) * s2;
+  const f16x2_t c = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(p67, p23, kLo)) * s2;
+  const f16x2_t d = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(p67, p23, kHi)) * s2;
+  f16x8_t r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
 template <int MS>
 constexpr int a_chunks() {
   return (MS * 32 + kChunkRows - 1) / kChunkRows;
@@ -269,7 +293,8 @@ __device__ __forceinline__ void gemm_tile(const TileView& tv, const GemmSrc& S, 
           const _Float16 sc = e8m0_f16(st.s[ns][p]);
           const f16x2_t s2 = {sc, sc};
 #pragma unroll
-          for (int d = 0; d < 4; ++d) bf[ns][p][d] = mx4_f16x8(st.q[ns][p][d], s2);
+          for (int d = 0; d < 4; ++d)
+            bf[ns][p][d] = MS == 1 ? mx4_f16x8_cvt(st.q[ns][p][d], s2) : mx4_f16x8(st.q[ns][p][d], s2);
         } else {
           const _Float16 sc = __builtin_bit_cast(_Float16, (uint16_t)st.s[ns][p]);
           const f16x2_t s2 = {sc, sc};
