@@ -64,10 +64,12 @@ class Hip:
         return out.value
 
 
-def counted_traffic(kernel: str, workload: str, gemm: bool, fmt: str = "int4"):
+def counted_traffic(kernel: str, workload: str, gemm: bool, fmt: str = "int4",
+                    layout: str = "rows"):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary (profiles/<workload>_gemv_hbm_counters.md), or None when there is
-    none or the kernel sources changed since the counters were taken."""
+    summary (profiles/<workload>_<gemv|gemm>_hbm_counters.md), or None when
+    there is none, it was taken for another weight layout, or the kernel
+    sources changed since the counters were taken."""
     import hashlib
     if fmt != "int4":
         return None
@@ -84,6 +86,8 @@ def counted_traffic(kernel: str, workload: str, gemm: bool, fmt: str = "int4"):
     for src in ("device.h", "kernels.h") + srcs:
         h.update(open(os.path.join(ROOT, "quantized_expert_mlp_amd", "csrc", src), "rb").read())
     if kv.get("kernel") != kernel or kv.get("source_sha256") != h.hexdigest()[:16]:
+        return None
+    if kv.get("layout", "rows") != layout:
         return None
     return int(kv["traffic_bytes_per_launch"])
 
@@ -405,7 +409,7 @@ def main():
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
     roof["kernel"] = dom
     roof["intensity_flop_per_byte"] = round(work[dom]["flops"] / work[dom]["bytes"], 1)
-    roof["traffic"] = counted_traffic(dom, wl.name, gemm, args.format)
+    roof["traffic"] = counted_traffic(dom, wl.name, gemm, args.format, args.layout)
     layer_bytes = sum(w_["bytes"] for w_ in work.values())
     layer_flops = sum(w_["flops"] for w_ in work.values())
     log("stage device time (us): " + ", ".join("%s %.2f" % (k_, v * 1e3)
