@@ -148,11 +148,13 @@ def router_topk(logits: np.ndarray, k: int, route_scale: float = 1.0, top_p: flo
 
 
 def permute(idx: np.ndarray, E: int):
-    """(off int32 [E+1], sorted int32 [T*k], row_of int32 [T*k])."""
+    """(off int32 [E+1], sorted int32 [T*k], row_of int32 [T*k]).  Picks
+    outside [0, E) belong to no bucket: row_of -1, and only the first off[E]
+    entries of sorted are written."""
     idx = _c(idx, np.int32)
     T, k = idx.shape
     off = np.empty(E + 1, dtype=np.int32)
-    srt = np.empty(T * k, dtype=np.int32)
+    srt = np.full(T * k, -1, dtype=np.int32)
     row_of = np.empty(T * k, dtype=np.int32)
     lib().oracle_permute(_p(idx), T, k, E, _p(off), _p(srt), _p(row_of))
     return off, srt, row_of

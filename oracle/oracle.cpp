@@ -370,15 +370,25 @@ void oracle_router_topk(const float* logits, int64_t T, int64_t E, int64_t k, do
 // Slot s = t*k + j.  off[E+1] is the exclusive scan of the counts; within a
 // bucket the slots appear in ascending slot order; row_of[s] is the row of
 // slot s in the sorted order, so sorted[row_of[s]] == s.
+// A pick outside [0, E) belongs to no bucket.  Reading: expert top-p (see
+// top_p_row) leaves a dropped pick as index -1, and a dropped pick is routed
+// nowhere, so it is counted in no bucket, takes no row (row_of[s] = -1) and
+// off[E] counts the valid picks only; sorted holds those off[E] slots.
 void oracle_permute(const int32_t* idx, int64_t T, int64_t k, int64_t E, int32_t* off,
                     int32_t* sorted, int32_t* row_of) {
   const int64_t S = T * k;
+  auto valid = [&](int64_t s) { return idx[s] >= 0 && idx[s] < E; };
   std::vector<int64_t> cnt(E, 0);
-  for (int64_t s = 0; s < S; ++s) cnt[idx[s]]++;
+  for (int64_t s = 0; s < S; ++s)
+    if (valid(s)) cnt[idx[s]]++;
   off[0] = 0;
   for (int64_t e = 0; e < E; ++e) off[e + 1] = off[e] + (int32_t)cnt[e];
   std::vector<int64_t> cur(off, off + E);
   for (int64_t s = 0; s < S; ++s) {
+    if (!valid(s)) {
+      row_of[s] = -1;
+      continue;
+    }
     const int64_t r = cur[idx[s]]++;
     sorted[r] = (int32_t)s;
     row_of[s] = (int32_t)r;

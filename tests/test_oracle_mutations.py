@@ -32,6 +32,10 @@ MUTATIONS = {
         "std::vector<int64_t> cur(off, off + E);\n  for (int64_t s = 0; s < S; ++s) {",
         "std::vector<int64_t> cur(off, off + E);\n  for (int64_t s = S - 1; s >= 0; --s) {",
         ["test_permute_matches_stable_sort"]),
+    "dropped_pick_counted": ("if (valid(s)) cnt[idx[s]]++;", "if (idx[s] >= 0) cnt[idx[s] % E]++;",
+                             ["test_permute_drops_out_of_range_picks"]),
+    "dropped_pick_keeps_a_row": ("      row_of[s] = -1;\n      continue;", "      row_of[s] = 0;\n      continue;",
+                                 ["test_permute_drops_out_of_range_picks"]),
     "silu_dropped": ("h[n] = g * sigmoid(g) * u;", "h[n] = g * u;",
                      ["test_expert_closed_form_uniform_planes"]),
     "down_reads_gate_row_count": (

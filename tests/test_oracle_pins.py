@@ -335,6 +335,31 @@ def test_permute_matches_stable_sort(orc):
             assert np.all(flat[srt[off[e]:off[e + 1]]] == e)
 
 
+def test_permute_drops_out_of_range_picks(orc):
+    """A pick outside [0, E) (top-p's -1, or any index past the experts) is in
+    no bucket: the buckets are those of the valid picks alone, in slot order,
+    row_of is -1 for the dropped slots and off[E] counts the valid ones.
+    Checked against brute force: the valid slots' stable sort by expert."""
+    rng = np.random.default_rng(12)
+    for T, k, E, frac in [(300, 4, 16, 0.1), (9, 8, 256, 0.5), (50, 3, 5, 1.0), (64, 2, 7, 0.0)]:
+        idx = rng.integers(0, E, (T, k)).astype(np.int32)
+        bad = rng.random((T, k)) < frac
+        idx[bad] = np.where(rng.random(int(bad.sum())) < 0.5, -1, E + rng.integers(0, 9))
+        off, srt, row_of = orc.permute(idx, E)
+        flat = idx.ravel()
+        valid = (flat >= 0) & (flat < E)
+        slots = np.nonzero(valid)[0]
+        want_sorted = slots[np.argsort(flat[valid], kind="stable")]
+        assert off[0] == 0 and off[E] == valid.sum()
+        assert np.array_equal(off, np.concatenate([[0], np.cumsum(np.bincount(flat[valid],
+                                                                              minlength=E))]))
+        assert np.array_equal(srt[: off[E]], want_sorted)
+        assert np.all(row_of[~valid] == -1)
+        assert np.array_equal(srt[row_of[valid]], slots)
+        for e in range(E):
+            assert set(srt[off[e]:off[e + 1]].tolist()) == set(np.nonzero(flat == e)[0].tolist())
+
+
 # -------------------------------------------------------------- expert MLP --
 
 def _tiny_planes(rng, H, I):
