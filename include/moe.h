@@ -168,31 +168,55 @@ int moe_router_topk(const float *logits, int32_t T, int32_t E, int32_t k, float 
 
 /*
  * Token-to-expert permutation (the bucket schedule of the dasLLAMA PR's routed
- * block: per-expert counts, exclusive scan, slots placed in slot order), one
- * workgroup with an LDS histogram, LDS scan and stable scatter.
+ * block: per-expert counts, exclusive scan, slots placed in slot order).  Up
+ * to 4096 slots one workgroup does it all (LDS histogram, LDS scan, stable
+ * scatter); beyond, three launches over blocks of 1024 slots (per-block
+ * counts, one offsets pass, per-block scatters with the same in-slot-order
+ * ranking), which need scratch.
  *   idx    : int32 [T][k] expert picks; slot s = t*k + j.
  *   off    : int32 [E+1] out, exclusive scan of the per-expert slot counts.
  *   sorted : int32 [T*k] out, slot ids grouped by expert, ascending within a
  *            bucket (sorted[off[e] .. off[e+1]) are expert e's slots).
  *   row_of : int32 [T*k] out, inverse map: sorted[row_of[s]] == s.
+ *   ws     : device scratch of at least moe_permute_workspace_bytes(T, k, E)
+ *            bytes, 256-byte aligned (may be NULL when that is 0); its
+ *            contents on entry are ignored.
  * A pick outside [0, E) is dropped: it is counted nowhere, sorted holds only
  * valid slots (off[E] = their number) and row_of[s] = -1 for it.
- * Errors: INVALID_ARG (null pointer, T < 1, k < 1); UNSUPPORTED (E > 256).
+ * Errors: INVALID_ARG (null pointer, T < 1, k < 1, misaligned ws);
+ *         UNSUPPORTED (E > 256, T*k >= 2^31); WORKSPACE (ws_bytes short).
  */
 int moe_permute(const int32_t *idx, int32_t T, int32_t k, int32_t E, int32_t *off,
-                int32_t *sorted, int32_t *row_of, moe_stream_t stream);
+                int32_t *sorted, int32_t *row_of, void *ws, size_t ws_bytes,
+                moe_stream_t stream);
+
+/* Scratch bytes moe_permute needs for these sizes: 0 up to 4096 slots,
+ * 4 * ceil(T*k / 1024) * E beyond (0 also for sizes moe_permute rejects).
+ * Host only. */
+size_t moe_permute_workspace_bytes(int32_t T, int32_t k, int32_t E);
 
 /*
  * The routed experts' SwiGLU MLPs with the weighted combine fused into the
- * down projection's epilogue:
- *   y[t][:] = sum over slots s = t*k+j in the buckets of w[s] * MLP_e(x[t]).
+ * down projection's epilogue (the colibri PR's fused expert group, its
+ * Summary: gate and up products with the SiLU product formed on the device,
+ * then down, the hidden row never leaving the device; the dasLLAMA PR's
+ * routed block: each bucket's rows gathered through the slot map, and the
+ * combine weighting each slot's down row by its routing weight onto the
+ * token's output row):
+ *   y[t][:] = sum over slots s = t*k+j in the buckets of w[s] * MLP_e(x[t]),
+ *   MLP_e(x) = Wd_e (silu(Wg_e x) * (Wu_e x)),  silu(z) = z / (1 + exp(-z)).
  *   shape  : host pointer; T, H, E, k, I, group, path, layout, format are
  *            used (SI ignored).
- *   x      : bf16 bits [T][H].
+ *   x      : bf16 bits [T][H], 16-byte aligned.
  *   off, sorted : as written by moe_permute.
  *   w      : fp32 [T][k] combine weights (from moe_router_topk).
  *   gate, up, down : 4-bit planes in shape->format and shape->layout.
- *   y      : fp32 [T][H] out, OVERWRITTEN (not accumulated).
+ *   y      : fp32 [T][H] out, OVERWRITTEN (not accumulated), 16-byte aligned.
+ * Value range: both paths keep the hidden row h = silu(g) * u in fp16, so a
+ * hidden value beyond 65504 in magnitude becomes +-inf and its output row
+ * non-finite (the call still returns MOE_OK); the MFMA path (path GEMM, or
+ * AUTO at prefill sizes) also feeds x as fp16, so it serves |x| < 65520
+ * (activations with |x| < 2^-14 keep fp16's subnormal spacing, 2^-24).
  *   ws     : device scratch of at least moe_workspace_bytes(shape) bytes,
  *            256-byte aligned; its contents on entry are ignored.
  * The order in which a token's k terms are added to y is not fixed (device
@@ -216,11 +240,12 @@ int moe_expert_mlp(const moe_shape *shape, const uint16_t *x, const int32_t *off
  *                I = shape->SI, or NULL (then shape->SI must be 0).
  *   shared_gate: fp32 [H] gate vector g, or NULL for an ungated shared expert
  *                (added at weight one).  Ignored without a shared expert.
- *   y          : fp32 [T][H] out, overwritten.
+ *   y          : fp32 [T][H] out, overwritten, 16-byte aligned.
  *   idx_out    : int32 [T][k] out, or NULL.
  *   w_out      : fp32 [T][k] out, or NULL.
  *   logits_out : fp32 [T][E] out (the logits used), or NULL.
  *   ws         : as for moe_expert_mlp.
+ * Value range: as for moe_expert_mlp (the shared expert's hidden row too).
  * Errors: as moe_expert_mlp.
  */
 int moe_layer(const moe_shape *shape, const uint16_t *x, const float *logits,
@@ -314,24 +339,36 @@ size_t moe_workspace_bytes(const moe_shape *shape);
 const char *moe_status_string(int status);
 
 /*
- * Test hook: runs the kernels' own device int4 decode on one plane and writes
- * the decoded weights as fp32 [N][K] (device pointer `out`).
- *   mode 0: the exact value (nibble - 8) * scale, via the decode the GEMV
- *           kernels use (bf16 offset encoding of the nibble);
- *   mode 1: the fp16 operand the MFMA kernels feed, widened to fp32 (the
- *           exact value rounded to fp16, nearest-even).
+ * Test hook: runs one of the kernels' own device int4 decoders (the same
+ * __device__ routine their main loops call) over one plane (q [N][K/2]
+ * nibbles, s [N][K/32] fp16 bits) and writes what it stands for as fp32
+ * [N][K] (device pointer `out`), in the plane's element order:
+ *   mode 0: the gate/up GEMV's decoder (each nibble as the exact bf16 value
+ *           128 + nibble), its offset and scale undone exactly in fp32: the
+ *           exact weight (nibble - 8) * scale;
+ *   mode 1: the MFMA GEMM's decoder for tiles of 2-4 row subtiles: its fp16
+ *           operand, the exact weight rounded once to fp16 (nearest even);
+ *   mode 2: the MFMA GEMM's decoder for one-subtile tiles: its fp16 operand,
+ *           the same value as mode 1 for every scale with |s| <= 8188;
+ *   mode 3: the down GEMV's decoder (each nibble as the exact fp16 value
+ *           1024 + nibble), offset and scale undone exactly: the exact weight.
  * Errors: INVALID_ARG (null, N < 1, K % 32 != 0, misaligned, bad mode).
  */
 int moe_debug_dequant_int4(moe_q4 plane, int32_t N, int32_t K, int32_t mode, float *out,
                            moe_stream_t stream);
 
 /*
- * Test hook: the MFMA kernels' MXFP4 decode of one plane (q [N][K/2] e2m1
- * nibbles, s [N][K/32] ue8m0 bytes), written as fp32 [N][K]: the fp16
- * operand e2m1 * 2^(e - 127) rounded to nearest even, widened to fp32.
- * Errors: INVALID_ARG (null, N < 1, K % 32 != 0, misaligned).
+ * Test hook: the kernels' MXFP4 decoders over one plane (q [N][K/2] e2m1
+ * nibbles, s [N][K/32] ue8m0 bytes), written as fp32 [N][K]:
+ *   mode 0: the GEMVs' decoder (each byte's e2m1 pair by the packed fp4
+ *           conversion) times the fp32 group scale 2^(e - 127): the exact
+ *           weight for every e (NaN for e = 255);
+ *   mode 1: the MFMA GEMM's decoder for tiles of 2-4 row subtiles: its fp16
+ *           operand e2m1 * 2^(e - 127) rounded to nearest even;
+ *   mode 2: the MFMA GEMM's decoder for one-subtile tiles: the same operand.
+ * Errors: INVALID_ARG (null, N < 1, K % 32 != 0, misaligned, bad mode).
  */
-int moe_debug_dequant_mxfp4(moe_q4 plane, int32_t N, int32_t K, float *out,
+int moe_debug_dequant_mxfp4(moe_q4 plane, int32_t N, int32_t K, int32_t mode, float *out,
                             moe_stream_t stream);
 
 #ifdef __cplusplus

@@ -24,7 +24,8 @@ MOE_FORMAT_INT4, MOE_FORMAT_MXFP4 = range(2)
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = range(2)
 
 # Every symbol include/moe.h declares.
-EXPORTS = ("moe_router_topk", "moe_permute", "moe_expert_mlp", "moe_layer",
+EXPORTS = ("moe_router_topk", "moe_permute", "moe_permute_workspace_bytes", "moe_expert_mlp",
+           "moe_layer",
            "moe_layer_profiled", "moe_pack_weights", "moe_workspace_bytes",
            "moe_status_string", "moe_debug_dequant_int4", "moe_debug_dequant_mxfp4",
            "moe_layer_residual_rmsnorm")
@@ -63,7 +64,9 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         P, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
         L.moe_router_topk.argtypes = [P, i32, i32, i32, f32, f32, i32, P, P, P, P]
-        L.moe_permute.argtypes = [P, i32, i32, i32, P, P, P, P]
+        L.moe_permute.argtypes = [P, i32, i32, i32, P, P, P, P, ctypes.c_size_t, P]
+        L.moe_permute_workspace_bytes.argtypes = [i32, i32, i32]
+        L.moe_permute_workspace_bytes.restype = ctypes.c_size_t
         L.moe_expert_mlp.argtypes = [ctypes.POINTER(moe_shape), P, P, P, P, moe_q4, moe_q4,
                                      moe_q4, P, P, ctypes.c_size_t, P]
         L.moe_layer.argtypes = [ctypes.POINTER(moe_shape), P, P, P, moe_q4, moe_q4, moe_q4,
@@ -78,7 +81,7 @@ def lib() -> ctypes.CDLL:
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_debug_dequant_int4.argtypes = [moe_q4, i32, i32, i32, P, P]
-        L.moe_debug_dequant_mxfp4.argtypes = [moe_q4, i32, i32, P, P]
+        L.moe_debug_dequant_mxfp4.argtypes = [moe_q4, i32, i32, i32, P, P]
         L.moe_pack_weights.argtypes = [moe_q4, i32, i32, i32, i32, moe_q4, P]
         for name in ("moe_router_topk", "moe_permute", "moe_expert_mlp", "moe_layer",
                      "moe_layer_profiled", "moe_pack_weights", "moe_debug_dequant_int4",
@@ -140,9 +143,14 @@ def moe_router_topk(logits, T, E, k, route_scale, idx, w, stream=None, top_p=0.0
                                                     _ptr(w), _stream(stream)))
 
 
-def moe_permute(idx, T, k, E, off, sorted_, row_of, stream=None) -> None:
+def moe_permute_workspace_bytes(T, k, E) -> int:
+    return lib().moe_permute_workspace_bytes(int(T), int(k), int(E))
+
+
+def moe_permute(idx, T, k, E, off, sorted_, row_of, ws=None, ws_bytes=0, stream=None) -> None:
     _check("moe_permute", lib().moe_permute(_ptr(idx), T, k, E, _ptr(off), _ptr(sorted_),
-                                            _ptr(row_of), _stream(stream)))
+                                            _ptr(row_of), _ptr(ws), int(ws_bytes),
+                                            _stream(stream)))
 
 
 def moe_expert_mlp(shape: moe_shape, x, off, sorted_, w, gate, up, down, y, ws, ws_bytes,
@@ -204,6 +212,6 @@ def moe_debug_dequant_int4(plane, N, K, mode, out, stream=None) -> None:
         q4(plane), N, K, mode, _ptr(out), _stream(stream)))
 
 
-def moe_debug_dequant_mxfp4(plane, N, K, out, stream=None) -> None:
+def moe_debug_dequant_mxfp4(plane, N, K, out, stream=None, mode=1) -> None:
     _check("moe_debug_dequant_mxfp4", lib().moe_debug_dequant_mxfp4(
-        q4(plane), N, K, _ptr(out), _stream(stream)))
+        q4(plane), N, K, int(mode), _ptr(out), _stream(stream)))

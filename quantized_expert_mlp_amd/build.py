@@ -28,10 +28,19 @@ def hipcc() -> str:
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
-    # keep hipcc from forming packed-fp32 VALU instructions
+    # keep hipcc from forming packed-fp32 VALU instructions (the device pass
+    # honours it; the host pass prints HOST_FEATURE_NOTE and ignores it, and
+    # the driver cannot forward a -Xclang pair to the device pass alone)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-munsafe-fp-atomics", "-Wall", "-Wno-unused-function",
 ]
+HOST_FEATURE_NOTE = "'-packed-fp32-ops' is not a recognized feature for this target (ignoring feature)"
+
+
+def _diagnostics(stderr: str) -> str:
+    """The compiler's messages without the host pass's note about the
+    device-only feature flag above (one per file; every other line kept)."""
+    return "\n".join(l for l in stderr.splitlines() if l.strip() != HOST_FEATURE_NOTE)
 
 
 def build(verbose: bool = False) -> str:
@@ -41,13 +50,14 @@ def build(verbose: bool = False) -> str:
 
     def compile_one(src):
         obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
-        lang = ["-x", "hip"] if src.endswith(".hip") else ["-x", "hip"]
+        lang = ["-x", "hip"]
         cmd = [cc] + FLAGS + ["-I", INCLUDE, "-I", CSRC] + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
-            raise RuntimeError("hipcc failed for %s:\n%s" % (src, r.stderr))
-        if verbose and r.stderr.strip():
-            print(r.stderr, file=sys.stderr)
+            raise RuntimeError("hipcc failed for %s:\n%s" % (src, _diagnostics(r.stderr)))
+        msg = _diagnostics(r.stderr)
+        if msg.strip():
+            print("%s:\n%s" % (src, msg), file=sys.stderr)
         return obj
 
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:

@@ -204,6 +204,80 @@ __device__ __forceinline__ _Float16 e8m0_f16(uint32_t e) {
   return (_Float16)f;
 }
 
+// int4 operands of one packed word for one-subtile MFMA tiles.  The word's
+// bytes are reordered to (b0, b2, b1, b3), so its low nibbles read e0, e4, e2,
+// e6 and its high nibbles e1, e5, e3, e7.  A byte 0000nnnn read as fp8 e4m3
+// is n * 2^-9 exactly (n < 8 as a subnormal), so gfx950's packed fp8
+// conversion at scale 2^9 turns each half of the masked word into an exact
+// fp16 pair of nibbles in the operand order ([e0,e4], [e2,e6] / [e1,e5],
+// [e3,e7]).  One fused multiply-add n * s + m8s with m8s = -8 s rounds
+// (n - 8) * s once: the same operands as q4_f16x8 in fewer instructions,
+// provided -8 s is itself an fp16 number, i.e. |s| <= 8188.  Beyond that
+// m8s is -inf and every weight of the group with n >= 1 comes out -inf or
+// NaN (q4_f16x8 still rounds each product once; for such scales weights of
+// nibble 0 overflow on both).
+__device__ __forceinline__ f16x8_t q4_f16x8_cvt(uint32_t w, f16x2_t s2, f16x2_t m8s2) {
+  const uint32_t r = __builtin_amdgcn_perm(w, w, 0x03010200u);  // bytes b0, b2, b1, b3
+  const uint32_t lo = r & 0x0F0F0F0Fu, hi = (r >> 4) & 0x0F0F0F0Fu;
+  const f16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, false);  // [e0, e4]
+  const f16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, true);   // [e2, e6]
+  const f16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 512.0f, false);  // [e1, e5]
+  const f16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 512.0f, true);   // [e3, e7]
+  const f16x2_t ra = __builtin_elementwise_fma(a, s2, m8s2);
+  const f16x2_t rb = __builtin_elementwise_fma(b, s2, m8s2);
+  const f16x2_t rc = __builtin_elementwise_fma(c, s2, m8s2);
+  const f16x2_t rd = __builtin_elementwise_fma(d, s2, m8s2);
+  f16x8_t o;
+  o[0] = ra[0]; o[1] = ra[1]; o[2] = rb[0]; o[3] = rb[1];
+  o[4] = rc[0]; o[5] = rc[1]; o[6] = rd[0]; o[7] = rd[1];
+  return o;
+}
+
+// The two e2m1 codes of byte B of w (low nibble first) as an fp16 pair, by
+// gfx950's packed fp4 conversion with unit scale: every e2m1 value is an
+// fp16 number, so the pair is exact.
+template <int B>
+__device__ __forceinline__ uint32_t e2m1_pair(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, B));
+}
+
+// MXFP4 operands of one packed word for one-subtile MFMA tiles, where the
+// decode VALU outweighs the MFMA work of a K step: the packed fp4 conversion
+// at unit scale gives the exact fp16 pairs [e0,e1], [e2,e3], [e4,e5], [e6,e7]
+// (one per byte, low nibble first), one v_perm_b32 per pair regroups them
+// into the operand order of mx4_f16x8, and the packed multiply by [s, s]
+// rounds the exact product once: the same operands as mx4_f16x8, with fewer
+// instructions.  (Beside the MFMA work of wider tiles the table decode of
+// mx4_f16x8 measured faster.)
+__device__ __forceinline__ f16x8_t mx4_f16x8_cvt(uint32_t w, f16x2_t s2) {
+  constexpr uint32_t kLo = 0x05040100u, kHi = 0x07060302u;  // [src1, src0] low / high halves
+  const uint32_t p01 = e2m1_pair<0>(w), p23 = e2m1_pair<1>(w);
+  const uint32_t p45 = e2m1_pair<2>(w), p67 = e2m1_pair<3>(w);
+  const f16x2_t a = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(p45, p01, kLo)) * s2;
+  const f16x2_t b = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(p45, p01, kHi)) * s2;
+  const f16x2_t c = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(p67, p23, kLo)) * s2;
+  const f16x2_t d = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(p67, p23, kHi)) * s2;
+  f16x8_t r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
+// int4 decode, fp16 offset form (the down GEMV): 16-bit halves 0x64 0e = the
+// exact fp16 value 1024 + e, in the pair order of q4_bf16_pairs.
+__device__ __forceinline__ Q4Pairs q4_f16_pairs(uint32_t w) { return q4_pairs_with(w, 0x64646464u); }
+
+__device__ __forceinline__ float half_bits_to_f32(uint32_t v) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)v);
+}
+
+// ue8m0 group exponent e -> 2^(e - 127) in fp32 (the GEMV's MXFP4 scale):
+// e << 23 for 1 <= e <= 254, 2^-127 (an fp32 subnormal) for e = 0, NaN for
+// e = 255.  Exact for every e.
+__device__ __forceinline__ float e8m0_f32(uint32_t e) {
+  return __uint_as_float(e == 0 ? 0x00400000u : e == 255 ? 0x7FC00000u : e << 23);
+}
+
 // Position, within an aligned block of 8, at which element i is stored in the
 // MFMA kernels' fp16 activation buffers (inverse of the order 0,4,1,5,2,6,3,7).
 __device__ __forceinline__ int perm8_pos(int i) { return ((i & 3) << 1) | (i >> 2); }

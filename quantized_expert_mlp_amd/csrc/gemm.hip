@@ -168,55 +168,6 @@ __device__ __forceinline__ bool tile_of(const Buckets& b, const GemmArgs& a, Til
   return true;
 }
 
-// MXFP4 operands of one packed word for one-subtile tiles, where the decode
-// VALU outweighs the MFMA work of a K step: gfx950's packed fp4 conversion at
-// unit scale gives the exact fp16 pairs [e0,e1], [e2,e3], [e4,e5], [e6,e7]
-// (one per byte, low nibble first), one v_perm_b32 per pair regroups them
-// into the operand order of mx4_f16x8, and the packed multiply by [s, s]
-// rounds the exact product once: the same operands as mx4_f16x8, with fewer
-// instructions.  (Beside the MFMA work of wider tiles the table decode of
-// mx4_f16x8 measured faster.)
-__device__ __forceinline__ f16x8_t mx4_f16x8_cvt(uint32_t w, f16x2_t s2) {
-  constexpr uint32_t kLo = 0x05040100u, kHi = 0x07060302u;  // [src1, src0] low / high halves
-  const uint32_t p01 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0));
-  const uint32_t p23 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1));
-  const uint32_t p45 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2));
-  const uint32_t p67 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3));
-  const f16x2_t a = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(p45, p01, kLo)) * s2;
-  const f16x2_t b = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(p45, p01, kHi)) * s2;
-  const f16x2_t c = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(p67, p23, kLo)) * s2;
-  const f16x2_t d = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(p67, p23, kHi)) * s2;
-  f16x8_t r;
-  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
-  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
-  return r;
-}
-
-// int4 operands of one packed word for one-subtile tiles.  The word's bytes
-// are reordered to (b0, b2, b1, b3), so its low nibbles read e0, e4, e2, e6
-// and its high nibbles e1, e5, e3, e7.  A byte 0000nnnn read as fp8 e4m3 is
-// n * 2^-9 exactly (n < 8 as a subnormal), so gfx950's packed fp8 conversion
-// at scale 2^9 turns each half of the masked word into an exact fp16 pair of
-// nibbles in the operand order ([e0,e4], [e2,e6] / [e1,e5], [e3,e7]).  One
-// fused multiply-add n * s + (-8 s) - with -8 s exact in fp16 - rounds
-// (n - 8) * s once: the same operands as q4_f16x8, in fewer instructions.
-__device__ __forceinline__ f16x8_t q4_f16x8_cvt(uint32_t w, f16x2_t s2, f16x2_t m8s2) {
-  const uint32_t r = __builtin_amdgcn_perm(w, w, 0x03010200u);  // bytes b0, b2, b1, b3
-  const uint32_t lo = r & 0x0F0F0F0Fu, hi = (r >> 4) & 0x0F0F0F0Fu;
-  const f16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, false);  // [e0, e4]
-  const f16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, true);   // [e2, e6]
-  const f16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 512.0f, false);  // [e1, e5]
-  const f16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 512.0f, true);   // [e3, e7]
-  const f16x2_t ra = __builtin_elementwise_fma(a, s2, m8s2);
-  const f16x2_t rb = __builtin_elementwise_fma(b, s2, m8s2);
-  const f16x2_t rc = __builtin_elementwise_fma(c, s2, m8s2);
-  const f16x2_t rd = __builtin_elementwise_fma(d, s2, m8s2);
-  f16x8_t o;
-  o[0] = ra[0]; o[1] = ra[1]; o[2] = rb[0]; o[3] = rb[1];
-  o[4] = rc[0]; o[5] = rc[1]; o[6] = rd[0]; o[7] = rd[1];
-  return o;
-}
-
 template <int MS>
 constexpr int a_chunks() {
   return (MS * 32 + kChunkRows - 1) / kChunkRows;

@@ -64,10 +64,6 @@ __device__ __forceinline__ uint4 load_w16(const void* p) {
 #endif
 }
 
-__device__ __forceinline__ float half_bits_to_f32(uint32_t v) {
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)v);
-}
-
 // Re-pair one aligned block of 8 16-bit activations (natural pairs n0..n3 =
 // [x0,x1],[x2,x3],[x4,x5],[x6,x7]) into the operand order of the decode
 // ([x0,x4],[x1,x5],[x2,x6],[x3,x7]).
@@ -118,21 +114,13 @@ __device__ __forceinline__ float dot_group_f16(uint4 w, const uint32_t* a) {
   float s = 0.f;
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
-    const Q4Pairs p = q4_pairs_with(ws[d], 0x64646464u);
+    const Q4Pairs p = q4_f16_pairs(ws[d]);
     s = dot2_f16(p.p0, a[4 * d + 0], s);
     s = dot2_f16(p.p1, a[4 * d + 1], s);
     s = dot2_f16(p.p2, a[4 * d + 2], s);
     s = dot2_f16(p.p3, a[4 * d + 3], s);
   }
   return s;
-}
-
-// The two e2m1 codes of byte B of w (low nibble first) as an fp16 pair, by
-// gfx950's packed fp4 conversion with unit scale: every e2m1 value is an
-// fp16 number, so the pair is exact.
-template <int B>
-__device__ __forceinline__ uint32_t e2m1_pair(uint32_t w) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, B));
 }
 
 // sum_i e2m1(e_i) a_i over one 32-input group (4 packed words) of MXFP4
@@ -169,11 +157,7 @@ struct GemvFmt<kFmtInt4> {
 template <>
 struct GemvFmt<kFmtMxfp4> {
   using S = uint8_t;  // ue8m0 exponent
-  // 2^(e - 127) in fp32: e << 23 for 1 <= e <= 254, 2^-127 (subnormal) for
-  // e = 0, NaN for e = 255.
-  static __device__ __forceinline__ float scale(uint32_t e) {
-    return __uint_as_float(e == 0 ? 0x00400000u : e == 255 ? 0x7FC00000u : e << 23);
-  }
+  static __device__ __forceinline__ float scale(uint32_t e) { return e8m0_f32(e); }
 };
 
 struct BucketView {

@@ -181,8 +181,17 @@ hipError_t launch_gemm_down(const Buckets& b, int max_tiles, const uint16_t* h16
                             const uint8_t* dq, const void* ds, const float* w, float* y,
                             const SharedGemm* shared, bool tiled, int fmt, const Launch& L);
 
-// mode 0: int4 GEMV decode; 1: int4 MFMA operand; 2: MXFP4 MFMA operand (s
-// holds ue8m0 bytes).
+// Decoders the debug hook runs (s holds fp16 bits for the int4 ones, ue8m0
+// bytes for the MXFP4 ones).
+enum DebugDecoder : int {
+  kDebugQ4GemvGateUp = 0,  // q4_bf16_pairs (gate/up GEMV), exact weight
+  kDebugQ4Mfma = 1,        // q4_f16x8 (MFMA tiles of 2-4 row subtiles), fp16 operand
+  kDebugQ4MfmaCvt = 2,     // q4_f16x8_cvt (one-subtile MFMA tiles), fp16 operand
+  kDebugQ4GemvDown = 3,    // q4_f16_pairs (down GEMV), exact weight
+  kDebugMx4Gemv = 4,       // e2m1_pair x e8m0_f32 (both GEMVs), exact weight
+  kDebugMx4Mfma = 5,       // mx4_f16x8 (MFMA tiles of 2-4 row subtiles), fp16 operand
+  kDebugMx4MfmaCvt = 6,    // mx4_f16x8_cvt (one-subtile MFMA tiles), fp16 operand
+};
 hipError_t launch_debug_dequant(const uint8_t* q, const void* s, int N, int K, int mode,
                                 float* out, const Launch& L);
 

@@ -103,8 +103,13 @@ hipError_t launch_pack_weights(const uint8_t* sq, const void* ss, int E, int N, 
   return hipGetLastError();
 }
 
-// Decode one plane with the kernels' own routines.  One thread per packed
-// 32-bit word (8 nibbles).
+// Decode one plane with the kernels' own routines (the ones their main loops
+// call), one thread per packed 32-bit word (8 nibbles), and write what each
+// decoder stands for as fp32: the GEMV decoders' exact weight (their offset
+// form and group scale undone exactly in fp32), the MFMA decoders' fp16
+// operand widened.  The decoders' output orders are undone here: pairs
+// (j, j+4) for the offset forms, natural pairs for e2m1_pair, the order
+// 0,4,1,5,2,6,3,7 for the MFMA operands.
 __global__ __launch_bounds__(256) void debug_dequant_kernel(const uint8_t* __restrict__ q,
                                                             const void* __restrict__ s,
                                                             int N, int K, int mode,
@@ -117,33 +122,49 @@ __global__ __launch_bounds__(256) void debug_dequant_kernel(const uint8_t* __res
   const uint32_t wv = reinterpret_cast<const uint32_t*>(q)[i];
   const int64_t g = n * (K / 32) + kk0 / 32;
   float* o = out + n * K + kk0;
-  if (mode == 2) {
-    const _Float16 sh = e8m0_f16(static_cast<const uint8_t*>(s)[g]);
+  if (mode >= kDebugMx4Gemv) {  // MXFP4: ue8m0 scale bytes
+    const uint32_t e = static_cast<const uint8_t*>(s)[g];
+    if (mode == kDebugMx4Gemv) {
+      const float sc = e8m0_f32(e);
+      const uint32_t pr[4] = {e2m1_pair<0>(wv), e2m1_pair<1>(wv), e2m1_pair<2>(wv),
+                              e2m1_pair<3>(wv)};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        o[2 * j] = half_bits_to_f32(pr[j] & 0xFFFFu) * sc;
+        o[2 * j + 1] = half_bits_to_f32(pr[j] >> 16) * sc;
+      }
+      return;
+    }
+    const _Float16 sh = e8m0_f16(e);
     const f16x2_t s2 = {sh, sh};
-    const f16x8_t v = mx4_f16x8(wv, s2);
+    const f16x8_t v = mode == kDebugMx4Mfma ? mx4_f16x8(wv, s2) : mx4_f16x8_cvt(wv, s2);
 #pragma unroll
     for (int j = 0; j < 8; ++j) o[j] = (float)v[perm8_pos(j)];
     return;
   }
   const uint16_t sb = static_cast<const uint16_t*>(s)[g];
-  if (mode == 0) {
-    // bf16 offset form: pair j holds elements j and j+4 as 128 + nibble.
-    const Q4Pairs p = q4_bf16_pairs(wv);
-    const float sc = (float)__builtin_bit_cast(_Float16, sb);
+  if (mode == kDebugQ4GemvGateUp || mode == kDebugQ4GemvDown) {
+    // offset forms: pair j holds elements j and j+4 as 128 + e (bf16) or
+    // 1024 + e (fp16)
+    const bool gu = mode == kDebugQ4GemvGateUp;
+    const Q4Pairs p = gu ? q4_bf16_pairs(wv) : q4_f16_pairs(wv);
+    const float sc = half_bits_to_f32(sb), off = gu ? 136.0f : 1032.0f;
     const uint32_t pr[4] = {p.p0, p.p1, p.p2, p.p3};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float lo = bf16_to_f32(pr[j] & 0xFFFF), hi = bf16_to_f32(pr[j] >> 16);
-      o[j] = (lo - 136.0f) * sc;
-      o[j + 4] = (hi - 136.0f) * sc;
+      const uint32_t lo = pr[j] & 0xFFFFu, hi = pr[j] >> 16;
+      o[j] = ((gu ? bf16_to_f32(lo) : half_bits_to_f32(lo)) - off) * sc;
+      o[j + 4] = ((gu ? bf16_to_f32(hi) : half_bits_to_f32(hi)) - off) * sc;
     }
-  } else {
-    const _Float16 sh = __builtin_bit_cast(_Float16, sb);
-    const f16x2_t s2 = {sh, sh};
-    const f16x8_t v = q4_f16x8(wv, s2);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) o[j] = (float)v[perm8_pos(j)];
+    return;
   }
+  const _Float16 sh = __builtin_bit_cast(_Float16, sb);
+  const f16x2_t s2 = {sh, sh};
+  // the one-subtile tiles' -8 s, formed as the GEMM forms it
+  const f16x2_t m8s2 = s2 * f16x2_t{(_Float16)-8.0f, (_Float16)-8.0f};
+  const f16x8_t v = mode == kDebugQ4Mfma ? q4_f16x8(wv, s2) : q4_f16x8_cvt(wv, s2, m8s2);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o[j] = (float)v[perm8_pos(j)];
 }
 
 hipError_t launch_debug_dequant(const uint8_t* q, const void* s, int N, int K, int mode,

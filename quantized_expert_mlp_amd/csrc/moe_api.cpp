@@ -271,14 +271,26 @@ int moe_pack_weights(moe_q4 src, int32_t E, int32_t N, int32_t K, int32_t format
                                              moe::Launch{reinterpret_cast<hipStream_t>(stream)}));
 }
 
+size_t moe_permute_workspace_bytes(int32_t T, int32_t k, int32_t E) {
+  if (T < 1 || k < 1 || E < 1 || E > 256 || (int64_t)T * k >= (int64_t)1 << 31) return 0;
+  const int64_t slots = (int64_t)T * k;
+  if (slots <= moe::kPermuteOneBlockMax) return 0;
+  return sizeof(int32_t) * (size_t)moe::permute_scratch_words(slots, E);
+}
+
 int moe_permute(const int32_t* idx, int32_t T, int32_t k, int32_t E, int32_t* off,
-                int32_t* sorted, int32_t* row_of, moe_stream_t stream) {
+                int32_t* sorted, int32_t* row_of, void* ws, size_t ws_bytes,
+                moe_stream_t stream) {
   if (!idx || !off || !sorted || !row_of || T < 1 || k < 1 || E < 1) return MOE_ERR_INVALID_ARG;
-  if (!aligned(idx, 4) || !aligned(off, 4) || !aligned(sorted, 4) || !aligned(row_of, 4))
+  if (!aligned(idx, 4) || !aligned(off, 4) || !aligned(sorted, 4) || !aligned(row_of, 4) ||
+      !aligned(ws, kAlign))
     return MOE_ERR_INVALID_ARG;
   if (E > 256) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)T * k >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
-  return hip_status(moe::launch_permute(idx, T, k, E, off, sorted, row_of, nullptr, nullptr,
+  const size_t need = moe_permute_workspace_bytes(T, k, E);
+  if (ws_bytes < need || (need && !ws)) return MOE_ERR_WORKSPACE;
+  return hip_status(moe::launch_permute(idx, T, k, E, off, sorted, row_of, nullptr,
+                                        need ? static_cast<int32_t*>(ws) : nullptr,
                                         moe::Launch{reinterpret_cast<hipStream_t>(stream)}));
 }
 
@@ -288,7 +300,7 @@ int moe_expert_mlp(const moe_shape* sh, const uint16_t* x, const int32_t* off,
   int rc = check_shape(sh);
   if (rc != MOE_OK) return rc;
   if (!x || !off || !sorted || !w || !y || !ws) return MOE_ERR_INVALID_ARG;
-  if (!aligned(x, 16) || !aligned(y, 4) || !aligned(w, 4) || !aligned(ws, kAlign))
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(w, 4) || !aligned(ws, kAlign))
     return MOE_ERR_INVALID_ARG;
   if (!plane_ok(gate) || !plane_ok(up) || !plane_ok(down)) return MOE_ERR_INVALID_ARG;
   bool gemm = false;
@@ -313,7 +325,7 @@ static int layer_impl(const moe_shape* sh, const uint16_t* x, const float* logit
   if (rc != MOE_OK) return rc;
   if (!x || !y || !ws) return MOE_ERR_INVALID_ARG;
   if ((logits == nullptr) == (w_router == nullptr)) return MOE_ERR_INVALID_ARG;
-  if (!aligned(x, 16) || !aligned(y, 4) || !aligned(ws, kAlign)) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ws, kAlign)) return MOE_ERR_INVALID_ARG;
   if (logits && !aligned(logits, 4)) return MOE_ERR_INVALID_ARG;
   if (w_router && !aligned(w_router, 16)) return MOE_ERR_INVALID_ARG;
   if ((idx_out && !aligned(idx_out, 4)) || (w_out && !aligned(w_out, 4)) ||
@@ -450,15 +462,18 @@ int moe_layer_profiled(const moe_shape* sh, const uint16_t* x, const float* logi
 
 int moe_debug_dequant_int4(moe_q4 plane, int32_t N, int32_t K, int32_t mode, float* out,
                            moe_stream_t stream) {
-  if (!plane_ok(plane) || !out || N < 1 || K < 32 || K % 32 || (mode != 0 && mode != 1))
+  if (!plane_ok(plane) || !out || N < 1 || K < 32 || K % 32 || mode < 0 || mode > 3)
     return MOE_ERR_INVALID_ARG;
   return hip_status(moe::launch_debug_dequant(plane.q, plane.s, N, K, mode, out,
                                               moe::Launch{reinterpret_cast<hipStream_t>(stream)}));
 }
 
-int moe_debug_dequant_mxfp4(moe_q4 plane, int32_t N, int32_t K, float* out, moe_stream_t stream) {
-  if (!plane_ok(plane) || !out || N < 1 || K < 32 || K % 32) return MOE_ERR_INVALID_ARG;
-  return hip_status(moe::launch_debug_dequant(plane.q, plane.s, N, K, 2, out,
+int moe_debug_dequant_mxfp4(moe_q4 plane, int32_t N, int32_t K, int32_t mode, float* out,
+                            moe_stream_t stream) {
+  if (!plane_ok(plane) || !out || N < 1 || K < 32 || K % 32 || mode < 0 || mode > 2)
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_debug_dequant(plane.q, plane.s, N, K, moe::kDebugMx4Gemv + mode,
+                                              out,
                                               moe::Launch{reinterpret_cast<hipStream_t>(stream)}));
 }
 

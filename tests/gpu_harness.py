@@ -87,6 +87,32 @@ def tiled_reference(q: np.ndarray, s: np.ndarray):
     return np.ascontiguousarray(qt).reshape(E, N, Kh), np.ascontiguousarray(st).reshape(E, N, K // 32)
 
 
+# Canary words written past the end of every output and the workspace: a
+# kernel that stores past its buffer changes them.
+CANARY_WORDS = 64
+CANARY_U32 = np.uint32(0x7FA5C3E1)  # a NaN payload no kernel writes
+
+
+class Canaried:
+    """A device buffer of `shape` (a view) followed by CANARY_WORDS canary
+    words; check() asserts the canary is intact."""
+
+    def __init__(self, shape, dtype, fill, what):
+        n = int(np.prod(shape))
+        itemsize = torch.empty((), dtype=dtype).element_size()
+        extra = CANARY_WORDS * 4 // itemsize
+        assert n * itemsize % 4 == 0
+        self.full = torch.empty(n + extra, dtype=dtype, device="cuda")
+        self.full.view(torch.int32)[n * itemsize // 4:].fill_(int(CANARY_U32.view(np.int32)))
+        self.view = self.full[:n].view(*shape)
+        self.view.fill_(fill)
+        self.n, self.itemsize, self.what = n, itemsize, what
+
+    def check(self):
+        tail = host(self.full.view(torch.int32)[self.n * self.itemsize // 4:]).view(np.uint32)
+        assert np.all(tail == CANARY_U32), "%s: write past the end of the buffer" % self.what
+
+
 def run_layer(d: DeviceLayer, logits=None, use_router=False, path=moe.MOE_PATH_AUTO,
               route_scale=1.0, ws_extra=0):
     """moe_layer through the C ABI.  logits: host array to feed (given logits),
@@ -98,21 +124,23 @@ def run_layer(d: DeviceLayer, logits=None, use_router=False, path=moe.MOE_PATH_A
                         route_scale=route_scale, path=path, layout=d.layout, format=d.format)
     nbytes = moe.moe_workspace_bytes(sh)
     assert nbytes > 0
-    ws = torch.empty(nbytes + ws_extra, dtype=torch.uint8, device="cuda")
-    ws.fill_(0xFF)  # poison: nothing may depend on the workspace's prior contents
-    y = torch.full((T, wl.H), float("nan"), dtype=torch.float32, device="cuda")
-    idx = torch.full((T, wl.k), -7, dtype=torch.int32, device="cuda")
-    w = torch.full((T, wl.k), float("nan"), dtype=torch.float32, device="cuda")
-    lo = torch.full((T, wl.E), float("nan"), dtype=torch.float32, device="cuda")
+    # poison: nothing may depend on the workspace's prior contents
+    ws = Canaried((nbytes + ws_extra,), torch.uint8, 0xFF, "workspace")
+    y = Canaried((T, wl.H), torch.float32, float("nan"), "y")
+    idx = Canaried((T, wl.k), torch.int32, -7, "idx")
+    w = Canaried((T, wl.k), torch.float32, float("nan"), "w")
+    lo = Canaried((T, wl.E), torch.float32, float("nan"), "logits_out")
     if use_router:
         lg, wr = None, d.w_router
     else:
         lg = dev(logits.astype(np.float32)) if logits is not None else d.logits
         wr = None
     moe.moe_layer(sh, d.x, lg, wr, d.planes["gate"], d.planes["up"], d.planes["down"], d.shared,
-                  d.shared_gate, y, idx, w, lo, ws, nbytes)
+                  d.shared_gate, y.view, idx.view, w.view, lo.view, ws.view, nbytes)
     torch.cuda.synchronize()
-    return host(y), host(idx), host(w), host(lo)
+    for c in (ws, y, idx, w, lo):
+        c.check()
+    return host(y.view), host(idx.view), host(w.view), host(lo.view)
 
 
 def y_errors(y: np.ndarray, y_ref: np.ndarray) -> np.ndarray:

@@ -82,10 +82,25 @@ def test_router_topk_rejects(L):
 
 def test_permute_rejects(L):
     f = L.moe_permute
-    assert f(None, 4, 2, 8, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
-    assert f(FAKE, 4, 2, 8, None, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
-    assert f(FAKE, 0, 2, 8, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
-    assert f(FAKE, 4, 2, 257, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert f(None, 4, 2, 8, FAKE, FAKE, FAKE, None, 0, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(FAKE, 4, 2, 8, None, FAKE, FAKE, None, 0, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(FAKE, 0, 2, 8, FAKE, FAKE, FAKE, None, 0, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(FAKE, 4, 2, 257, FAKE, FAKE, FAKE, None, 0, None) == moe.MOE_ERR_UNSUPPORTED
+    # above 4096 slots the multi-workgroup permutation needs its scratch
+    need = moe.moe_permute_workspace_bytes(2048, 8, 256)
+    assert need == 4 * 16 * 256
+    assert f(FAKE, 2048, 8, 256, FAKE, FAKE, FAKE, None, 0, None) == moe.MOE_ERR_WORKSPACE
+    assert f(FAKE, 2048, 8, 256, FAKE, FAKE, FAKE, FAKE, need - 1, None) == moe.MOE_ERR_WORKSPACE
+    assert f(FAKE, 2048, 8, 256, FAKE, FAKE, FAKE, FAKE + 64, need, None) == \
+        moe.MOE_ERR_INVALID_ARG                                          # misaligned scratch
+
+
+def test_permute_workspace_bytes(L):
+    assert moe.moe_permute_workspace_bytes(512, 8, 256) == 0            # 4096 slots: one workgroup
+    assert moe.moe_permute_workspace_bytes(513, 8, 256) == 4 * 5 * 256
+    assert moe.moe_permute_workspace_bytes(700, 8, 32) == 4 * 6 * 32
+    for bad in [(0, 8, 256), (4, 0, 8), (4, 2, 0), (4, 2, 257)]:
+        assert moe.moe_permute_workspace_bytes(*bad) == 0, bad
 
 
 def _q(ok=True):
@@ -108,6 +123,8 @@ def test_layer_rejects(L):
     assert call(x=FAKE + 2) == moe.MOE_ERR_INVALID_ARG             # misaligned activations
     assert call(gate=_q(False)) == moe.MOE_ERR_INVALID_ARG          # misaligned plane
     assert call(ws=FAKE + 64) == moe.MOE_ERR_INVALID_ARG            # misaligned workspace
+    assert call(y=FAKE + 4) == moe.MOE_ERR_INVALID_ARG              # y cleared with 16-byte stores
+    assert call(y=FAKE + 8, shape=_shape(path=moe.MOE_PATH_GEMV)) == moe.MOE_ERR_INVALID_ARG
     assert call(ws_bytes=ws_need - 1) == moe.MOE_ERR_WORKSPACE
     assert call(shape=_shape(SI=64)) == moe.MOE_ERR_INVALID_ARG     # SI without shared planes
     assert call(shape=_shape(E=512, k=2)) == moe.MOE_ERR_UNSUPPORTED
@@ -142,6 +159,7 @@ def test_expert_mlp_rejects(L):
                          _q(), _q(), _q(), kw.get("y", FAKE), FAKE, kw.get("ws_bytes", need), None]
     assert f(*args(x=None)) == moe.MOE_ERR_INVALID_ARG
     assert f(*args(y=None)) == moe.MOE_ERR_INVALID_ARG
+    assert f(*args(y=FAKE + 4)) == moe.MOE_ERR_INVALID_ARG
     assert f(*args(ws_bytes=0)) == moe.MOE_ERR_WORKSPACE
     assert f(*args(shape=_shape(path=moe.MOE_PATH_GEMV, H=16384))) == moe.MOE_ERR_UNSUPPORTED
 
@@ -195,14 +213,16 @@ def test_pack_weights_rejects(L):
 def test_debug_dequant_rejects(L):
     f = L.moe_debug_dequant_int4
     assert f(_q(), 4, 48, 0, FAKE, None) == moe.MOE_ERR_INVALID_ARG   # K % 32
-    assert f(_q(), 4, 64, 2, FAKE, None) == moe.MOE_ERR_INVALID_ARG   # mode
+    assert f(_q(), 4, 64, 4, FAKE, None) == moe.MOE_ERR_INVALID_ARG   # mode
+    assert f(_q(), 4, 64, -1, FAKE, None) == moe.MOE_ERR_INVALID_ARG
     assert f(_q(), 0, 64, 0, FAKE, None) == moe.MOE_ERR_INVALID_ARG
     assert f(_q(False), 4, 64, 0, FAKE, None) == moe.MOE_ERR_INVALID_ARG
     g = L.moe_debug_dequant_mxfp4
-    assert g(_q(), 4, 48, FAKE, None) == moe.MOE_ERR_INVALID_ARG      # K % 32
-    assert g(_q(), 0, 64, FAKE, None) == moe.MOE_ERR_INVALID_ARG
-    assert g(_q(False), 4, 64, FAKE, None) == moe.MOE_ERR_INVALID_ARG
-    assert g(_q(), 4, 64, None, None) == moe.MOE_ERR_INVALID_ARG
+    assert g(_q(), 4, 48, 0, FAKE, None) == moe.MOE_ERR_INVALID_ARG   # K % 32
+    assert g(_q(), 4, 64, 3, FAKE, None) == moe.MOE_ERR_INVALID_ARG   # mode
+    assert g(_q(), 0, 64, 1, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert g(_q(False), 4, 64, 1, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert g(_q(), 4, 64, 1, None, None) == moe.MOE_ERR_INVALID_ARG
 
 
 def test_product_path_has_no_oracle_dependency():

@@ -1,7 +1,8 @@
 """GPU tests of MXFP4 expert weights (e2m1 nibbles, one ue8m0 exponent per 32
-inputs): the MFMA kernels' decode against the oracle's exact weights rounded
-to fp16 (bit-exact), and the whole layer on MXFP4 planes against the CPU
-oracle at mid sizes on both expert paths and at every full workload size."""
+inputs): the MFMA decoders at the ends of the exponent range (their bit-exact
+pins over every exponent are in test_gpu_decoders.py), and the whole layer on
+MXFP4 planes against the CPU oracle at mid sizes on both expert paths and at
+every full workload size."""
 import numpy as np
 import pytest
 import torch
@@ -22,45 +23,32 @@ def _gpu():
     moe.lib()
 
 
-def _decode(q, s):
+def _decode(q, s, mode):
     N, K = q.shape[0], q.shape[1] * 2
     out = torch.full((N, K), float("nan"), dtype=torch.float32, device="cuda")
-    moe.moe_debug_dequant_mxfp4((dev(q), dev(s)), N, K, out)
+    moe.moe_debug_dequant_mxfp4((dev(q), dev(s)), N, K, out, mode=mode)
     torch.cuda.synchronize()
     return host(out)
 
 
-@pytest.mark.parametrize("N,K", [(8, 64), (64, 256), (3, 6144), (96, 1408)])
-def test_debug_dequant_mxfp4_bit_exact(N, K):
-    """Over the exponents whose scale is an fp16 number (103..142), the operand
-    is the exact weight rounded once to fp16 (nearest even)."""
-    say("mxfp4 dequant N=%d K=%d" % (N, K))
-    rng = np.random.default_rng([N, K, 4])
-    q = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
-    s = rng.integers(103, 143, (N, K // 32), dtype=np.uint8)
-    s[0, : min(2, K // 32)] = [103, 142][: min(2, K // 32)]
-    with np.errstate(over="ignore"):  # e >= 141 overflows fp16 for the larger codes
-        want = oracle.dequant(q, s, "mxfp4").astype(np.float16).astype(np.float32)
-    got = _decode(q, s)
-    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
-
-
 def test_debug_dequant_mxfp4_scale_range_ends():
     """For e <= 99 every weight, |e2m1| * 2^(e - 127) <= 6 * 2^-28, rounds to a
-    signed zero in fp16 (the kernel's scale is zero there); e = 255 is NaN (the
-    MX format's NaN scale) for every element of its group."""
+    signed zero in fp16 (the MFMA decoders' scale is zero there); e = 255 is
+    NaN (the MX format's NaN scale) for every element of its group."""
     rng = np.random.default_rng(5)
     N, K = 4, 128
     q = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
     s = np.array([[0, 1, 50, 99]] * N, dtype=np.uint8)
     s[3, 2] = 255
     ref = oracle.dequant(q, s, "mxfp4")
-    got = _decode(q, s)
     nan = np.isnan(ref)
-    assert np.array_equal(np.isnan(got), nan) and nan[3, 64:96].all() and nan.sum() == 32
+    assert nan[3, 64:96].all() and nan.sum() == 32
     want = ref.astype(np.float16).astype(np.float32)
-    assert np.array_equal(got[~nan].view(np.uint32), want[~nan].view(np.uint32))
-    assert np.all(got[~nan] == 0.0)
+    for mode in (1, 2):
+        got = _decode(q, s, mode)
+        assert np.array_equal(np.isnan(got), nan)
+        assert np.array_equal(got[~nan].view(np.uint32), want[~nan].view(np.uint32))
+        assert np.all(got[~nan] == 0.0)
 
 
 @pytest.mark.parametrize("path", [moe.MOE_PATH_GEMV, moe.MOE_PATH_GEMM])

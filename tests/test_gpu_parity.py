@@ -13,7 +13,7 @@ import torch
 import moe_synth as S
 import oracle
 import quantized_expert_mlp_amd as moe
-from gpu_harness import (DeviceLayer, assert_w_close, assert_y_close, dev, host,
+from gpu_harness import (Canaried, DeviceLayer, assert_w_close, assert_y_close, dev, host,
                          logits_bound, run_layer, say, valid_topk)
 
 pytestmark = pytest.mark.gpu
@@ -26,23 +26,6 @@ def _gpu():
     moe.lib()
     oracle.lib()
     oracle.set_threads(16)
-
-
-# ---------------------------------------------------------------- decode --
-
-@pytest.mark.parametrize("N,K", [(8, 64), (64, 256), (3, 6144), (96, 1408)])
-def test_debug_dequant_bit_exact(N, K):
-    say("dequant N=%d K=%d" % (N, K))
-    q, s = S.draw_plane(N, K, np.random.default_rng(N * 7 + K))
-    ref = oracle.dequant(q, s)
-    dq, ds = dev(q), dev(s)
-    for mode in (0, 1):
-        out = torch.empty((N, K), dtype=torch.float32, device="cuda")
-        moe.moe_debug_dequant_int4((dq, ds), N, K, mode, out)
-        torch.cuda.synchronize()
-        got = host(out)
-        want = ref.astype(np.float32) if mode == 0 else ref.astype(np.float16).astype(np.float32)
-        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), "mode %d" % mode
 
 
 # ---------------------------------------------------------------- router --
@@ -71,9 +54,27 @@ def test_router_topk(T, E, k):
 
 # ----------------------------------------------------------- permutation --
 
+def _permute_dev(idx, E):
+    """moe_permute through the C ABI with canaried outputs and, above 4096
+    slots, its scratch (the multi-workgroup path)."""
+    T, k = idx.shape
+    off = Canaried((E + 1,), torch.int32, -5, "off")
+    srt = Canaried((T * k,), torch.int32, -5, "sorted")
+    row = Canaried((T * k,), torch.int32, -5, "row_of")
+    nb = moe.moe_permute_workspace_bytes(T, k, E)
+    ws = Canaried((max(nb, 4),), torch.uint8, 0xEE, "permute scratch")
+    moe.moe_permute(dev(idx), T, k, E, off.view, srt.view, row.view, ws.view if nb else None, nb)
+    torch.cuda.synchronize()
+    for c in (off, srt, row, ws):
+        c.check()
+    return host(off.view), host(srt.view), host(row.view), nb
+
+
 @pytest.mark.parametrize("T,k,E", [(4, 2, 8), (1, 8, 256), (32, 8, 128), (512, 4, 60),
-                                   (2048, 8, 256), (1500, 3, 7), (37, 1, 256)])
+                                   (2048, 8, 256), (1500, 3, 7), (37, 1, 256), (700, 8, 32)])
 def test_permute(T, k, E):
+    """Bit-exact against the oracle; 2048 x 8 (16384 slots), 1500 x 3 and
+    700 x 8 run the multi-workgroup path with the caller's scratch."""
     say("permute T=%d k=%d E=%d" % (T, k, E))
     rng = np.random.default_rng(T + 31 * k + E)
     if E >= k:
@@ -81,37 +82,31 @@ def test_permute(T, k, E):
     else:
         idx = rng.integers(0, E, (T, k)).astype(np.int32)
     off_r, srt_r, row_r = oracle.permute(idx, E)
-    off = torch.full((E + 1,), -5, dtype=torch.int32, device="cuda")
-    srt = torch.full((T * k,), -5, dtype=torch.int32, device="cuda")
-    row = torch.full((T * k,), -5, dtype=torch.int32, device="cuda")
-    moe.moe_permute(dev(idx), T, k, E, off, srt, row)
-    torch.cuda.synchronize()
-    assert np.array_equal(host(off), off_r)
-    assert np.array_equal(host(srt), srt_r)
-    assert np.array_equal(host(row), row_r)
+    off, srt, row, nb = _permute_dev(idx, E)
+    assert (nb > 0) == (T * k > 4096)
+    assert np.array_equal(off, off_r)
+    assert np.array_equal(srt, srt_r)
+    assert np.array_equal(row, row_r)
 
 
-def test_permute_drops_out_of_range_picks():
-    T, k, E = 300, 4, 16
+@pytest.mark.parametrize("T,k,E", [(300, 4, 16), (2048, 8, 256)])
+def test_permute_drops_out_of_range_picks(T, k, E):
+    """Picks outside [0, E) (top-p's -1, or past the experts) against the
+    oracle's dropped-pick rule, on the one-workgroup and the multi-workgroup
+    permutation: off bit-exact, the valid slots' rows bit-exact, row_of -1 for
+    the dropped ones."""
     rng = np.random.default_rng(5)
     idx = rng.integers(0, E, (T, k)).astype(np.int32)
     bad = rng.random((T, k)) < 0.1
     idx[bad] = np.where(rng.random(bad.sum()) < 0.5, -1, E + 3)
-    flat = idx.ravel()
-    valid = (flat >= 0) & (flat < E)
-    off = torch.empty(E + 1, dtype=torch.int32, device="cuda")
-    srt = torch.full((T * k,), -5, dtype=torch.int32, device="cuda")
-    row = torch.full((T * k,), -5, dtype=torch.int32, device="cuda")
-    moe.moe_permute(dev(idx), T, k, E, off, srt, row)
-    torch.cuda.synchronize()
-    cnt = np.bincount(flat[valid], minlength=E)
-    assert np.array_equal(host(off), np.concatenate([[0], np.cumsum(cnt)]))
-    nval = int(valid.sum())
-    order = np.nonzero(valid)[0][np.argsort(flat[valid], kind="stable")]
-    assert np.array_equal(host(srt)[:nval], order)
-    r = host(row)
-    assert np.all(r[~valid] == -1)
-    assert np.array_equal(host(srt)[r[valid]], np.nonzero(valid)[0])
+    off_r, srt_r, row_r = oracle.permute(idx, E)
+    off, srt, row, _ = _permute_dev(idx, E)
+    nval = int(off_r[E])
+    assert nval < T * k
+    assert np.array_equal(off, off_r)
+    assert np.array_equal(srt[:nval], srt_r[:nval])
+    assert np.all(srt[nval:] == -5)  # nothing written past the valid slots
+    assert np.array_equal(row, row_r)
 
 
 # ------------------------------------------------------------ whole layer --
@@ -184,9 +179,39 @@ def test_expert_mlp_direct():
         assert_y_close(host(y), y_ref, "expert_mlp path %d" % path)
 
 
+@pytest.mark.parametrize("path", [moe.MOE_PATH_GEMV, moe.MOE_PATH_GEMM])
+def test_layer_large_activations(path):
+    """Activations over fp16's range (x ~ N(0, 1500^2), one entry in a
+    hundred at +-4e4..65280, the largest bf16 below fp16's overflow), with
+    scales of 6.2e-5..9e-5 so that the hidden row stays an fp16 number (at
+    most 2.7e4 here, over every expert and token): the
+    MFMA path's fp16 copy of x is exact there and both paths stay within the
+    bar of the oracle."""
+    wl = _mid("mid_large_x", 33, 96, 512, 8, 2, 192)
+    say("large activations path=%d" % path)
+    inp = S.make_layer_inputs(wl, seed=0)
+    rng = np.random.default_rng(33)
+    x = rng.standard_normal((wl.T, wl.H)).astype(np.float32) * 1500
+    big = rng.random((wl.T, wl.H)) < 0.01
+    x[big] = (rng.choice([-1.0, 1.0], int(big.sum())) *
+              rng.uniform(4e4, 65280.0, int(big.sum()))).astype(np.float32)
+    inp.x = S.f32_to_bf16_bits(np.clip(x, -65280.0, 65280.0))
+    assert np.abs(S.bf16_bits_to_f32(inp.x)).max() <= 65280.0
+    for p in S.PLANES:
+        q, s_ = inp.planes[p]
+        s_ = (rng.uniform(6.2e-5, 9e-5, s_.shape)).astype(np.float16).view(np.uint16)
+        inp.planes[p] = (q, s_)
+    d = DeviceLayer(inp)
+    y_ref, idx_ref, _ = oracle.layer(inp.x, inp.logits, wl.k, inp.planes)
+    assert np.all(np.isfinite(y_ref))
+    y, idx, _, _ = run_layer(d, path=path)
+    assert np.array_equal(idx, idx_ref)
+    assert_y_close(y, y_ref, "large activations path %d" % path)
+
+
 # ------------------------------------------------- full-size workloads --
 
-SAMPLE_ROWS = {"prefill_shared": 48, "prefill_skewed": 64}
+SAMPLE_ROWS = {"prefill_shared": 128, "prefill_skewed": 128}
 
 
 def _rows(wl):
