@@ -80,6 +80,8 @@ enum moe_status {
   MOE_ERR_UNSUPPORTED = 2, /* outside the shapes the kernels serve         */
   MOE_ERR_WORKSPACE = 3,   /* ws_bytes smaller than moe_workspace_bytes()  */
   MOE_ERR_HIP = 4,         /* a HIP launch reported an error               */
+  MOE_ERR_SCRATCH_LIMIT = 5, /* moe_layer_static: the shape needs more
+                                scratch than MOE_STATIC_SCRATCH_BYTES      */
 };
 
 /* Expert MLP path.  AUTO picks the streaming GEMV when the expected rows per
@@ -252,6 +254,32 @@ int moe_layer(const moe_shape *shape, const uint16_t *x, const float *logits,
               const float *w_router, moe_q4 gate, moe_q4 up, moe_q4 down, const moe_q4 *shared,
               const float *shared_gate, float *y, int32_t *idx_out, float *w_out,
               float *logits_out, void *ws, size_t ws_bytes, moe_stream_t stream);
+
+/*
+ * moe_layer for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same work with
+ * the same arguments except the workspace, which is a device array the
+ * library owns, MOE_STATIC_SCRATCH_BYTES (16 MiB) per GPU, held from the
+ * first call on that GPU until the process ends.  The call itself allocates
+ * and frees nothing.
+ *   Limit: shapes whose moe_workspace_bytes() exceeds the static scratch are
+ *          rejected with MOE_ERR_SCRATCH_LIMIT before anything is enqueued
+ *          (16 MiB serves decode and decode-batch sizes and prefill up to
+ *          about 500 tokens at H = 2048, I = 1408 with a 5632-wide shared
+ *          expert; not the 2048-token, 6144-wide prefill).
+ *   Sharing: every call on one GPU uses that GPU's one scratch array, which
+ *          keeps the last call's contents (nothing in it needs clearing: each
+ *          call writes what it reads).  Calls that overlap on one GPU (two
+ *          streams, or two host threads) race on it: the caller orders them.
+ *   stream : must belong to the current device (whose scratch is used).
+ * Errors: as moe_layer, plus SCRATCH_LIMIT; HIP if the scratch's device
+ *         address cannot be obtained.
+ */
+#define MOE_STATIC_SCRATCH_BYTES (16u << 20)
+int moe_layer_static(const moe_shape *shape, const uint16_t *x, const float *logits,
+                     const float *w_router, moe_q4 gate, moe_q4 up, moe_q4 down,
+                     const moe_q4 *shared, const float *shared_gate, float *y, int32_t *idx_out,
+                     float *w_out, float *logits_out, moe_stream_t stream);
 
 /*
  * The layer with its combine folded into the residual step (the dasLLAMA

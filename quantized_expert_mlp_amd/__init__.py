@@ -17,7 +17,9 @@ from typing import Optional, Sequence, Tuple
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmoe.so")
 
-MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+(MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP,
+ MOE_ERR_SCRATCH_LIMIT) = range(6)
+MOE_STATIC_SCRATCH_BYTES = 16 << 20
 MOE_PATH_AUTO, MOE_PATH_GEMV, MOE_PATH_GEMM = range(3)
 MOE_LAYOUT_ROWS, MOE_LAYOUT_TILED = range(2)
 MOE_FORMAT_INT4, MOE_FORMAT_MXFP4 = range(2)
@@ -28,7 +30,7 @@ EXPORTS = ("moe_router_topk", "moe_permute", "moe_permute_workspace_bytes", "moe
            "moe_layer",
            "moe_layer_profiled", "moe_pack_weights", "moe_workspace_bytes",
            "moe_status_string", "moe_debug_dequant_int4", "moe_debug_dequant_mxfp4",
-           "moe_layer_residual_rmsnorm")
+           "moe_layer_residual_rmsnorm", "moe_layer_static")
 STAGES = ("start", "logits", "topk", "permute", "activations", "gate_up", "shared_gate_up",
           "down", "shared_down")
 
@@ -73,6 +75,7 @@ def lib() -> ctypes.CDLL:
                                 ctypes.POINTER(moe_q4), P, P, P, P, P, P, ctypes.c_size_t, P]
         L.moe_layer_profiled.argtypes = L.moe_layer.argtypes + [ctypes.POINTER(ctypes.c_void_p),
                                                                 i32]
+        L.moe_layer_static.argtypes = L.moe_layer.argtypes[:13] + [P]
         L.moe_layer_residual_rmsnorm.argtypes = [
             ctypes.POINTER(moe_shape), P, P, P, moe_q4, moe_q4, moe_q4, ctypes.POINTER(moe_q4), P,
             P, P, ctypes.c_float, P, P, P, P, ctypes.c_size_t, P]
@@ -85,7 +88,8 @@ def lib() -> ctypes.CDLL:
         L.moe_pack_weights.argtypes = [moe_q4, i32, i32, i32, i32, moe_q4, P]
         for name in ("moe_router_topk", "moe_permute", "moe_expert_mlp", "moe_layer",
                      "moe_layer_profiled", "moe_pack_weights", "moe_debug_dequant_int4",
-                     "moe_debug_dequant_mxfp4", "moe_layer_residual_rmsnorm"):
+                     "moe_debug_dequant_mxfp4", "moe_layer_residual_rmsnorm",
+                     "moe_layer_static"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -170,6 +174,21 @@ def moe_layer(shape: moe_shape, x, logits, w_router, gate, up, down,
         ctypes.byref(shape), _ptr(x), _ptr(logits), _ptr(w_router), q4(gate), q4(up), q4(down),
         sh_arr, _ptr(shared_gate), _ptr(y), _ptr(idx_out), _ptr(w_out), _ptr(logits_out),
         _ptr(ws), int(ws_bytes), _stream(stream)))
+
+
+def moe_layer_static(shape: moe_shape, x, logits, w_router, gate, up, down,
+                     shared: Optional[Sequence[Tuple]], shared_gate, y, idx_out, w_out,
+                     logits_out, stream=None) -> None:
+    """moe_layer on the library's static per-GPU scratch (no workspace argument,
+    no allocation); shapes needing more than MOE_STATIC_SCRATCH_BYTES raise
+    MoeError with status MOE_ERR_SCRATCH_LIMIT."""
+    sh_arr = None
+    if shared is not None:
+        sh_arr = (moe_q4 * 3)(*[q4(p) for p in shared])
+    _check("moe_layer_static", lib().moe_layer_static(
+        ctypes.byref(shape), _ptr(x), _ptr(logits), _ptr(w_router), q4(gate), q4(up), q4(down),
+        sh_arr, _ptr(shared_gate), _ptr(y), _ptr(idx_out), _ptr(w_out), _ptr(logits_out),
+        _stream(stream)))
 
 
 def moe_layer_residual_rmsnorm(shape: moe_shape, x, logits, w_router, gate, up, down,

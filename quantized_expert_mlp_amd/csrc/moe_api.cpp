@@ -3,8 +3,17 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "moe.h"
 #include "kernels.h"
+
+// The workspace of moe_layer_static: device memory owned by the library, one
+// copy per GPU (each device that runs the library holds it until the process
+// ends).  Host code never passes this name to a kernel: its host-side symbol
+// is a stand-in, not a device address; the device address comes from
+// hipGetSymbolAddress, once per device (static_scratch below).
+static __device__ __align__(256) char scratch[MOE_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -108,6 +117,25 @@ P* at(void* ws, size_t off) {
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// Device address of the static scratch on the current device, looked up on
+// the first call made with that device current and kept per device.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int static_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
 
 // Optional per-stage events (moe_layer_profiled): stage i's kernel is launched
 // with events[2i] / events[2i+1] recorded at its start and end; a stage a call
@@ -227,6 +255,7 @@ const char* moe_status_string(int status) {
     case MOE_ERR_UNSUPPORTED: return "unsupported shape";
     case MOE_ERR_WORKSPACE: return "workspace too small";
     case MOE_ERR_HIP: return "HIP launch error";
+    case MOE_ERR_SCRATCH_LIMIT: return "shape needs more than the static scratch";
     default: return "unknown status";
   }
 }
@@ -425,6 +454,21 @@ int moe_layer(const moe_shape* sh, const uint16_t* x, const float* logits,
               float* logits_out, void* ws, size_t ws_bytes, moe_stream_t stream) {
   return layer_impl(sh, x, logits, w_router, gate, up, down, shared, shared_gate, y, idx_out,
                     w_out, logits_out, ws, ws_bytes, stream, nullptr);
+}
+
+int moe_layer_static(const moe_shape* sh, const uint16_t* x, const float* logits,
+                     const float* w_router, moe_q4 gate, moe_q4 up, moe_q4 down,
+                     const moe_q4* shared, const float* shared_gate, float* y, int32_t* idx_out,
+                     float* w_out, float* logits_out, moe_stream_t stream) {
+  // A shape the layer does not serve needs 0 bytes; layer_impl then returns
+  // its own error before anything is enqueued.
+  const size_t need = moe_workspace_bytes(sh);
+  if (need > (size_t)MOE_STATIC_SCRATCH_BYTES) return MOE_ERR_SCRATCH_LIMIT;
+  void* ws = nullptr;
+  const int rc = static_scratch(&ws);
+  if (rc != MOE_OK) return rc;
+  return layer_impl(sh, x, logits, w_router, gate, up, down, shared, shared_gate, y, idx_out,
+                    w_out, logits_out, ws, (size_t)MOE_STATIC_SCRATCH_BYTES, stream, nullptr);
 }
 
 int moe_layer_residual_rmsnorm(const moe_shape* sh, const uint16_t* x, const float* logits,
