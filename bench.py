@@ -15,8 +15,11 @@ through 4 independent weight sets (router workloads).
 
 Prints one JSON line on stdout: the headline tokens/s, the dominant kernel's
 roofline fraction (its duration measured with HIP events on the launch
-stream through moe_layer_profiled), and the CPU oracle's rate on a bounded
-sample of the same workload.  Details go to stderr.
+stream through moe_layer_profiled), the per-stage device times of the
+stages that ran, a "prefill" object with the same figures for the skewed
+2048-token prefill (tiled weights, the library's AUTO path, the same steps
+and warmup; the metric's MFMA half), and the CPU oracle's rate on a bounded
+sample of the headline workload.  Details go to stderr.
 """
 import argparse
 import ctypes
@@ -52,11 +55,15 @@ class Hip:
         self.L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                ctypes.c_void_p]
         self.L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.L.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
 
     def event(self) -> int:
         e = ctypes.c_void_p()
         assert self.L.hipEventCreate(ctypes.byref(e)) == 0
         return e.value
+
+    def record(self, e: int, stream: int) -> None:
+        assert self.L.hipEventRecord(e, stream) == 0
 
     def ms(self, a: int, b: int) -> float:
         out = ctypes.c_float()
@@ -242,6 +249,202 @@ def cpu_baseline(wl, seconds_hint: float, fmt: str = "int4", router: str = "soft
             "sample": sample, "seconds": round(dt, 2)}
 
 
+def cpu_info():
+    """The host's CPU count, the CPUs this process may run on, and the model."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        allowed = len(os.sched_getaffinity(0))
+    except AttributeError:
+        allowed = os.cpu_count()
+    return {"host_cpus": os.cpu_count(), "allowed_cpus": allowed, "cpu_model": model}
+
+
+def measure(wl, args, layout, path_name, hip, steps, warmup, fold=False):
+    """Time exactly `steps` moe_layer calls (after `warmup`) on workload wl,
+    then the same calls through moe_layer_profiled for per-stage device time
+    and the dominant kernel's roofline.  Returns a dict."""
+    import torch
+
+    import quantized_expert_mlp_amd as moe
+
+    T = wl.T
+    nsets = WEIGHT_SETS.get(wl.name, 1)
+    log("workload %s: %s; %d weight set(s), layout %s" % (wl.name, wl.description, nsets, layout))
+    t0 = time.perf_counter()
+    tiled = layout == "tiled"
+    mx = args.format == "mxfp4"
+    sets = build_sets(wl, nsets, tiled=tiled, fmt=args.format)
+    log("inputs resident in %.1f s" % (time.perf_counter() - t0))
+
+    bias_np = router_bias(args.router, wl.E)
+    bias = None if bias_np is None else torch.from_numpy(bias_np).cuda()
+    rc = dict(top_p=args.top_p, router=args.router, bias=bias_np)
+
+    # per-step inputs: logits pool (given-logit workloads) or weight-set rotation
+    if wl.logits in ("given", "zipf"):
+        pool_np = [S.draw_logits(wl, seed=100 + i) for i in range(LOGIT_POOL)] \
+            if wl.T == 1 else [S.draw_logits(wl, seed=100 + i) for i in range(4)]
+        pool = [torch.from_numpy(p).cuda() for p in pool_np]
+        counts = [routing_counts(p, wl.k, **rc) for p in pool_np]
+    else:
+        pool_np, pool = None, None
+        counts = []
+        for s in sets:  # byte accounting only: which experts the router picks
+            L = S.bf16_bits_to_f32(s["inp"].x) @ s["inp"].w_router.T
+            counts.append(routing_counts(L, wl.k, **rc))
+    touched = [c[0] for c in counts]
+    nvar = len(pool) if pool is not None else len(sets)
+
+    path = {"auto": moe.MOE_PATH_AUTO, "gemv": moe.MOE_PATH_GEMV, "gemm": moe.MOE_PATH_GEMM}[path_name]
+    sh = moe.make_shape(T, wl.H, wl.E, wl.k, wl.I, wl.SI, path=path,
+                        layout=moe.MOE_LAYOUT_TILED if tiled else moe.MOE_LAYOUT_ROWS,
+                        format=moe.MOE_FORMAT_MXFP4 if mx else moe.MOE_FORMAT_INT4,
+                        top_p=args.top_p,
+                        score=moe.MOE_SCORE_SIGMOID if args.router.startswith("sigmoid")
+                        else moe.MOE_SCORE_SOFTMAX, select_bias=bias)
+    if moe.moe_workspace_bytes(sh) == 0:
+        sys.exit("bench.py: workload %s is not served with --path %s --layout %s --format %s"
+                 % (wl.name, path_name, layout, args.format))
+    # the library's AUTO rule (MOE_PATH_AUTO)
+    gemm = path_name == "gemm" or (path_name == "auto" and (tiled or (T * wl.k) >= 8 * wl.E))
+    nbytes = moe.moe_workspace_bytes(sh)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    y = torch.empty((T, wl.H), dtype=torch.float32, device="cuda")
+    if fold:
+        residual = torch.from_numpy(S.draw_residual(wl)).cuda()
+        norm_w = torch.from_numpy(S.draw_norm_weight(wl)).cuda()
+        x_next = torch.empty((T, wl.H), dtype=torch.int16, device="cuda")
+
+    def call(i, events=None):
+        s = sets[i % len(sets)] if pool is None else sets[0]
+        lg = pool[i % len(pool)] if pool is not None else None
+        wr = s["w_router"] if pool is None else None
+        if fold and events is None:
+            moe.moe_layer_residual_rmsnorm(sh, s["x"], lg, wr, s["planes"]["gate"],
+                                           s["planes"]["up"], s["planes"]["down"], s["shared"],
+                                           s["shared_gate"], residual, norm_w, 1e-6, x_next,
+                                           None, None, ws, nbytes)
+            return None
+        args_ = (sh, s["x"], lg, wr, s["planes"]["gate"], s["planes"]["up"], s["planes"]["down"],
+                 s["shared"], s["shared_gate"], y, None, None, None, ws, nbytes)
+        if events is None:
+            moe.moe_layer(*args_)
+            return None
+        return moe.moe_layer_profiled(*args_, events=events)
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly `steps` layer calls
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        call(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / steps
+    tokens_per_s = T * steps / wall
+
+    # ---- per-stage device time (HIP events on the launch stream); with
+    # fold these come from moe_layer_profiled, whose kernels are the folded
+    # step's except the final norm launch.  Only stages whose kernels ran.
+    ev = [[hip.event() for _ in range(2 * len(moe.STAGES))] for _ in range(steps)]
+    ran = set()
+    for i in range(steps):
+        ran.update(call(i, ev[i]))
+    torch.cuda.synchronize()
+    stage_ms = {name: 0.0 for name in moe.STAGES[1:] if name in ran}
+    for i in range(steps):
+        for j, name in enumerate(moe.STAGES):
+            if name in stage_ms:
+                stage_ms[name] += hip.ms(ev[i][2 * j], ev[i][2 * j + 1])
+    for k_ in stage_ms:
+        stage_ms[k_] /= steps
+    U = float(np.mean([touched[i % nvar] for i in range(steps)]))
+    kept_slots = float(np.mean([counts[i % nvar][1] for i in range(steps)]))
+    work = stage_work(wl, T, U, gemm, args.format, kept_slots)
+    dom = max((s_ for s_ in ("gate_up", "down", "shared_gate_up", "shared_down") if s_ in stage_ms),
+              key=lambda s_: stage_ms[s_])
+    dur_s = stage_ms[dom] * 1e-3
+    # The roof the kernel is held to: the MFMA peak when its arithmetic
+    # intensity reaches half the ridge point (peak flops / peak bytes, about
+    # 312 flop/byte), else HBM bandwidth (the GEMV, and the MFMA path at
+    # decode-sized batches, where each expert's weights serve a few rows).
+    ridge = MFMA_F16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    mfma_bound = gemm and work[dom]["flops"] >= 0.5 * ridge * work[dom]["bytes"]
+    if mfma_bound:
+        achieved = work[dom]["flops"] / dur_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFS, 4)}
+    else:
+        achieved = work[dom]["bytes"] / dur_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    roof["kernel"] = dom
+    roof["kernel_us"] = round(stage_ms[dom] * 1e3, 3)
+    roof["algorithmic_bytes"] = int(work[dom]["bytes"])
+    roof["algorithmic_flops"] = int(work[dom]["flops"])
+    roof["intensity_flop_per_byte"] = round(work[dom]["flops"] / work[dom]["bytes"], 1)
+    roof["traffic"] = counted_traffic(dom, wl.name, gemm, args.format, layout)
+    layer_bytes = sum(w_["bytes"] for w_ in work.values())
+    layer_flops = sum(w_["flops"] for w_ in work.values())
+    log("stage device time (us): " + ", ".join("%s %.2f" % (k_, v * 1e3)
+                                                for k_, v in stage_ms.items()))
+    log("touched experts per call %.1f; layer: %.2f us/step wall, %.1f GB/s, %.1f TFLOP/s"
+        % (U, ms_per_step * 1e3, layer_bytes / (ms_per_step * 1e-3) / 1e9,
+           layer_flops / (ms_per_step * 1e-3) / 1e12))
+    log("dominant kernel %s: %.2f us, %s" % (dom, stage_ms[dom] * 1e3, roof))
+    del sets, pool, ws
+    torch.cuda.empty_cache()
+    return {
+        "ms_per_step": ms_per_step, "tokens_per_s": tokens_per_s, "gemm": gemm,
+        "stage_us": {k_: round(v * 1e3, 3) for k_, v in stage_ms.items()},
+        "roofline": roof, "nvar": nvar, "pool": pool_np is not None,
+        "layer": {"touched_experts": round(U, 1),
+                  "tflops": round(layer_flops / (ms_per_step * 1e-3) / 1e12, 1),
+                  "gbs": round(layer_bytes / (ms_per_step * 1e-3) / 1e9, 1)},
+    }
+
+
+def read_probe(hip):
+    """Best streaming-read rate of moe_debug_read_probe over sizes and
+    launch widths (the practical HBM read ceiling for the decode GEMVs)."""
+    import torch
+
+    import quantized_expert_mlp_amd as moe
+
+    buf = torch.randint(0, 1 << 30, (1 << 28,), dtype=torch.int32, device="cuda")  # 1 GiB
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream()
+    rows = []
+    for nbytes in (113_246_208, 1 << 30):
+        for wgs in (1024, 2048, 4096, 8192):
+            for _ in range(5):
+                moe.moe_debug_read_probe(buf, nbytes, wgs, sink)
+            e = [hip.event() for _ in range(2)]
+            best = None
+            for _ in range(20):
+                hip.record(e[0], st.cuda_stream)
+                moe.moe_debug_read_probe(buf, nbytes, wgs, sink)
+                hip.record(e[1], st.cuda_stream)
+                torch.cuda.synchronize()
+                ms = hip.ms(e[0], e[1])
+                best = ms if best is None else min(best, ms)
+            rows.append({"bytes": nbytes, "workgroups": wgs, "best_us": round(best * 1e3, 2),
+                         "gbs": round(nbytes / (best * 1e-3) / 1e9, 1)})
+            log("read probe %d bytes, %d workgroups: %.2f us, %.1f GB/s"
+                % (nbytes, wgs, best * 1e3, rows[-1]["gbs"]))
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -265,10 +468,19 @@ def main():
                     choices=["softmax", "sigmoid", "softmax-bias", "sigmoid-bias"],
                     help="router: the plain softmax top-k, or a variant (sigmoid scores "
                          "and/or a seeded selection bias)")
+    ap.add_argument("--prefill-workload", default="prefill_skewed",
+                    choices=[w for w in S.WORKLOADS if w.startswith("prefill")],
+                    help="the prefill workload timed beside a decode headline (the metric's "
+                         "prefill half), with --prefill-layout weights through AUTO")
+    ap.add_argument("--prefill-layout", default="tiled", choices=["rows", "tiled"])
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy (HBM counter calibration)")
+    ap.add_argument("--probe-read", action="store_true",
+                    help="only run the streaming-read probe (moe_debug_read_probe) and print "
+                         "its rates")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -293,151 +505,52 @@ def main():
         return
     moe.lib()
     hip = Hip()
-    wl = S.WORKLOADS[args.workload]
-    T = wl.T
-    nsets = WEIGHT_SETS.get(wl.name, 1)
-    log("workload %s: %s; %d weight set(s)" % (wl.name, wl.description, nsets))
-    t0 = time.perf_counter()
-    tiled = args.layout == "tiled"
-    mx = args.format == "mxfp4"
-    sets = build_sets(wl, nsets, tiled=tiled, fmt=args.format)
-    log("inputs resident in %.1f s" % (time.perf_counter() - t0))
-
+    if args.probe_read:
+        print(json.dumps({"probe": "moe_debug_read_probe", "rows": read_probe(hip)}), flush=True)
+        return
     if args.router != "softmax" and 0.0 < args.top_p < 1.0:
         sys.exit("bench.py: --top-p applies to the plain softmax router only")
-    bias_np = router_bias(args.router, wl.E)
-    bias = None if bias_np is None else torch.from_numpy(bias_np).cuda()
-    rc = dict(top_p=args.top_p, router=args.router, bias=bias_np)
 
-    # per-step inputs: logits pool (given-logit workloads) or weight-set rotation
-    if wl.logits in ("given", "zipf"):
-        pool_np = [S.draw_logits(wl, seed=100 + i) for i in range(LOGIT_POOL)] \
-            if wl.T == 1 else [S.draw_logits(wl, seed=100 + i) for i in range(4)]
-        pool = [torch.from_numpy(p).cuda() for p in pool_np]
-        counts = [routing_counts(p, wl.k, **rc) for p in pool_np]
-    else:
-        pool_np, pool = None, None
-        counts = []
-        for s in sets:  # byte accounting only: which experts the router picks
-            L = S.bf16_bits_to_f32(s["inp"].x) @ s["inp"].w_router.T
-            counts.append(routing_counts(L, wl.k, **rc))
-    touched = [c[0] for c in counts]
-    nvar = len(pool) if pool is not None else len(sets)
+    wl = S.WORKLOADS[args.workload]
+    m = measure(wl, args, args.layout, args.path, hip, args.steps, args.warmup, fold=args.fold)
+    gemm = m["gemm"]
+    mx = args.format == "mxfp4"
 
-    path = {"auto": moe.MOE_PATH_AUTO, "gemv": moe.MOE_PATH_GEMV, "gemm": moe.MOE_PATH_GEMM}[args.path]
-    sh = moe.make_shape(T, wl.H, wl.E, wl.k, wl.I, wl.SI, path=path,
-                        layout=moe.MOE_LAYOUT_TILED if tiled else moe.MOE_LAYOUT_ROWS,
-                        format=moe.MOE_FORMAT_MXFP4 if mx else moe.MOE_FORMAT_INT4,
-                        top_p=args.top_p,
-                        score=moe.MOE_SCORE_SIGMOID if args.router.startswith("sigmoid")
-                        else moe.MOE_SCORE_SOFTMAX, select_bias=bias)
-    if moe.moe_workspace_bytes(sh) == 0:
-        sys.exit("bench.py: this workload is not served with --path %s --layout %s --format %s"
-                 % (args.path, args.layout, args.format))
-    # the library's AUTO rule (MOE_PATH_AUTO)
-    gemm = args.path == "gemm" or (args.path == "auto" and (tiled or (T * wl.k) >= 8 * wl.E))
-    nbytes = moe.moe_workspace_bytes(sh)
-    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-    y = torch.empty((T, wl.H), dtype=torch.float32, device="cuda")
-    if args.fold:
-        residual = torch.from_numpy(S.draw_residual(wl)).cuda()
-        norm_w = torch.from_numpy(S.draw_norm_weight(wl)).cuda()
-        x_next = torch.empty((T, wl.H), dtype=torch.int16, device="cuda")
-
-    def call(i, events=None):
-        s = sets[i % len(sets)] if pool is None else sets[0]
-        lg = pool[i % len(pool)] if pool is not None else None
-        wr = s["w_router"] if pool is None else None
-        if args.fold and events is None:
-            moe.moe_layer_residual_rmsnorm(sh, s["x"], lg, wr, s["planes"]["gate"],
-                                           s["planes"]["up"], s["planes"]["down"], s["shared"],
-                                           s["shared_gate"], residual, norm_w, 1e-6, x_next,
-                                           None, None, ws, nbytes)
-            return
-        args_ = (sh, s["x"], lg, wr, s["planes"]["gate"], s["planes"]["up"], s["planes"]["down"],
-                 s["shared"], s["shared_gate"], y, None, None, None, ws, nbytes)
-        if events is None:
-            moe.moe_layer(*args_)
-        else:
-            moe.moe_layer_profiled(*args_, events=events)
-
-    for i in range(args.warmup):
-        call(i)
-    torch.cuda.synchronize()
-
-    # ---- timed region: exactly `steps` layer calls
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        call(i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-    tokens_per_s = T * args.steps / wall
-
-    # ---- per-stage device time (HIP events on the launch stream); with --fold
-    # these come from moe_layer_profiled, whose kernels are the folded step's
-    # except the final norm launch
-    ev = [[hip.event() for _ in range(2 * len(moe.STAGES))] for _ in range(args.steps)]
-    for i in range(args.steps):
-        call(i, ev[i])
-    torch.cuda.synchronize()
-    stage_ms = {name: 0.0 for name in moe.STAGES[1:]}
-    for i in range(args.steps):
-        for j in range(1, len(moe.STAGES)):
-            stage_ms[moe.STAGES[j]] += hip.ms(ev[i][2 * j], ev[i][2 * j + 1])
-    for k_ in stage_ms:
-        stage_ms[k_] /= args.steps
-    U = float(np.mean([touched[i % nvar] for i in range(args.steps)]))
-    kept_slots = float(np.mean([counts[i % nvar][1] for i in range(args.steps)]))
-    work = stage_work(wl, T, U, gemm, args.format, kept_slots)
-    dom = max(("gate_up", "down", "shared_gate_up", "shared_down"), key=lambda s_: stage_ms[s_])
-    dur_s = stage_ms[dom] * 1e-3
-    # The roof the kernel is held to: the MFMA peak when its arithmetic
-    # intensity reaches half the ridge point (peak flops / peak bytes, about
-    # 312 flop/byte), else HBM bandwidth (the GEMV, and the MFMA path at
-    # decode-sized batches, where each expert's weights serve a few rows).
-    ridge = MFMA_F16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9)
-    mfma_bound = gemm and work[dom]["flops"] >= 0.5 * ridge * work[dom]["bytes"]
-    if mfma_bound:
-        achieved = work[dom]["flops"] / dur_s / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFS,
-                "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFS, 4)}
-    else:
-        achieved = work[dom]["bytes"] / dur_s / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    roof["kernel"] = dom
-    roof["intensity_flop_per_byte"] = round(work[dom]["flops"] / work[dom]["bytes"], 1)
-    roof["traffic"] = counted_traffic(dom, wl.name, gemm, args.format, args.layout)
-    layer_bytes = sum(w_["bytes"] for w_ in work.values())
-    layer_flops = sum(w_["flops"] for w_ in work.values())
-    log("stage device time (us): " + ", ".join("%s %.2f" % (k_, v * 1e3)
-                                                for k_, v in stage_ms.items()))
-    log("touched experts per call %.1f; layer: %.2f us/step wall, %.1f GB/s, %.1f TFLOP/s"
-        % (U, ms_per_step * 1e3, layer_bytes / (ms_per_step * 1e-3) / 1e9,
-           layer_flops / (ms_per_step * 1e-3) / 1e12))
-    log("dominant kernel %s: %.2f us, %s" % (dom, stage_ms[dom] * 1e3, roof))
+    prefill = None
+    if not args.no_prefill and not wl.name.startswith("prefill"):
+        pw = S.WORKLOADS[args.prefill_workload]
+        pm = measure(pw, args, args.prefill_layout, "auto", hip, args.steps, args.warmup)
+        prefill = {
+            "workload": pw.name, "description": pw.description,
+            "layout": args.prefill_layout, "path": "auto",
+            "expert_path": "grouped fp16 MFMA GEMM" if pm["gemm"] else "streaming GEMV",
+            "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(pm["ms_per_step"], 5),
+            "tokens_per_s": round(pm["tokens_per_s"], 1),
+            "layer": pm["layer"], "roofline": pm["roofline"], "stage_us": pm["stage_us"],
+        }
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, args.cpu_seconds, args.format, args.router, bias_np)
+        cpu = cpu_baseline(wl, args.cpu_seconds, args.format, args.router,
+                           router_bias(args.router, wl.E))
+        cpu.update(cpu_info())
         log("cpu oracle: %s" % cpu)
 
     out = {
         "metric": METRIC,
-        "value": round(tokens_per_s, 2),
+        "value": round(m["tokens_per_s"], 2),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": round(m["ms_per_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f16" if gemm or mx else "bf16",
         "data": "synthetic",
-        "config": {"workload": wl.name, "description": wl.description, "T": T, "H": wl.H,
+        "config": {"workload": wl.name, "description": wl.description, "T": wl.T, "H": wl.H,
                    "E": wl.E, "k": wl.k, "I": wl.I, "SI": wl.SI,
                    "weights": ("mxfp4: e2m1, ue8m0 exponent per 32 inputs" if mx
                                else "int4 offset-binary, fp16 scale per 32 inputs"),
@@ -449,10 +562,12 @@ def main():
                             if args.fold else "layer (moe_layer)"),
                    "expert_path": "grouped fp16 MFMA GEMM" if gemm else
                    "streaming %s GEMV" % args.format,
-                   "input_rotation": ("%d logits rows" % nvar) if pool is not None
-                   else ("%d weight sets" % nvar)},
-        "roofline": roof,
-        "stage_us": {k_: round(v * 1e3, 3) for k_, v in stage_ms.items()},
+                   "input_rotation": ("%d logits rows" % m["nvar"]) if m["pool"]
+                   else ("%d weight sets" % m["nvar"])},
+        "roofline": m["roofline"],
+        "stage_us": m["stage_us"],
+        "layer": m["layer"],
+        "prefill": prefill,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -317,8 +317,13 @@ int moe_layer_residual_rmsnorm(const moe_shape *shape, const uint16_t *x, const 
  * start and end on `stream`; hipEventElapsedTime(events[2i], events[2i+1]) is
  * the kernel's device time (per-stage stamps in the spirit of the dasLLAMA
  * PR's per-role profile).  A stage the call does not run gets its two events
- * recorded back to back (zero-length interval).
- *   events   : host array of n_events hipEvent_t, n_events >= 2*MOE_STAGE_COUNT.
+ * recorded back to back (an interval of no kernel, which measures only the
+ * stream's gap there: it is not a stage time).
+ *   events    : host array of n_events hipEvent_t, n_events >= 2*MOE_STAGE_COUNT.
+ *   stage_ran : host int32 [MOE_STAGE_COUNT] out, or NULL: 1 for each stage
+ *               whose kernel the call launched, 0 for the others (the fused
+ *               small-batch routing runs inside the gate/up launch, so its
+ *               top-k and permutation stages read 0).
  * Errors: as moe_layer, plus INVALID_ARG for a null or short event list.
  */
 enum moe_stage {
@@ -342,7 +347,7 @@ int moe_layer_profiled(const moe_shape *shape, const uint16_t *x, const float *l
                        const moe_q4 *shared, const float *shared_gate, float *y,
                        int32_t *idx_out, float *w_out, float *logits_out, void *ws,
                        size_t ws_bytes, moe_stream_t stream, void *const *events,
-                       int32_t n_events);
+                       int32_t n_events, int32_t *stage_ran);
 
 /*
  * Regroup E experts' 4-bit planes from the row layout into the tiled layout
@@ -398,6 +403,20 @@ int moe_debug_dequant_int4(moe_q4 plane, int32_t N, int32_t K, int32_t mode, flo
  */
 int moe_debug_dequant_mxfp4(moe_q4 plane, int32_t N, int32_t K, int32_t mode, float *out,
                             moe_stream_t stream);
+
+/*
+ * Measurement hook: a streaming read of `bytes` (a multiple of 16) of device
+ * memory at src (16-byte aligned) by `workgroups` workgroups of 256 threads,
+ * each thread loading 16-byte words with the nontemporal hint of the GEMVs'
+ * weight stream, in a grid-stride loop.  Nothing is written except, in a
+ * case no real data produces (every word of a thread's xor fold all ones),
+ * up to 256 words of sink (device, 4-byte aligned).  Timed by the caller, it
+ * gives the practical HBM read rate the decode GEMVs are compared with.
+ * Errors: INVALID_ARG (null, misaligned, bytes, workgroups outside
+ *         1..2^20).
+ */
+int moe_debug_read_probe(const void *src, size_t bytes, int32_t workgroups, uint32_t *sink,
+                         moe_stream_t stream);
 
 #ifdef __cplusplus
 }

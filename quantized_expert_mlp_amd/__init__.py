@@ -30,7 +30,7 @@ EXPORTS = ("moe_router_topk", "moe_permute", "moe_permute_workspace_bytes", "moe
            "moe_layer",
            "moe_layer_profiled", "moe_pack_weights", "moe_workspace_bytes",
            "moe_status_string", "moe_debug_dequant_int4", "moe_debug_dequant_mxfp4",
-           "moe_layer_residual_rmsnorm", "moe_layer_static")
+           "moe_layer_residual_rmsnorm", "moe_layer_static", "moe_debug_read_probe")
 STAGES = ("start", "logits", "topk", "permute", "activations", "gate_up", "shared_gate_up",
           "down", "shared_down")
 
@@ -74,7 +74,7 @@ def lib() -> ctypes.CDLL:
         L.moe_layer.argtypes = [ctypes.POINTER(moe_shape), P, P, P, moe_q4, moe_q4, moe_q4,
                                 ctypes.POINTER(moe_q4), P, P, P, P, P, P, ctypes.c_size_t, P]
         L.moe_layer_profiled.argtypes = L.moe_layer.argtypes + [ctypes.POINTER(ctypes.c_void_p),
-                                                                i32]
+                                                                i32, P]
         L.moe_layer_static.argtypes = L.moe_layer.argtypes[:13] + [P]
         L.moe_layer_residual_rmsnorm.argtypes = [
             ctypes.POINTER(moe_shape), P, P, P, moe_q4, moe_q4, moe_q4, ctypes.POINTER(moe_q4), P,
@@ -86,10 +86,11 @@ def lib() -> ctypes.CDLL:
         L.moe_debug_dequant_int4.argtypes = [moe_q4, i32, i32, i32, P, P]
         L.moe_debug_dequant_mxfp4.argtypes = [moe_q4, i32, i32, i32, P, P]
         L.moe_pack_weights.argtypes = [moe_q4, i32, i32, i32, i32, moe_q4, P]
+        L.moe_debug_read_probe.argtypes = [P, ctypes.c_size_t, i32, P, P]
         for name in ("moe_router_topk", "moe_permute", "moe_expert_mlp", "moe_layer",
                      "moe_layer_profiled", "moe_pack_weights", "moe_debug_dequant_int4",
                      "moe_debug_dequant_mxfp4", "moe_layer_residual_rmsnorm",
-                     "moe_layer_static"):
+                     "moe_layer_static", "moe_debug_read_probe"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -207,17 +208,21 @@ def moe_layer_residual_rmsnorm(shape: moe_shape, x, logits, w_router, gate, up, 
 
 def moe_layer_profiled(shape: moe_shape, x, logits, w_router, gate, up, down,
                        shared: Optional[Sequence[Tuple]], shared_gate, y, idx_out, w_out,
-                       logits_out, ws, ws_bytes, events: Sequence[int], stream=None) -> None:
+                       logits_out, ws, ws_bytes, events: Sequence[int], stream=None):
     """moe_layer with stage i's kernel bracketed by hipEvent_t handles
-    events[2i] (start) and events[2i+1] (end); len(events) >= 2 * len(STAGES)."""
+    events[2i] (start) and events[2i+1] (end); len(events) >= 2 * len(STAGES).
+    Returns the names of the stages whose kernels the call launched."""
     sh_arr = None
     if shared is not None:
         sh_arr = (moe_q4 * 3)(*[q4(p) for p in shared])
     ev = (ctypes.c_void_p * len(events))(*events)
+    ran = (ctypes.c_int32 * len(STAGES))()
     _check("moe_layer_profiled", lib().moe_layer_profiled(
         ctypes.byref(shape), _ptr(x), _ptr(logits), _ptr(w_router), q4(gate), q4(up), q4(down),
         sh_arr, _ptr(shared_gate), _ptr(y), _ptr(idx_out), _ptr(w_out), _ptr(logits_out),
-        _ptr(ws), int(ws_bytes), _stream(stream), ev, len(events)))
+        _ptr(ws), int(ws_bytes), _stream(stream), ev, len(events),
+        ctypes.cast(ran, ctypes.c_void_p)))
+    return [name for name, r in zip(STAGES, ran) if r]
 
 
 def moe_pack_weights(src, E, N, K, dst, stream=None, format=MOE_FORMAT_INT4) -> None:
@@ -234,3 +239,8 @@ def moe_debug_dequant_int4(plane, N, K, mode, out, stream=None) -> None:
 def moe_debug_dequant_mxfp4(plane, N, K, out, stream=None, mode=1) -> None:
     _check("moe_debug_dequant_mxfp4", lib().moe_debug_dequant_mxfp4(
         q4(plane), N, K, int(mode), _ptr(out), _stream(stream)))
+
+
+def moe_debug_read_probe(src, nbytes, workgroups, sink, stream=None) -> None:
+    _check("moe_debug_read_probe", lib().moe_debug_read_probe(
+        _ptr(src), int(nbytes), int(workgroups), _ptr(sink), _stream(stream)))

@@ -157,8 +157,8 @@ __device__ __forceinline__ bool tile_of(const Buckets& b, const GemmArgs& a, Til
   *src = 0;
   const int n_tiles = b.sched[1];
   if (u >= n_tiles) return false;
-  if (thin_first) {  // start with the thin experts' tiles, which end the list
-    u += b.sched[2];
+  if (thin_first) {  // start with the thin experts' sched[2] tiles, which end the list
+    u += n_tiles - b.sched[2];
     if (u >= n_tiles) u -= n_tiles;
   }
   const int4 t = reinterpret_cast<const int4*>(b.sched + sched_tiles_offset(b.E))[u];

@@ -181,6 +181,12 @@ hipError_t launch_gemm_down(const Buckets& b, int max_tiles, const uint16_t* h16
                             const uint8_t* dq, const void* ds, const float* w, float* y,
                             const SharedGemm* shared, bool tiled, int fmt, const Launch& L);
 
+// Streaming-read probe over bytes (a multiple of 16) of src with the given
+// number of 256-thread workgroups; sink holds 256 words (written only in a
+// case the probe's inputs never produce).
+hipError_t launch_read_probe(const void* src, int64_t bytes, int workgroups, uint32_t* sink,
+                             const Launch& L);
+
 // Decoders the debug hook runs (s holds fp16 bits for the int4 ones, ue8m0
 // bytes for the MXFP4 ones).
 enum DebugDecoder : int {

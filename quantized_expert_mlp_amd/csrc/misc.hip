@@ -103,6 +103,35 @@ hipError_t launch_pack_weights(const uint8_t* sq, const void* ss, int E, int N, 
   return hipGetLastError();
 }
 
+// Streaming-read probe (the practical HBM read ceiling the GEMVs are held
+// against): each thread reads 16-byte words of src with the nontemporal hint
+// the GEMV weight stream uses, in a grid-stride loop, and folds them with
+// xor.  The fold is stored only when it equals ~0 in every word, which keeps
+// the loads alive without a store per thread.
+__global__ __launch_bounds__(256) void read_probe_kernel(const u32x4_t* __restrict__ src,
+                                                         int64_t words,
+                                                         uint32_t* __restrict__ sink) {
+  const int64_t nthr = (int64_t)gridDim.x * blockDim.x;
+  u32x4_t acc = {0u, 0u, 0u, 0u};
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 3 * nthr < words; i += 4 * nthr) {
+    const u32x4_t a = __builtin_nontemporal_load(src + i);
+    const u32x4_t b = __builtin_nontemporal_load(src + i + nthr);
+    const u32x4_t c = __builtin_nontemporal_load(src + i + 2 * nthr);
+    const u32x4_t d = __builtin_nontemporal_load(src + i + 3 * nthr);
+    acc ^= a ^ b ^ c ^ d;
+  }
+  for (; i < words; i += nthr) acc ^= __builtin_nontemporal_load(src + i);
+  if ((acc[0] & acc[1] & acc[2] & acc[3]) == 0xFFFFFFFFu) sink[threadIdx.x] = acc[0];
+}
+
+hipError_t launch_read_probe(const void* src, int64_t bytes, int workgroups, uint32_t* sink,
+                             const Launch& L) {
+  MOE_LAUNCH(L, read_probe_kernel, dim3(workgroups), dim3(256), 0,
+             static_cast<const u32x4_t*>(src), bytes / 16, sink);
+  return hipGetLastError();
+}
+
 // Decode one plane with the kernels' own routines (the ones their main loops
 // call), one thread per packed 32-bit word (8 nibbles), and write what each
 // decoder stands for as fp32: the GEMV decoders' exact weight (their offset

@@ -140,18 +140,23 @@ int static_scratch(void** out) {
 // Optional per-stage events (moe_layer_profiled): stage i's kernel is launched
 // with events[2i] / events[2i+1] recorded at its start and end; a stage a call
 // does not run gets both events recorded back to back, so every pair is valid.
+// ran (nullable, host): ran[i] is set to 1 for a stage whose kernel is
+// launched, 0 for one the call skips.
 struct Stages {
   void* const* ev;
   hipStream_t st;
+  int32_t* ran = nullptr;
   moe::Launch at(int i) const {
     moe::Launch L{st};
     if (ev) {
       L.start = reinterpret_cast<hipEvent_t>(ev[2 * i]);
       L.stop = reinterpret_cast<hipEvent_t>(ev[2 * i + 1]);
     }
+    if (ran) ran[i] = 1;
     return L;
   }
   bool skip(int i) const {
+    if (ran) ran[i] = 0;
     if (!ev) return true;
     return hipEventRecord(reinterpret_cast<hipEvent_t>(ev[2 * i]), st) == hipSuccess &&
            hipEventRecord(reinterpret_cast<hipEvent_t>(ev[2 * i + 1]), st) == hipSuccess;
@@ -349,7 +354,8 @@ static int layer_impl(const moe_shape* sh, const uint16_t* x, const float* logit
                       const float* w_router, moe_q4 gate, moe_q4 up, moe_q4 down,
                       const moe_q4* shared, const float* shared_gate, float* y, int32_t* idx_out,
                       float* w_out, float* logits_out, void* ws, size_t ws_bytes,
-                      moe_stream_t stream, void* const* events, bool accumulate = false) {
+                      moe_stream_t stream, void* const* events, bool accumulate = false,
+                      int32_t* stage_ran = nullptr) {
   int rc = check_shape(sh);
   if (rc != MOE_OK) return rc;
   if (!x || !y || !ws) return MOE_ERR_INVALID_ARG;
@@ -377,7 +383,7 @@ static int layer_impl(const moe_shape* sh, const uint16_t* x, const float* logit
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int T = sh->T, H = sh->H, E = sh->E, k = sh->k;
   const bool gated = shared && shared_gate;
-  const Stages sg{events, st};
+  const Stages sg{events, st, stage_ran};
   if (!sg.skip(MOE_STAGE_START)) return MOE_ERR_HIP;
 
   // 1. logits (and the shared gate logit as one more router row)
@@ -494,15 +500,24 @@ int moe_layer_profiled(const moe_shape* sh, const uint16_t* x, const float* logi
                        const moe_q4* shared, const float* shared_gate, float* y,
                        int32_t* idx_out, float* w_out, float* logits_out, void* ws,
                        size_t ws_bytes, moe_stream_t stream, void* const* events,
-                       int32_t n_events) {
+                       int32_t n_events, int32_t* stage_ran) {
   if (!events || n_events < 2 * MOE_STAGE_COUNT) return MOE_ERR_INVALID_ARG;
   for (int i = 0; i < 2 * MOE_STAGE_COUNT; ++i)
     if (!events[i]) return MOE_ERR_INVALID_ARG;
   return layer_impl(sh, x, logits, w_router, gate, up, down, shared, shared_gate, y, idx_out,
-                    w_out, logits_out, ws, ws_bytes, stream, events);
+                    w_out, logits_out, ws, ws_bytes, stream, events, false, stage_ran);
 }
 
 
+
+int moe_debug_read_probe(const void* src, size_t bytes, int32_t workgroups, uint32_t* sink,
+                         moe_stream_t stream) {
+  if (!src || !sink || bytes < 16 || bytes % 16 || !aligned(src, 16) || !aligned(sink, 4) ||
+      workgroups < 1 || workgroups > (1 << 20))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_read_probe(src, (int64_t)bytes, workgroups, sink,
+                                           moe::Launch{reinterpret_cast<hipStream_t>(stream)}));
+}
 
 int moe_debug_dequant_int4(moe_q4 plane, int32_t N, int32_t K, int32_t mode, float* out,
                            moe_stream_t stream) {

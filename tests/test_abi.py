@@ -225,6 +225,15 @@ def test_debug_dequant_rejects(L):
     assert g(_q(), 4, 64, 1, None, None) == moe.MOE_ERR_INVALID_ARG
 
 
+def test_read_probe_rejects(L):
+    f = L.moe_debug_read_probe
+    assert f(None, 1024, 64, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(FAKE, 1000, 64, FAKE, None) == moe.MOE_ERR_INVALID_ARG     # bytes % 16
+    assert f(FAKE + 8, 1024, 64, FAKE, None) == moe.MOE_ERR_INVALID_ARG  # misaligned
+    assert f(FAKE, 1024, 0, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(FAKE, 1024, 64, None, None) == moe.MOE_ERR_INVALID_ARG
+
+
 def test_product_path_has_no_oracle_dependency():
     """The product package neither imports nor links the oracle."""
     pkg = os.path.join(ROOT, "quantized_expert_mlp_amd")

@@ -320,7 +320,14 @@ def test_layer_profiled_matches_layer(path):
         args = (sh, d.x, None, d.w_router, d.planes["gate"], d.planes["up"], d.planes["down"],
                 d.shared, d.shared_gate, y, idx, w, None, ws, nb)
         if profiled:
-            moe.moe_layer_profiled(*args, events=events)
+            ran = moe.moe_layer_profiled(*args, events=events)
+            # 200 tokens: separate top-k and permutation launches; the MFMA
+            # path's logits launch writes the fp16 activations and its
+            # routed launches carry the shared expert's tiles
+            want = ["logits", "topk", "permute", "gate_up", "down"]
+            if path == moe.MOE_PATH_GEMV:
+                want += ["shared_gate_up", "shared_down"]
+            assert sorted(ran) == sorted(want), ran
         else:
             moe.moe_layer(*args)
         torch.cuda.synchronize()
