@@ -52,7 +52,7 @@ def lib():
         L.oracle_e8m0_to_double.restype = ctypes.c_double
         L.oracle_router_logits.argtypes = [P, P, P, i64, i64, i64, P]
         L.oracle_router_topk.argtypes = [P, i64, i64, i64, ctypes.c_double, ctypes.c_double,
-                                         ctypes.c_int, P, P, P, P]
+                                         ctypes.c_int, P, i64, i64, P, P, P]
         L.oracle_permute.argtypes = [P, i64, i64, i64, P, P, P]
         L.oracle_expert_forward.argtypes = [P] * 6 + [i64, i64, P, P, P, ctypes.c_int]
         L.oracle_layer.argtypes = [P] * 13 + [i64, P, P, P]
@@ -68,7 +68,8 @@ class _Shape(ctypes.Structure):
                 ("k", ctypes.c_int64), ("I", ctypes.c_int64), ("SI", ctypes.c_int64),
                 ("route_scale", ctypes.c_double), ("fmt", ctypes.c_int64),
                 ("top_p", ctypes.c_double), ("gate", ctypes.c_int64),
-                ("bias", ctypes.c_void_p)]
+                ("bias", ctypes.c_void_p), ("n_group", ctypes.c_int64),
+                ("topk_group", ctypes.c_int64)]
 
 
 # Weight formats: int4 nibble-8 with fp16 scale bits (uint16), MXFP4 e2m1 with
@@ -132,10 +133,12 @@ GATES = {"softmax": 0, "sigmoid": 1}
 
 
 def router_topk(logits: np.ndarray, k: int, route_scale: float = 1.0, top_p: float = 1.0,
-                gate: str = "softmax", bias: Optional[np.ndarray] = None):
+                gate: str = "softmax", bias: Optional[np.ndarray] = None, n_group: int = 0,
+                topk_group: int = 0):
     """(idx int32 [T][k], w fp32 [T][k], w fp64 [T][k]); with 0 < top_p < 1
     the picks past the top-p prefix are -1 with weight 0.  gate/bias select a
-    router variant (sigmoid scores, a selection bias [E])."""
+    router variant (sigmoid scores, a selection bias [E]); n_group > 1 the
+    grouped routing (topk_group groups kept)."""
     logits = _c(logits, np.float32)
     T, E = logits.shape
     idx = np.empty((T, k), dtype=np.int32)
@@ -143,7 +146,7 @@ def router_topk(logits: np.ndarray, k: int, route_scale: float = 1.0, top_p: flo
     w64 = np.empty((T, k), dtype=np.float64)
     bias = _c(bias, np.float32)
     lib().oracle_router_topk(_p(logits), T, E, k, float(route_scale), float(top_p), GATES[gate],
-                             _p(bias), _p(idx), _p(w), _p(w64))
+                             _p(bias), int(n_group), int(topk_group), _p(idx), _p(w), _p(w64))
     return idx, w, w64
 
 
@@ -178,7 +181,8 @@ def expert_forward(gate, up, down, x64: np.ndarray, fmt: str = "int4"):
 def layer(x: np.ndarray, logits: np.ndarray, k: int, planes: Dict[str, tuple],
           shared: Optional[Dict[str, tuple]] = None, shared_gate: Optional[np.ndarray] = None,
           rows: Optional[Sequence[int]] = None, route_scale: float = 1.0, fmt: str = "int4",
-          top_p: float = 1.0, gate: str = "softmax", bias: Optional[np.ndarray] = None):
+          top_p: float = 1.0, gate: str = "softmax", bias: Optional[np.ndarray] = None,
+          n_group: int = 0, topk_group: int = 0):
     """The whole layer on the token rows ``rows`` (default: all).
 
     planes: {"gate": (q [E][I][H/2], s [E][I][H/32]), "up": ..., "down": (q [E][H][I/2], s)}
@@ -212,7 +216,7 @@ def layer(x: np.ndarray, logits: np.ndarray, k: int, planes: Dict[str, tuple],
     n = T if rows_a is None else len(rows_a)
     bias = _c(bias, np.float32)
     sh = _Shape(T, H, E, k, I, SI, float(route_scale), fid, float(top_p), GATES[gate],
-                None if bias is None else bias.ctypes.data)
+                None if bias is None else bias.ctypes.data, int(n_group), int(topk_group))
     y = np.empty((n, H), dtype=np.float32)
     idx = np.empty((n, k), dtype=np.int32)
     w = np.empty((n, k), dtype=np.float32)

@@ -240,18 +240,25 @@ int64_t top_p_row(const float* L, int64_t E, int64_t k, double top_p, double sca
 }
 
 // Router variants that [dasllama]'s MoE seat lists as declined shapes (a
-// non-softmax gate, a router or selection bias) without defining them.
-// Reading: the published DeepSeek-V3 routing without expert groups -
+// non-softmax gate, a router or selection bias) without defining them, and
+// the grouped noaux_tc router that [vllmcpp]'s router dispatch names without
+// defining it.  Reading: the published DeepSeek-V3 routing -
 //   score s_e = softmax(L)_e (gate 0) or sigmoid(L_e) (gate 1),
-//   selection key s_e + b_e (b the selection bias, zero when absent), the
-//   top-k keys in rank order, the lower index winning a tie,
+//   selection key s_e + b_e (b the selection bias, zero when absent);
+//   with n_group > 1 (grouped routing) the E experts form n_group groups of
+//   E / n_group consecutive experts, a group's score is the sum of its two
+//   largest keys (its one key for groups of one expert), the topk_group
+//   groups with the largest scores are kept (the lower group index winning
+//   a tie), and only the kept groups' experts can be picked;
+//   the top-k keys among the pickable experts in rank order, the lower
+//   index winning a tie,
 //   weights from the unbiased scores of the picks, renormalised to sum to
 //   one, times the routed scale: w_j = scale * s_j / sum_j' s_j'.
 // For the softmax gate the full denominator cancels in the weights, so they
 // are exp(L_j - m) / sum_j' exp(L_j' - m) with m the largest picked logit.
 // Everything in fp64.
-void variant_row(const float* L, int64_t E, int64_t k, int gate, const float* bias, double scale,
-                 int32_t* idx, double* w) {
+void variant_row(const float* L, int64_t E, int64_t k, int gate, const float* bias,
+                 int64_t n_group, int64_t topk_group, double scale, int32_t* idx, double* w) {
   std::vector<double> s(E), key(E);
   if (gate == 1) {
     for (int64_t e = 0; e < E; ++e) s[e] = sigmoid((double)L[e]);
@@ -263,11 +270,32 @@ void variant_row(const float* L, int64_t E, int64_t k, int gate, const float* bi
     for (int64_t e = 0; e < E; ++e) s[e] = std::exp((double)L[e] - m) / den;
   }
   for (int64_t e = 0; e < E; ++e) key[e] = s[e] + (bias ? (double)bias[e] : 0.0);
+  std::vector<char> pickable(E, 1);
+  if (n_group > 1) {
+    const int64_t gsz = E / n_group;
+    std::vector<double> gscore(n_group);
+    for (int64_t g = 0; g < n_group; ++g) {
+      // the group's keys, largest first
+      std::vector<double> kg(key.begin() + g * gsz, key.begin() + (g + 1) * gsz);
+      std::sort(kg.begin(), kg.end(), [](double a, double b) { return a > b; });
+      gscore[g] = gsz >= 2 ? kg[0] + kg[1] : kg[0];
+    }
+    std::vector<char> kept(n_group, 0);
+    for (int64_t j = 0; j < topk_group; ++j) {
+      int64_t best = -1;
+      for (int64_t g = 0; g < n_group; ++g) {
+        if (kept[g]) continue;
+        if (best < 0 || gscore[g] > gscore[best]) best = g;  // strict: lower index keeps a tie
+      }
+      kept[best] = 1;
+    }
+    for (int64_t e = 0; e < E; ++e) pickable[e] = kept[e / gsz];
+  }
   std::vector<char> taken(E, 0);
   for (int64_t j = 0; j < k; ++j) {
     int64_t best = -1;
     for (int64_t e = 0; e < E; ++e) {
-      if (taken[e]) continue;
+      if (taken[e] || !pickable[e]) continue;
       if (best < 0 || key[e] > key[best]) best = e;
     }
     taken[best] = 1;
@@ -279,16 +307,18 @@ void variant_row(const float* L, int64_t E, int64_t k, int gate, const float* bi
 }
 
 // One token row's routing: the plain softmax router (select_row,
-// weights_row, then the optional top-p), or a variant (variant_row; top-p is
-// not defined for variants and is ignored).  Returns the kept picks.
+// weights_row, then the optional top-p), or a variant, grouped or not
+// (variant_row; top-p is not defined for variants and is ignored).  Returns
+// the kept picks.  n_group <= 1 means no grouping.
 int64_t route_row(const float* L, int64_t E, int64_t k, double scale, double top_p, int gate,
-                  const float* bias, int32_t* idx, double* w) {
-  if (gate == 0 && !bias) {
+                  const float* bias, int64_t n_group, int64_t topk_group, int32_t* idx,
+                  double* w) {
+  if (gate == 0 && !bias && n_group <= 1) {
     select_row(L, E, k, idx);
     weights_row(L, idx, k, scale, w);
     return top_p_row(L, E, k, top_p, scale, idx, w);
   }
-  variant_row(L, E, k, gate, bias, scale, idx, w);
+  variant_row(L, E, k, gate, bias, n_group, topk_group, scale, idx, w);
   return k;
 }
 
@@ -349,15 +379,16 @@ void oracle_router_logits(const uint16_t* x, const float* wr, const float* gate_
 
 // Softmax -> top-k -> renormalise for every token row, then the optional
 // expert top-p (top_p_row; top_p outside (0, 1) = off); or a router variant
-// (gate 1 = sigmoid, bias [E] nullable: variant_row).  idx [T][k]
+// (gate 1 = sigmoid, bias [E] nullable, n_group > 1 grouped: variant_row).  idx [T][k]
 // position-major in rank order (-1 for a pick top-p drops), w [T][k] rounded
 // to fp32; w64 (nullable) receives the unrounded fp64 weights.
 void oracle_router_topk(const float* logits, int64_t T, int64_t E, int64_t k, double route_scale,
-                        double top_p, int gate, const float* bias, int32_t* idx, float* w,
-                        double* w64) {
+                        double top_p, int gate, const float* bias, int64_t n_group,
+                        int64_t topk_group, int32_t* idx, float* w, double* w64) {
   std::vector<double> wr(k);
   for (int64_t t = 0; t < T; ++t) {
-    route_row(logits + t * E, E, k, route_scale, top_p, gate, bias, idx + t * k, wr.data());
+    route_row(logits + t * E, E, k, route_scale, top_p, gate, bias, n_group, topk_group,
+              idx + t * k, wr.data());
     for (int64_t j = 0; j < k; ++j) {
       w[t * k + j] = (float)wr[j];
       if (w64) w64[t * k + j] = wr[j];
@@ -437,6 +468,7 @@ struct oracle_shape {
   double top_p;  // expert top-p after the top-k (outside (0, 1) = off)
   int64_t gate;  // router score: 0 = softmax, 1 = sigmoid
   const float* bias;  // selection bias [E], or null
+  int64_t n_group, topk_group;  // grouped routing (n_group <= 1: none)
 };
 
 // The whole layer for the token rows listed in `rows` (all T rows when rows is
@@ -471,7 +503,8 @@ void oracle_layer(const oracle_shape* sh, const uint16_t* x, const float* logits
     std::vector<int32_t> idx(k);
     std::vector<double> w(k);
     const int64_t kept = route_row(logits + t * E, E, k, sh->route_scale, sh->top_p,
-                                   (int)sh->gate, sh->bias, idx.data(), w.data());
+                                   (int)sh->gate, sh->bias, sh->n_group, sh->topk_group,
+                                   idx.data(), w.data());
     if (has_shared) {
       double gw = 1.0;
       if (shared_gate) {

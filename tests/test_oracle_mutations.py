@@ -87,6 +87,17 @@ MUTATIONS = {
     "variant_tie_to_higher_index": ("if (best < 0 || key[e] > key[best]) best = e;",
                                     "if (best < 0 || key[e] >= key[best]) best = e;",
                                     ["test_variant_ties_lower_index"]),
+    "group_score_top1_only": ("gscore[g] = gsz >= 2 ? kg[0] + kg[1] : kg[0];", "gscore[g] = kg[0];",
+                              ["test_grouped_closed_form", "test_grouped_brute_force"]),
+    "group_tie_to_higher_index": ("if (best < 0 || gscore[g] > gscore[best]) best = g;",
+                                  "if (best < 0 || gscore[g] >= gscore[best]) best = g;",
+                                  ["test_grouped_brute_force"]),
+    "masked_experts_keyed_zero": ("for (int64_t e = 0; e < E; ++e) pickable[e] = kept[e / gsz];",
+                                  "for (int64_t e = 0; e < E; ++e) if (!kept[e / gsz]) key[e] = 0.0;",
+                                  ["test_grouped_closed_form"]),
+    "groups_strided": ("for (int64_t e = 0; e < E; ++e) pickable[e] = kept[e / gsz];",
+                       "for (int64_t e = 0; e < E; ++e) pickable[e] = kept[e % n_group];",
+                       ["test_grouped_closed_form", "test_grouped_brute_force"]),
     "combine_uses_first_weight": ("acc[h] += w[j] * o[h];", "acc[h] += w[0] * o[h];",
                                   ["test_layer_equals_dense_masked_mixture"]),
 }

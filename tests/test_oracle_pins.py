@@ -720,3 +720,110 @@ def test_layer_variant_is_mixture_over_picks(orc):
         ref = (s[t, sel][:, None] * dense[t, sel]).sum(0) / s[t, sel].sum()
         assert list(idx[t]) == sel
         assert np.allclose(y[t], ref, rtol=1e-6, atol=1e-6 * np.abs(ref).max())
+
+
+# ------------------------------------------- grouped routing (noaux_tc) --
+
+def test_grouped_closed_form(orc):
+    """E = 8 in four groups of two, keep two groups, k = 2, sigmoid scores.
+    Expert 0 has the largest key, but its group's score (sigma(5) + sigma(-5)
+    = 1) ranks below groups 1 (2 sigma(2) = 1.76) and 2 (2 sigma(1) = 1.46),
+    so the picks are experts 2 and 3 (equal keys: the lower index first) at
+    weight 1/2 each; the plain top-2 would take expert 0.  A uniform negative
+    bias (every key below zero) changes nothing: experts outside the kept
+    groups are out of the selection, not given a key of zero."""
+    L = np.array([[5.0, -5.0, 2.0, 2.0, 1.0, 1.0, 0.0, 0.0]], np.float32)
+    idx, w, _ = orc.router_topk(L, 2, 1.0, gate="sigmoid", n_group=4, topk_group=2)
+    assert list(idx[0]) == [2, 3] and np.allclose(w[0], [0.5, 0.5], rtol=1e-12)
+    plain, _, _ = orc.router_topk(L, 2, 1.0, gate="sigmoid")
+    assert list(plain[0]) == [0, 2]
+    b = np.full(8, -1.0, np.float32)
+    idx, w, _ = orc.router_topk(L, 2, 3.0, gate="sigmoid", bias=b, n_group=4, topk_group=2)
+    assert list(idx[0]) == [2, 3] and np.allclose(w[0], [1.5, 1.5], rtol=1e-12)
+    # keep three groups, k = 3: group 3 (score 1.0) ties group 0 (1.0 up to
+    # rounding, sigma(5) + sigma(-5) in fp64), so the third kept group is one
+    # of them: with group 0, expert 0's key ranks first; with group 3, expert
+    # 4 (sigma(1)) is the third pick
+    idx, _, _ = orc.router_topk(L, 3, 1.0, gate="sigmoid", n_group=4, topk_group=3)
+    assert list(idx[0]) in ([0, 2, 3], [2, 3, 4])
+
+
+def _brute_grouped(key, s, k, n_group, topk_group):
+    """Picks and weights by exhaustion: the kept groups are the subset of
+    topk_group groups with the largest total score (the lexicographically
+    smallest such subset on ties), a group's score the sum of its two
+    largest keys; the picks a full stable sort of the kept experts.  Subsets
+    are compared by their scores sorted in descending order: the largest such
+    tuple is that of a largest-total subset (the top scores), and equal
+    tuples are equal totals, with no fp rounding of sums in the way."""
+    E = len(key)
+    gsz = E // n_group
+    gs = []
+    for g in range(n_group):
+        top = sorted(key[g * gsz:(g + 1) * gsz], reverse=True)
+        gs.append(top[0] + top[1] if gsz >= 2 else top[0])
+    best = None
+    for sub in itertools.combinations(range(n_group), topk_group):  # ascending tuples
+        tot = sorted((gs[g] for g in sub), reverse=True)
+        if best is None or tot > best[0]:
+            best = (tot, sub)
+    allowed = [e for e in range(E) if e // gsz in best[1]]
+    sel = sorted(allowed, key=lambda e: (-key[e], e))[:k]
+    w = np.array([s[e] for e in sel]) / sum(s[e] for e in sel)
+    return sel, w
+
+
+def test_grouped_brute_force(orc):
+    """Small rows with many exact ties (integer logits from {0, 1, 2}, biases
+    from three values): the oracle's grouped picks and weights against
+    exhaustion over the group subsets, for both score functions."""
+    for E, n_group, topk_group, k in [(8, 4, 2, 3), (12, 3, 2, 5), (12, 6, 3, 4), (16, 8, 4, 8),
+                                      (6, 6, 2, 2), (10, 2, 1, 5)]:
+        _grouped_brute_force_case(orc, E, n_group, topk_group, k)
+
+
+def _grouped_brute_force_case(orc, E, n_group, topk_group, k):
+    rng = np.random.default_rng(E * 100 + n_group * 10 + k)
+    T = 60
+    L = rng.integers(0, 3, (T, E)).astype(np.float32)
+    b = rng.choice(np.array([0.0, 0.125, -0.25], np.float32), E)
+    for gate in ("sigmoid", "softmax"):
+        idx, _, w64 = orc.router_topk(L, k, 1.0, gate=gate, bias=b, n_group=n_group,
+                                      topk_group=topk_group)
+        Ld = L.astype(np.float64)
+        s = scipy.special.expit(Ld) if gate == "sigmoid" else scipy.special.softmax(Ld, axis=1)
+        for t in range(T):
+            key = [float(s[t, e]) + float(b[e]) for e in range(E)]
+            sel, w = _brute_grouped(key, s[t], k, n_group, topk_group)
+            assert list(idx[t]) == sel, (gate, t)
+            assert np.allclose(w64[t], w, rtol=1e-12)
+
+
+def test_grouped_reductions(orc):
+    """Keeping every group, or groups of one expert with as many kept as
+    picks, is the ungrouped variant."""
+    rng = np.random.default_rng(53)
+    T, E, k = 40, 32, 6
+    L = (1.5 * rng.standard_normal((T, E))).astype(np.float32)
+    b = rng.normal(0, 0.05, E).astype(np.float32)
+    plain = orc.router_topk(L, k, 1.0, gate="sigmoid", bias=b)
+    for ng, tg in [(4, 4), (8, 8), (32, k)]:
+        g = orc.router_topk(L, k, 1.0, gate="sigmoid", bias=b, n_group=ng, topk_group=tg)
+        assert np.array_equal(plain[0], g[0]), (ng, tg)
+        assert np.array_equal(plain[2], g[2])
+
+
+def test_layer_grouped_is_mixture_over_picks(orc):
+    x, logits, planes, _ = _tiny_layer_inputs(seed=54, E=6)
+    T, E, k = x.shape[0], 6, 2
+    b = np.random.default_rng(55).normal(0, 0.3, E).astype(np.float32)
+    y, idx, w = orc.layer(x, logits, k, planes, gate="sigmoid", bias=b, n_group=3, topk_group=1)
+    dense = _expert_outputs(orc, x, planes, E)
+    s = scipy.special.expit(logits.astype(np.float64))
+    for t in range(T):
+        key = [float(s[t, e]) + float(b[e]) for e in range(E)]
+        sel, wt = _brute_grouped(key, s[t], k, 3, 1)
+        assert sel[0] // 2 == sel[1] // 2  # one kept group of two experts: both picked
+        ref = (wt[:, None] * dense[t, sel]).sum(0)
+        assert np.allclose(y[t], ref, rtol=1e-6, atol=1e-6 * np.abs(ref).max())
+        assert list(idx[t]) == sel
