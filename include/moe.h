@@ -112,11 +112,11 @@ typedef struct {
  * layout a moe_layout and format a moe_format (both for every plane of the
  * call, shared ones included), top_p the expert top-p applied after the
  * top-k (see moe_router_topk; 0, the zero-initialised value, keeps all k),
- * score a moe_score and select_bias a DEVICE pointer to fp32 [E] or NULL
- * (the router variant of moe_router_topk; zero-initialised = the plain
- * softmax router).
+ * score a moe_score and select_bias a DEVICE pointer to fp32 [E] or NULL,
+ * n_group and topk_group the grouped routing (the router variant of
+ * moe_router_topk; zero-initialised = the plain softmax router).
  * Served: 1 <= k <= min(E, 64), E <= 256, H % 64 == 0, I % 64 == 0,
- * SI % 64 == 0, T >= 1, T*k < 2^31. */
+ * SI % 64 == 0, T >= 1, T*k < 2^31, n_group <= 16. */
 typedef struct {
   int32_t T, H, E, k, I, SI;
   int32_t group;
@@ -127,6 +127,7 @@ typedef struct {
   float top_p;
   int32_t score;
   const float *select_bias;
+  int32_t n_group, topk_group;
 } moe_shape;
 
 /*
@@ -160,13 +161,26 @@ typedef struct {
  *            sum_j' s_j' over the picks (the bias steers the selection only).
  *            Top-p is not defined for variants: 0 < top_p < 1 with a variant
  *            is UNSUPPORTED.
+ *   n_group, topk_group : grouped routing (the noaux_tc router the vllm.cpp
+ *            PR's dispatch names without defining it; read as the published
+ *            DeepSeek-V3 grouped top-k).  n_group 0 or 1: no grouping.  With
+ *            n_group > 1 (dividing E, at most 16) the experts form n_group
+ *            groups of E / n_group consecutive experts; a group's score is
+ *            the sum of its two largest keys s_e + b_e (its one key for
+ *            groups of one expert), in fp64; the topk_group groups with the
+ *            largest scores are kept (the lower group index wins a tie) and
+ *            the picks are the k largest keys among the kept groups' experts
+ *            only, weighted as for the variants above.  A grouped router is
+ *            a variant (for top-p).
  * Errors: INVALID_ARG (null pointer, T < 1, k < 1, k > E, unknown score,
- *         misaligned select_bias); UNSUPPORTED (E > 256, k > 64, top-p with a
- *         variant).
+ *         misaligned select_bias, n_group < 0, n_group > 1 not dividing E,
+ *         topk_group outside 1..n_group, fewer than k experts in topk_group
+ *         groups); UNSUPPORTED (E > 256, k > 64, top-p with a variant,
+ *         n_group > 16).
  */
 int moe_router_topk(const float *logits, int32_t T, int32_t E, int32_t k, float route_scale,
-                    float top_p, int32_t score, const float *select_bias, int32_t *idx, float *w,
-                    moe_stream_t stream);
+                    float top_p, int32_t score, const float *select_bias, int32_t n_group,
+                    int32_t topk_group, int32_t *idx, float *w, moe_stream_t stream);
 
 /*
  * Token-to-expert permutation (the bucket schedule of the dasLLAMA PR's routed

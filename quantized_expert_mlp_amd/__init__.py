@@ -51,7 +51,8 @@ class moe_shape(ctypes.Structure):
                 ("group", ctypes.c_int32), ("route_scale", ctypes.c_float),
                 ("path", ctypes.c_int32), ("layout", ctypes.c_int32),
                 ("format", ctypes.c_int32), ("top_p", ctypes.c_float),
-                ("score", ctypes.c_int32), ("select_bias", ctypes.c_void_p)]
+                ("score", ctypes.c_int32), ("select_bias", ctypes.c_void_p),
+                ("n_group", ctypes.c_int32), ("topk_group", ctypes.c_int32)]
 
 
 _lib = None
@@ -65,7 +66,7 @@ def lib() -> ctypes.CDLL:
             raise RuntimeError("libmoe.so is not built: run python -m quantized_expert_mlp_amd.build")
         L = ctypes.CDLL(LIB_PATH)
         P, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
-        L.moe_router_topk.argtypes = [P, i32, i32, i32, f32, f32, i32, P, P, P, P]
+        L.moe_router_topk.argtypes = [P, i32, i32, i32, f32, f32, i32, P, i32, i32, P, P, P]
         L.moe_permute.argtypes = [P, i32, i32, i32, P, P, P, P, ctypes.c_size_t, P]
         L.moe_permute_workspace_bytes.argtypes = [i32, i32, i32]
         L.moe_permute_workspace_bytes.restype = ctypes.c_size_t
@@ -122,12 +123,13 @@ def _check(fn: str, rc: int) -> None:
 
 def make_shape(T, H, E, k, I, SI=0, route_scale=1.0, path=MOE_PATH_AUTO, group=32,
                layout=MOE_LAYOUT_ROWS, format=MOE_FORMAT_INT4, top_p=0.0,
-               score=MOE_SCORE_SOFTMAX, select_bias=None) -> moe_shape:
+               score=MOE_SCORE_SOFTMAX, select_bias=None, n_group=0,
+               topk_group=0) -> moe_shape:
     """select_bias: a device tensor fp32 [E] (or a raw pointer); the caller
     keeps it alive for as long as the shape is used."""
     return moe_shape(int(T), int(H), int(E), int(k), int(I), int(SI), int(group),
                      float(route_scale), int(path), int(layout), int(format), float(top_p),
-                     int(score), _ptr(select_bias))
+                     int(score), _ptr(select_bias), int(n_group), int(topk_group))
 
 
 def q4(plane: Tuple) -> moe_q4:
@@ -142,10 +144,11 @@ def moe_workspace_bytes(shape: moe_shape) -> int:
 
 
 def moe_router_topk(logits, T, E, k, route_scale, idx, w, stream=None, top_p=0.0,
-                    score=MOE_SCORE_SOFTMAX, select_bias=None) -> None:
+                    score=MOE_SCORE_SOFTMAX, select_bias=None, n_group=0, topk_group=0) -> None:
     _check("moe_router_topk", lib().moe_router_topk(_ptr(logits), T, E, k, route_scale, top_p,
-                                                    int(score), _ptr(select_bias), _ptr(idx),
-                                                    _ptr(w), _stream(stream)))
+                                                    int(score), _ptr(select_bias), int(n_group),
+                                                    int(topk_group), _ptr(idx), _ptr(w),
+                                                    _stream(stream)))
 
 
 def moe_permute_workspace_bytes(T, k, E) -> int:

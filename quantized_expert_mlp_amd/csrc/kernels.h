@@ -70,14 +70,24 @@ hipError_t launch_router_logits(const uint16_t* x, const float* wr, const float*
 //                 Plain softmax router only.
 //   score, bias : router variant.  score 0 = softmax probability, 1 = sigmoid
 //                 of the logit; bias (nullable, fp32 [E]) is added to the
-//                 score for the selection only.  With score 0 and no bias the
-//                 plain router runs (selection on the logits themselves).
+//                 score for the selection only.  With score 0, no bias and no
+//                 grouping the plain router runs (selection on the logits
+//                 themselves).
+//   n_group, topk_group : grouped routing when n_group > 1 (n_group divides
+//                 E, at most kMaxGroups; 1 <= topk_group <= n_group): only
+//                 the experts of the topk_group groups with the largest
+//                 top-2 key sums can be picked.
+constexpr int kMaxGroups = 16;
 struct RouterSpec {
   float route_scale;
   float top_p;
   int score;
   const float* bias;
-  __host__ __device__ bool variant() const { return score != 0 || bias != nullptr; }
+  int n_group = 0;
+  int topk_group = 0;
+  __host__ __device__ bool variant() const {
+    return score != 0 || bias != nullptr || n_group > 1;
+  }
 };
 
 hipError_t launch_topk(const float* logits, int ld, int T, int E, int k, const RouterSpec& rs,

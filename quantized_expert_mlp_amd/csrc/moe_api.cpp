@@ -24,18 +24,28 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-// Router variant checks: a known score function, an aligned bias, and top-p
-// only with the plain softmax router.
-int check_router(int32_t score, const float* bias, float top_p) {
+// Router variant checks: a known score function, an aligned bias, a grouping
+// that divides the experts into at most kMaxGroups groups whose kept part
+// holds at least k experts, and top-p only with the plain softmax router.
+int check_router(int32_t score, const float* bias, float top_p, int32_t n_group,
+                 int32_t topk_group, int32_t E, int32_t k) {
   if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
   if (bias && !aligned(bias, 4)) return MOE_ERR_INVALID_ARG;
-  const bool variant = score != MOE_SCORE_SOFTMAX || bias != nullptr;
+  if (n_group < 0) return MOE_ERR_INVALID_ARG;
+  if (n_group > 1) {
+    if (n_group > moe::kMaxGroups) return MOE_ERR_UNSUPPORTED;
+    if (E % n_group || topk_group < 1 || topk_group > n_group ||
+        (int64_t)topk_group * (E / n_group) < k)
+      return MOE_ERR_INVALID_ARG;
+  }
+  const bool variant = score != MOE_SCORE_SOFTMAX || bias != nullptr || n_group > 1;
   if (variant && top_p > 0.0f && top_p < 1.0f) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
 moe::RouterSpec router_spec(const moe_shape* sh) {
-  return moe::RouterSpec{sh->route_scale, sh->top_p, sh->score, sh->select_bias};
+  return moe::RouterSpec{sh->route_scale, sh->top_p,  sh->score,
+                         sh->select_bias, sh->n_group, sh->topk_group};
 }
 
 // Shape checks shared by every entry point that takes a moe_shape.
@@ -52,7 +62,8 @@ int check_shape(const moe_shape* sh) {
   if (sh->H % 64 || sh->I % 64 || sh->SI % 64) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)sh->T * sh->k >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)sh->T * sh->H >= (int64_t)1 << 40) return MOE_ERR_UNSUPPORTED;
-  return check_router(sh->score, sh->select_bias, sh->top_p);
+  return check_router(sh->score, sh->select_bias, sh->top_p, sh->n_group, sh->topk_group, sh->E,
+                      sh->k);
 }
 
 bool gemv_ok(const moe_shape* sh) {
@@ -273,16 +284,17 @@ size_t moe_workspace_bytes(const moe_shape* sh) {
 }
 
 int moe_router_topk(const float* logits, int32_t T, int32_t E, int32_t k, float route_scale,
-                    float top_p, int32_t score, const float* select_bias, int32_t* idx, float* w,
-                    moe_stream_t stream) {
+                    float top_p, int32_t score, const float* select_bias, int32_t n_group,
+                    int32_t topk_group, int32_t* idx, float* w, moe_stream_t stream) {
   if (!logits || !idx || !w || T < 1 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID_ARG;
   if (!aligned(logits, 4) || !aligned(idx, 4) || !aligned(w, 4)) return MOE_ERR_INVALID_ARG;
-  const int rc = check_router(score, select_bias, top_p);
+  const int rc = check_router(score, select_bias, top_p, n_group, topk_group, E, k);
   if (rc != MOE_OK) return rc;
   if (E > 256 || k > 64) return MOE_ERR_UNSUPPORTED;
-  return hip_status(moe::launch_topk(logits, E, T, E, k,
-                                     moe::RouterSpec{route_scale, top_p, score, select_bias},
-                                     idx, w, moe::Launch{reinterpret_cast<hipStream_t>(stream)}));
+  return hip_status(moe::launch_topk(
+      logits, E, T, E, k,
+      moe::RouterSpec{route_scale, top_p, score, select_bias, n_group, topk_group}, idx, w,
+      moe::Launch{reinterpret_cast<hipStream_t>(stream)}));
 }
 
 int moe_pack_weights(moe_q4 src, int32_t E, int32_t N, int32_t K, int32_t format, moe_q4 dst,

@@ -175,15 +175,22 @@ __device__ __forceinline__ void topk_group(const float* __restrict__ logits, int
 
 // Router variants (the dasLLAMA PR's MoE seat lists a non-softmax gate and a
 // router or selection bias among the shapes it declines, without defining
-// them; read as the published DeepSeek-V3 routing without expert groups):
-// score s_e = softmax(L)_e (rs.score 0) or sigmoid(L_e) (rs.score 1) in fp64,
-// selection key s_e + b_e (b = rs.bias, zero when null), the k largest keys
-// in rank order with the lower index winning a tie, and weights from the
-// picks' unbiased scores renormalised, times route_scale:
+// them; the vllm.cpp PR's dispatch names the grouped noaux_tc router; read
+// as the published DeepSeek-V3 routing): score s_e = softmax(L)_e (rs.score
+// 0) or sigmoid(L_e) (rs.score 1) in fp64, selection key s_e + b_e (b =
+// rs.bias, zero when null); with rs.n_group > 1 the experts form n_group
+// groups of E / n_group consecutive experts, a group scores the sum of its
+// two largest keys, and only the experts of the rs.topk_group best groups
+// (the lower group index winning a tie) stay in the selection; the k
+// largest keys in rank order with the lower index winning a tie, and
+// weights from the picks' unbiased scores renormalised, times route_scale:
 //   w_j = route_scale * s_j / sum_j' s_j'.
 // Same lane mapping as topk_group; the keys are fp64, so each round's
 // arg-max is a xor butterfly of (key, index, score) over the group's lanes.
-// Top-p does not apply.
+// Group scores: per expert group, each lane's two largest keys of that
+// group, merged by a xor butterfly; group g's score then sits in group lane
+// g (n_group <= kMaxGroups <= G), and the kept groups are found with the
+// same arg-max rounds over those lanes.  Top-p does not apply.
 __device__ __forceinline__ bool beats_d(double ov, int oi, double bv, int bi) {
   return (ov > bv) | ((ov == bv) & (oi < bi));
 }
@@ -236,6 +243,55 @@ __device__ void topk_group_variant(const float* __restrict__ logits, int ld, int
     const int e = gl + G * r;
     key[r] = live[r] ? sc[r] + (rs.bias ? (double)rs.bias[e] : 0.0) : ninf;
     id[r] = live[r] ? e : kRetired;
+  }
+  if (rs.n_group > 1) {  // uniform over the launch
+    const int ng = rs.n_group, gsz = E / ng;
+    double my_gs = ninf;  // group gl's score, held in group lane gl
+    for (int g = 0; g < ng; ++g) {
+      double a1 = ninf, a2 = ninf;  // this lane's two largest keys of group g
+#pragma unroll
+      for (int r = 0; r < V; ++r) {
+        const int e = gl + G * r;
+        const double kk = (live[r] && e / gsz == g) ? key[r] : ninf;
+        a2 = fmax(a2, fmin(a1, kk));
+        a1 = fmax(a1, kk);
+      }
+#pragma unroll
+      for (int o = G / 2; o > 0; o >>= 1) {  // top two of both lanes' top twos
+        const double b1 = __shfl_xor(a1, o, 64), b2 = __shfl_xor(a2, o, 64);
+        const double n2 = fmax(fmin(a1, b1), fmax(a2, b2));
+        a1 = fmax(a1, b1);
+        a2 = n2;
+      }
+      const double gsc = gsz >= 2 ? a1 + a2 : a1;
+      my_gs = gl == g ? gsc : my_gs;
+    }
+    uint32_t kept = 0;
+    double gv = gl < ng ? my_gs : ninf;
+    int gi = gl < ng ? gl : kRetired;
+    for (int j = 0; j < rs.topk_group; ++j) {
+      double bv = gv;
+      int bi = gi;
+#pragma unroll
+      for (int o = G / 2; o > 0; o >>= 1) {
+        const double ov = __shfl_xor(bv, o, 64);
+        const int oi = __shfl_xor(bi, o, 64);
+        const bool take = beats_d(ov, oi, bv, bi);
+        bv = take ? ov : bv;
+        bi = take ? oi : bi;
+      }
+      kept |= 1u << bi;  // every lane of the group holds the winner
+      const bool mine = gi == bi;
+      gv = mine ? ninf : gv;
+      gi = mine ? kRetired : gi;
+    }
+#pragma unroll
+    for (int r = 0; r < V; ++r) {  // experts of the other groups leave the selection
+      const int e = gl + G * r;
+      const bool out = live[r] && !((kept >> (e / gsz)) & 1u);
+      key[r] = out ? ninf : key[r];
+      id[r] = out ? kRetired : id[r];
+    }
   }
   int my_idx = -1;
   double my_s = 0.0;

@@ -65,19 +65,32 @@ FAKE = 1 << 20  # a non-null, 256-aligned address; never dereferenced by these c
 
 def test_router_topk_rejects(L):
     f = L.moe_router_topk
-    assert f(None, 4, 8, 2, 1.0, 0.0, 0, None, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
-    assert f(FAKE, 0, 8, 2, 1.0, 0.0, 0, None, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
-    assert f(FAKE, 4, 8, 9, 1.0, 0.0, 0, None, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
-    assert f(FAKE, 4, 8, 0, 1.0, 0.0, 0, None, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
-    assert f(FAKE + 2, 4, 8, 2, 1.0, 0.0, 0, None, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
-    assert f(FAKE, 4, 257, 2, 1.0, 0.0, 0, None, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
-    assert f(FAKE, 4, 256, 65, 1.0, 0.7, 0, None, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert f(None, 4, 8, 2, 1.0, 0.0, 0, None, 0, 0, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(FAKE, 0, 8, 2, 1.0, 0.0, 0, None, 0, 0, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(FAKE, 4, 8, 9, 1.0, 0.0, 0, None, 0, 0, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(FAKE, 4, 8, 0, 1.0, 0.0, 0, None, 0, 0, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(FAKE + 2, 4, 8, 2, 1.0, 0.0, 0, None, 0, 0, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(FAKE, 4, 257, 2, 1.0, 0.0, 0, None, 0, 0, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert f(FAKE, 4, 256, 65, 1.0, 0.7, 0, None, 0, 0, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
     # router variants: unknown score, misaligned bias, top-p with a variant
-    assert f(FAKE, 4, 8, 2, 1.0, 0.0, 2, None, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
-    assert f(FAKE, 4, 8, 2, 1.0, 0.0, -1, None, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
-    assert f(FAKE, 4, 8, 2, 1.0, 0.0, 0, FAKE + 2, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
-    assert f(FAKE, 4, 8, 2, 1.0, 0.5, 1, None, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
-    assert f(FAKE, 4, 8, 2, 1.0, 0.5, 0, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert f(FAKE, 4, 8, 2, 1.0, 0.0, 2, None, 0, 0, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(FAKE, 4, 8, 2, 1.0, 0.0, -1, None, 0, 0, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(FAKE, 4, 8, 2, 1.0, 0.0, 0, FAKE + 2, 0, 0, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(FAKE, 4, 8, 2, 1.0, 0.5, 1, None, 0, 0, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert f(FAKE, 4, 8, 2, 1.0, 0.5, 0, FAKE, 0, 0, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    # grouped routing: E % n_group, topk_group range, enough kept experts,
+    # at most 16 groups, no top-p
+    G = lambda ng, tg, k=2, E=8, p=0.0: f(FAKE, 4, E, k, 1.0, p, 1, None, ng, tg, FAKE, FAKE, None)
+    assert G(3, 1) == moe.MOE_ERR_INVALID_ARG                       # 8 % 3
+    assert G(4, 0) == moe.MOE_ERR_INVALID_ARG
+    assert G(4, 5) == moe.MOE_ERR_INVALID_ARG
+    assert G(4, 1, k=3) == moe.MOE_ERR_INVALID_ARG                  # one group of 2 < k
+    assert G(-1, 0) == moe.MOE_ERR_INVALID_ARG
+    assert G(32, 4, E=64) == moe.MOE_ERR_UNSUPPORTED
+    assert G(4, 2, p=0.5) == moe.MOE_ERR_UNSUPPORTED
+    assert moe.moe_workspace_bytes(_shape(n_group=4, topk_group=2)) > 0
+    assert moe.moe_workspace_bytes(_shape(n_group=3, topk_group=1)) == 0
+    assert moe.moe_workspace_bytes(_shape(n_group=4, topk_group=1, k=4)) == 0
 
 
 def test_permute_rejects(L):
