@@ -57,6 +57,8 @@ def lib():
         L.oracle_expert_forward.argtypes = [P] * 6 + [i64, i64, P, P, P, ctypes.c_int]
         L.oracle_layer.argtypes = [P] * 13 + [i64, P, P, P]
         L.oracle_add_rmsnorm.argtypes = [P, P, P, i64, i64, ctypes.c_double, P, P]
+        L.oracle_add_rmsnorm_router.argtypes = [P, P, P, i64, i64, ctypes.c_double, P, i64, P,
+                                                P, P]
         L.oracle_double_to_bf16.argtypes = [ctypes.c_double]
         L.oracle_double_to_bf16.restype = ctypes.c_uint16
         _lib = L
@@ -241,3 +243,21 @@ def add_rmsnorm(r: np.ndarray, y: np.ndarray, g: np.ndarray, eps: float):
     n_out = np.empty((T, H), dtype=np.uint16)
     lib().oracle_add_rmsnorm(_p(r), _p(y), _p(g), T, H, float(eps), _p(r_out), _p(n_out))
     return r_out, n_out
+
+
+def add_rmsnorm_router(r: np.ndarray, y: np.ndarray, g: np.ndarray, eps: float,
+                       w_router: np.ndarray):
+    """add_rmsnorm followed by the next layer's router logits of the bf16
+    normed row: (r + y fp32 [T][H], bf16 bits [T][H], logits fp32 [T][E])."""
+    r = _c(r, np.float32)
+    y = _c(y, np.float32)
+    g = _c(g, np.float32)
+    w_router = _c(w_router, np.float32)
+    T, H = r.shape
+    E = w_router.shape[0]
+    r_out = np.empty((T, H), dtype=np.float32)
+    n_out = np.empty((T, H), dtype=np.uint16)
+    logits = np.empty((T, E), dtype=np.float32)
+    lib().oracle_add_rmsnorm_router(_p(r), _p(y), _p(g), T, H, float(eps), _p(w_router), E,
+                                    _p(r_out), _p(n_out), _p(logits))
+    return r_out, n_out, logits

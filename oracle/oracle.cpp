@@ -461,6 +461,21 @@ void oracle_add_rmsnorm(const float* r, const float* y, const float* g, int64_t 
 
 uint16_t oracle_double_to_bf16(double v) { return double_to_bf16(v); }
 
+// The residual step with the next layer's router folded in ([dasllama-fold]
+// norms the row for the next layer; the vllm.cpp PR's closing hypotheses
+// fold the router into the preceding kernel): oracle_add_rmsnorm, then the
+// next layer's router logits of the bf16 normed row n_out, as
+// oracle_router_logits computes them (fp64 sums of the exact products,
+// rounded to fp32): logits[t][e] = sum_h n_out[t][h] * wr[e][h], [T][E].
+// Reading: the router reads the row in the activation format the next
+// layer receives (bf16), not the unrounded fp64 norm.
+void oracle_add_rmsnorm_router(const float* r, const float* y, const float* g, int64_t T,
+                               int64_t H, double eps, const float* wr, int64_t E, float* r_out,
+                               uint16_t* n_out, float* logits) {
+  oracle_add_rmsnorm(r, y, g, T, H, eps, r_out, n_out);
+  oracle_router_logits(n_out, wr, nullptr, T, H, E, logits);
+}
+
 struct oracle_shape {
   int64_t T, H, E, k, I, SI;
   double route_scale;

@@ -98,6 +98,12 @@ MUTATIONS = {
     "groups_strided": ("for (int64_t e = 0; e < E; ++e) pickable[e] = kept[e / gsz];",
                        "for (int64_t e = 0; e < E; ++e) pickable[e] = kept[e % n_group];",
                        ["test_grouped_closed_form", "test_grouped_brute_force"]),
+    "folded_router_first_row_only": ("oracle_router_logits(n_out, wr, nullptr, T, H, E, logits);",
+                                     "oracle_router_logits(n_out, wr, nullptr, 1, H, E, logits);",
+                                     ["test_add_rmsnorm_router_one_hot_rows"]),
+    "folded_router_rows_off_by_one": ("oracle_router_logits(n_out, wr, nullptr, T, H, E, logits);",
+                                       "oracle_router_logits(n_out, wr + H, nullptr, T, H, E - 1, logits);",
+                                       ["test_add_rmsnorm_router_one_hot_rows"]),
     "combine_uses_first_weight": ("acc[h] += w[j] * o[h];", "acc[h] += w[0] * o[h];",
                                   ["test_layer_equals_dense_masked_mixture"]),
 }

@@ -827,3 +827,51 @@ def test_layer_grouped_is_mixture_over_picks(orc):
         ref = (wt[:, None] * dense[t, sel]).sum(0)
         assert np.allclose(y[t], ref, rtol=1e-6, atol=1e-6 * np.abs(ref).max())
         assert list(idx[t]) == sel
+
+
+# ------------------------------- residual step with the next router folded --
+
+def test_add_rmsnorm_router_one_hot_rows(orc):
+    """One-hot router rows read single features of the bf16 normed row
+    exactly (a product by one, no sum), and a row of twos doubles it; the
+    first outputs equal add_rmsnorm's."""
+    rng = np.random.default_rng(57)
+    T, H = 4, 256
+    r = rng.standard_normal((T, H)).astype(np.float32)
+    y = (0.1 * rng.standard_normal((T, H))).astype(np.float32)
+    g = (1.0 + 0.2 * rng.standard_normal(H)).astype(np.float32)
+    cols = [0, 17, 255, 128]
+    W = np.zeros((len(cols) + 1, H), np.float32)
+    for e, c in enumerate(cols):
+        W[e, c] = 1.0
+    W[-1, 3] = 2.0
+    r_out, n_out, L = orc.add_rmsnorm_router(r, y, g, 1e-6, W)
+    r2, n2 = orc.add_rmsnorm(r, y, g, 1e-6)
+    assert np.array_equal(r_out, r2) and np.array_equal(n_out, n2)
+    nf = S.bf16_bits_to_f32(n_out)
+    assert np.array_equal(L[:, :len(cols)], nf[:, cols])
+    assert np.array_equal(L[:, -1], 2.0 * nf[:, 3])
+
+
+def test_add_rmsnorm_router_matches_library(orc):
+    """The logits are the fp64 matrix product of the bf16 normed row (as
+    bf16, not the unrounded norm) with the router plane, rounded to fp32;
+    checked against torch's rms_norm, bf16 rounding and float64 matmul."""
+    import torch
+    rng = np.random.default_rng(58)
+    T, H, E, eps = 6, 512, 24, 1e-5
+    r = rng.standard_normal((T, H)).astype(np.float32)
+    y = (0.1 * rng.standard_normal((T, H))).astype(np.float32)
+    g = (1.0 + 0.2 * rng.standard_normal(H)).astype(np.float32)
+    W = rng.normal(0, 0.02, (E, H)).astype(np.float32)
+    _, n_out, L = orc.add_rmsnorm_router(r, y, g, eps, W)
+    r64 = torch.from_numpy((r.astype(np.float64) + y.astype(np.float64)).astype(np.float32)
+                           .astype(np.float64))
+    nrm = torch.nn.functional.rms_norm(r64, (H,), torch.from_numpy(g.astype(np.float64)), eps)
+    xb = nrm.to(torch.bfloat16).to(torch.float64)
+    assert np.array_equal(S.f32_to_bf16_bits(xb.numpy().astype(np.float32)), n_out)
+    ref = (xb @ torch.from_numpy(W.astype(np.float64)).T).numpy().astype(np.float32)
+    assert np.max(np.abs(L - ref) / np.maximum(np.abs(ref), 1e-30)) <= 2.0 ** -24 * 1.0001
+    # the unrounded norm would give different logits
+    unrounded = (nrm @ torch.from_numpy(W.astype(np.float64)).T).numpy().astype(np.float32)
+    assert not np.array_equal(L, unrounded)
