@@ -414,6 +414,55 @@ def measure(wl, args, layout, path_name, hip, steps, warmup, fold=False):
     }
 
 
+def fold_router_chain(wl, args, hip, steps, warmup):
+    """The decode layer chained through its residual step, two ways, each
+    step a full layer: (a) the step's own router GEMM launch from w_router
+    (moe_layer_residual_rmsnorm with w_router), (b) the router folded into the
+    previous step's norm launch (next_w_router), its logits the given logits
+    of the next step.  Returns ms/step of both."""
+    import torch
+
+    import quantized_expert_mlp_amd as moe
+
+    sets = build_sets(wl, 1)
+    s = sets[0]
+    W = torch.from_numpy(np.random.default_rng([wl.wid, 92]).normal(
+        0.0, 0.02, (wl.E, wl.H)).astype(np.float32)).cuda()
+    sh = moe.make_shape(wl.T, wl.H, wl.E, wl.k, wl.I, wl.SI)
+    nbytes = moe.moe_workspace_bytes(sh)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    residual = torch.from_numpy(S.draw_residual(wl)).cuda()
+    norm_w = torch.from_numpy(S.draw_norm_weight(wl)).cuda()
+    x = [s["x"].clone(), s["x"].clone()]
+    lg = [torch.from_numpy(S.draw_logits(wl, seed=100)).cuda(),
+          torch.empty((wl.T, wl.E), dtype=torch.float32, device="cuda")]
+    P = s["planes"]
+
+    def step_unfused(i):
+        moe.moe_layer_residual_rmsnorm(sh, x[i % 2], None, W, P["gate"], P["up"], P["down"],
+                                       s["shared"], s["shared_gate"], residual, norm_w, 1e-6,
+                                       x[(i + 1) % 2], None, None, ws, nbytes)
+
+    def step_folded(i):
+        moe.moe_layer_residual_rmsnorm(sh, x[i % 2], lg[i % 2], None, P["gate"], P["up"],
+                                       P["down"], s["shared"], s["shared_gate"], residual, norm_w,
+                                       1e-6, x[(i + 1) % 2], None, None, ws, nbytes,
+                                       next_w_router=W, next_E=wl.E, next_logits=lg[(i + 1) % 2])
+
+    out = {}
+    for name, fn in (("own_router_launch", step_unfused), ("router_folded_into_norm", step_folded)):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            fn(i)
+        torch.cuda.synchronize()
+        out[name] = round((time.perf_counter() - t0) * 1e3 / steps, 5)
+        log("fold chain %s: %.2f us/step" % (name, out[name] * 1e3))
+    return out
+
+
 def read_probe(hip):
     """Best streaming-read rate of moe_debug_read_probe over sizes and
     launch widths (the practical HBM read ceiling for the decode GEMVs)."""
@@ -478,6 +527,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy (HBM counter calibration)")
+    ap.add_argument("--fold-router", action="store_true",
+                    help="only time the layer chained through its residual step with its own "
+                         "router GEMM launch against the router folded into the previous "
+                         "step's norm launch, and print both")
     ap.add_argument("--probe-read", action="store_true",
                     help="only run the streaming-read probe (moe_debug_read_probe) and print "
                          "its rates")
@@ -510,6 +563,12 @@ def main():
         return
     if args.router != "softmax" and 0.0 < args.top_p < 1.0:
         sys.exit("bench.py: --top-p applies to the plain softmax router only")
+    if args.fold_router:
+        wl = S.WORKLOADS[args.workload]
+        print(json.dumps({"fold_router_chain": wl.name, "steps": args.steps,
+                          "ms_per_step": fold_router_chain(wl, args, hip, args.steps,
+                                                           args.warmup)}), flush=True)
+        return
 
     wl = S.WORKLOADS[args.workload]
     m = measure(wl, args, args.layout, args.path, hip, args.steps, args.warmup, fold=args.fold)

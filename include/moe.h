@@ -305,22 +305,36 @@ int moe_layer_static(const moe_shape *shape, const uint16_t *x, const float *log
  * The down pass adds into `residual` directly (no separate FFN output), and
  * one more launch writes the normed row in the layer's activation format, so
  * x_next can be the next layer's x.
+ * With next_w_router, that launch also computes the next layer's router
+ * logits from the bf16 normed rows (the vllm.cpp PR's closing hypothesis:
+ * the router folded into the preceding kernel, fewer launches per step):
+ *   next_logits[t][e] = sum_h x_next[t][h] * next_w_router[e][h]   (fp32)
+ * so the next layer's call can take them as its given logits instead of
+ * launching its own router GEMM.  Up to 32 tokens and H <= 6144 this is one
+ * launch; beyond, the norm launch is followed by the router-logits kernel
+ * over x_next (the same logits, up to fp32 summation order).
  *   residual : fp32 [T][H], in/out, 16-byte aligned; must not overlap any
  *              other argument.
  *   norm_w   : fp32 [H], the next layer's norm weight, 16-byte aligned.
  *   eps      : >= 0, added to the mean square inside the root.
  *   x_next   : bf16 bits [T][H] out, 16-byte aligned; may be x itself (x is
  *              no longer read when it is written).
+ *   next_w_router : fp32 [next_E][H], 16-byte aligned, the next layer's
+ *              router plane, or NULL (then next_logits must be NULL too and
+ *              next_E is ignored).
+ *   next_logits : fp32 [T][next_E] out, or NULL.
  *   the rest : as for moe_layer (no logits_out).
  * The order of the terms added into a residual element is not fixed (device
  * atomics); the result differs from an ordered sum by fp32 rounding only.
  * Errors: as moe_layer, plus INVALID_ARG for a null or misaligned residual,
- *         norm_w or x_next, or a negative or NaN eps.
+ *         norm_w, x_next or next_w_router, a negative or NaN eps, exactly one
+ *         of next_w_router / next_logits given, or next_E < 1 with them.
  */
 int moe_layer_residual_rmsnorm(const moe_shape *shape, const uint16_t *x, const float *logits,
                                const float *w_router, moe_q4 gate, moe_q4 up, moe_q4 down,
                                const moe_q4 *shared, const float *shared_gate, float *residual,
                                const float *norm_w, float eps, uint16_t *x_next,
+                               const float *next_w_router, int32_t next_E, float *next_logits,
                                int32_t *idx_out, float *w_out, void *ws, size_t ws_bytes,
                                moe_stream_t stream);
 

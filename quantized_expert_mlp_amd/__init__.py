@@ -79,7 +79,7 @@ def lib() -> ctypes.CDLL:
         L.moe_layer_static.argtypes = L.moe_layer.argtypes[:13] + [P]
         L.moe_layer_residual_rmsnorm.argtypes = [
             ctypes.POINTER(moe_shape), P, P, P, moe_q4, moe_q4, moe_q4, ctypes.POINTER(moe_q4), P,
-            P, P, ctypes.c_float, P, P, P, P, ctypes.c_size_t, P]
+            P, P, ctypes.c_float, P, P, i32, P, P, P, P, ctypes.c_size_t, P]
         L.moe_workspace_bytes.argtypes = [ctypes.POINTER(moe_shape)]
         L.moe_workspace_bytes.restype = ctypes.c_size_t
         L.moe_status_string.argtypes = [ctypes.c_int]
@@ -197,16 +197,19 @@ def moe_layer_static(shape: moe_shape, x, logits, w_router, gate, up, down,
 
 def moe_layer_residual_rmsnorm(shape: moe_shape, x, logits, w_router, gate, up, down,
                                shared: Optional[Sequence[Tuple]], shared_gate, residual, norm_w,
-                               eps, x_next, idx_out, w_out, ws, ws_bytes, stream=None) -> None:
+                               eps, x_next, idx_out, w_out, ws, ws_bytes, stream=None,
+                               next_w_router=None, next_E=0, next_logits=None) -> None:
     """moe_layer whose combine adds into `residual` (fp32, in/out), followed by
-    x_next = bf16(RMSnorm(residual) * norm_w)."""
+    x_next = bf16(RMSnorm(residual) * norm_w), and with next_w_router
+    ([next_E][H] fp32) the next layer's logits of x_next into next_logits."""
     sh_arr = None
     if shared is not None:
         sh_arr = (moe_q4 * 3)(*[q4(p) for p in shared])
     _check("moe_layer_residual_rmsnorm", lib().moe_layer_residual_rmsnorm(
         ctypes.byref(shape), _ptr(x), _ptr(logits), _ptr(w_router), q4(gate), q4(up), q4(down),
         sh_arr, _ptr(shared_gate), _ptr(residual), _ptr(norm_w), float(eps), _ptr(x_next),
-        _ptr(idx_out), _ptr(w_out), _ptr(ws), int(ws_bytes), _stream(stream)))
+        _ptr(next_w_router), int(next_E), _ptr(next_logits), _ptr(idx_out), _ptr(w_out),
+        _ptr(ws), int(ws_bytes), _stream(stream)))
 
 
 def moe_layer_profiled(shape: moe_shape, x, logits, w_router, gate, up, down,

@@ -161,6 +161,20 @@ hipError_t launch_pack_weights(const uint8_t* sq, const void* ss, int E, int N, 
 hipError_t launch_rmsnorm(const float* r, const float* g, int T, int H, float eps, uint16_t* out,
                           const Launch& L);
 
+// The same, plus the next layer's router logits of the normed bf16 rows,
+// logits[t][e] = sum_h n[t][h] * wr[e][h] (fp32 [T][E]).  One launch (the
+// router folded into the norm kernel) when fold_router_served(T, H); else
+// the norm launch and then the router-logits kernel over n.
+constexpr int kFoldRouterRows = 4;     // token rows per workgroup of the fold
+constexpr int kFoldRouterMaxT = 32;    // larger batches take the two launches
+constexpr int kFoldRouterMaxH = 6144;  // the normed rows live in LDS (48 KiB)
+__host__ __device__ constexpr bool fold_router_served(int T, int H) {
+  return T <= kFoldRouterMaxT && H <= kFoldRouterMaxH;
+}
+hipError_t launch_rmsnorm_router(const float* r, const float* g, int T, int H, float eps,
+                                 uint16_t* out, const float* wr, int E, float* logits,
+                                 const Launch& L);
+
 // bf16 x [T][H] -> fp16 copy with each block of 8 in the order 0,4,1,5,2,6,3,7.
 hipError_t launch_convert_x16(const uint16_t* x, int T, int H, uint16_t* x16, const Launch& L);
 

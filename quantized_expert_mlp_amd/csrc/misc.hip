@@ -32,14 +32,10 @@ hipError_t launch_convert_x16(const uint16_t* x, int T, int H, uint16_t* x16, co
 // thread per pass, the sum of squares in fp32 (wave DPP sums, then LDS across
 // the 4 waves), one IEEE divide and square root per row, then a second pass
 // over the row (L2-resident) for the products, rounded to nearest even.
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ r,
-                                                      const float* __restrict__ g, int H,
-                                                      float eps, uint16_t* __restrict__ out) {
-  __shared__ float part[4];
-  const int64_t row = blockIdx.x;
-  const float4* r4 = reinterpret_cast<const float4*>(r + row * H);
-  const float4* g4 = reinterpret_cast<const float4*>(g);
-  const int n4 = H / 4;
+// Every thread of the 256-thread workgroup calls row_inv_rms; part holds 4
+// floats.
+__device__ __forceinline__ float row_inv_rms(const float4* __restrict__ r4, int n4, int H,
+                                             float eps, float* part) {
   float ss = 0.f;
   for (int i = threadIdx.x; i < n4; i += 256) {
     const float4 v = r4[i];
@@ -49,19 +45,105 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
   if ((threadIdx.x & 63) == 63) part[threadIdx.x >> 6] = ss;
   __syncthreads();
   const float tot = (part[0] + part[1]) + (part[2] + part[3]);
-  const float inv = 1.0f / sqrtf(tot / (float)H + eps);
+  return 1.0f / sqrtf(tot / (float)H + eps);
+}
+
+__device__ __forceinline__ uint2 norm4_bf16(float4 v, float4 w, float inv) {
+  const uint32_t b0 = f32_to_bf16_rne(v.x * inv * w.x), b1 = f32_to_bf16_rne(v.y * inv * w.y);
+  const uint32_t b2 = f32_to_bf16_rne(v.z * inv * w.z), b3 = f32_to_bf16_rne(v.w * inv * w.w);
+  return make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+}
+
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ r,
+                                                      const float* __restrict__ g, int H,
+                                                      float eps, uint16_t* __restrict__ out) {
+  __shared__ float part[4];
+  const int64_t row = blockIdx.x;
+  const float4* r4 = reinterpret_cast<const float4*>(r + row * H);
+  const float4* g4 = reinterpret_cast<const float4*>(g);
+  const int n4 = H / 4;
+  const float inv = row_inv_rms(r4, n4, H, eps, part);
   uint2* o4 = reinterpret_cast<uint2*>(out + row * H);
-  for (int i = threadIdx.x; i < n4; i += 256) {
-    const float4 v = r4[i], w = g4[i];
-    const uint32_t b0 = f32_to_bf16_rne(v.x * inv * w.x), b1 = f32_to_bf16_rne(v.y * inv * w.y);
-    const uint32_t b2 = f32_to_bf16_rne(v.z * inv * w.z), b3 = f32_to_bf16_rne(v.w * inv * w.w);
-    o4[i] = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
-  }
+  for (int i = threadIdx.x; i < n4; i += 256) o4[i] = norm4_bf16(r4[i], g4[i], inv);
 }
 
 hipError_t launch_rmsnorm(const float* r, const float* g, int T, int H, float eps, uint16_t* out,
                           const Launch& L) {
   MOE_LAUNCH(L, rmsnorm_kernel, dim3(T), dim3(256), 0, r, g, H, eps, out);
+  return hipGetLastError();
+}
+
+// The same step with the next layer's router folded into its epilogue (the
+// vllm.cpp PR's closing hypothesis: the router folded into the preceding
+// kernel, fewer launches per step).  Workgroup (bx, by) takes token rows
+// by*kFoldRouterRows .. +kFoldRouterRows-1: it normalises them exactly as
+// rmsnorm_kernel does (every workgroup of a row block recomputes the norm
+// from the L2-resident residual rows), keeps the bf16 rows in LDS, writes
+// them to out when bx == 0, and wave w computes router row e = 4*bx + w of
+// the next layer's logits, L[t][e] = sum_h float(n[t][h]) * wr[e][h] in fp32
+// (16-byte router loads, a DPP sum across the wave).  Dynamic LDS:
+// kFoldRouterRows * H bf16.
+__global__ __launch_bounds__(256) void rmsnorm_router_kernel(
+    const float* __restrict__ r, const float* __restrict__ g, int T, int H, float eps,
+    uint16_t* __restrict__ out, const float* __restrict__ wr, int E, float* __restrict__ logits) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
+  __shared__ float part[kFoldRouterRows][4];
+  const int t0 = blockIdx.y * kFoldRouterRows;
+  const int nt = min(kFoldRouterRows, T - t0);
+  const int n4 = H / 4;
+  const float4* g4 = reinterpret_cast<const float4*>(g);
+  for (int tt = 0; tt < nt; ++tt) {
+    const float4* r4 = reinterpret_cast<const float4*>(r + (int64_t)(t0 + tt) * H);
+    const float inv = row_inv_rms(r4, n4, H, eps, part[tt]);
+    uint2* x4 = reinterpret_cast<uint2*>(xs + tt * H);
+    uint2* o4 = reinterpret_cast<uint2*>(out + (int64_t)(t0 + tt) * H);
+    for (int i = threadIdx.x; i < n4; i += 256) {
+      const uint2 b = norm4_bf16(r4[i], g4[i], inv);
+      x4[i] = b;
+      if (blockIdx.x == 0) o4[i] = b;
+    }
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (e >= E) return;
+  const float4* w4 = reinterpret_cast<const float4*>(wr + (int64_t)e * H);
+  float acc[kFoldRouterRows];
+#pragma unroll
+  for (int tt = 0; tt < kFoldRouterRows; ++tt) acc[tt] = 0.f;
+#pragma unroll 4
+  for (int i = lane; i < n4; i += 64) {
+    const float4 w = w4[i];
+#pragma unroll
+    for (int tt = 0; tt < kFoldRouterRows; ++tt) {
+      if (tt < nt) {
+        const uint2 b = reinterpret_cast<const uint2*>(xs + tt * H)[i];
+        acc[tt] += bf16_to_f32(b.x & 0xFFFFu) * w.x + bf16_to_f32(b.x >> 16) * w.y +
+                   bf16_to_f32(b.y & 0xFFFFu) * w.z + bf16_to_f32(b.y >> 16) * w.w;
+      }
+    }
+  }
+#pragma unroll
+  for (int tt = 0; tt < kFoldRouterRows; ++tt) {
+    const float v = group_sum<64>(acc[tt]);
+    if (lane == 63 && tt < nt) logits[(int64_t)(t0 + tt) * E + e] = v;
+  }
+}
+
+hipError_t launch_rmsnorm_router(const float* r, const float* g, int T, int H, float eps,
+                                 uint16_t* out, const float* wr, int E, float* logits,
+                                 const Launch& L) {
+  if (!fold_router_served(T, H)) {
+    // large batches: the norm launch, then the router-logits kernel over the
+    // normed rows (the same logits, two launches)
+    const Launch first{L.st, L.start, nullptr}, last{L.st, nullptr, L.stop};
+    MOE_LAUNCH(first, rmsnorm_kernel, dim3(T), dim3(256), 0, r, g, H, eps, out);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_router_logits(out, wr, nullptr, T, H, E, logits, E, nullptr, last);
+  }
+  const dim3 grid((E + 3) / 4, (T + kFoldRouterRows - 1) / kFoldRouterRows);
+  MOE_LAUNCH(L, rmsnorm_router_kernel, grid, dim3(256),
+             (size_t)kFoldRouterRows * H * sizeof(uint16_t), r, g, T, H, eps, out, wr, E, logits);
   return hipGetLastError();
 }
 

@@ -493,18 +493,26 @@ int moe_layer_residual_rmsnorm(const moe_shape* sh, const uint16_t* x, const flo
                                const float* w_router, moe_q4 gate, moe_q4 up, moe_q4 down,
                                const moe_q4* shared, const float* shared_gate, float* residual,
                                const float* norm_w, float eps, uint16_t* x_next,
+                               const float* next_w_router, int32_t next_E, float* next_logits,
                                int32_t* idx_out, float* w_out, void* ws, size_t ws_bytes,
                                moe_stream_t stream) {
   if (!residual || !norm_w || !x_next || !aligned(residual, 16) || !aligned(norm_w, 16) ||
       !aligned(x_next, 16) || !(eps >= 0.0f))
+    return MOE_ERR_INVALID_ARG;
+  if ((next_w_router == nullptr) != (next_logits == nullptr)) return MOE_ERR_INVALID_ARG;
+  if (next_w_router &&
+      (next_E < 1 || !aligned(next_w_router, 16) || !aligned(next_logits, 4)))
     return MOE_ERR_INVALID_ARG;
   if (sh && sh->H % 4) return MOE_ERR_UNSUPPORTED;
   const int rc = layer_impl(sh, x, logits, w_router, gate, up, down, shared, shared_gate,
                             residual, idx_out, w_out, nullptr, ws, ws_bytes, stream, nullptr,
                             true);
   if (rc != MOE_OK) return rc;
-  return hip_status(moe::launch_rmsnorm(residual, norm_w, sh->T, sh->H, eps, x_next,
-                                        moe::Launch{reinterpret_cast<hipStream_t>(stream)}));
+  const moe::Launch L{reinterpret_cast<hipStream_t>(stream)};
+  if (next_w_router)
+    return hip_status(moe::launch_rmsnorm_router(residual, norm_w, sh->T, sh->H, eps, x_next,
+                                                 next_w_router, next_E, next_logits, L));
+  return hip_status(moe::launch_rmsnorm(residual, norm_w, sh->T, sh->H, eps, x_next, L));
 }
 
 int moe_layer_profiled(const moe_shape* sh, const uint16_t* x, const float* logits,

@@ -150,9 +150,10 @@ def test_residual_rmsnorm_rejects(L):
     need = moe.moe_workspace_bytes(sh)
     f = L.moe_layer_residual_rmsnorm
 
-    def call(residual=FAKE, norm_w=FAKE, eps=1e-6, x_next=FAKE, shape=sh):
+    def call(residual=FAKE, norm_w=FAKE, eps=1e-6, x_next=FAKE, shape=sh, nwr=None, nE=0,
+             nlog=None):
         return f(ctypes.byref(shape), FAKE, FAKE, None, _q(), _q(), _q(), None, None, residual,
-                 norm_w, eps, x_next, None, None, FAKE, need, None)
+                 norm_w, eps, x_next, nwr, nE, nlog, None, None, FAKE, need, None)
 
     assert call(residual=None) == moe.MOE_ERR_INVALID_ARG
     assert call(norm_w=None) == moe.MOE_ERR_INVALID_ARG
@@ -162,6 +163,12 @@ def test_residual_rmsnorm_rejects(L):
     assert call(eps=-1.0) == moe.MOE_ERR_INVALID_ARG
     assert call(eps=float("nan")) == moe.MOE_ERR_INVALID_ARG
     assert call(shape=_shape(H=96)) == moe.MOE_ERR_UNSUPPORTED
+    # the next layer's router: both buffers or neither, next_E >= 1, aligned
+    assert call(nwr=FAKE, nE=8) == moe.MOE_ERR_INVALID_ARG          # no logits buffer
+    assert call(nlog=FAKE, nE=8) == moe.MOE_ERR_INVALID_ARG         # no router plane
+    assert call(nwr=FAKE, nE=0, nlog=FAKE) == moe.MOE_ERR_INVALID_ARG
+    assert call(nwr=FAKE + 4, nE=8, nlog=FAKE) == moe.MOE_ERR_INVALID_ARG
+    assert call(nwr=FAKE, nE=8, nlog=FAKE + 2) == moe.MOE_ERR_INVALID_ARG
 
 
 def test_expert_mlp_rejects(L):
