@@ -42,13 +42,14 @@
  * nibble an OCP MX e2m1 code (bit 3 sign, bits 2..1 exponent with bias 1,
  * bit 0 mantissa: 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives); s = ue8m0
  * exponent bytes, uint8 [E][N][K/32], scale 2^(e - 127), e = 255 is NaN.  The
- * MFMA path feeds the fp16 value e2m1 * 2^(e - 127) rounded to nearest even
- * for 103 <= e <= 142 (the exact weight for 104 <= e <= 140; past 140 the
- * larger codes overflow to +-inf).  Outside that range the scale itself is
- * not an fp16 number: e <= 102 gives zero weights, 143 <= e <= 254 +-inf
- * (NaN for a zero code), e = 255 NaN.  The GEMV path dots the exact e2m1
- * values with fp16 activations and scales each group's fp32 partial by
- * 2^(e - 127) in fp32.
+ * GEMV path dots the exact e2m1 values with fp16 activations and scales each
+ * group's fp32 partial by 2^(e - 127) in fp32.  The MFMA path serves every
+ * exponent too: per weight row it feeds the fp16 value e2m1 * 2^(e - 127 -
+ * shift), with shift = (the row's largest finite exponent) - 140, and
+ * multiplies the fp32 accumulator by 2^shift; groups within 36 of their
+ * row's largest exponent are exact, a group 37 below rounds once to fp16's
+ * subnormal grid, groups further below contribute zero (weights below 2^-34
+ * of the row's largest), e = 255 gives NaN.
  *
  * Tiled planes (moe_shape.layout = MOE_LAYOUT_TILED, written by
  * moe_pack_weights): the same bytes regrouped so that the grouped MFMA GEMM

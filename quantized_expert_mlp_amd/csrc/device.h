@@ -195,12 +195,29 @@ __device__ __forceinline__ f16x8_t mx4_f16x8(uint32_t w, f16x2_t s2) {
   return r;
 }
 
-// ue8m0 group exponent e -> the fp16 scale 2^(e - 127), rounded to nearest
-// even from the exact fp32 power of two: exact for 103 <= e <= 142 (fp16
-// subnormals included), zero below, +inf from 143 to 254; e = 255 (NaN in
-// the MX format) gives NaN.
-__device__ __forceinline__ _Float16 e8m0_f16(uint32_t e) {
-  const float f = e == 255u ? __builtin_nanf("") : __uint_as_float(e << 23);
+// MXFP4 on the MFMA path over every ue8m0 exponent.  The fp16 operand is
+// e2m1 * 2^(e - 127 - shift), with shift chosen per weight row (over the
+// groups a workgroup contracts, agreed by the two lanes feeding that output
+// column) so that the row's largest finite exponent lands on kMxTopExp = 140,
+// the top of the window 104..140 in which every e2m1 value times 2^(e - 127)
+// is an exact fp16 number; the epilogue multiplies the fp32 accumulator by
+// 2^shift (ldexp, exact unless the result leaves fp32's range).  A group
+// within 36 of its row's largest exponent is therefore exact; one 37 below
+// rounds once to fp16's subnormal grid; one 38 or more below contributes
+// zero (its scale is no fp16 number: its weights are under 2^-22 * 2^shift,
+// below 2^-34 of the row's largest weight).  e = 255 (NaN in the MX format)
+// stays NaN, and a row of NaN groups only takes shift 0.
+constexpr int kMxTopExp = 140;
+
+// shift for a row whose largest finite exponent is emax (-1: none).
+__device__ __forceinline__ int mx_row_shift(int emax) { return emax < 0 ? 0 : emax - kMxTopExp; }
+
+// The fp16 scale 2^(e - 127 - shift), rounded to nearest even from the exact
+// fp32 power of two (zero when e - shift <= 0; +inf past 142), NaN for e = 255.
+__device__ __forceinline__ _Float16 e8m0_f16_shifted(uint32_t e, int shift) {
+  const int eb = (int)e - shift;
+  const float f = e == 255u ? __builtin_nanf("")
+                            : eb <= 0 ? 0.0f : __uint_as_float((uint32_t)min(eb, 254) << 23);
   return (_Float16)f;
 }
 

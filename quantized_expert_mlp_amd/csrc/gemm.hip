@@ -20,9 +20,10 @@
 //   B (16 k x 32 cols)  lane l: col l%32, k 8*(l/32)..+7  (weights)
 //   D (32 x 32, fp32)   lane l: col l%32, rows 8*(v/4) + 4*(l/32) + v%4.
 // The weight operand is the exact dequantised value ((nibble-8)*scale, or
-// e2m1(nibble)*2^(e-127)) rounded once to fp16; fp16 and bf16 MFMA have the same peak on gfx950, and fp16's
-// 11-bit significand keeps the layer within its tolerance where bf16 would
-// not.  Activations are fp16 copies stored with each block of 8 in the order
+// e2m1(nibble)*2^(e-127) scaled by a per-row power of two that the epilogue
+// undoes, see e8m0_f16_shifted) rounded once to fp16; fp16 and bf16 MFMA
+// have the same peak on gfx950, and fp16's 11-bit significand keeps the
+// layer within its tolerance where bf16 would not.  Activations are fp16 copies stored with each block of 8 in the order
 // 0,4,1,5,2,6,3,7, matching the nibble pairing of the decode.
 //
 // K mapping inside one 64-deep step: lane (j, hf) = (l%32, l/32) loads the 16
@@ -248,6 +249,28 @@ __device__ __forceinline__ void gemm_tile(const TileView& tv, const GemmSrc& S, 
     }
   };
 
+  // MXFP4: each weight row's shift (see e8m0_f16_shifted), from the largest
+  // finite exponent of the groups this workgroup contracts, agreed between
+  // the lanes j and j + 32 that feed the same output column.
+  int mx_shift[NS][P];
+#pragma unroll
+  for (int ns = 0; ns < NS; ++ns)
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      mx_shift[ns][p] = 0;
+      if constexpr (FMT == kFmtMxfp4) {
+        int m = -1;
+        const SElem* sp = bs_ptr[ns][p];
+#pragma unroll 8
+        for (int s2 = 0; s2 < n; ++s2) {
+          const int e = sp[stride * s2];
+          m = (e != 255 && e > m) ? e : m;
+        }
+        m = max(m, __shfl_xor(m, 32, 64));
+        mx_shift[ns][p] = mx_row_shift(m);
+      }
+    }
+
   f32x16_t acc[MS][NS][P];
 #pragma unroll
   for (int m = 0; m < MS; ++m)
@@ -266,7 +289,7 @@ __device__ __forceinline__ void gemm_tile(const TileView& tv, const GemmSrc& S, 
 #pragma unroll
       for (int p = 0; p < P; ++p) {
         if constexpr (FMT == kFmtMxfp4) {
-          const _Float16 sc = e8m0_f16(st.s[ns][p]);
+          const _Float16 sc = e8m0_f16_shifted(st.s[ns][p], mx_shift[ns][p]);
           const f16x2_t s2 = {sc, sc};
 #pragma unroll
           for (int d = 0; d < 4; ++d)
@@ -352,12 +375,18 @@ __device__ __forceinline__ void gemm_tile(const TileView& tv, const GemmSrc& S, 
         const int i = m * 32 + 8 * (v >> 2) + 4 * hf + (v & 3);
         if (i >= tv.nrows) continue;
         if (MODE == 0) {
-          const float g = acc[m][ns][0][v], u = acc[m][ns][P - 1][v];
+          float g = acc[m][ns][0][v], u = acc[m][ns][P - 1][v];
+          if constexpr (FMT == kFmtMxfp4) {
+            g = ldexpf(g, mx_shift[ns][0]);
+            u = ldexpf(u, mx_shift[ns][P - 1]);
+          }
           const float hv = g / (1.0f + __expf(-g)) * u;
           const _Float16 hh = (_Float16)hv;
           S.hout[(int64_t)(tv.row0 + i) * N + perm_col(col)] = __builtin_bit_cast(uint16_t, hh);
         } else {
-          unsafeAtomicAdd(&a.y[(int64_t)row_tok[i] * a.H + col], row_w[i] * acc[m][ns][0][v]);
+          const float o = FMT == kFmtMxfp4 ? ldexpf(acc[m][ns][0][v], mx_shift[ns][0])
+                                           : acc[m][ns][0][v];
+          unsafeAtomicAdd(&a.y[(int64_t)row_tok[i] * a.H + col], row_w[i] * o);
         }
       }
     }

@@ -246,11 +246,17 @@ __global__ __launch_bounds__(256) void debug_dequant_kernel(const uint8_t* __res
       }
       return;
     }
-    const _Float16 sh = e8m0_f16(e);
+    // the row's shift over all its groups, as a workgroup contracting the
+    // whole row forms it; the operand widened and scaled back by 2^shift
+    const uint8_t* srow = static_cast<const uint8_t*>(s) + n * (K / 32);
+    int m = -1;
+    for (int gg = 0; gg < K / 32; ++gg) m = (srow[gg] != 255 && srow[gg] > m) ? srow[gg] : m;
+    const int shift = mx_row_shift(m);
+    const _Float16 sh = e8m0_f16_shifted(e, shift);
     const f16x2_t s2 = {sh, sh};
     const f16x8_t v = mode == kDebugMx4Mfma ? mx4_f16x8(wv, s2) : mx4_f16x8_cvt(wv, s2);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) o[j] = (float)v[perm8_pos(j)];
+    for (int j = 0; j < 8; ++j) o[j] = ldexpf((float)v[perm8_pos(j)], shift);
     return;
   }
   const uint16_t sb = static_cast<const uint16_t*>(s)[g];

@@ -9,7 +9,9 @@ int4 (offset-binary nibble - 8, one fp16 scale per 32 inputs):
   mode 3  down GEMV decoder (fp16 1024 + n)      -> the exact weight
 MXFP4 (e2m1 nibble, one ue8m0 exponent per 32 inputs):
   mode 0  GEMV decoder (packed fp4 conversion x fp32 2^(e-127)) -> exact weight
-  mode 1  MFMA decoder, tiles of 2-4 subtiles    -> exact weight rounded to fp16
+  mode 1  MFMA decoder, tiles of 2-4 subtiles    -> fp16 operand at the row's
+          shift, undone: exact for groups within 36 of the row's largest
+          exponent, then once-rounded, then zero
   mode 2  MFMA decoder, one-subtile tiles        -> the same
 
 Coverage is exhaustive where it is cheap: every finite fp16 scale with every
@@ -168,24 +170,57 @@ def test_mxfp4_gemv_decoder_exact_every_exponent():
     _bits_equal(_mx(q, s, 0), want, "mxfp4 mode 0")
 
 
-def test_mxfp4_mfma_decoders_fp16_window():
-    """Modes 1 and 2: over the exponents whose scale is an fp16 number
-    (103..142) the operand is the exact weight rounded once to fp16."""
-    q, s = _all_exponents_plane(103, 142)
-    with np.errstate(over="ignore"):
-        want = oracle.dequant(q, s, "mxfp4").astype(np.float16).astype(np.float32)
+def _mx_mfma_expected(q, s):
+    """What the MFMA decoders feed, undone: per row, shift = (largest finite
+    exponent) - 140; a group with e - shift >= 103 is the exact weight scaled
+    by 2^-shift rounded once to fp16, a group below that is a signed zero;
+    times 2^shift in fp64 (exact), then fp32."""
+    w = oracle.dequant(q, s, "mxfp4")
+    emax = np.where(s != 255, s.astype(np.int64), -1).max(axis=1)
+    shift = np.where(emax < 0, 0, emax - 140)
+    eb = np.repeat(s.astype(np.int64) - shift[:, None], 32, axis=1)
+    with np.errstate(over="ignore", invalid="ignore"):
+        op = np.ldexp(w, -shift[:, None]).astype(np.float16).astype(np.float64)
+        op = np.where((eb <= 102) & ~np.isnan(op), 0.0 * np.sign(w), op)
+        return np.ldexp(op, shift[:, None]).astype(np.float32)
+
+
+def test_mxfp4_mfma_decoders_every_exponent():
+    """Modes 1 and 2 on rows of one exponent: the exact weight for every e
+    (the row's shift puts its scale at the top of fp16's exact window), NaN
+    for e = 255, and the largest codes overflowing fp32 at e >= 254 as the
+    exact weights do."""
+    q, s = _all_exponents_plane()
+    with np.errstate(over="ignore", invalid="ignore"):
+        want = oracle.dequant(q, s, "mxfp4").astype(np.float32)
+    assert np.array_equal(_mx_mfma_expected(q, s).view(np.uint32), want.view(np.uint32))
     for mode in (1, 2):
         _bits_equal(_mx(q, s, mode), want, "mxfp4 mode %d" % mode)
+
+
+def test_mxfp4_mfma_decoders_exponent_spans():
+    """Rows whose groups span 0..60 binades below their largest exponent, at
+    every position of that largest exponent: groups within 36 exact, 37
+    below rounded once to the subnormal grid, further below zero."""
+    rng = np.random.default_rng(44)
+    N, K = 512, 256
+    top = rng.integers(0, 255, N)
+    s = np.clip(top[:, None] - rng.integers(0, 61, (N, K // 32)), 0, 254).astype(np.uint8)
+    s[np.arange(N), rng.integers(0, K // 32, N)] = top  # the row's largest, somewhere
+    s[::17, 3] = 255                                    # NaN groups beside finite ones
+    q = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    want = _mx_mfma_expected(q, s)
+    for mode in (1, 2):
+        _bits_equal(_mx(q, s, mode), want, "mxfp4 spans mode %d" % mode, signed_zero=False)
 
 
 def test_mxfp4_decoders_random_planes():
     for N, K in [(8, 64), (64, 256), (3, 6144), (96, 1408)]:
         rng = np.random.default_rng([N, K, 4])
         q = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
-        s = rng.integers(103, 143, (N, K // 32), dtype=np.uint8)
+        s = rng.integers(103, 107, (N, K // 32), dtype=np.uint8)
         ref = oracle.dequant(q, s, "mxfp4")
-        with np.errstate(over="ignore"):
-            want16 = ref.astype(np.float16).astype(np.float32)
         _bits_equal(_mx(q, s, 0), ref.astype(np.float32), "mx random mode 0")
-        for mode in (1, 2):
-            _bits_equal(_mx(q, s, mode), want16, "mx random N=%d K=%d mode %d" % (N, K, mode))
+        for mode in (1, 2):  # spans of at most 3 binades: exact
+            _bits_equal(_mx(q, s, mode), ref.astype(np.float32),
+                        "mx random N=%d K=%d mode %d" % (N, K, mode))
