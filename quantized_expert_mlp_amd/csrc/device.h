@@ -22,6 +22,36 @@ __device__ __forceinline__ uint4 load_stream16(const void* p) {
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// 16-byte load from global memory, for a pointer the compiler cannot prove
+// global (one picked from an array of planes): a generic (flat) load would
+// make the compiler's wait counting fall back to waiting for every
+// outstanding load.
+typedef __attribute__((address_space(1))) const u32x4_t global_u32x4_t;
+__device__ __forceinline__ u32x4_t load_global16(const void* p) {
+  return *(global_u32x4_t*)(p);
+}
+
+// Wave-uniform scalar loads (s_load, counted apart from the vector loads):
+// the address must be the same in every lane, which readfirstlane makes
+// explicit.  For words the kernel reads but does not write.
+typedef __attribute__((address_space(4))) const int32_t const_i32_t;
+typedef __attribute__((address_space(4))) const float const_f32_t;
+// readfirstlane of a 64-bit address, as two 32-bit halves; the builtin
+// returns int, so each half is taken back as uint32_t before widening (a
+// sign-extended low half would corrupt the upper word of the address).
+__device__ __forceinline__ uint64_t uniform_address(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return (uint64_t)lo | ((uint64_t)hi << 32);
+}
+__device__ __forceinline__ int32_t load_uniform_i32(const int32_t* p) {
+  return *(const_i32_t*)(uniform_address(p));
+}
+__device__ __forceinline__ float load_uniform_f32(const float* p) {
+  return *(const_f32_t*)(uniform_address(p));
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float((uint32_t)b << 16);
 }

@@ -51,6 +51,12 @@
 #ifndef MOE_GEMV_NT
 #define MOE_GEMV_NT 1
 #endif
+#ifndef MOE_GEMV_WG_WAVES
+#define MOE_GEMV_WG_WAVES 4  // waves per workgroup, gate/up (one routing prologue each)
+#endif
+#ifndef MOE_GEMV_WG_WAVES_DOWN
+#define MOE_GEMV_WG_WAVES_DOWN 4  // waves per workgroup, down
+#endif
 
 namespace moe {
 
@@ -274,15 +280,20 @@ template <int P, int RB, int RPI, int SB>
 struct ScaleStage {
   static constexpr int kMaxPlaneBytes = 512;
   uint4 v;
+  // Every lane loads (no branch around the load, so the compiler's wait
+  // counts stay exact): lanes past the batch's chunks, and chunks of rows
+  // past N, re-read the plane's last chunk; stage() publishes only the
+  // batch's own chunks and rows past N are never stored.
   template <typename T>
   __device__ __forceinline__ void load(const T* const* sp, int n0, int N, int G) {
     const int lane = threadIdx.x & 63;
     const int pbytes = RB * RPI * G * SB, chunks = pbytes / 16;
     const int p = lane / chunks, j = lane - p * chunks;
-    const int64_t at = (int64_t)n0 * G * SB + 16 * j;
-    v = make_uint4(0, 0, 0, 0);
-    if (p < P && at + 16 <= (int64_t)N * G * SB)
-      v = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(sp[p]) + at);
+    const int64_t last = (int64_t)N * G * SB - 16;
+    int64_t at = (int64_t)n0 * G * SB + 16 * j;
+    at = at < last ? at : last;
+    const u32x4_t w = load_global16(reinterpret_cast<const char*>(sp[p < P ? p : P - 1]) + at);
+    v = make_uint4(w[0], w[1], w[2], w[3]);
   }
   // Publish this batch's chunks; the slot's previous contents (read by other
   // lanes for the previous batch) are overwritten only after those reads.
@@ -308,8 +319,13 @@ struct ScaleStage {
 
 }  // namespace
 
+constexpr int kGuWaves = MOE_GEMV_WG_WAVES, kDnWaves = MOE_GEMV_WG_WAVES_DOWN;
+// the fused routing gives thread e expert e's offset (E <= 256) and wave t token t
+static_assert(kGuWaves >= 4 && kGuWaves <= 16 && kDnWaves >= 1 && kDnWaves <= 16, "waves");
+
 template <int LPR, int GPL, int MT, int RB, int ROUTE_V, bool SLDS, int FMT>
-__global__ __launch_bounds__(256) void gemv_gate_up_kernel(
+
+__global__ __launch_bounds__(64 * kGuWaves) void gemv_gate_up_kernel(
     Buckets b, const uint16_t* __restrict__ x, int H, int I, const uint8_t* __restrict__ gq,
     const void* __restrict__ gs, const uint8_t* __restrict__ uq, const void* __restrict__ us,
     uint16_t* __restrict__ h, float* __restrict__ y_zero, int64_t y_elems, int nit,
@@ -324,7 +340,7 @@ __global__ __launch_bounds__(256) void gemv_gate_up_kernel(
   }
   // ROUTE_V > 0: routing folded in (ROUTE_V logit registers per lane).
   __shared__ SmallRoute sr;
-  __shared__ uint32_t sslot[4][ScaleStage<2, RB, 64 / LPR, 2>::kMaxPlaneBytes * 2 / 4];
+  __shared__ uint32_t sslot[kGuWaves][ScaleStage<2, RB, 64 / LPR, 2>::kMaxPlaneBytes * 2 / 4];
   BucketView bv;
   const int32_t* rows_sorted = b.sorted;
   if constexpr (ROUTE_V > 0) {
@@ -338,7 +354,13 @@ __global__ __launch_bounds__(256) void gemv_gate_up_kernel(
   } else {
     if (!bucket_of(b, &bv)) return;
   }
-  auto token_at = [&](int r) { return b.shared_T > 0 ? r : rows_sorted[r] / b.k; };
+  // the token of bucket row r (wave-uniform; from LDS with the fused routing,
+  // else a scalar load)
+  auto token_at = [&](int r) {
+    if (b.shared_T > 0) return r;
+    if constexpr (ROUTE_V > 0) return rows_sorted[r] / b.k;
+    return load_uniform_i32(rows_sorted + r) / b.k;
+  };
 
   constexpr int RPI = 64 / LPR;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -349,7 +371,7 @@ __global__ __launch_bounds__(256) void gemv_gate_up_kernel(
   const uint8_t* uqe = uq + bv.e * pb;
   const SE* spl[2] = {static_cast<const SE*>(gs) + bv.e * sb,
                       static_cast<const SE*>(us) + bv.e * sb};
-  const int rbase = (blockIdx.x * 4 + wave) * (nit * RPI);  // first row of the wave
+  const int rbase = (blockIdx.x * kGuWaves + wave) * (nit * RPI);  // first row of the wave
   const int row0 = rbase + rl;
   uint32_t* slot = sslot[wave];
   using SS = ScaleStage<2, RB, RPI, (int)sizeof(SE)>;
@@ -362,31 +384,31 @@ __global__ __launch_bounds__(256) void gemv_gate_up_kernel(
       uint32_t sg[RB][GPL], su[RB][GPL];  // per-lane scale bits when !SLDS
       SS sc;                              // staged scales when SLDS
     };
+    // Unconditional loads (exact wait counts, so the next batch stays in
+    // flight while this one is reduced): rows past I re-read row I - 1
+    // (never stored), groups past G re-read group G - 1 (masked in compute).
     auto load = [&](Batch& bt, int i0) {
       if constexpr (SLDS) bt.sc.load(spl, rbase + i0 * RPI, I, G);
 #pragma unroll
       for (int r = 0; r < RB; ++r) {
-        const int n = row0 + (i0 + r) * RPI;
+        const int n = min(row0 + (i0 + r) * RPI, I - 1);
 #pragma unroll
         for (int gi = 0; gi < GPL; ++gi) {
-          const int g = kl + gi * LPR;
-          if (n < I && g < G) {
-            bt.g[r][gi] = load_w16(gqe + (int64_t)n * (H / 2) + 16 * g);
-            bt.u[r][gi] = load_w16(uqe + (int64_t)n * (H / 2) + 16 * g);
-            if constexpr (!SLDS) {
-              bt.sg[r][gi] = spl[0][(int64_t)n * G + g];
-              bt.su[r][gi] = spl[1][(int64_t)n * G + g];
-            }
-          } else {
-            bt.g[r][gi] = bt.u[r][gi] = make_uint4(0, 0, 0, 0);
-            if constexpr (!SLDS) bt.sg[r][gi] = bt.su[r][gi] = 0;
+          const int g = min(kl + gi * LPR, G - 1);
+          bt.g[r][gi] = load_w16(gqe + (int64_t)n * (H / 2) + 16 * g);
+          bt.u[r][gi] = load_w16(uqe + (int64_t)n * (H / 2) + 16 * g);
+          if constexpr (!SLDS) {
+            bt.sg[r][gi] = spl[0][(int64_t)n * G + g];
+            bt.su[r][gi] = spl[1][(int64_t)n * G + g];
           }
         }
       }
     };
-    Batch A, B;
-    load(A, 0);  // weights first: they do not wait for the activation prologue
-
+    // The activation rows are loaded first and the first weight batch right
+    // after them: loads complete in order, so waiting for the activations
+    // leaves the weights in flight while the activations are prepared.
+    // Unconditional loads (a clamped group), zeroed where they are not this
+    // lane's: no branch for the compiler's wait counting.
     uint32_t xa[MT][GPL][16];
     float corr[MT][GPL];
 #pragma unroll
@@ -394,19 +416,27 @@ __global__ __launch_bounds__(256) void gemv_gate_up_kernel(
       const uint16_t* xr = x + (int64_t)token_at(bv.r0 + m0 + min(t, nt - 1)) * H;
 #pragma unroll
       for (int gi = 0; gi < GPL; ++gi) {
-        const int g = kl + gi * LPR;
-        uint32_t nat[16];
-        if (t < nt && g < G) {
-          const uint4* src = reinterpret_cast<const uint4*>(xr + 32 * g);
+        const uint4* src = reinterpret_cast<const uint4*>(xr + 32 * min(kl + gi * LPR, G - 1));
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const uint4 v = src[c];
-            nat[4 * c] = v.x; nat[4 * c + 1] = v.y; nat[4 * c + 2] = v.z; nat[4 * c + 3] = v.w;
-          }
-        } else {
-#pragma unroll
-          for (int c = 0; c < 16; ++c) nat[c] = 0;
+        for (int c = 0; c < 4; ++c) {
+          const uint4 v = src[c];
+          xa[t][gi][4 * c] = v.x; xa[t][gi][4 * c + 1] = v.y;
+          xa[t][gi][4 * c + 2] = v.z; xa[t][gi][4 * c + 3] = v.w;
         }
+      }
+    }
+    Batch A, B;
+    __builtin_amdgcn_sched_barrier(0);  // keep the activation loads ahead of the weights
+    load(A, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+#pragma unroll
+      for (int gi = 0; gi < GPL; ++gi) {
+        const bool own = t < nt && kl + gi * LPR < G;
+        uint32_t nat[16];
+#pragma unroll
+        for (int c = 0; c < 16; ++c) nat[c] = own ? xa[t][gi][c] : 0u;
         float sum = 0.f;
         if constexpr (FMT == kFmtMxfp4) {
           // natural-order fp16 pairs (the MXFP4 decode yields natural pairs)
@@ -445,16 +475,20 @@ __global__ __launch_bounds__(256) void gemv_gate_up_kernel(
             sub = bt.su[r][gi];
           }
           const float fsg = F::scale(sgb), fsu = F::scale(sub);
+          const bool live = g < G;
 #pragma unroll
           for (int t = 0; t < MT; ++t) {
             if (t < nt) {
+              float dg, du;
               if constexpr (FMT == kFmtMxfp4) {
-                ag[t] += fsg * dot_group_mx(bt.g[r][gi], xa[t][gi]);
-                au[t] += fsu * dot_group_mx(bt.u[r][gi], xa[t][gi]);
+                dg = fsg * dot_group_mx(bt.g[r][gi], xa[t][gi]);
+                du = fsu * dot_group_mx(bt.u[r][gi], xa[t][gi]);
               } else {
-                ag[t] += fsg * (dot_group_bf16(bt.g[r][gi], xa[t][gi]) - corr[t][gi]);
-                au[t] += fsu * (dot_group_bf16(bt.u[r][gi], xa[t][gi]) - corr[t][gi]);
+                dg = fsg * (dot_group_bf16(bt.g[r][gi], xa[t][gi]) - corr[t][gi]);
+                du = fsu * (dot_group_bf16(bt.u[r][gi], xa[t][gi]) - corr[t][gi]);
               }
+              ag[t] += live ? dg : 0.f;
+              au[t] += live ? du : 0.f;
             }
           }
         }
@@ -471,28 +505,36 @@ __global__ __launch_bounds__(256) void gemv_gate_up_kernel(
         }
       }
     };
+    // Batches i0, i0 + RB, ... (nit a multiple of RB): the loop body's
+    // loads are all in range, the last one or two batches are peeled, so
+    // no load sits behind a branch and each reduction waits only for its
+    // own batch while the next one is in flight.
+    int i0 = 0;
 #pragma unroll 1
-    for (int i0 = 0;;) {
-      if (i0 + RB < nit) load(B, i0 + RB);
+    for (; i0 + 2 * RB < nit; i0 += 2 * RB) {
+      load(B, i0 + RB);
       compute(A, i0);
-      i0 += RB;
-      if (i0 >= nit) break;
-      if (i0 + RB < nit) load(A, i0 + RB);
-      compute(B, i0);
-      i0 += RB;
-      if (i0 >= nit) break;
+      load(A, i0 + 2 * RB);
+      compute(B, i0 + RB);
+    }
+    if (i0 + RB < nit) {
+      load(B, i0 + RB);
+      compute(A, i0);
+      compute(B, i0 + RB);
+    } else {
+      compute(A, i0);
     }
   }
 }
 
 template <int LPR, int GPL, int MT, int RB, bool SLDS, int FMT>
-__global__ __launch_bounds__(256) void gemv_down_kernel(
+__global__ __launch_bounds__(64 * kDnWaves) void gemv_down_kernel(
     Buckets b, const uint16_t* __restrict__ h, int H, int I, const uint8_t* __restrict__ dq,
     const void* __restrict__ ds, const float* __restrict__ w,
     const float* __restrict__ gate_logit, int gate_ld, float* __restrict__ y, int nit) {
   using F = GemvFmt<FMT>;
   using SE = typename F::S;
-  __shared__ uint32_t sslot[4][ScaleStage<1, RB, 64 / LPR, 2>::kMaxPlaneBytes / 4];
+  __shared__ uint32_t sslot[kDnWaves][ScaleStage<1, RB, 64 / LPR, 2>::kMaxPlaneBytes / 4];
   BucketView bv;
   if (!bucket_of(b, &bv)) return;
 
@@ -503,7 +545,7 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(
   const int64_t pb = (int64_t)H * (I / 2), sb = (int64_t)H * G;
   const uint8_t* dqe = dq + bv.e * pb;
   const SE* spl[1] = {static_cast<const SE*>(ds) + bv.e * sb};
-  const int rbase = (blockIdx.x * 4 + wave) * (nit * RPI);
+  const int rbase = (blockIdx.x * kDnWaves + wave) * (nit * RPI);
   const int row0 = rbase + rl;
   uint32_t* slot = sslot[wave];
   using SS = ScaleStage<1, RB, RPI, (int)sizeof(SE)>;
@@ -515,57 +557,64 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(
       uint32_t sd[RB][GPL];  // per-lane scale bits when !SLDS
       SS sc;
     };
+    // Unconditional loads, as in the gate/up kernel: rows past H re-read row
+    // H - 1 (never stored), groups past G re-read group G - 1 (masked).
     auto load = [&](Batch& bt, int i0) {
       if constexpr (SLDS) bt.sc.load(spl, rbase + i0 * RPI, H, G);
 #pragma unroll
       for (int r = 0; r < RB; ++r) {
-        const int n = row0 + (i0 + r) * RPI;
+        const int n = min(row0 + (i0 + r) * RPI, H - 1);
 #pragma unroll
         for (int gi = 0; gi < GPL; ++gi) {
-          const int g = kl + gi * LPR;
-          if (n < H && g < G) {
-            bt.d[r][gi] = load_w16(dqe + (int64_t)n * (I / 2) + 16 * g);
-            if constexpr (!SLDS) bt.sd[r][gi] = spl[0][(int64_t)n * G + g];
-          } else {
-            bt.d[r][gi] = make_uint4(0, 0, 0, 0);
-            if constexpr (!SLDS) bt.sd[r][gi] = 0;
-          }
+          const int g = min(kl + gi * LPR, G - 1);
+          bt.d[r][gi] = load_w16(dqe + (int64_t)n * (I / 2) + 16 * g);
+          if constexpr (!SLDS) bt.sd[r][gi] = spl[0][(int64_t)n * G + g];
         }
       }
     };
-    Batch A, B;
-    load(A, 0);  // weights first: they do not wait for the activation prologue
-
+    // Activations (the hidden rows) first, then the first weight batch, as in
+    // the gate/up kernel; the token and combine weight of each row are
+    // wave-uniform scalar loads, counted apart from the vector loads.
     uint32_t xa[MT][GPL][16];
     float corr[MT][GPL], wt[MT];
     int tok[MT];
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
       const int r = bv.r0 + m0 + min(t, nt - 1);
-      if (b.shared_T > 0) {
-        tok[t] = r;
-        wt[t] = gate_logit ? sigmoidf_acc(gate_logit[(int64_t)r * gate_ld]) : 1.0f;
-      } else {
-        const int s = b.sorted[r];
-        tok[t] = s / b.k;
-        wt[t] = w[s];
-      }
       const uint16_t* hr = h + (int64_t)r * I;
 #pragma unroll
       for (int gi = 0; gi < GPL; ++gi) {
-        const int g = kl + gi * LPR;
-        uint32_t nat[16];
-        if (t < nt && g < G) {
-          const uint4* src = reinterpret_cast<const uint4*>(hr + 32 * g);
+        const uint4* src = reinterpret_cast<const uint4*>(hr + 32 * min(kl + gi * LPR, G - 1));
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const uint4 v = src[c];
-            nat[4 * c] = v.x; nat[4 * c + 1] = v.y; nat[4 * c + 2] = v.z; nat[4 * c + 3] = v.w;
-          }
-        } else {
-#pragma unroll
-          for (int c = 0; c < 16; ++c) nat[c] = 0;
+        for (int c = 0; c < 4; ++c) {
+          const uint4 v = src[c];
+          xa[t][gi][4 * c] = v.x; xa[t][gi][4 * c + 1] = v.y;
+          xa[t][gi][4 * c + 2] = v.z; xa[t][gi][4 * c + 3] = v.w;
         }
+      }
+    }
+    Batch A, B;
+    __builtin_amdgcn_sched_barrier(0);  // keep the activation loads ahead of the weights
+    load(A, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const int r = bv.r0 + m0 + min(t, nt - 1);
+      if (b.shared_T > 0) {
+        tok[t] = r;
+        wt[t] = gate_logit ? sigmoidf_acc(load_uniform_f32(gate_logit + (int64_t)r * gate_ld))
+                           : 1.0f;
+      } else {
+        const int s = load_uniform_i32(b.sorted + r);
+        tok[t] = s / b.k;
+        wt[t] = load_uniform_f32(w + s);
+      }
+#pragma unroll
+      for (int gi = 0; gi < GPL; ++gi) {
+        const bool own = t < nt && kl + gi * LPR < G;
+        uint32_t nat[16];
+#pragma unroll
+        for (int c = 0; c < 16; ++c) nat[c] = own ? xa[t][gi][c] : 0u;
         float sum = 0.f;
         if constexpr (FMT == kFmtMxfp4) {
 #pragma unroll
@@ -597,13 +646,16 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(
           if constexpr (SLDS) sdb = SS::get(slot, 0, r * RPI + rl, g < G ? g : 0, G);
           else sdb = bt.sd[r][gi];
           const float fsd = F::scale(sdb);
+          const bool live = g < G;
 #pragma unroll
           for (int t = 0; t < MT; ++t) {
             if (t < nt) {
+              float dd;
               if constexpr (FMT == kFmtMxfp4)
-                acc[t] += fsd * dot_group_mx(bt.d[r][gi], xa[t][gi]);
+                dd = fsd * dot_group_mx(bt.d[r][gi], xa[t][gi]);
               else
-                acc[t] += fsd * (dot_group_f16(bt.d[r][gi], xa[t][gi]) - corr[t][gi]);
+                dd = fsd * (dot_group_f16(bt.d[r][gi], xa[t][gi]) - corr[t][gi]);
+              acc[t] += live ? dd : 0.f;
             }
           }
         }
@@ -616,16 +668,24 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(
         }
       }
     };
+    // Batches i0, i0 + RB, ... (nit a multiple of RB): the loop body's
+    // loads are all in range, the last one or two batches are peeled, so
+    // no load sits behind a branch and each reduction waits only for its
+    // own batch while the next one is in flight.
+    int i0 = 0;
 #pragma unroll 1
-    for (int i0 = 0;;) {
-      if (i0 + RB < nit) load(B, i0 + RB);
+    for (; i0 + 2 * RB < nit; i0 += 2 * RB) {
+      load(B, i0 + RB);
       compute(A, i0);
-      i0 += RB;
-      if (i0 >= nit) break;
-      if (i0 + RB < nit) load(A, i0 + RB);
-      compute(B, i0);
-      i0 += RB;
-      if (i0 >= nit) break;
+      load(A, i0 + 2 * RB);
+      compute(B, i0 + RB);
+    }
+    if (i0 + RB < nit) {
+      load(B, i0 + RB);
+      compute(A, i0);
+      compute(B, i0 + RB);
+    } else {
+      compute(A, i0);
     }
   }
 }
@@ -696,17 +756,17 @@ hipError_t gemv_gate_up_launch(const Buckets& b, int max_buckets, const uint16_t
   const int mt = pow2_floor_min(b.max_rows, sh.gpl == 1 ? 4 : 2);
   const int buckets = b.shared_T > 0 ? 1 : max_buckets;
   const int nit = rows_per_wave(I, 64 / sh.lpr, buckets, rb_for(sh.gpl), mt);
-  const int rpb = 4 * nit * (64 / sh.lpr);
+  const int rpb = kGuWaves * nit * (64 / sh.lpr);
   const bool slds = scales_via_lds<FMT>(H);
   dim3 grid((I + rpb - 1) / rpb, buckets);
 #define GU(LP, GP, MTv, RV)                                                                      \
   do {                                                                                           \
     if (slds)                                                                                    \
       MOE_LAUNCH(L, (gemv_gate_up_kernel<LP, GP, MTv, rb_for(GP), RV, true, FMT>), grid,         \
-                 dim3(256), 0, b, x, H, I, gq, gs, uq, us, h, y_zero, y_elems, nit, ra);         \
+                 dim3(64 * kGuWaves), 0, b, x, H, I, gq, gs, uq, us, h, y_zero, y_elems, nit, ra);         \
     else                                                                                         \
       MOE_LAUNCH(L, (gemv_gate_up_kernel<LP, GP, MTv, rb_for(GP), RV, false, FMT>), grid,        \
-                 dim3(256), 0, b, x, H, I, gq, gs, uq, us, h, y_zero, y_elems, nit, ra);         \
+                 dim3(64 * kGuWaves), 0, b, x, H, I, gq, gs, uq, us, h, y_zero, y_elems, nit, ra);         \
   } while (0)
 #define X(LP, GP)                                                                                \
   if (sh.lpr == LP && sh.gpl == GP) {                                                            \
@@ -748,16 +808,16 @@ hipError_t gemv_down_launch(const Buckets& b, int max_buckets, const uint16_t* h
   // more rows in flight
   const int nit = rows_per_wave(H, 64 / sh.lpr, buckets, rb_for(sh.gpl), mt,
                                 mt == 1 ? MOE_GEMV_WAVES_DOWN1 : MOE_GEMV_WAVES);
-  const int rpb = 4 * nit * (64 / sh.lpr);
+  const int rpb = kDnWaves * nit * (64 / sh.lpr);
   const bool slds = scales_via_lds<FMT>(I);
   dim3 grid((H + rpb - 1) / rpb, buckets);
 #define DN(LP, GP, MTv)                                                                          \
   do {                                                                                           \
     if (slds)                                                                                    \
-      MOE_LAUNCH(L, (gemv_down_kernel<LP, GP, MTv, rb_for(GP), true, FMT>), grid, dim3(256), 0,  \
+      MOE_LAUNCH(L, (gemv_down_kernel<LP, GP, MTv, rb_for(GP), true, FMT>), grid, dim3(64 * kDnWaves), 0,  \
                  b, h, H, I, dq, ds, w, gate_logit, gate_ld, y, nit);                            \
     else                                                                                         \
-      MOE_LAUNCH(L, (gemv_down_kernel<LP, GP, MTv, rb_for(GP), false, FMT>), grid, dim3(256), 0, \
+      MOE_LAUNCH(L, (gemv_down_kernel<LP, GP, MTv, rb_for(GP), false, FMT>), grid, dim3(64 * kDnWaves), 0, \
                  b, h, H, I, dq, ds, w, gate_logit, gate_ld, y, nit);                            \
   } while (0)
 #define X(LP, GP)                                                                                \

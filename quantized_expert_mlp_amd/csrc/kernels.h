@@ -121,7 +121,10 @@ hipError_t launch_schedule_from_offsets(const int32_t* off, int E, int64_t slots
 // redoes the (cheap, deterministic) top-k and bucket build in LDS, and
 // workgroup (0,0) publishes idx, w, off, sorted, row_of and the schedule for
 // the down launch.
-constexpr int kFusedRouteMaxT = 4;
+#ifndef MOE_FUSED_ROUTE_MAX_T
+#define MOE_FUSED_ROUTE_MAX_T 4
+#endif
+constexpr int kFusedRouteMaxT = MOE_FUSED_ROUTE_MAX_T;
 constexpr int kFusedRouteMaxSlots = 64;
 struct RouteArgs {
   const float* logits;  // [T][ld]
