@@ -187,88 +187,128 @@ __device__ __forceinline__ bool bucket_of(const Buckets& b, BucketView* v) {
   return true;
 }
 
-// Bucket build of the fused small-batch routing (see RouteArgs), in LDS.
+// The fused small-batch routing (see RouteArgs), held in each wave's
+// registers: lane s < T*k holds slot s's row (pos; -1 for a pick outside
+// [0, E), which top-p writes as -1: it gets no row and no bucket); the
+// bucket of this workgroup's blockIdx.y is wave-uniform, and blockIdx.y <
+// n_touched says it exists.
 struct SmallRoute {
-  int32_t pick[kFusedRouteMaxSlots];
-  int32_t sorted[kFusedRouteMaxSlots];
-  int32_t first[kFusedRouteMaxSlots];
-  int4 bucket[kFusedRouteMaxSlots];
-  int n_touched;
+  int pos;            // per lane
+  int n_touched;      // uniform
+  int e, r0, M;       // uniform: bucket blockIdx.y, when blockIdx.y < n_touched
 };
 
-// Waves t < T take token t's top-k (the routing weights only in workgroup
-// (0,0), which publishes them for the down launch; the others need the picks
-// alone); then slot s (thread s) finds its row in
-// the expert-major, slot-ascending order - #slots with a smaller expert plus
-// #earlier slots with the same expert - exactly the permutation of the
-// standalone kernels, which also drop a pick outside [0, E) (top-p's -1):
-// it gets no row (row_of -1) and no bucket.  Every thread of the workgroup
-// must call this.
+// One token: the bucket of blockIdx.y is pick j = k - 1 - blockIdx.y, its
+// one row is row j (slot j), so a workgroup needs only the first j + 1
+// arg-max rounds (with the plain softmax router and no top-p; all k
+// otherwise) and every wave takes them itself - no LDS, no barrier.  The
+// down launch reads buckets u < (valid picks) as pick u: top-p's dropped
+// picks are a suffix.  Workgroup (0,0) runs all k, forms the weights and publishes
+// the picks, slot order, row_of and the bucket list for the down launch
+// (the expert offsets are not formed: nothing reads them on this path).
+//
+// More tokens: wave t < T takes token t's top-k and the picks pass through
+// LDS; rows are expert-major and slot-ascending, the permutation of the
+// standalone kernels.  Every wave, from the S = T*k picks in its lanes,
+// counts for slot s the valid slots with a smaller expert (less), the
+// earlier ones with the same expert (rank) and all with the same expert
+// (M): row = less + rank, and the slot with rank 0 opens its expert's
+// bucket, whose index is the number of distinct experts below it.
+// Workgroup (0,0) publishes the picks and weights, the permutation, the
+// expert offsets and the bucket list.
+//
+// Every thread of the workgroup must call this.
 template <int V>
-__device__ void small_route(const RouteArgs& ra, int k, SmallRoute& sr) {
-  const int tid = threadIdx.x, wave = tid >> 6;
+__device__ void small_route(const RouteArgs& ra, int k, int32_t* pick_lds, SmallRoute& sr) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const bool publish = blockIdx.x == 0 && blockIdx.y == 0;
+  auto valid = [&](int e2) { return e2 >= 0 && e2 < ra.E; };
+  int e = -1;
+  if (ra.T == 1) {  // uniform over the launch
+    // the first-dispatched workgroups (low blockIdx.y), which the hardware
+    // favours, take the picks decided last
+    const int j = k - 1 - (int)blockIdx.y;
+    const bool pw = publish && wave == 0;
+    topk_group<V, 64>(ra.logits, ra.ld, 1, 0, ra.E, k, ra.rs, pw ? ra.idx : nullptr,
+                      pw ? ra.w : nullptr, nullptr, nullptr, 0, pw, &e,
+                      publish ? k : max(j + 1, 1));
+    const int pj = j >= 0 ? __builtin_amdgcn_readlane(e, j) : -1;
+    const bool mine = lane < k && valid(e);
+    const int n_valid = __builtin_popcountll(__builtin_amdgcn_ballot_w64(mine));  // whole wave
+    sr.pos = mine ? lane : -1;
+    sr.n_touched = (int)blockIdx.y + (valid(pj) ? 1 : 0);
+    sr.e = pj;
+    sr.r0 = j;
+    sr.M = 1;
+    if (pw) {
+      if (lane < k) {
+        if (mine) {
+          ra.sorted[lane] = lane;
+          reinterpret_cast<int4*>(ra.sched + sched_touched_offset())[lane] = make_int4(e, lane, 1, 0);
+        }
+        ra.row_of[lane] = mine ? lane : -1;
+      }
+      if (lane == 0) {
+        ra.sched[0] = n_valid;
+        ra.sched[1] = 0;
+      }
+    }
+    return;
+  }
   const int S = ra.T * k;
   if (wave < ra.T)
-    topk_group<V, 64>(ra.logits, ra.ld, ra.T, wave, ra.E, k, ra.rs,
-                      publish ? ra.idx : nullptr, publish ? ra.w : nullptr, sr.pick, nullptr, 0,
-                      publish);
+    topk_group<V, 64>(ra.logits, ra.ld, ra.T, wave, ra.E, k, ra.rs, publish ? ra.idx : nullptr,
+                      publish ? ra.w : nullptr, pick_lds, nullptr, 0, publish);
   __syncthreads();
-  auto valid = [&](int e2) { return e2 >= 0 && e2 < ra.E; };
-  int less = 0, rank = 0, first = 0, e = -1;
-  if (tid < S) {
-    e = sr.pick[tid];
-    if (valid(e)) {
-      first = 1;
+  e = lane < S ? pick_lds[lane] : -1;
+  int less = 0, rank = 0, M = 0;
+  for (int s2 = 0; s2 < S; ++s2) {
+    const int e2 = __builtin_amdgcn_readlane(e, s2);
+    if (valid(e2)) {  // uniform
+      less += e2 < e;
+      M += e2 == e;
+      rank += (e2 == e) & (s2 < lane);
+    }
+  }
+  const bool mine = lane < S && valid(e);
+  const bool first = mine && rank == 0;
+  const uint64_t opens = __builtin_amdgcn_ballot_w64(first);
+  int u = 0;  // distinct experts below e
+  for (uint64_t m = opens; m != 0; m &= m - 1)
+    u += __builtin_amdgcn_readlane(e, (int)__builtin_ctzll(m)) < e;
+  sr.pos = mine ? less + rank : -1;
+  sr.n_touched = __builtin_popcountll(opens);
+  const uint64_t here = __builtin_amdgcn_ballot_w64(first && u == (int)blockIdx.y);
+  sr.e = sr.r0 = sr.M = 0;
+  if (here != 0) {
+    const int s = (int)__builtin_ctzll(here);
+    sr.e = __builtin_amdgcn_readlane(e, s);
+    sr.r0 = __builtin_amdgcn_readlane(less, s);
+    sr.M = __builtin_amdgcn_readlane(M, s);
+  }
+  if (publish) {
+    if (wave == 0) {
+      if (lane < S) {
+        if (mine) ra.sorted[less + rank] = lane;
+        ra.row_of[lane] = mine ? less + rank : -1;
+      }
+      if (first) reinterpret_cast<int4*>(ra.sched + sched_touched_offset())[u] = make_int4(e, less, M, 0);
+      if (lane == 0) {
+        ra.sched[0] = sr.n_touched;
+        ra.sched[1] = 0;
+      }
+    }
+    // expert offsets: thread x < E counts the valid slots below expert x
+    for (int x = tid; x <= ra.E; x += blockDim.x) {
+      int o = 0;
       for (int s2 = 0; s2 < S; ++s2) {
-        const int e2 = sr.pick[s2];
-        less += valid(e2) && e2 < e;
-        if (s2 < tid && e2 == e) {
-          ++rank;
-          first = 0;
-        }
+        const int e2 = __builtin_amdgcn_readlane(e, s2);
+        o += valid(e2) && (x == ra.E || e2 < x);
       }
-      sr.sorted[less + rank] = tid;
-      if (publish) {
-        ra.sorted[less + rank] = tid;
-        ra.row_of[tid] = less + rank;
-      }
-    } else if (publish) {
-      ra.row_of[tid] = -1;
-    }
-    sr.first[tid] = first;
-  }
-  if (publish && tid < ra.E) {
-    int o = 0, nv = 0;
-    for (int s2 = 0; s2 < S; ++s2) {
-      o += valid(sr.pick[s2]) && sr.pick[s2] < tid;
-      nv += valid(sr.pick[s2]);
-    }
-    ra.off[tid] = o;
-    if (tid == 0) ra.off[ra.E] = nv;  // the valid slots
-  }
-  __syncthreads();
-  if (tid < S && first) {
-    int u = 0, M = 0;
-    for (int s2 = 0; s2 < S; ++s2) {
-      u += sr.first[s2] && sr.pick[s2] < e;
-      M += sr.pick[s2] == e;
-    }
-    sr.bucket[u] = make_int4(e, less, M, 0);
-    if (publish) reinterpret_cast<int4*>(ra.sched + sched_touched_offset())[u] = sr.bucket[u];
-  }
-  if (tid == 0) {
-    int n = 0;
-    for (int s2 = 0; s2 < S; ++s2) n += sr.first[s2];
-    sr.n_touched = n;
-    if (publish) {
-      ra.sched[0] = n;
-      ra.sched[1] = 0;
+      ra.off[x] = o;
     }
   }
-  __syncthreads();
 }
-
 
 // One row batch's scales for P planes, staged through a wave-private LDS slot.
 // Rows n0 .. n0 + RB*RPI - 1 of a plane are contiguous (RB*RPI*G scales of SB
@@ -339,27 +379,26 @@ __global__ __launch_bounds__(64 * kGuWaves) void gemv_gate_up_kernel(
       y_zero[i] = 0.f;
   }
   // ROUTE_V > 0: routing folded in (ROUTE_V logit registers per lane).
-  __shared__ SmallRoute sr;
+  __shared__ int32_t pick_lds[kFusedRouteMaxSlots];
   __shared__ uint32_t sslot[kGuWaves][ScaleStage<2, RB, 64 / LPR, 2>::kMaxPlaneBytes * 2 / 4];
   BucketView bv;
-  const int32_t* rows_sorted = b.sorted;
+  SmallRoute sr;
   if constexpr (ROUTE_V > 0) {
-    small_route<ROUTE_V>(ra, b.k, sr);
+    small_route<ROUTE_V>(ra, b.k, pick_lds, sr);
     if ((int)blockIdx.y >= sr.n_touched) return;
-    const int4 t = sr.bucket[blockIdx.y];
-    bv.e = t.x;
-    bv.r0 = t.y;
-    bv.M = t.z;
-    rows_sorted = sr.sorted;
+    bv.e = sr.e;
+    bv.r0 = sr.r0;
+    bv.M = sr.M;
   } else {
     if (!bucket_of(b, &bv)) return;
   }
-  // the token of bucket row r (wave-uniform; from LDS with the fused routing,
-  // else a scalar load)
+  // the token of bucket row r (wave-uniform; with the fused routing the slot
+  // whose row is r, from the lanes' rows, else a scalar load)
   auto token_at = [&](int r) {
     if (b.shared_T > 0) return r;
-    if constexpr (ROUTE_V > 0) return rows_sorted[r] / b.k;
-    return load_uniform_i32(rows_sorted + r) / b.k;
+    if constexpr (ROUTE_V > 0)
+      return (int)__builtin_ctzll(__builtin_amdgcn_ballot_w64(sr.pos == r)) / b.k;
+    return load_uniform_i32(b.sorted + r) / b.k;
   };
 
   constexpr int RPI = 64 / LPR;

@@ -118,9 +118,10 @@ hipError_t launch_schedule_from_offsets(const int32_t* off, int E, int64_t slots
 
 // Routing folded into the gate/up GEMV for very small batches (T <=
 // kFusedRouteMaxT tokens, T*k <= kFusedRouteMaxSlots slots): every workgroup
-// redoes the (cheap, deterministic) top-k and bucket build in LDS, and
-// workgroup (0,0) publishes idx, w, off, sorted, row_of and the schedule for
-// the down launch.
+// redoes the (deterministic) top-k and bucket build in registers, and
+// workgroup (0,0) publishes idx, w, sorted, row_of and the schedule for the
+// down launch, and off for more than one token (one token's rows follow the
+// rank of the pick, not the expert order).
 #ifndef MOE_FUSED_ROUTE_MAX_T
 #define MOE_FUSED_ROUTE_MAX_T 4
 #endif

@@ -44,6 +44,13 @@ __device__ __forceinline__ void argmax_step(float& bv, int& bi) {
   bi = take ? oi : bi;
 }
 
+// max(v, v of the DPP source lane); lanes outside ROW_MASK read INT_MIN
+// (the identity) and keep v.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int imax_step(int v) {
+  return max(v, __builtin_amdgcn_update_dpp((int)0x80000000, v, CTRL, ROW_MASK, 0xF, false));
+}
+
 __device__ __forceinline__ float readlane_f(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
@@ -62,20 +69,27 @@ template <int V, int G>
 __device__ void topk_group_variant(const float* __restrict__ logits, int ld, int T, int t0, int E,
                                    int k, const RouterSpec& rs, int32_t* __restrict__ idx,
                                    float* __restrict__ w, int32_t* idx_lds, float* w_lds,
-                                   int lds_t0);
+                                   int lds_t0, int* lane_pick);
 
 // need_w = false: the caller uses the picks only (w and w_lds are not
 // written); with expert top-p on, the weights decide the picks and are
-// formed anyway.
+// formed anyway.  lane_pick, when non-null, receives in each lane the pick
+// its group lane holds (group lane j < k: pick j, -1 if dropped; others -1).
+// rounds < k (one token per wave, need_w false, no top-p, plain softmax
+// router; ignored otherwise): stop after the first `rounds` picks, which
+// are final (pick j is decided in round j); only the first `rounds` lanes
+// are then written.
 template <int V, int G>
 __device__ __forceinline__ void topk_group(const float* __restrict__ logits, int ld, int T, int t0,
                                            int E, int k, const RouterSpec& rs,
                                            int32_t* __restrict__ idx, float* __restrict__ w,
                                            int32_t* idx_lds = nullptr, float* w_lds = nullptr,
-                                           int lds_t0 = 0, bool need_w = true) {
+                                           int lds_t0 = 0, bool need_w = true,
+                                           int* lane_pick = nullptr, int rounds = 64) {
   static_assert(G == 16 || G == 32 || G == 64, "group size");
   if (rs.variant()) {  // uniform over the launch
-    topk_group_variant<V, G>(logits, ld, T, t0, E, k, rs, idx, w, idx_lds, w_lds, lds_t0);
+    topk_group_variant<V, G>(logits, ld, T, t0, E, k, rs, idx, w, idx_lds, w_lds, lds_t0,
+                             lane_pick);
     return;
   }
   const float route_scale = rs.route_scale, top_p = rs.top_p;
@@ -95,6 +109,53 @@ __device__ __forceinline__ void topk_group(const float* __restrict__ logits, int
   }
   float my_val = 0.f;
   int my_idx = -1;
+  if constexpr (G == 64) {
+    // One token per wave: each round is a plain max over the wave, then the
+    // winner is the lowest expert holding that value - registers in
+    // ascending order, inside a register the lowest lane of the ballot -
+    // found with scalar bit scans.  The max runs on integer keys that order
+    // like the logits (sign-magnitude flipped to two's complement, -0 keyed
+    // as +0 so that key equality is float equality), where each DPP step is
+    // one integer max.
+    int key[V];
+#pragma unroll
+    for (int r = 0; r < V; ++r) {
+      const int bits = __float_as_int(val[r]);
+      key[r] = bits == (int)0x80000000 ? 0 : bits < 0 ? bits ^ 0x7FFFFFFF : bits;
+    }
+    constexpr int kRetiredKey = (int)0x80000000;  // below -inf's key
+    const int nr = (!need_w && !(top_p > 0.f && top_p < 1.f)) ? min(rounds, k) : k;
+    for (int j = 0; j < nr; ++j) {
+      int m = key[0];
+#pragma unroll
+      for (int r = 1; r < V; ++r) m = max(m, key[r]);
+      m = imax_step<kDppXor1>(m);
+      m = imax_step<kDppXor2>(m);
+      m = imax_step<kDppHalfMirror>(m);
+      m = imax_step<kDppMirror>(m);
+      m = imax_step<kDppBcast15, 0xA>(m);
+      m = imax_step<kDppBcast31, 0x8>(m);
+      m = __builtin_amdgcn_readlane(m, 63);
+      int wr = V, wl = 0;
+#pragma unroll
+      for (int r = V - 1; r >= 0; --r) {
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(key[r] == m);
+        if (hit != 0) {
+          wr = r;
+          wl = (int)__builtin_ctzll(hit);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < V; ++r) {
+        const bool mine = r == wr && lane == wl;
+        key[r] = mine ? kRetiredKey : key[r];
+        val[r] = mine ? ninf : val[r];
+      }
+      const float mv = __int_as_float(m < 0 ? m ^ 0x7FFFFFFF : m);
+      my_val = lane == j ? mv : my_val;
+      my_idx = lane == j ? wr * 64 + wl : my_idx;
+    }
+  } else {
   for (int j = 0; j < k; ++j) {
     float bv = val[0];
     int bi = id[0];
@@ -131,11 +192,14 @@ __device__ __forceinline__ void topk_group(const float* __restrict__ logits, int
     my_val = gl == j ? cv : my_val;
     my_idx = gl == j ? ci : my_idx;
   }
+  }
   if (!need_w && !(top_p > 0.f && top_p < 1.f)) {
-    if (tok && gl < k) {
+    const int done = G == 64 ? min(rounds, k) : k;  // picks formed
+    if (tok && gl < done) {
       if (idx) idx[(int64_t)t * k + gl] = my_idx;
       if (idx_lds) idx_lds[(t - lds_t0) * k + gl] = my_idx;
     }
+    if (lane_pick) *lane_pick = tok && gl < done ? my_idx : -1;
     return;
   }
   // weights: group lane 0 holds the top logit
@@ -171,6 +235,7 @@ __device__ __forceinline__ void topk_group(const float* __restrict__ logits, int
     if (idx_lds) idx_lds[(t - lds_t0) * k + gl] = iv;
     if (w_lds) w_lds[(t - lds_t0) * k + gl] = wv;
   }
+  if (lane_pick) *lane_pick = tok && gl < k ? (keep ? my_idx : -1) : -1;
 }
 
 // Router variants (the dasLLAMA PR's MoE seat lists a non-softmax gate and a
@@ -199,7 +264,7 @@ template <int V, int G>
 __device__ void topk_group_variant(const float* __restrict__ logits, int ld, int T, int t0, int E,
                                    int k, const RouterSpec& rs, int32_t* __restrict__ idx,
                                    float* __restrict__ w, int32_t* idx_lds, float* w_lds,
-                                   int lds_t0) {
+                                   int lds_t0, int* lane_pick) {
   const int lane = threadIdx.x & 63;
   const int gl = lane % G;
   const int t = t0 + lane / G;
@@ -333,6 +398,7 @@ __device__ void topk_group_variant(const float* __restrict__ logits, int ld, int
     if (idx_lds) idx_lds[(t - lds_t0) * k + gl] = my_idx;
     if (w_lds) w_lds[(t - lds_t0) * k + gl] = wv;
   }
+  if (lane_pick) *lane_pick = tok && gl < k ? my_idx : -1;
 }
 
 // Lanes per token: the smallest group that holds the row in 4 registers and
