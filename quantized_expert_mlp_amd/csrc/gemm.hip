@@ -42,8 +42,14 @@
 #ifndef MOE_GEMM_DB
 #define MOE_GEMM_DB 2  // weight register stages
 #endif
-#ifndef MOE_GEMM_DOWN_THIN_FIRST
-#define MOE_GEMM_DOWN_THIN_FIRST 1  // down pass: thin experts' tiles first
+
+// Dispatch order of the thin experts' tiles: 0 last, 1 first, 2 spread
+// evenly among the wide ones.
+#ifndef MOE_GEMM_THIN_ORDER_GU
+#define MOE_GEMM_THIN_ORDER_GU 0  // gate/up pass
+#endif
+#ifndef MOE_GEMM_THIN_ORDER_DN
+#define MOE_GEMM_THIN_ORDER_DN 1  // down pass
 #endif
 #ifndef MOE_GEMM_OCC
 #define MOE_GEMM_OCC 2  // workgroups per CU
@@ -140,7 +146,7 @@ struct GemmArgs {
 // (consecutive workgroups share a tile), so each source's grid is exactly
 // its own width.
 __device__ __forceinline__ bool tile_of(const Buckets& b, const GemmArgs& a, TileView* v,
-                                        int* src, int* cblk, bool thin_first) {
+                                        int* src, int* cblk, int order) {
   int wg = blockIdx.x;
   const int shared_wgs = a.shared_tiles * a.gx[1];
   if (wg < shared_wgs) {
@@ -158,9 +164,18 @@ __device__ __forceinline__ bool tile_of(const Buckets& b, const GemmArgs& a, Til
   *src = 0;
   const int n_tiles = b.sched[1];
   if (u >= n_tiles) return false;
-  if (thin_first) {  // start with the thin experts' sched[2] tiles, which end the list
-    u += n_tiles - b.sched[2];
+  // The list holds the wide experts' tiles, then the sched[2] one-tile thin
+  // experts' (at most 32 rows); `order` places the thin ones in dispatch
+  // order: 0 last, 1 first, 2 spread evenly among the wide ones.
+  const int n_thin = b.sched[2], n_wide = n_tiles - n_thin;
+  if (order == 1) {
+    u += n_wide;
     if (u >= n_tiles) u -= n_tiles;
+  } else if (order == 2 && n_thin > 0) {
+    // slots [0, u) hold c(u) = floor(u * n_thin / n_tiles) thin tiles
+    const int c0 = (int)((int64_t)u * n_thin / n_tiles);
+    const int c1 = (int)((int64_t)(u + 1) * n_thin / n_tiles);
+    u = c1 > c0 ? n_wide + c0 : u - c0;
   }
   const int4 t = reinterpret_cast<const int4*>(b.sched + sched_tiles_offset(b.E))[u];
   v->e = t.x;
@@ -281,66 +296,79 @@ __device__ __forceinline__ void gemm_tile(const TileView& tv, const GemmSrc& S, 
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[m][ns][p][v] = 0.f;
 
-  // Decoded weight operands: word d of a lane's 16 bytes feeds MFMA d.
-  typedef f16x8_t BFrag[NS][P][4];
-  auto decode = [&](const BStage<P, NS>& st, BFrag& bf) __attribute__((always_inline)) {
+  // Decoded weight operands: word d of a lane's 16 bytes feeds MFMA d.  The
+  // group scale pairs of a stage first, then one word at a time.
+  struct BScale {
+    f16x2_t s2[NS][P], m8s2[NS][P];
+  };
+  auto scales = [&](const BStage<P, NS>& st) __attribute__((always_inline)) {
+    BScale r;
 #pragma unroll
     for (int ns = 0; ns < NS; ++ns)
 #pragma unroll
       for (int p = 0; p < P; ++p) {
-        if constexpr (FMT == kFmtMxfp4) {
-          const _Float16 sc = e8m0_f16_shifted(st.s[ns][p], mx_shift[ns][p]);
-          const f16x2_t s2 = {sc, sc};
+        _Float16 sc;
+        if constexpr (FMT == kFmtMxfp4) sc = e8m0_f16_shifted(st.s[ns][p], mx_shift[ns][p]);
+        else sc = __builtin_bit_cast(_Float16, (uint16_t)st.s[ns][p]);
+        r.s2[ns][p] = f16x2_t{sc, sc};
+        r.m8s2[ns][p] = r.s2[ns][p] * f16x2_t{(_Float16)-8.0f, (_Float16)-8.0f};
+      }
+    return r;
+  };
+  typedef f16x8_t BWord[NS][P];
+  auto decode_word = [&](const BStage<P, NS>& st, const BScale& sc, int d, BWord& bw)
+      __attribute__((always_inline)) {
 #pragma unroll
-          for (int d = 0; d < 4; ++d)
-            bf[ns][p][d] = MS == 1 ? mx4_f16x8_cvt(st.q[ns][p][d], s2) : mx4_f16x8(st.q[ns][p][d], s2);
-        } else {
-          const _Float16 sc = __builtin_bit_cast(_Float16, (uint16_t)st.s[ns][p]);
-          const f16x2_t s2 = {sc, sc};
-          if constexpr (MS == 1) {
-            const f16x2_t m8s2 = s2 * f16x2_t{(_Float16)-8.0f, (_Float16)-8.0f};
+    for (int ns = 0; ns < NS; ++ns)
 #pragma unroll
-            for (int d = 0; d < 4; ++d) bf[ns][p][d] = q4_f16x8_cvt(st.q[ns][p][d], s2, m8s2);
-          } else {
-#pragma unroll
-            for (int d = 0; d < 4; ++d) bf[ns][p][d] = q4_f16x8(st.q[ns][p][d], s2);
-          }
-        }
+      for (int p = 0; p < P; ++p) {
+        if constexpr (FMT == kFmtMxfp4)
+          bw[ns][p] = MS == 1 ? mx4_f16x8_cvt(st.q[ns][p][d], sc.s2[ns][p])
+                              : mx4_f16x8(st.q[ns][p][d], sc.s2[ns][p]);
+        else if constexpr (MS == 1)
+          bw[ns][p] = q4_f16x8_cvt(st.q[ns][p][d], sc.s2[ns][p], sc.m8s2[ns][p]);
+        else
+          bw[ns][p] = q4_f16x8(st.q[ns][p][d], sc.s2[ns][p]);
       }
   };
 
   // Register rings: A(s) lives in as[s % DA] from its load (step s-DA)
   // until its LDS write (end of step s-1); B(s) lives in bs[s % DB] from its
-  // load (step s-DB) until its decode at the start of step s.
+  // load (step s-DB) until the start of step s, where it is copied out and
+  // its slot refilled.
   constexpr int DA = MOE_GEMM_DA, DB = MOE_GEMM_DB;
   constexpr int U = lcm_c(DA, DB);
   AStage<NA> as[DA];
   BStage<P, NS> bs[DB];
 
-  // One K step at ring phase u (s % U == u).
+  // One K step at ring phase u (s % U == u).  Word 0 is decoded before the
+  // MFMAs; word d + 1 is decoded while the MFMAs of word d run, so the
+  // decode's VALU work overlaps the matrix pipe inside one wave.
   auto step = [&](int s, auto uc) __attribute__((always_inline)) {
     constexpr int u = decltype(uc)::value;
-    BFrag bf;
-    decode(bs[u % DB], bf);
+    const BStage<P, NS> cur = bs[u % DB];
+    const BScale sc = scales(cur);
+    BWord bw[2];
+    decode_word(cur, sc, 0, bw[0]);
     b_load(bs[u % DB], min(s + DB, n - 1));
     a_load(as[u % DA], min(s + DA, n - 1));
     __builtin_amdgcn_sched_barrier(0);
-    const char* cur = lds[s & 1];
+    const char* cur_lds = lds[s & 1];
+    static_for<4>([&](auto dc) __attribute__((always_inline)) {
+      constexpr int d = decltype(dc)::value;
+      if constexpr (d < 3) decode_word(cur, sc, d + 1, bw[(d + 1) & 1]);
 #pragma unroll
-    for (int m = 0; m < MS; ++m) {
-      const char* ar = cur + (m * 32 + j) * kPitch + hf * 64;
-      f16x8_t af[4];
-#pragma unroll
-      for (int d = 0; d < 4; ++d) af[d] = *reinterpret_cast<const f16x8_t*>(ar + 16 * d);
-#pragma unroll
-      for (int d = 0; d < 4; ++d)
+      for (int m = 0; m < MS; ++m) {
+        const f16x8_t af =
+            *reinterpret_cast<const f16x8_t*>(cur_lds + (m * 32 + j) * kPitch + hf * 64 + 16 * d);
 #pragma unroll
         for (int ns = 0; ns < NS; ++ns)
 #pragma unroll
           for (int p = 0; p < P; ++p)
             acc[m][ns][p] =
-                __builtin_amdgcn_mfma_f32_32x32x16_f16(af[d], bf[ns][p][d], acc[m][ns][p], 0, 0, 0);
-    }
+                __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bw[d & 1][ns][p], acc[m][ns][p], 0, 0, 0);
+      }
+    });
     __builtin_amdgcn_sched_barrier(0);
     a_store(as[(u + 1) % DA], lds[(s + 1) & 1]);
     __syncthreads();
@@ -411,7 +439,8 @@ __global__ __launch_bounds__(kThreads, MOE_GEMM_OCC) void gemm_kernel(Buckets b,
   }
   TileView tv;
   int src = 0, cblk = 0;
-  if (!tile_of(b, a, &tv, &src, &cblk, MODE == 1 && MOE_GEMM_DOWN_THIN_FIRST)) return;
+  if (!tile_of(b, a, &tv, &src, &cblk, MODE == 0 ? MOE_GEMM_THIN_ORDER_GU : MOE_GEMM_THIN_ORDER_DN))
+    return;
   const GemmSrc S = src ? a.src[1] : a.src[0];
   if (MODE == 1 && (int)blockIdx.z >= S.ksplit) return;
 
