@@ -160,6 +160,30 @@ def test_layer_mid(wl, path):
     assert_y_close(y, y_ref, "%s path %d" % (wl.name, path))
 
 
+@pytest.mark.parametrize("k", [8, 64])
+@pytest.mark.parametrize("kind", ["integers", "signed_zeros"])
+def test_layer_one_token_ties(kind, k):
+    """One token through the GEMV's fused routing (each workgroup runs only
+    the arg-max rounds its pick needs, every wave on its own) with logits
+    full of exact ties: picks bit-exact (the lower index wins), weights and
+    y against the oracle."""
+    wl = _mid("one_token_ties_k%d" % k, 45, 1, 2048, 256, k, 1536)
+    say("one-token ties %s k=%d" % (kind, k))
+    inp = S.make_layer_inputs(wl, seed=11)
+    d = DeviceLayer(inp)
+    rng = np.random.default_rng([k, 45])
+    if kind == "integers":
+        L = rng.integers(0, 3, size=(1, wl.E)).astype(np.float32)
+    else:  # zeros of both signs, a few larger logits spread among them
+        L = np.where(rng.random((1, wl.E)) < 0.5, np.float32(-0.0), np.float32(0.0))
+        L[0, rng.choice(wl.E, k // 2, replace=False)] = 1.0
+    y_ref, idx_ref, w_ref = oracle.layer(inp.x, L, wl.k, inp.planes)
+    y, idx, w, _ = run_layer(d, logits=L, path=moe.MOE_PATH_GEMV)
+    assert np.array_equal(idx, idx_ref)
+    assert_w_close(w, w_ref, wl.name)
+    assert_y_close(y, y_ref, wl.name)
+
+
 def test_expert_mlp_direct():
     wl = _mid("mlp_direct", 25, 150, 256, 10, 3, 192)
     say("expert_mlp %s" % wl.name)
