@@ -53,7 +53,8 @@
  *
  * Tiled planes (moe_shape.layout = MOE_LAYOUT_TILED, written by
  * moe_pack_weights): the same bytes regrouped so that the grouped MFMA GEMM
- * reads each weight block as one contiguous kilobyte.  Per expert, the block
+ * and the tiled GEMV read each weight block as one contiguous kilobyte.  Per
+ * expert, the block
  * of rows 32*b .. 32*b+31 and inputs 64*c .. 64*c+63 is 1024 bytes at byte
  * ((b*(K/64) + c) * 1024); inside it, the 16 bytes of row 32*b+j for scale
  * group 2*c+h (inputs 64*c+32*h .. +31, same nibble order as above) sit at
@@ -86,11 +87,13 @@ enum moe_status {
 };
 
 /* Expert MLP path.  AUTO picks the streaming GEMV when the expected rows per
- * expert are few (decode) and the grouped MFMA GEMM otherwise (prefill). */
+ * expert are few (decode) and the grouped MFMA GEMM otherwise (prefill); see
+ * moe_layout for the rule on each layout. */
 enum moe_path { MOE_PATH_AUTO = 0, MOE_PATH_GEMV = 1, MOE_PATH_GEMM = 2 };
 
-/* Weight plane layout (see above).  TILED planes are served by the grouped
- * MFMA GEMM only (path AUTO or GEMM); ROWS planes by both paths. */
+/* Weight plane layout (see above), served by both paths.  AUTO takes the
+ * GEMV on TILED planes for up to 4 tokens (T*k <= 64), the MFMA GEMM beyond;
+ * on ROWS planes it takes the GEMV while T*k < 8E. */
 enum moe_layout { MOE_LAYOUT_ROWS = 0, MOE_LAYOUT_TILED = 1 };
 
 /* Weight format (see above), for every plane of a call. */
@@ -238,8 +241,9 @@ size_t moe_permute_workspace_bytes(int32_t T, int32_t k, int32_t E);
  *            256-byte aligned; its contents on entry are ignored.
  * The order in which a token's k terms are added to y is not fixed (device
  * atomics); the result differs from an ordered sum only by fp32 rounding.
- * Errors: INVALID_ARG, UNSUPPORTED (also for path GEMV with TILED planes),
- *         WORKSPACE, HIP.
+ * Errors: INVALID_ARG, UNSUPPORTED (also for path GEMV with TILED planes
+ *         whose K/32 prepared activation groups exceed 48 KB of LDS, K >
+ *         19648), WORKSPACE, HIP.
  */
 int moe_expert_mlp(const moe_shape *shape, const uint16_t *x, const int32_t *off,
                    const int32_t *sorted, const float *w, moe_q4 gate, moe_q4 up, moe_q4 down,

@@ -16,7 +16,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 LIB = os.path.join(PKG, "libmoe.so")
-SOURCES = ["moe_api.cpp", "routing.hip", "gemv.hip", "gemv_mxfp4.hip", "gemm.hip", "misc.hip"]
+SOURCES = ["moe_api.cpp", "routing.hip", "gemv.hip", "gemv_mxfp4.hip", "gemv_tiled.hip", "gemm.hip",
+           "misc.hip"]
 
 
 def hipcc() -> str:

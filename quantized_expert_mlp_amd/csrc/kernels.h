@@ -155,6 +155,19 @@ hipError_t launch_gemv_down(const Buckets& b, int max_buckets, const uint16_t* h
                             const Launch& L);
 bool gemv_supported(int K);
 
+// The same two GEMVs over tiled planes (gemv_tiled.hip): a workgroup per
+// 32-row block row of a bucket, its four waves splitting K.  Bucket and
+// routing arguments as above.
+hipError_t launch_gemv_tiled_gate_up(const Buckets& b, int max_buckets, const uint16_t* x, int H,
+                                     int I, const uint8_t* gq, const void* gs, const uint8_t* uq,
+                                     const void* us, uint16_t* h, float* y_zero, int64_t y_elems,
+                                     int fmt, const Launch& L, const RouteArgs* route = nullptr);
+hipError_t launch_gemv_tiled_down(const Buckets& b, int max_buckets, const uint16_t* h, int H,
+                                  int I, const uint8_t* dq, const void* ds, const float* w,
+                                  const float* gate_logit, int gate_ld, float* y, int fmt,
+                                  const Launch& L);
+bool gemv_tiled_supported(int K);
+
 // Grouped MFMA GEMM (prefill), fp16 operands with fp32 accumulation.
 // Row layout -> tiled layout of E experts' planes q [E][N][K/2], s [E][N][K/32]
 // (scale elements of the format fmt).

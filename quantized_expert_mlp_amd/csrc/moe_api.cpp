@@ -67,25 +67,32 @@ int check_shape(const moe_shape* sh) {
 }
 
 bool gemv_ok(const moe_shape* sh) {
+  if (sh->layout == MOE_LAYOUT_TILED)
+    return moe::gemv_tiled_supported(sh->H) && moe::gemv_tiled_supported(sh->I) &&
+           (sh->SI == 0 || moe::gemv_tiled_supported(sh->SI));
   return moe::gemv_supported(sh->H) && moe::gemv_supported(sh->I) &&
          (sh->SI == 0 || moe::gemv_supported(sh->SI));
 }
 
 // The grouped MFMA GEMM is taken when an expert's bucket is expected to hold
-// at least 8 rows (slots / E >= 8), or when the GEMV cannot serve the shape
-// (tiled planes included).
+// at least 8 rows (slots / E >= 8), or when the GEMV cannot serve the shape.
+// Tiled planes take the GEMV only for the few tokens its fused routing
+// serves (beyond that the MFMA GEMM reads them faster).
 int pick_gemm(const moe_shape* sh, bool* gemm) {
   const int64_t slots = (int64_t)sh->T * sh->k;
   switch (sh->path) {
     case MOE_PATH_GEMV:
-      if (!gemv_ok(sh) || sh->layout == MOE_LAYOUT_TILED) return MOE_ERR_UNSUPPORTED;
+      if (!gemv_ok(sh)) return MOE_ERR_UNSUPPORTED;
       *gemm = false;
       return MOE_OK;
     case MOE_PATH_GEMM:
       *gemm = true;
       return MOE_OK;
     default:
-      *gemm = sh->layout == MOE_LAYOUT_TILED || !gemv_ok(sh) || slots >= 8 * (int64_t)sh->E;
+      if (sh->layout == MOE_LAYOUT_TILED)
+        *gemm = !gemv_ok(sh) || sh->T > moe::kFusedRouteMaxT || slots > moe::kFusedRouteMaxSlots;
+      else
+        *gemm = !gemv_ok(sh) || slots >= 8 * (int64_t)sh->E;
       return MOE_OK;
   }
 }
@@ -201,23 +208,25 @@ int run_mlp(const moe_shape* sh, bool gemm, const Layout& L, void* ws, const uin
     uint16_t* hs = at<uint16_t>(ws, L.hs);
     const int max_buckets = (int)(slots < E ? slots : E);
     if (!sg.skip(MOE_STAGE_ACTIVATIONS)) return MOE_ERR_HIP;
-    err = moe::launch_gemv_gate_up(routed, max_buckets, x, H, I, gate.q, gate.s, up.q, up.s, h,
-                                   y_zero, y_elems, fmt, sg.at(MOE_STAGE_GATE_UP), route);
+    const bool tiled = sh->layout == MOE_LAYOUT_TILED;
+    auto gate_up = tiled ? moe::launch_gemv_tiled_gate_up : moe::launch_gemv_gate_up;
+    auto down_ = tiled ? moe::launch_gemv_tiled_down : moe::launch_gemv_down;
+    err = gate_up(routed, max_buckets, x, H, I, gate.q, gate.s, up.q, up.s, h, y_zero, y_elems, fmt,
+                  sg.at(MOE_STAGE_GATE_UP), route);
     if (err != hipSuccess) return MOE_ERR_HIP;
     if (shared) {
-      err = moe::launch_gemv_gate_up(sharedb, 1, x, H, sh->SI, shared[0].q, shared[0].s,
-                                     shared[1].q, shared[1].s, hs, nullptr, 0, fmt,
-                                     sg.at(MOE_STAGE_SHARED_GATE_UP));
+      err = gate_up(sharedb, 1, x, H, sh->SI, shared[0].q, shared[0].s, shared[1].q, shared[1].s,
+                    hs, nullptr, 0, fmt, sg.at(MOE_STAGE_SHARED_GATE_UP), nullptr);
       if (err != hipSuccess) return MOE_ERR_HIP;
     } else if (!sg.skip(MOE_STAGE_SHARED_GATE_UP)) {
       return MOE_ERR_HIP;
     }
-    err = moe::launch_gemv_down(routed, max_buckets, h, H, I, down.q, down.s, w, nullptr, 0, y,
-                                fmt, sg.at(MOE_STAGE_DOWN));
+    err = down_(routed, max_buckets, h, H, I, down.q, down.s, w, nullptr, 0, y, fmt,
+                sg.at(MOE_STAGE_DOWN));
     if (err != hipSuccess) return MOE_ERR_HIP;
     if (shared) {
-      err = moe::launch_gemv_down(sharedb, 1, hs, H, sh->SI, shared[2].q, shared[2].s, nullptr,
-                                  gate_logit, gate_ld, y, fmt, sg.at(MOE_STAGE_SHARED_DOWN));
+      err = down_(sharedb, 1, hs, H, sh->SI, shared[2].q, shared[2].s, nullptr, gate_logit,
+                  gate_ld, y, fmt, sg.at(MOE_STAGE_SHARED_DOWN));
       if (err != hipSuccess) return MOE_ERR_HIP;
     } else if (!sg.skip(MOE_STAGE_SHARED_DOWN)) {
       return MOE_ERR_HIP;

@@ -186,10 +186,17 @@ def test_expert_mlp_rejects(L):
 
 def test_tiled_layout_shape_rules(L):
     tiled = dict(layout=moe.MOE_LAYOUT_TILED)
-    assert moe.moe_workspace_bytes(_shape(**tiled)) > 0                      # AUTO -> MFMA path
+    assert moe.moe_workspace_bytes(_shape(**tiled)) > 0
     assert moe.moe_workspace_bytes(_shape(path=moe.MOE_PATH_GEMM, **tiled)) > 0
-    assert moe.moe_workspace_bytes(_shape(path=moe.MOE_PATH_GEMV, **tiled)) == 0
+    assert moe.moe_workspace_bytes(_shape(path=moe.MOE_PATH_GEMV, **tiled)) > 0
     assert moe.moe_workspace_bytes(_shape(layout=2)) == 0
+    # AUTO on tiled planes: the GEMV for up to four tokens (no fp16 activation
+    # copy in its workspace), the MFMA GEMM beyond
+    for T, path in ((1, moe.MOE_PATH_GEMV), (4, moe.MOE_PATH_GEMV), (5, moe.MOE_PATH_GEMM),
+                    (2048, moe.MOE_PATH_GEMM)):
+        dims = dict(T=T, H=6144, E=256, k=8, I=2048, **tiled)
+        assert moe.moe_workspace_bytes(_shape(**dims)) == \
+            moe.moe_workspace_bytes(_shape(path=path, **dims)), T
 
 
 def test_mxfp4_format_shape_rules(L):
@@ -199,7 +206,7 @@ def test_mxfp4_format_shape_rules(L):
     assert moe.moe_workspace_bytes(_shape(path=moe.MOE_PATH_GEMV, **mx)) > 0
     assert moe.moe_workspace_bytes(_shape(layout=moe.MOE_LAYOUT_TILED, **mx)) > 0
     assert moe.moe_workspace_bytes(_shape(layout=moe.MOE_LAYOUT_TILED, path=moe.MOE_PATH_GEMV,
-                                          **mx)) == 0
+                                          **mx)) > 0
     assert moe.moe_workspace_bytes(_shape(format=2)) == 0
     assert moe.moe_workspace_bytes(_shape(format=-1)) == 0
     # the AUTO rule does not depend on the format: decode takes the GEMV path

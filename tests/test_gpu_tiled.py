@@ -1,7 +1,8 @@
 """GPU tests of the tiled weight layout: moe_pack_weights against the layout's
 definition (bit-exact, both scale sizes), and the whole layer on tiled int4
-and MXFP4 planes against the CPU oracle, at mid sizes and at the full prefill
-sizes."""
+and MXFP4 planes against the CPU oracle on both expert paths (the streaming
+GEMV over tiled blocks and the MFMA GEMM), at mid sizes and at the full
+decode, decode-batch and prefill sizes."""
 import numpy as np
 import pytest
 import torch
@@ -43,43 +44,53 @@ def test_pack_matches_layout_definition(E, N, K, fmt):
     assert np.array_equal(host(ds, st), s_ref)
 
 
+PATHS = {"auto": moe.MOE_PATH_AUTO, "gemv": moe.MOE_PATH_GEMV, "gemm": moe.MOE_PATH_GEMM}
+
+
+# AUTO takes the tiled GEMV for up to four tokens (its fused routing) and
+# the MFMA GEMM beyond; both paths are also forced on every shape
+@pytest.mark.parametrize("path", list(PATHS))
 @pytest.mark.parametrize("wl", MID, ids=[w.name for w in MID])
-def test_layer_mid_tiled(wl):
-    say("tiled layer %s" % wl.name)
+def test_layer_mid_tiled(wl, path):
+    say("tiled layer %s path %s" % (wl.name, path))
     inp = S.make_layer_inputs(wl, seed=0)
     d = DeviceLayer(inp).tiled()
     L = _oracle_logits(inp)
     y_ref, idx_ref, w_ref = oracle.layer(inp.x, L, wl.k, inp.planes, inp.shared, inp.shared_gate,
                                          route_scale=0.75)
-    y, idx, w, lo = run_layer(d, logits=L, route_scale=0.75)
+    y, idx, w, lo = run_layer(d, logits=L, route_scale=0.75, path=PATHS[path])
     assert np.array_equal(idx, idx_ref)
     assert_w_close(w, w_ref, wl.name)
     assert_y_close(y, y_ref, "%s tiled" % wl.name)
 
 
+@pytest.mark.parametrize("path", ["auto", "gemv"])
 @pytest.mark.parametrize("wl", MID, ids=[w.name for w in MID])
-def test_layer_mid_tiled_mxfp4(wl):
-    say("tiled mxfp4 layer %s" % wl.name)
+def test_layer_mid_tiled_mxfp4(wl, path):
+    say("tiled mxfp4 layer %s path %s" % (wl.name, path))
     inp = S.make_layer_inputs(wl, seed=0, fmt="mxfp4")
     d = DeviceLayer(inp).tiled()
     L = _oracle_logits(inp)
     y_ref, idx_ref, _ = oracle.layer(inp.x, L, wl.k, inp.planes, inp.shared, inp.shared_gate,
                                      fmt="mxfp4")
-    y, idx, _, _ = run_layer(d, logits=L)
+    y, idx, _, _ = run_layer(d, logits=L, path=PATHS[path])
     assert np.array_equal(idx, idx_ref)
     assert_y_close(y, y_ref, "%s tiled mxfp4" % wl.name)
 
 
-@pytest.mark.parametrize("name,fmt", [("prefill_shared", "int4"), ("prefill_skewed", "int4"),
-                                      ("prefill_skewed", "mxfp4")])
-def test_layer_full_size_tiled(name, fmt):
+@pytest.mark.parametrize("name,fmt,path", [("prefill_shared", "int4", "auto"),
+                                           ("prefill_skewed", "int4", "auto"),
+                                           ("prefill_skewed", "mxfp4", "auto"),
+                                           ("decode", "int4", "auto"), ("decode", "mxfp4", "auto"),
+                                           ("decode_batch", "int4", "gemv")])
+def test_layer_full_size_tiled(name, fmt, path):
     wl = S.WORKLOADS[name]
-    say("full-size tiled layer %s %s (%s)" % (name, fmt, wl.description))
+    say("full-size tiled layer %s %s path %s (%s)" % (name, fmt, path, wl.description))
     inp = S.make_layer_inputs(wl, seed=0, fmt=fmt)
     d = DeviceLayer(inp).tiled()
     L = _oracle_logits(inp)
     rows = _rows(wl)
-    y, idx, w, _ = run_layer(d, logits=L)
+    y, idx, w, _ = run_layer(d, logits=L, path=PATHS[path])
     idx_ref, w_ref, _ = oracle.router_topk(L, wl.k)
     assert np.array_equal(idx, idx_ref)
     assert_w_close(w, w_ref, name)
