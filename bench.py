@@ -89,7 +89,10 @@ def counted_traffic(kernel: str, workload: str, gemm: bool, fmt: str = "int4",
             k_, v_ = line.split(":", 1)
             kv[k_.strip()] = v_.strip()
     h = hashlib.sha256()
-    srcs = ("gemm.hip",) if gemm else ("topk.h", "gemv_impl.h", "gemv.hip")
+    if gemm:
+        srcs = ("gemm.hip",)
+    else:
+        srcs = ("topk.h", "gemv_impl.h", "gemv_tiled.hip" if layout == "tiled" else "gemv.hip")
     for src in ("device.h", "kernels.h") + srcs:
         h.update(open(os.path.join(ROOT, "quantized_expert_mlp_amd", "csrc", src), "rb").read())
     if kv.get("kernel") != kernel or kv.get("source_sha256") != h.hexdigest()[:16]:
@@ -302,18 +305,23 @@ def measure(wl, args, layout, path_name, hip, steps, warmup, fold=False):
     touched = [c[0] for c in counts]
     nvar = len(pool) if pool is not None else len(sets)
 
+    def shape(path):
+        return moe.make_shape(T, wl.H, wl.E, wl.k, wl.I, wl.SI, path=path,
+                              layout=moe.MOE_LAYOUT_TILED if tiled else moe.MOE_LAYOUT_ROWS,
+                              format=moe.MOE_FORMAT_MXFP4 if mx else moe.MOE_FORMAT_INT4,
+                              top_p=args.top_p,
+                              score=moe.MOE_SCORE_SIGMOID if args.router.startswith("sigmoid")
+                              else moe.MOE_SCORE_SOFTMAX, select_bias=bias)
+
     path = {"auto": moe.MOE_PATH_AUTO, "gemv": moe.MOE_PATH_GEMV, "gemm": moe.MOE_PATH_GEMM}[path_name]
-    sh = moe.make_shape(T, wl.H, wl.E, wl.k, wl.I, wl.SI, path=path,
-                        layout=moe.MOE_LAYOUT_TILED if tiled else moe.MOE_LAYOUT_ROWS,
-                        format=moe.MOE_FORMAT_MXFP4 if mx else moe.MOE_FORMAT_INT4,
-                        top_p=args.top_p,
-                        score=moe.MOE_SCORE_SIGMOID if args.router.startswith("sigmoid")
-                        else moe.MOE_SCORE_SOFTMAX, select_bias=bias)
+    sh = shape(path)
     if moe.moe_workspace_bytes(sh) == 0:
         sys.exit("bench.py: workload %s is not served with --path %s --layout %s --format %s"
                  % (wl.name, path_name, layout, args.format))
-    # the library's AUTO rule (MOE_PATH_AUTO)
-    gemm = path_name == "gemm" or (path_name == "auto" and (tiled or (T * wl.k) >= 8 * wl.E))
+    # the path AUTO takes: the GEMV's workspace holds no fp16 activation copy,
+    # so AUTO sized like the GEMV (and the GEMV served) means the GEMV
+    gemm = path_name == "gemm" or (path_name == "auto" and moe.moe_workspace_bytes(sh) !=
+                                   moe.moe_workspace_bytes(shape(moe.MOE_PATH_GEMV)))
     nbytes = moe.moe_workspace_bytes(sh)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     y = torch.empty((T, wl.H), dtype=torch.float32, device="cuda")
@@ -502,9 +510,10 @@ def main():
     ap.add_argument("--workload", default="decode", choices=list(S.WORKLOADS))
     ap.add_argument("--path", default="auto", choices=["auto", "gemv", "gemm"],
                     help="expert-MLP path (auto: the library's choice)")
-    ap.add_argument("--layout", default="rows", choices=["rows", "tiled"],
-                    help="weight plane layout (tiled: packed once with moe_pack_weights, "
-                         "served by the MFMA path)")
+    ap.add_argument("--layout", default="tiled", choices=["rows", "tiled"],
+                    help="weight plane layout (tiled: packed once with moe_pack_weights, as at "
+                         "weight-load time, served by both expert paths; rows: the planes as "
+                         "drawn)")
     ap.add_argument("--format", default="int4", choices=["int4", "mxfp4"],
                     help="expert weight format (mxfp4: e2m1 nibbles, ue8m0 exponent per 32 "
                          "inputs)")

@@ -18,7 +18,13 @@ namespace moe {
 
 namespace {
 
-constexpr int kTiledWaves = 4;
+#ifndef MOE_TILED_WAVES
+#define MOE_TILED_WAVES 4  // waves per workgroup, each a share of the K blocks
+#endif
+#ifndef MOE_TILED_RB
+#define MOE_TILED_RB 2  // K blocks per load batch (two batches in flight)
+#endif
+constexpr int kTiledWaves = MOE_TILED_WAVES;
 
 // One prepared activation group: 16 words for the dot routines and the
 // group's offset correction (zero for MXFP4).  80 bytes, 16-byte aligned.
@@ -143,7 +149,7 @@ __device__ __forceinline__ void tiled_steps(const uint4* const (&q)[P],
 }
 
 // Sum of v over the two half-group lanes of a row (l and l ^ 32), then over
-// the four waves in a fixed order through red (kTiledWaves * 32 floats);
+// the waves in a fixed order through red (kTiledWaves * 32 floats);
 // the result is valid in wave 0's lanes 0..31.  Every thread calls.
 __device__ __forceinline__ float tiled_reduce(float v, float* red) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -281,7 +287,7 @@ __global__ __launch_bounds__(64 * kTiledWaves) void gemv_tiled_down_kernel(
 // One token per pass: a bucket of M rows streams its weights M times (the
 // path serves a few tokens, whose buckets are mostly single rows); K steps
 // per load batch.
-constexpr int kTiledMT = 1, kTiledRB = 2;
+constexpr int kTiledMT = 1, kTiledRB = MOE_TILED_RB;
 
 size_t tiled_lds_bytes(int K, int mt) { return (size_t)mt * (K / 32) * sizeof(TiledAct); }
 
