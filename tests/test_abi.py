@@ -197,6 +197,15 @@ def test_tiled_layout_shape_rules(L):
         dims = dict(T=T, H=6144, E=256, k=8, I=2048, **tiled)
         assert moe.moe_workspace_bytes(_shape(**dims)) == \
             moe.moe_workspace_bytes(_shape(path=path, **dims)), T
+    # the tiled GEMV holds the token's prepared row in 48 KB of LDS (80 bytes
+    # per 32 inputs): K <= 19648; beyond it AUTO takes the MFMA GEMM and an
+    # explicit GEMV is refused
+    for H, gemv in ((19648, True), (19712, False)):
+        dims = dict(T=1, H=H, E=16, k=2, I=128, **tiled)
+        ws_gemv = moe.moe_workspace_bytes(_shape(path=moe.MOE_PATH_GEMV, **dims))
+        assert (ws_gemv > 0) == gemv, H
+        want = ws_gemv if gemv else moe.moe_workspace_bytes(_shape(path=moe.MOE_PATH_GEMM, **dims))
+        assert moe.moe_workspace_bytes(_shape(**dims)) == want, H
 
 
 def test_mxfp4_format_shape_rules(L):

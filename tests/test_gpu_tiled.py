@@ -12,7 +12,7 @@ import oracle
 import quantized_expert_mlp_amd as moe
 from gpu_harness import (DeviceLayer, assert_w_close, assert_y_close, dev, host, run_layer, say,
                          tiled_reference)
-from test_gpu_parity import MID, SAMPLE_ROWS, _oracle_logits, _rows
+from test_gpu_parity import MID, SAMPLE_ROWS, _mid, _oracle_logits, _rows
 
 pytestmark = pytest.mark.gpu
 
@@ -76,6 +76,25 @@ def test_layer_mid_tiled_mxfp4(wl, path):
     y, idx, _, _ = run_layer(d, logits=L, path=PATHS[path])
     assert np.array_equal(idx, idx_ref)
     assert_y_close(y, y_ref, "%s tiled mxfp4" % wl.name)
+
+
+# the widest K the tiled GEMV serves (its prepared row fills 48 KB of LDS:
+# 614 groups of 80 bytes), on gate/up (K = H) and on down (K = I)
+WIDEST = [_mid("tiled_widest_h", 40, 2, 19648, 4, 2, 128), _mid("tiled_widest_i", 41, 3, 128, 4, 2, 19648)]
+
+
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
+@pytest.mark.parametrize("wl", WIDEST, ids=[w.name for w in WIDEST])
+def test_layer_tiled_gemv_widest(wl, fmt):
+    say("tiled GEMV at its widest K: %s %s" % (wl.name, fmt))
+    inp = S.make_layer_inputs(wl, seed=0, fmt=fmt)
+    d = DeviceLayer(inp).tiled()
+    L = _oracle_logits(inp)
+    y_ref, idx_ref, w_ref = oracle.layer(inp.x, L, wl.k, inp.planes, fmt=fmt)
+    y, idx, w, _ = run_layer(d, logits=L, path=moe.MOE_PATH_GEMV)
+    assert np.array_equal(idx, idx_ref)
+    assert_w_close(w, w_ref, wl.name)
+    assert_y_close(y, y_ref, "%s %s" % (wl.name, fmt))
 
 
 @pytest.mark.parametrize("name,fmt,path", [("prefill_shared", "int4", "auto"),
