@@ -78,12 +78,18 @@ def _check(r, r_out, n_out, y_ref, g, what):
     assert ulps.max() <= 1, what
 
 
-@pytest.mark.parametrize("path", [moe.MOE_PATH_GEMV, moe.MOE_PATH_GEMM])
+# (path, layout): both paths on row planes, the GEMV on tiled planes
+PATH_LAYOUTS = [(moe.MOE_PATH_GEMV, "rows"), (moe.MOE_PATH_GEMM, "rows"), (moe.MOE_PATH_GEMV, "tiled")]
+
+
+@pytest.mark.parametrize("path,layout", PATH_LAYOUTS, ids=["gemv", "gemm", "tiled_gemv"])
 @pytest.mark.parametrize("wl", MID, ids=[w.name for w in MID])
-def test_fold_mid(wl, path):
-    say("fold %s path=%d" % (wl.name, path))
+def test_fold_mid(wl, path, layout):
+    say("fold %s path=%d %s" % (wl.name, path, layout))
     inp = S.make_layer_inputs(wl, seed=0)
     d = DeviceLayer(inp)
+    if layout == "tiled":
+        d = d.tiled()
     L = _oracle_logits(inp)
     r = S.draw_residual(wl, T=inp.x.shape[0])
     g = S.draw_norm_weight(wl)
@@ -92,13 +98,16 @@ def test_fold_mid(wl, path):
     _check(r, r_out, n_out, y_ref, g, wl.name)
 
 
-@pytest.mark.parametrize("name,fmt", [("decode", "int4"), ("decode", "mxfp4"),
-                                      ("prefill_shared", "int4")])
-def test_fold_full_size(name, fmt):
+@pytest.mark.parametrize("name,fmt,layout", [("decode", "int4", "rows"), ("decode", "int4", "tiled"),
+                                             ("decode", "mxfp4", "rows"), ("decode", "mxfp4", "tiled"),
+                                             ("prefill_shared", "int4", "rows")])
+def test_fold_full_size(name, fmt, layout):
     wl = S.WORKLOADS[name]
-    say("fold full-size %s %s" % (name, fmt))
+    say("fold full-size %s %s %s" % (name, fmt, layout))
     inp = S.make_layer_inputs(wl, seed=0, fmt=fmt)
     d = DeviceLayer(inp)
+    if layout == "tiled":
+        d = d.tiled()
     L = _oracle_logits(inp)
     r = S.draw_residual(wl)
     g = S.draw_norm_weight(wl)

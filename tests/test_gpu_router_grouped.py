@@ -163,14 +163,20 @@ GROUPED_MID = [(MID[0], 4, 2), (MID[4], 8, 4), (MID[5], 4, 2), (MID[6], 8, 4), (
                (_mid("grouped_route", 34, 40, 256, 256, 8, 128), 8, 4)]
 
 
-@pytest.mark.parametrize("path", [moe.MOE_PATH_GEMV, moe.MOE_PATH_GEMM])
+# (path, layout): both paths on row planes, the GEMV on tiled planes
+PATH_LAYOUTS = [(moe.MOE_PATH_GEMV, "rows"), (moe.MOE_PATH_GEMM, "rows"), (moe.MOE_PATH_GEMV, "tiled")]
+
+
+@pytest.mark.parametrize("path,layout", PATH_LAYOUTS, ids=["gemv", "gemm", "tiled_gemv"])
 @pytest.mark.parametrize("case", GROUPED_MID, ids=[c[0].name for c in GROUPED_MID])
-def test_layer_mid_grouped(case, path):
+def test_layer_mid_grouped(case, path, layout):
     wl, ng, tg = case
     gate = "sigmoid"
-    say("grouped layer %s n_group=%d topk_group=%d path=%d" % (wl.name, ng, tg, path))
+    say("grouped layer %s n_group=%d topk_group=%d path=%d %s" % (wl.name, ng, tg, path, layout))
     inp = S.make_layer_inputs(wl, seed=7)
     d = DeviceLayer(inp)
+    if layout == "tiled":
+        d = d.tiled()
     L = _oracle_logits(inp)
     b = _bias(gate, wl.E, 3)
     ok = _decided_rows(L, wl.k, gate, b, ng, tg)
@@ -185,16 +191,19 @@ def test_layer_mid_grouped(case, path):
     assert_y_close(y, y_ref, "%s grouped" % wl.name)
 
 
-@pytest.mark.parametrize("name", ["decode", "prefill_skewed"])
-def test_layer_full_size_grouped(name):
+@pytest.mark.parametrize("name,layout", [("decode", "rows"), ("decode", "tiled"),
+                                         ("prefill_skewed", "rows")])
+def test_layer_full_size_grouped(name, layout):
     """E = 256, n_group = 8, topk_group = 4, k = 8 at full size: the GEMV's
     fused routing (decode) and the separate top-k launch (the 16384-slot
     skewed prefill); the route kernel's case is grouped_route above."""
     wl = S.WORKLOADS[name]
     gate = "sigmoid"
-    say("full-size grouped layer %s" % name)
+    say("full-size grouped layer %s %s" % (name, layout))
     inp = S.make_layer_inputs(wl, seed=0)
     d = DeviceLayer(inp)
+    if layout == "tiled":
+        d = d.tiled()
     L = _oracle_logits(inp)
     b = _bias(gate, wl.E, 4)
     ok = _decided_rows(L, wl.k, gate, b, 8, 4)

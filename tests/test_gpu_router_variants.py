@@ -136,13 +136,19 @@ def _run_variant(d, L, gate, bias, path, scale=1.0):
     return host(y), host(idx), host(w)
 
 
-@pytest.mark.parametrize("path", [moe.MOE_PATH_GEMV, moe.MOE_PATH_GEMM])
+# (path, layout): both paths on row planes, the GEMV on tiled planes
+PATH_LAYOUTS = [(moe.MOE_PATH_GEMV, "rows"), (moe.MOE_PATH_GEMM, "rows"), (moe.MOE_PATH_GEMV, "tiled")]
+
+
+@pytest.mark.parametrize("path,layout", PATH_LAYOUTS, ids=["gemv", "gemm", "tiled_gemv"])
 @pytest.mark.parametrize("wl", MID, ids=[w.name for w in MID])
-def test_layer_mid_variant(wl, path):
+def test_layer_mid_variant(wl, path, layout):
     gate = "sigmoid"
-    say("variant layer %s path=%d" % (wl.name, path))
+    say("variant layer %s path=%d %s" % (wl.name, path, layout))
     inp = S.make_layer_inputs(wl, seed=6)
     d = DeviceLayer(inp)
+    if layout == "tiled":
+        d = d.tiled()
     L = _oracle_logits(inp)
     b = _bias(gate, wl.E, 1)
     assert np.all(_decided_rows(L, wl.k, gate, b))
@@ -155,16 +161,20 @@ def test_layer_mid_variant(wl, path):
     assert_y_close(y, y_ref, "%s variant" % wl.name)
 
 
-@pytest.mark.parametrize("name,gate", [("decode", "sigmoid"), ("decode_batch", "softmax"),
-                                       ("prefill_skewed", "sigmoid")])
-def test_layer_full_size_variant(name, gate):
+@pytest.mark.parametrize("name,gate,layout", [("decode", "sigmoid", "rows"),
+                                              ("decode", "sigmoid", "tiled"),
+                                              ("decode_batch", "softmax", "rows"),
+                                              ("prefill_skewed", "sigmoid", "rows")])
+def test_layer_full_size_variant(name, gate, layout):
     """One workload per routing path: the GEMV's fused routing (decode), the
     one-workgroup route kernel (decode_batch, 256 slots) and the separate
     top-k launch (the 16384-slot skewed prefill)."""
     wl = S.WORKLOADS[name]
-    say("full-size variant layer %s %s" % (name, gate))
+    say("full-size variant layer %s %s %s" % (name, gate, layout))
     inp = S.make_layer_inputs(wl, seed=0)
     d = DeviceLayer(inp)
+    if layout == "tiled":
+        d = d.tiled()
     L = _oracle_logits(inp)
     b = _bias(gate, wl.E, 2)
     ok = _decided_rows(L, wl.k, gate, b)

@@ -74,13 +74,19 @@ def _run_top_p(d, L, p, path):
     return host(y), host(idx), host(w)
 
 
-@pytest.mark.parametrize("path", [moe.MOE_PATH_GEMV, moe.MOE_PATH_GEMM])
+# (path, layout): both paths on row planes, the GEMV on tiled planes
+PATH_LAYOUTS = [(moe.MOE_PATH_GEMV, "rows"), (moe.MOE_PATH_GEMM, "rows"), (moe.MOE_PATH_GEMV, "tiled")]
+
+
+@pytest.mark.parametrize("path,layout", PATH_LAYOUTS, ids=["gemv", "gemm", "tiled_gemv"])
 @pytest.mark.parametrize("wl", MID, ids=[w.name for w in MID])
-def test_layer_mid_top_p(wl, path):
+def test_layer_mid_top_p(wl, path, layout):
     p = 0.6
-    say("top-p layer %s path=%d" % (wl.name, path))
+    say("top-p layer %s path=%d %s" % (wl.name, path, layout))
     inp = S.make_layer_inputs(wl, seed=5)
     d = DeviceLayer(inp)
+    if layout == "tiled":
+        d = d.tiled()
     L = _oracle_logits(inp)
     assert np.all(_decided_rows(L, wl.k, p))
     y_ref, idx_ref, _ = oracle.layer(inp.x, L, wl.k, inp.planes, inp.shared, inp.shared_gate,
@@ -90,13 +96,16 @@ def test_layer_mid_top_p(wl, path):
     assert_y_close(y, y_ref, "%s top-p" % wl.name)
 
 
-@pytest.mark.parametrize("name", ["decode", "decode_batch", "prefill_skewed"])
-def test_layer_full_size_top_p(name):
+@pytest.mark.parametrize("name,layout", [("decode", "rows"), ("decode", "tiled"),
+                                         ("decode_batch", "rows"), ("prefill_skewed", "rows")])
+def test_layer_full_size_top_p(name, layout):
     p = 0.7
     wl = S.WORKLOADS[name]
-    say("full-size top-p layer %s" % name)
+    say("full-size top-p layer %s %s" % (name, layout))
     inp = S.make_layer_inputs(wl, seed=0)
     d = DeviceLayer(inp)
+    if layout == "tiled":
+        d = d.tiled()
     L = _oracle_logits(inp)
     ok = _decided_rows(L, wl.k, p)
     y, idx, _ = _run_top_p(d, L, p, moe.MOE_PATH_AUTO)
