@@ -70,6 +70,15 @@ class Hip:
         assert self.L.hipEventElapsedTime(ctypes.byref(out), a, b) == 0
         return out.value
 
+    # hipDeviceAttribute_t values (hip_runtime_api.h): peak shader and
+    # memory clocks, in kHz
+    ATTR_CLOCK_RATE, ATTR_MEMORY_CLOCK_RATE = 5, 60
+
+    def attribute(self, attr: int, device: int = 0) -> int:
+        v = ctypes.c_int()
+        assert self.L.hipDeviceGetAttribute(ctypes.byref(v), attr, device) == 0
+        return v.value
+
 
 def counted_traffic(kernel: str, workload: str, gemm: bool, fmt: str = "int4",
                     layout: str = "rows"):
@@ -248,8 +257,16 @@ def cpu_baseline(wl, seconds_hint: float, fmt: str = "int4", router: str = "soft
         sample = "%d decode tokens (distinct logits rows), %d threads" % (n, threads)
     else:
         sample = "%d of %d token rows, %d threads" % (n, wl.T, threads)
+    # the same on one thread, on a sample sized for about a third of the time
+    oracle.set_threads(1)
+    dt1 = run(1)
+    n1 = int(min(cap, max(1, round(seconds_hint / 3 / max(dt1, 1e-6)))))
+    dt1 = run(n1)
+    oracle.set_threads(threads)
     return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": sample, "seconds": round(dt, 2)}
+            "sample": sample, "seconds": round(dt, 2),
+            "single_thread": {"value": n1 / dt1, "unit": "tokens/s", "tokens": n1,
+                              "seconds": round(dt1, 2)}}
 
 
 def cpu_info():
@@ -351,15 +368,29 @@ def measure(wl, args, layout, path_name, hip, steps, warmup, fold=False):
         call(i)
     torch.cuda.synchronize()
 
-    # ---- timed region: exactly `steps` layer calls
+    # ---- timed region: exactly `steps` layer calls; HIP events on the launch
+    # stream between batches of `batch` calls give the spread over batches
+    batch = max(1, min(20, steps))
+    nb = steps // batch
+    bev = [hip.event() for _ in range(nb + 1)]
+    stream = torch.cuda.current_stream().cuda_stream
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
+        if i % batch == 0 and i // batch < nb:
+            hip.record(bev[i // batch], stream)
         call(i)
+        if i + 1 == nb * batch:
+            hip.record(bev[nb], stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / steps
     tokens_per_s = T * steps / wall
+    per_call = np.array([hip.ms(bev[j], bev[j + 1]) * 1e3 / batch for j in range(nb)])
+    timing = {"batch_calls": batch, "batches": nb,
+              "median_us_per_call": round(float(np.median(per_call)), 3),
+              "p10_us_per_call": round(float(np.percentile(per_call, 10)), 3),
+              "p90_us_per_call": round(float(np.percentile(per_call, 90)), 3)}
 
     # ---- per-stage device time (HIP events on the launch stream); with
     # fold these come from moe_layer_profiled, whose kernels are the folded
@@ -413,7 +444,7 @@ def measure(wl, args, layout, path_name, hip, steps, warmup, fold=False):
     del sets, pool, ws
     torch.cuda.empty_cache()
     return {
-        "ms_per_step": ms_per_step, "tokens_per_s": tokens_per_s, "gemm": gemm,
+        "ms_per_step": ms_per_step, "tokens_per_s": tokens_per_s, "gemm": gemm, "timing": timing,
         "stage_us": {k_: round(v * 1e3, 3) for k_, v in stage_ms.items()},
         "roofline": roof, "nvar": nvar, "pool": pool_np is not None,
         "layer": {"touched_experts": round(U, 1),
@@ -471,7 +502,7 @@ def fold_router_chain(wl, args, hip, steps, warmup):
     return out
 
 
-def read_probe(hip):
+def read_probe(hip, sizes=(113_246_208, 1 << 30), widths=(1024, 2048, 4096, 8192)):
     """Best streaming-read rate of moe_debug_read_probe over sizes and
     launch widths (the practical HBM read ceiling for the decode GEMVs)."""
     import torch
@@ -482,8 +513,8 @@ def read_probe(hip):
     sink = torch.zeros(256, dtype=torch.int32, device="cuda")
     st = torch.cuda.current_stream()
     rows = []
-    for nbytes in (113_246_208, 1 << 30):
-        for wgs in (1024, 2048, 4096, 8192):
+    for nbytes in sizes:
+        for wgs in widths:
             for _ in range(5):
                 moe.moe_debug_read_probe(buf, nbytes, wgs, sink)
             e = [hip.event() for _ in range(2)]
@@ -499,6 +530,8 @@ def read_probe(hip):
                          "gbs": round(nbytes / (best * 1e-3) / 1e9, 1)})
             log("read probe %d bytes, %d workgroups: %.2f us, %.1f GB/s"
                 % (nbytes, wgs, best * 1e3, rows[-1]["gbs"]))
+    del buf
+    torch.cuda.empty_cache()
     return rows
 
 
@@ -583,6 +616,20 @@ def main():
     m = measure(wl, args, args.layout, args.path, hip, args.steps, args.warmup, fold=args.fold)
     gemm = m["gemm"]
     mx = args.format == "mxfp4"
+    # an HBM-bound line is also held to this box's streaming-read probe
+    probe = None
+    if m["roofline"]["bound"] == "hbm":
+        best = max(read_probe(hip, sizes=(113_246_208,), widths=(2048, 4096)),
+                   key=lambda r: r["gbs"])
+        probe = {"kernel": "moe_debug_read_probe", "bytes": best["bytes"],
+                 "workgroups": best["workgroups"], "gbs": best["gbs"]}
+        m["roofline"]["probe_gbs"] = best["gbs"]
+        m["roofline"]["frac_of_probe"] = round(m["roofline"]["achieved"] / best["gbs"], 4)
+    props = torch.cuda.get_device_properties(0)
+    device = {"name": props.name, "arch": props.gcnArchName,
+              "compute_units": props.multi_processor_count,
+              "sclk_peak_mhz": hip.attribute(Hip.ATTR_CLOCK_RATE) // 1000,
+              "mclk_peak_mhz": hip.attribute(Hip.ATTR_MEMORY_CLOCK_RATE) // 1000}
 
     prefill = None
     if not args.no_prefill and not wl.name.startswith("prefill"):
@@ -596,6 +643,7 @@ def main():
             "ms_per_step": round(pm["ms_per_step"], 5),
             "tokens_per_s": round(pm["tokens_per_s"], 1),
             "layer": pm["layer"], "roofline": pm["roofline"], "stage_us": pm["stage_us"],
+            "timing": pm["timing"],
         }
 
     cpu = None
@@ -633,6 +681,9 @@ def main():
                    "input_rotation": ("%d logits rows" % m["nvar"]) if m["pool"]
                    else ("%d weight sets" % m["nvar"])},
         "roofline": m["roofline"],
+        "timing": m["timing"],
+        "hbm_probe": probe,
+        "device": device,
         "stage_us": m["stage_us"],
         "layer": m["layer"],
         "prefill": prefill,
