@@ -1,13 +1,17 @@
 // Streaming GEMV over tiled planes (moe_pack_weights' layout) for a handful
 // of tokens, so that one packed copy of the weights serves decode as well as
-// the grouped MFMA GEMM's prefill.
+// the grouped MFMA GEMM's prefill.  It computes what the row-layout GEMV does
+// (the colibri Vulkan-backend PR #418 expert triple: fused gate+up, SiLU
+// product, down with the routed slots weighted onto the output; int4 offset
+// binary or the later fmt=7 MXFP4, one scale per 32 inputs), with its
+// products, per-group scaling and routing prologue.
 //
 // A tiled block holds 32 rows x 64 inputs in one kilobyte, lane l's 16
 // bytes being row l%32, scale group 2c + l/32 - one load per lane reads a
-// block whole.  A workgroup of four waves owns one block row (32 weight
-// rows) of one bucket and splits its K steps (blocks) in four; each lane
-// accumulates its row's partial sums over its half-groups, the two halves
-// meet by a lane swap, the four waves' partials through LDS in a fixed
+// block whole.  A workgroup of kTiledWaves waves owns one block row (32
+// weight rows) of one bucket and splits its K steps (blocks) among them;
+// each lane accumulates its row's partial sums over its half-groups, the two
+// halves meet by a lane swap, the waves' partials through LDS in a fixed
 // order.  The activation row of the pass (one token) is prepared
 // once per workgroup in LDS in the form the dot routines take (the same
 // nibble pairing and offset correction as the row-layout GEMV), and a lane
