@@ -84,8 +84,6 @@ def _shifted_exponent_inputs(case):
 @pytest.mark.parametrize("path", [moe.MOE_PATH_GEMV, moe.MOE_PATH_GEMM])
 @pytest.mark.parametrize("case", ["small_down", "large_gate_up"])
 def test_layer_mxfp4_exponents_outside_fp16_window(case, path, layout):
-    if layout == "tiled" and path == moe.MOE_PATH_GEMV:
-        pytest.skip("tiled planes are served by the MFMA path only")
     say("mxfp4 exponents outside the fp16 window: %s path=%d %s" % (case, path, layout))
     inp = _shifted_exponent_inputs(case)
     d = DeviceLayer(inp)
