@@ -13,6 +13,8 @@ import quantized_expert_mlp_amd as moe
 from gpu_harness import (DeviceLayer, assert_w_close, assert_y_close, dev, host, run_layer, say,
                          tiled_reference)
 from test_gpu_parity import MID, SAMPLE_ROWS, _mid, _oracle_logits, _rows
+from test_gpu_router_grouped import _decided_rows as grouped_decided
+from test_gpu_top_p import _decided_rows as top_p_decided
 
 pytestmark = pytest.mark.gpu
 
@@ -76,6 +78,52 @@ def test_layer_mid_tiled_mxfp4(wl, path):
     y, idx, _, _ = run_layer(d, logits=L, path=PATHS[path])
     assert np.array_equal(idx, idx_ref)
     assert_y_close(y, y_ref, "%s tiled mxfp4" % wl.name)
+
+
+# AUTO's tiled GEMV at both limits of its fused routing (4 tokens, 64 slots),
+# with a bucket of up to 4 rows and a grouped and a top-p router on top
+FUSED_LIMIT = _mid("tiled_fused_limit", 42, 4, 512, 64, 16, 256)
+
+
+@pytest.mark.parametrize("router", ["softmax", "top_p", "grouped"])
+def test_layer_tiled_gemv_fused_route_limits(router):
+    wl = FUSED_LIMIT
+    say("tiled GEMV at the fused routing's limits (%s)" % router)
+    inp = S.make_layer_inputs(wl, seed=2)
+    d = DeviceLayer(inp).tiled()
+    L = _oracle_logits(inp)
+    # make every expert's bucket hold up to 4 rows: the tokens share most picks
+    L = (L + 3.0 * L[:1]).astype(np.float32)
+    kw, okw = {}, {}
+    if router == "top_p":
+        kw, okw = dict(top_p=0.8), dict(top_p=0.8)
+        assert np.all(top_p_decided(L, wl.k, 0.8))
+    elif router == "grouped":
+        kw = dict(score=moe.MOE_SCORE_SIGMOID, n_group=8, topk_group=4)
+        okw = dict(gate="sigmoid", n_group=8, topk_group=4)
+        assert np.all(grouped_decided(L, wl.k, "sigmoid", None, 8, 4))
+    sh = moe.make_shape(wl.T, wl.H, wl.E, wl.k, wl.I, 0, layout=d.layout, **kw)
+    nbytes = moe.moe_workspace_bytes(sh)
+    sh_gemv = moe.make_shape(wl.T, wl.H, wl.E, wl.k, wl.I, 0, layout=d.layout,
+                             path=moe.MOE_PATH_GEMV, **kw)
+    assert nbytes == moe.moe_workspace_bytes(sh_gemv)  # AUTO takes the GEMV here
+    ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda")
+    y = torch.full((wl.T, wl.H), float("nan"), dtype=torch.float32, device="cuda")
+    idx = torch.full((wl.T, wl.k), -7, dtype=torch.int32, device="cuda")
+    w = torch.full((wl.T, wl.k), float("nan"), dtype=torch.float32, device="cuda")
+    moe.moe_layer(sh, d.x, dev(L), None, d.planes["gate"], d.planes["up"], d.planes["down"],
+                  None, None, y, idx, w, None, ws, nbytes)
+    torch.cuda.synchronize()
+    y_ref, idx_ref, w_ref = oracle.layer(inp.x, L, wl.k, inp.planes, **okw)
+    got = host(idx)
+    assert np.array_equal(got, idx_ref)
+    counts = np.bincount(got[got >= 0].ravel(), minlength=wl.E)
+    assert counts.max() >= 2
+    # dropped picks (top-p) carry weight 0; the kept ones within the bar
+    got_w, kept = host(w), idx_ref >= 0
+    assert np.all(got_w[~kept] == 0.0)
+    assert_w_close(got_w[kept], w_ref[kept], wl.name)
+    assert_y_close(host(y), y_ref, "%s %s" % (wl.name, router))
 
 
 # the widest K the tiled GEMV serves (its prepared row fills 48 KB of LDS:
