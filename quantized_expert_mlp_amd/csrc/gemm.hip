@@ -43,6 +43,14 @@
 #define MOE_GEMM_DB 2  // weight register stages
 #endif
 
+#ifndef MOE_GEMM_W0_AHEAD
+// Decode the next K step's word 0 under this step's last MFMAs (bit 0: the
+// gate/up pass, bit 1: the down pass; int4 only).  On the skewed prefill it
+// takes the int4 down pass 645 -> 624 us, while gate/up and MXFP4 (whose
+// conversion decode is lighter) measured equal or slower.
+#define MOE_GEMM_W0_AHEAD 2
+#endif
+
 // Dispatch order of the thin experts' tiles: 0 last, 1 first, 2 spread
 // evenly among the wide ones.
 #ifndef MOE_GEMM_THIN_ORDER_GU
@@ -342,21 +350,31 @@ __device__ __forceinline__ void gemm_tile(const TileView& tv, const GemmSrc& S, 
   BStage<P, NS> bs[DB];
 
   // One K step at ring phase u (s % U == u).  Word 0 is decoded before the
-  // MFMAs; word d + 1 is decoded while the MFMAs of word d run, so the
-  // decode's VALU work overlaps the matrix pipe inside one wave.
+  // MFMAs (or, with kAhead, under the previous step's last MFMAs, into
+  // bw[0], which word 2's MFMAs no longer read); word d + 1 is decoded while
+  // the MFMAs of word d run, so the decode's VALU work overlaps the matrix
+  // pipe inside one wave.
+  constexpr bool kAhead = FMT == kFmtInt4 && (MOE_GEMM_W0_AHEAD & (MODE == 1 ? 2 : 1)) != 0;
+  BWord bw[2];
   auto step = [&](int s, auto uc) __attribute__((always_inline)) {
     constexpr int u = decltype(uc)::value;
     const BStage<P, NS> cur = bs[u % DB];
     const BScale sc = scales(cur);
-    BWord bw[2];
-    decode_word(cur, sc, 0, bw[0]);
+    if constexpr (!kAhead) decode_word(cur, sc, 0, bw[0]);
     b_load(bs[u % DB], min(s + DB, n - 1));
     a_load(as[u % DA], min(s + DA, n - 1));
     __builtin_amdgcn_sched_barrier(0);
     const char* cur_lds = lds[s & 1];
     static_for<4>([&](auto dc) __attribute__((always_inline)) {
       constexpr int d = decltype(dc)::value;
-      if constexpr (d < 3) decode_word(cur, sc, d + 1, bw[(d + 1) & 1]);
+      if constexpr (d < 3) {
+        decode_word(cur, sc, d + 1, bw[(d + 1) & 1]);
+      } else if constexpr (kAhead) {
+        // word 0 of step s + 1 from its ring slot (loaded a step ago; a
+        // past-the-end step re-reads the last one and is never used)
+        const BStage<P, NS>& nxt = bs[(u + 1) % DB];
+        decode_word(nxt, scales(nxt), 0, bw[0]);
+      }
 #pragma unroll
       for (int m = 0; m < MS; ++m) {
         const f16x8_t af =
@@ -381,6 +399,7 @@ __device__ __forceinline__ void gemm_tile(const TileView& tv, const GemmSrc& S, 
     a_load(as[decltype(i)::value], min((int)decltype(i)::value, n - 1));
   });
   a_store(as[0], lds[0]);
+  if constexpr (kAhead) decode_word(bs[0], scales(bs[0]), 0, bw[0]);
   __syncthreads();
   int s = 0;
   for (; s + U <= n; s += U)
