@@ -178,13 +178,16 @@ __device__ __forceinline__ bool bucket_of(const Buckets& b, BucketView* v) {
     v->M = b.shared_T;
     return true;
   }
+  // The entry is read together with the count (one memory round trip, not
+  // two): blockIdx.y is below the launch's bucket bound, which the list's
+  // capacity covers, and an entry past the count is never used.
   const int u = blockIdx.y;
-  if (u >= b.sched[0]) return false;
+  const int n = b.sched[0];
   const int4 t = reinterpret_cast<const int4*>(b.sched + sched_touched_offset())[u];
   v->e = t.x;
   v->r0 = t.y;
   v->M = t.z;
-  return true;
+  return u < n;
 }
 
 // The fused small-batch routing (see RouteArgs), held in each wave's
