@@ -130,7 +130,7 @@ struct GemmSrc {
   const uint8_t* q[2];   // weight planes: [E][N][K/2] nibbles
   const void* s[2];      // and their [E][N][K/32] scales (fp16 bits or ue8m0 bytes)
   uint16_t* hout;        // MODE 0 output, row stride N
-  int ksplit;            // MODE 1: K ranges over blockIdx.z
+  int ksplit;            // K ranges of one tile's column block (MODE 1; 1 for MODE 0)
   int tiled;             // planes in the tiled layout (1 KB per 32 rows x 64 k)
 };
 
@@ -148,18 +148,22 @@ struct GemmArgs {
   int64_t y_elems;       // (a multiple of 4)
 };
 
-// Tile and column block of this workgroup.  blockIdx.x runs first over the
-// shared expert's tiles (identity rows over all tokens), a.gx[1] column
-// blocks each, then over the routed tile list, a.gx[0] column blocks each
-// (consecutive workgroups share a tile), so each source's grid is exactly
-// its own width.
+// Tile, column block and K range of this workgroup.  blockIdx.x runs first
+// over the shared expert's tiles (identity rows over all tokens), a.gx[1]
+// column blocks times its ksplit K ranges each, then over the routed tile
+// list, a.gx[0] column blocks times its ksplit each (consecutive workgroups
+// share a tile, column blocks before K ranges), so each source's grid is
+// exactly its own size and the long shared-expert work is dispatched first,
+// all of its K ranges included.
 __device__ __forceinline__ bool tile_of(const Buckets& b, const GemmArgs& a, TileView* v,
-                                        int* src, int* cblk, int order) {
+                                        int* src, int* cblk, int* kz, int order) {
   int wg = blockIdx.x;
-  const int shared_wgs = a.shared_tiles * a.gx[1];
+  const int per1 = a.gx[1] * a.src[1].ksplit;
+  const int shared_wgs = a.shared_tiles * per1;
   if (wg < shared_wgs) {
-    const int u = wg / a.gx[1];
-    *cblk = wg - u * a.gx[1];
+    const int u = wg / per1, r = wg - u * per1;
+    *kz = r / a.gx[1];
+    *cblk = r - *kz * a.gx[1];
     *src = 1;
     v->e = 0;
     v->row0 = u * kBM;
@@ -167,8 +171,11 @@ __device__ __forceinline__ bool tile_of(const Buckets& b, const GemmArgs& a, Til
     return v->nrows > 0;
   }
   wg -= shared_wgs;
-  int u = wg / a.gx[0];
-  *cblk = wg - u * a.gx[0];
+  const int per0 = a.gx[0] * a.src[0].ksplit;
+  int u = wg / per0;
+  const int r = wg - u * per0;
+  *kz = r / a.gx[0];
+  *cblk = r - *kz * a.gx[0];
   *src = 0;
   const int n_tiles = b.sched[1];
   if (u >= n_tiles) return false;
@@ -457,11 +464,11 @@ __global__ __launch_bounds__(kThreads, MOE_GEMM_OCC) void gemm_kernel(Buckets b,
     for (int64_t i = gid; i < a.y_elems / 4; i += nthr) y4[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
   TileView tv;
-  int src = 0, cblk = 0;
-  if (!tile_of(b, a, &tv, &src, &cblk, MODE == 0 ? MOE_GEMM_THIN_ORDER_GU : MOE_GEMM_THIN_ORDER_DN))
+  int src = 0, cblk = 0, kz = 0;
+  if (!tile_of(b, a, &tv, &src, &cblk, &kz,
+               MODE == 0 ? MOE_GEMM_THIN_ORDER_GU : MOE_GEMM_THIN_ORDER_DN))
     return;
   const GemmSrc S = src ? a.src[1] : a.src[0];
-  if (MODE == 1 && (int)blockIdx.z >= S.ksplit) return;
 
   __shared__ __attribute__((aligned(16))) char lds[2][kBM * kPitch];
   __shared__ int row_tok[kBM];
@@ -491,9 +498,9 @@ __global__ __launch_bounds__(kThreads, MOE_GEMM_OCC) void gemm_kernel(Buckets b,
   const int nks = S.K / kKS;
   int k0 = 0, k1 = nks;
   if (MODE == 1) {
-    const int z = blockIdx.z, ks = S.ksplit;
-    k0 = (int)((int64_t)nks * z / ks);
-    k1 = (int)((int64_t)nks * (z + 1) / ks);
+    const int ks = S.ksplit;
+    k0 = (int)((int64_t)nks * kz / ks);
+    k1 = (int)((int64_t)nks * (kz + 1) / ks);
   }
 
   // Source row of each activation chunk this thread loads; rows past the
@@ -541,14 +548,16 @@ int64_t routed_tile_estimate(const Buckets& b) {
 }
 
 template <int P, int NS, int MODE>
-hipError_t launch_tiles(const Buckets& b, int max_tiles, GemmArgs a, int gz, int fmt,
-                        const Launch& L) {
+hipError_t launch_tiles(const Buckets& b, int max_tiles, GemmArgs a, int fmt, const Launch& L) {
   constexpr int BN = kWaves * 32 * NS;
   a.gx[0] = (a.src[0].N + BN - 1) / BN;
   a.gx[1] = a.shared_tiles > 0 ? (a.src[1].N + BN - 1) / BN : 1;
-  const int64_t wgs = (int64_t)a.shared_tiles * a.gx[1] + (int64_t)max_tiles * a.gx[0];
+  a.src[0].ksplit = std::max(a.src[0].ksplit, 1);
+  a.src[1].ksplit = std::max(a.src[1].ksplit, 1);
+  const int64_t wgs = (int64_t)a.shared_tiles * a.gx[1] * a.src[1].ksplit +
+                      (int64_t)max_tiles * a.gx[0] * a.src[0].ksplit;
   if (wgs < 1 || wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)wgs, 1, gz);
+  const dim3 grid((unsigned)wgs);
   if (fmt == kFmtMxfp4)
     MOE_LAUNCH(L, (gemm_kernel<P, NS, MODE, kFmtMxfp4>), grid, dim3(kThreads), 0, b, a);
   else
@@ -592,7 +601,7 @@ hipError_t launch_gemm_gate_up(const Buckets& b, int max_tiles, const uint16_t* 
     a.shared_tiles = (shared->T + kBM - 1) / kBM;
   }
   a.H = H;
-  return launch_tiles<2, kGateUpNS, 0>(b, max_tiles, a, 1, fmt, L);
+  return launch_tiles<2, kGateUpNS, 0>(b, max_tiles, a, fmt, L);
 }
 
 hipError_t launch_gemm_down(const Buckets& b, int max_tiles, const uint16_t* h16, int H, int I,
@@ -627,12 +636,8 @@ hipError_t launch_gemm_down(const Buckets& b, int max_tiles, const uint16_t* h16
     total += (int64_t)a.shared_tiles * gx * (shared->SI / kKS);
   }
   r.ksplit = down_split(I / kKS, total);
-  int gz = r.ksplit;
-  if (shared) {
-    a.src[1].ksplit = down_split(shared->SI / kKS, total);
-    gz = std::max(gz, a.src[1].ksplit);
-  }
-  return launch_tiles<1, kDownNS, 1>(b, max_tiles, a, gz, fmt, L);
+  if (shared) a.src[1].ksplit = down_split(shared->SI / kKS, total);
+  return launch_tiles<1, kDownNS, 1>(b, max_tiles, a, fmt, L);
 }
 
 }  // namespace moe
