@@ -59,6 +59,13 @@
 #ifndef MOE_GEMM_THIN_ORDER_DN
 #define MOE_GEMM_THIN_ORDER_DN 1  // down pass
 #endif
+// Rows per shared-expert tile in the gate/up pass: 64-row tiles halve the
+// longest workgroups' MFMA chain at the cost of decoding the shared weights
+// twice as often (prefill_shared gate/up 79.5 -> 76.0 us, MXFP4 87.5 -> 83.7
+// us against 128-row tiles; 96 no better).
+#ifndef MOE_GEMM_SHARED_ROWS_GU
+#define MOE_GEMM_SHARED_ROWS_GU 64
+#endif
 #ifndef MOE_GEMM_OCC
 #define MOE_GEMM_OCC 2  // workgroups per CU
 #endif
@@ -93,6 +100,9 @@ constexpr int gcd_c(int x, int y) { return y == 0 ? x : gcd_c(y, x % y); }
 constexpr int lcm_c(int x, int y) { return x / gcd_c(x, y) * y; }
 
 constexpr int kBM = kGemmTileRows;    // 128 rows per tile
+static_assert(MOE_GEMM_SHARED_ROWS_GU > 0 && MOE_GEMM_SHARED_ROWS_GU <= kBM &&
+                  MOE_GEMM_SHARED_ROWS_GU % 32 == 0,
+              "shared-expert tiles hold whole 32-row subtiles, at most a tile");
 constexpr int kKS = 64;               // K per step
 constexpr int kPitch = kKS * 2 + 16;  // LDS row pitch in bytes (padding breaks bank conflicts)
 constexpr int kWaves = MOE_GEMM_WAVES;
@@ -137,7 +147,8 @@ struct GemmSrc {
 struct GemmArgs {
   GemmSrc src[2];        // [0] routed buckets, [1] shared expert
   int shared_T;          // rows of the shared expert (0: none)
-  int shared_tiles;      // 128-row tiles of the shared expert
+  int shared_tiles;      // row tiles of the shared expert
+  int shared_rows;       // rows per shared-expert tile (at most kBM)
   int gx[2];             // column blocks of one tile: [0] routed, [1] shared
   const float* w;        // MODE 1 combine weights per slot
   const float* gate_logit;  // MODE 1 shared-expert gate logits (nullable)
@@ -166,8 +177,8 @@ __device__ __forceinline__ bool tile_of(const Buckets& b, const GemmArgs& a, Til
     *cblk = r - *kz * a.gx[1];
     *src = 1;
     v->e = 0;
-    v->row0 = u * kBM;
-    v->nrows = min(kBM, a.shared_T - v->row0);
+    v->row0 = u * a.shared_rows;
+    v->nrows = min(a.shared_rows, a.shared_T - v->row0);
     return v->nrows > 0;
   }
   wg -= shared_wgs;
@@ -598,7 +609,8 @@ hipError_t launch_gemm_gate_up(const Buckets& b, int max_tiles, const uint16_t* 
     sh.hout = shared->h16;
     sh.ksplit = 1;
     a.shared_T = shared->T;
-    a.shared_tiles = (shared->T + kBM - 1) / kBM;
+    a.shared_rows = MOE_GEMM_SHARED_ROWS_GU;
+    a.shared_tiles = (shared->T + a.shared_rows - 1) / a.shared_rows;
   }
   a.H = H;
   return launch_tiles<2, kGateUpNS, 0>(b, max_tiles, a, fmt, L);
@@ -630,6 +642,7 @@ hipError_t launch_gemm_down(const Buckets& b, int max_tiles, const uint16_t* h16
     sh.q[0] = sh.q[1] = shared->q[2];
     sh.s[0] = sh.s[1] = shared->s[2];
     a.shared_T = shared->T;
+    a.shared_rows = kBM;
     a.shared_tiles = (shared->T + kBM - 1) / kBM;
     a.gate_logit = shared->gate_logit;
     a.gate_ld = shared->gate_ld;
