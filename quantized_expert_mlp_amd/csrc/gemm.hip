@@ -59,12 +59,17 @@
 #ifndef MOE_GEMM_THIN_ORDER_DN
 #define MOE_GEMM_THIN_ORDER_DN 1  // down pass
 #endif
-// Rows per shared-expert tile in the gate/up pass: 64-row tiles halve the
-// longest workgroups' MFMA chain at the cost of decoding the shared weights
-// twice as often (prefill_shared gate/up 79.5 -> 76.0 us, MXFP4 87.5 -> 83.7
-// us against 128-row tiles; 96 no better).
+// Rows per shared-expert tile on tiled planes (row planes keep 128): 64-row
+// tiles halve the longest workgroups' MFMA chain at the cost of decoding the
+// shared weights twice as often.  prefill_shared gate/up 79.5 -> 76.0 us
+// (MXFP4 87.5 -> 83.7 us; 96 rows no better), down 66.2 -> 63.5 us; on row
+// planes, whose weight reads are already re-fetched per K step, the down
+// pass measured 79.4 -> 92.1 us.
 #ifndef MOE_GEMM_SHARED_ROWS_GU
 #define MOE_GEMM_SHARED_ROWS_GU 64
+#endif
+#ifndef MOE_GEMM_SHARED_ROWS_DN
+#define MOE_GEMM_SHARED_ROWS_DN 64
 #endif
 #ifndef MOE_GEMM_OCC
 #define MOE_GEMM_OCC 2  // workgroups per CU
@@ -101,7 +106,8 @@ constexpr int lcm_c(int x, int y) { return x / gcd_c(x, y) * y; }
 
 constexpr int kBM = kGemmTileRows;    // 128 rows per tile
 static_assert(MOE_GEMM_SHARED_ROWS_GU > 0 && MOE_GEMM_SHARED_ROWS_GU <= kBM &&
-                  MOE_GEMM_SHARED_ROWS_GU % 32 == 0,
+                  MOE_GEMM_SHARED_ROWS_GU % 32 == 0 && MOE_GEMM_SHARED_ROWS_DN > 0 &&
+                  MOE_GEMM_SHARED_ROWS_DN <= kBM && MOE_GEMM_SHARED_ROWS_DN % 32 == 0,
               "shared-expert tiles hold whole 32-row subtiles, at most a tile");
 constexpr int kKS = 64;               // K per step
 constexpr int kPitch = kKS * 2 + 16;  // LDS row pitch in bytes (padding breaks bank conflicts)
@@ -609,7 +615,7 @@ hipError_t launch_gemm_gate_up(const Buckets& b, int max_tiles, const uint16_t* 
     sh.hout = shared->h16;
     sh.ksplit = 1;
     a.shared_T = shared->T;
-    a.shared_rows = MOE_GEMM_SHARED_ROWS_GU;
+    a.shared_rows = tiled ? MOE_GEMM_SHARED_ROWS_GU : kBM;
     a.shared_tiles = (shared->T + a.shared_rows - 1) / a.shared_rows;
   }
   a.H = H;
@@ -642,8 +648,8 @@ hipError_t launch_gemm_down(const Buckets& b, int max_tiles, const uint16_t* h16
     sh.q[0] = sh.q[1] = shared->q[2];
     sh.s[0] = sh.s[1] = shared->s[2];
     a.shared_T = shared->T;
-    a.shared_rows = kBM;
-    a.shared_tiles = (shared->T + kBM - 1) / kBM;
+    a.shared_rows = tiled ? MOE_GEMM_SHARED_ROWS_DN : kBM;
+    a.shared_tiles = (shared->T + a.shared_rows - 1) / a.shared_rows;
     a.gate_logit = shared->gate_logit;
     a.gate_ld = shared->gate_ld;
     total += (int64_t)a.shared_tiles * gx * (shared->SI / kKS);
