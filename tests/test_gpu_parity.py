@@ -203,6 +203,42 @@ def test_expert_mlp_direct():
         assert_y_close(host(y), y_ref, "expert_mlp path %d" % path)
 
 
+def test_expert_mlp_repeated_picks():
+    """moe_expert_mlp on buckets a router never makes: every token picks
+    expert 0 three times, so its bucket holds 60 rows at T = 20, more rows
+    than tokens (two MFMA subtiles; the GEMV takes a token per row).  y
+    against the oracle's expert rows weighted and summed per pick."""
+    wl = _mid("mlp_repeats", 39, 20, 256, 4, 4, 192)
+    say("expert_mlp with repeated picks")
+    inp = S.make_layer_inputs(wl)
+    rng = np.random.default_rng(39)
+    idx = np.tile(np.array([0, 2, 0, 0], np.int32), (wl.T, 1))
+    idx[:, 1] = rng.integers(1, wl.E, wl.T)
+    w = rng.uniform(0.1, 1.0, idx.shape).astype(np.float32)
+    off, srt, _ = oracle.permute(idx, wl.E)
+    assert off[1] - off[0] == 3 * wl.T
+    x64 = S.bf16_bits_to_f32(inp.x).astype(np.float64)
+    pl = inp.planes
+    y_ref = np.zeros((wl.T, wl.H))
+    for t in range(wl.T):
+        for j in range(wl.k):
+            e = idx[t, j]
+            _, o = oracle.expert_forward((pl["gate"][0][e], pl["gate"][1][e]),
+                                         (pl["up"][0][e], pl["up"][1][e]),
+                                         (pl["down"][0][e], pl["down"][1][e]), x64[t])
+            y_ref[t] += float(w[t, j]) * o
+    d = DeviceLayer(inp)
+    for path in (moe.MOE_PATH_GEMV, moe.MOE_PATH_GEMM):
+        sh = moe.make_shape(wl.T, wl.H, wl.E, wl.k, wl.I, path=path)
+        nb = moe.moe_workspace_bytes(sh)
+        ws = torch.full((nb,), 0xEE, dtype=torch.uint8, device="cuda")
+        y = torch.full((wl.T, wl.H), float("nan"), device="cuda")
+        moe.moe_expert_mlp(sh, d.x, dev(off), dev(srt), dev(w), d.planes["gate"], d.planes["up"],
+                           d.planes["down"], y, ws, nb)
+        torch.cuda.synchronize()
+        assert_y_close(host(y), y_ref, "expert_mlp repeated picks path %d" % path)
+
+
 @pytest.mark.parametrize("path", [moe.MOE_PATH_GEMV, moe.MOE_PATH_GEMM])
 def test_layer_large_activations(path):
     """Activations over fp16's range (x ~ N(0, 1500^2), one entry in a
